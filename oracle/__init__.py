@@ -1,0 +1,179 @@
+"""CPU oracle for the MoE token dispatch / unpermute-combine path (ctypes shim over moe_oracle.c).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import this package. The HIP product path never does, and the two share
+no code.
+
+All functions take and return numpy arrays. bf16 tensors are ``uint16`` bit patterns.
+Each wrapper documents the passage of the source pages it follows in ``moe_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import build as _build, library_path
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    src = os.path.join(os.path.dirname(path), "moe_oracle.c")
+    if not os.path.exists(path) or os.path.getmtime(src) > os.path.getmtime(path):
+        _build()
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    lib.oracle_capacity.argtypes = [i64, i32, i32, i32, i32]
+    lib.oracle_capacity.restype = i64
+    lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
+    lib.oracle_route_topk.restype = ctypes.c_int
+    lib.oracle_build_index.argtypes = [P, P, i64, i32, i32, i32, i32] + [P] * 11
+    lib.oracle_build_index.restype = ctypes.c_int
+    lib.oracle_permute.argtypes = [P, i64, i64, i32, P, i64, P]
+    lib.oracle_permute.restype = ctypes.c_int
+    lib.oracle_unpermute_combine.argtypes = [P, i32, i64, i64, P, P, i64, i32, P, i32]
+    lib.oracle_unpermute_combine.restype = ctypes.c_int
+    lib.oracle_group_precombine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, i32, P, i64, P]
+    lib.oracle_group_precombine.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def _dt_of(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"hidden tensors must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def capacity(tokens: int, top_k: int, num_experts: int, cf_num: int, cf_den: int) -> int:
+    """Expert capacity ceil(tokens*top_k/num_experts*cf), cf = cf_num/cf_den, exact."""
+    v = _load().oracle_capacity(tokens, top_k, num_experts, cf_num, cf_den)
+    if v < 0:
+        raise ValueError("invalid capacity arguments")
+    return int(v)
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(_load().oracle_f32_to_bf16(float(x)))
+
+
+def route_topk(logits: np.ndarray, K: int):
+    """Top-K experts per token (ties -> lower id) and softmax over the K selected logits."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float32)
+    _check(_load().oracle_route_topk(_ptr(logits), T, E, K, _ptr(idx), _ptr(w)), "route_topk")
+    return idx, w
+
+
+def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_size: int = 0):
+    """Expert-major index (the dispatch "handle"). Returns a dict of numpy arrays."""
+    topk_idx = _c(topk_idx, np.int32)
+    T, K = topk_idx.shape
+    w = None if topk_w is None else _c(topk_w, np.float32)
+    rows = E * capacity if capacity > 0 else T * K
+    out = dict(
+        counts=np.zeros(E, np.int32),
+        group_list=np.zeros(E, np.int32),
+        kept_counts=np.zeros(E, np.int32),
+        sorted_indices=np.full(rows, -7, np.int32),
+        row_of=np.full((T, K), -7, np.int32),
+        permuted_probs=np.full(rows, np.nan, np.float32),
+    )
+    g_arrays = [None] * 5
+    if group_size > 0:
+        G = E // group_size
+        out.update(
+            slot_of=np.full((T, G), -7, np.int32),
+            gsrc=np.full(T * min(K, G), -7, np.int32),
+            esrc=np.full(rows, -7, np.int32),
+            group_counts=np.zeros(G, np.int32),
+            n_slots=np.zeros(1, np.int32),
+        )
+        g_arrays = [out["slot_of"], out["gsrc"], out["esrc"], out["group_counts"], out["n_slots"]]
+    rc = _load().oracle_build_index(
+        _ptr(topk_idx), _ptr(w), T, K, E, capacity, group_size,
+        _ptr(out["counts"]), _ptr(out["group_list"]), _ptr(out["kept_counts"]),
+        _ptr(out["sorted_indices"]), _ptr(out["row_of"]), _ptr(out["permuted_probs"]),
+        *[_ptr(a) for a in g_arrays])
+    _check(rc, "build_index")
+    if group_size > 0:
+        m = int(out["n_slots"][0])
+        out["gsrc"] = out["gsrc"][:m]
+    return out
+
+
+def permute(src: np.ndarray, src_row: np.ndarray) -> np.ndarray:
+    """dst[i] = src[src_row[i]] bitwise; rows outside [0, len(src)) give zeros."""
+    src = np.ascontiguousarray(src)
+    _dt_of(src)
+    src_rows, H = src.shape
+    src_row = _c(src_row, np.int32).reshape(-1)
+    dst = np.empty((src_row.shape[0], H), src.dtype)
+    rc = _load().oracle_permute(_ptr(src), src_rows, H, src.dtype.itemsize, _ptr(src_row),
+                                src_row.shape[0], _ptr(dst))
+    _check(rc, "permute")
+    return dst
+
+
+def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype) -> np.ndarray:
+    """out[t] = sum_k w[t,k] * y[row_of[t,k]] (float32 FMA chain in k order)."""
+    y = np.ascontiguousarray(y)
+    y_dt = _dt_of(y)
+    y_rows, H = y.shape
+    row_of = _c(row_of, np.int32)
+    T, K = row_of.shape
+    w = None if w is None else _c(w, np.float32).reshape(T, K)
+    out = np.empty((T, H), out_dtype)
+    out_dt = _dt_of(out)
+    rc = _load().oracle_unpermute_combine(_ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
+                                          T, K, _ptr(out), out_dt)
+    _check(rc, "unpermute_combine")
+    return out
+
+
+def group_precombine(y: np.ndarray, row_of, w, topk_idx, E: int, group_size: int,
+                     slot_of: np.ndarray, slots_cap: int) -> np.ndarray:
+    """Per-(token, group) weighted partial sums in float32, stored at slot_of[t, g]."""
+    y = np.ascontiguousarray(y)
+    y_dt = _dt_of(y)
+    y_rows, H = y.shape
+    row_of = _c(row_of, np.int32)
+    T, K = row_of.shape
+    topk_idx = _c(topk_idx, np.int32)
+    w = None if w is None else _c(w, np.float32)
+    slot_of = _c(slot_of, np.int32)
+    partials = np.full((slots_cap, H), np.nan, np.float32)
+    rc = _load().oracle_group_precombine(_ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
+                                         _ptr(topk_idx), T, K, E, group_size, _ptr(slot_of),
+                                         slots_cap, _ptr(partials))
+    _check(rc, "group_precombine")
+    return partials
