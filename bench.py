@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE token dispatch / unpermute-combine hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input, inputs already
+resident in HBM: route_topk -> build_index -> permute (x into expert-major rows) ->
+unpermute_combine (expert outputs back to token order, weighted). In group mode the permute is
+the two-stage dedup dispatch and the combine is the per-group pre-combine plus the final sum.
+
+Prints ONE JSON line. `value` is the whole step's algorithmic bytes (each stage's minimal HBM
+traffic, computed from the actual routing) divided by the measured step time. `roofline`
+describes the dominant kernel (permute or combine) with its own HIP-event time; `cpu_baseline`
+is the CPU oracle on the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+METRIC = "permute+combine effective HBM GB/s (% of peak) and routed tokens/s"
+KERNEL_SOURCES = {
+    "permute": ["unpermute_combine_amd/csrc/permute.hip", "unpermute_combine_amd/csrc/moe_common.h"],
+    "combine": ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csrc/moe_common.h"],
+}
+KERNEL_SYMBOLS = {"permute": "permute_vec16_kernel", "combine": "combine_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=3, help="named workload id (see workloads.py)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    return p.parse_args()
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: int):
+    """HBM bytes per launch from a committed PMC summary; None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_SYMBOLS[kernel]}__workload{workload}__pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_digest(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def to_dev(torch, a):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (no CPU path)", file=sys.stderr, flush=True)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    import unpermute_combine_amd as m
+    import workloads as wl
+
+    m.lib()  # fails loudly if the HIP library was not built
+    cid = args.workload
+    c = wl.WORKLOADS[cid]
+    T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
+    gs = c["group_size"]
+    cap = m.expert_capacity(T, K, E, *c["cf"]) if c["cf"] else 0
+    b = 2 if dt == "bf16" else 4
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    key = wl.workload_key(cid)
+
+    t0 = time.time()
+    logits_np = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])
+    x_np = wl.hidden_states(key, T, H, dt)
+    rows = E * cap if cap > 0 else T * K
+    y_np = None if c["identity_experts"] else wl.expert_outputs(key, rows, H, dt)
+    logits = to_dev(torch, logits_np)
+    x = to_dev(torch, x_np)
+    y = None if y_np is None else to_dev(torch, y_np)
+    log(f"[bench] workload {cid} ({c['name']}): inputs ready in {time.time() - t0:.1f}s")
+
+    # preallocated outputs: nothing is allocated inside the timed region
+    gi = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ix = m.alloc_index(T, K, E, cap, gs)
+    xp = torch.empty((rows, H), dtype=tdt, device="cuda")
+    out = torch.empty((T, H), dtype=tdt, device="cuda")
+    G = E // gs if gs else 0
+    gbuf = torch.empty((T * min(K, G), H), dtype=tdt, device="cuda") if gs else None
+    part = torch.empty((T * min(K, G), H), dtype=torch.float32, device="cuda") if gs else None
+
+    stages = ["route", "index", "permute", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        m.route_topk(logits, K, out=(gi, gw))
+        mark(1)
+        m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix)
+        mark(2)
+        if gs:
+            n = int(ix.n_slots.item())  # the group count is only known on the device
+            m.permute(x, ix.gsrc[:n], out=gbuf[:n])
+            m.permute(gbuf[:n], ix.esrc, out=xp)
+        else:
+            m.permute(x, ix.sorted_indices, out=xp)
+        mark(3)
+        src = xp if y is None else y
+        if gs:
+            m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part[:n])
+            m.unpermute_combine(part[:n], ix.slot_of, None, out=out)
+        else:
+            m.unpermute_combine(src, ix.row_of, gw, out=out)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    stage_us = {}
+    for i, name in enumerate(stages):
+        d = [evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.steps)]
+        stage_us[name] = float(np.mean(d))
+
+    # ---- algorithmic bytes from the actual routing
+    row_of = ix.row_of.cpu().numpy()
+    counts = ix.counts.cpu().numpy()
+    valid = int((row_of >= 0).sum())  # rows the combine reads
+    routed = int((row_of >= 0).any(axis=1).sum()) if K else 0  # distinct source rows the permute reads
+    bytes_route = T * E * 4 + T * K * 8
+    bytes_index = T * K * 8 + rows * 8 + T * K * 4 + E * 4 * 3
+    if gs:
+        n = int(ix.n_slots.item())
+        bytes_permute = (routed * H * b + n * 4 + n * H * b) + (n * H * b + rows * 4 + rows * H * b)
+        bytes_combine = (valid * H * b + 2 * T * K * 4 + n * H * 4) + (n * H * 4 + T * G * 4 + T * H * b)
+    else:
+        bytes_permute = routed * H * b + rows * 4 + rows * H * b
+        bytes_combine = valid * H * b + 2 * T * K * 4 + T * H * b
+    step_bytes = bytes_route + bytes_index + bytes_permute + bytes_combine
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    routed_per_s = T * K / (ms_per_step * 1e-3)
+
+    per_kernel = {"permute": (bytes_permute, stage_us["permute"]), "combine": (bytes_combine, stage_us["combine"])}
+    dom = max(per_kernel, key=lambda k: per_kernel[k][1])
+    dbytes, dus = per_kernel[dom]
+    achieved = dbytes / (dus * 1e-6) / 1e9
+    traffic = read_traffic(dom, cid) if not gs else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": KERNEL_SYMBOLS[dom], "algorithmic_bytes_per_launch": dbytes,
+                "avg_launch_us": round(dus, 2)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": c["name"], "T": T, "H": H, "E": E, "K": K, "capacity": cap,
+                   "group_size": gs, "zipf_s": c["zipf_s"], "seed_key": list(key)},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "routed_tokens_per_s": round(routed_per_s, 1),
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stage_gbs": {"permute": round(bytes_permute / (stage_us["permute"] * 1e-6) / 1e9, 1),
+                      "combine": round(bytes_combine / (stage_us["combine"] * 1e-6) / 1e9, 1)},
+        "max_expert_count": int(counts.max()), "empty_experts": int((counts == 0).sum()),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes):
+    """The CPU oracle as it stands (single thread) over the same whole workload, 2 passes."""
+    import numpy as np
+
+    import oracle
+
+    T, E, K, gs = c["T"], c["E"], c["K"], c["group_size"]
+    out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
+    best = None
+    for _ in range(2):
+        t0 = time.perf_counter()
+        idx, w = oracle.route_topk(logits_np, K)
+        ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs)
+        if gs:
+            gbuf = oracle.permute(x_np, ix["gsrc"])
+            xp = oracle.permute(gbuf, ix["esrc"])
+        else:
+            xp = oracle.permute(x_np, ix["sorted_indices"])
+        y = xp if y_np is None else y_np
+        if gs:
+            n = int(ix["n_slots"][0])
+            part = oracle.group_precombine(y, ix["row_of"], w, idx, E, gs, ix["slot_of"], n)
+            oracle.unpermute_combine(part, ix["slot_of"], None, out_dt)
+        else:
+            oracle.unpermute_combine(y, ix["row_of"], w, out_dt)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+        del xp
+    return {"value": round(step_bytes / best / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload ({c['name']}), one pass, best of 2, single thread",
+            "seconds_per_pass": round(best, 3),
+            "routed_tokens_per_s": round(T * K / best, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * moe_dispatch.h -- C ABI of the MI355X (gfx950) MoE token dispatch / unpermute-combine library
+ * (libmoe_dispatch.so).
+ *
+ * The operations follow these web pages (cited by title and section):
+ *   [Combine]   "03 · Combine 与 forward / backward 对称性" (llm-infra-atlas, EP chapter)
+ *   [Scratch]   "从零理解 MoE 算子：路由、专家并行与 Token 重排" (171host)
+ *   [CANN]      CANN Dispatch&Combine optimisation notes (cann.csdn.net), "Dispatch&Combine优化"
+ *   [Megatron]  "token dispatcher + fuse_a2a" (obnotes, Megatron/transformer-moe)
+ *
+ * Conventions for every call:
+ *   - Pointers to tensors are DEVICE memory owned by the caller (the library never allocates
+ *     and never frees). Tensors are row-major and contiguous. Indices and counts are int32,
+ *     router weights and probabilities float32, hidden rows float32 or bf16 (moe_dtype).
+ *   - Calls are asynchronous: they enqueue kernels on `stream` (a hipStream_t; NULL is the
+ *     null stream) and return. Results are visible to later work on the same stream.
+ *   - Argument errors are reported synchronously, before anything is launched:
+ *     MOE_ERR_INVALID (null pointer where data is needed, negative size, K < 1, K > E,
+ *     H < 1, group size not dividing E, ...) or MOE_ERR_UNSUPPORTED (E > 1024, K > 32, or a
+ *     combination the call does not implement). MOE_ERR_HIP means a launch failed.
+ *   - A size of zero tokens / rows is valid and launches nothing (an empty rank or an expert
+ *     with no tokens must work, [Scratch] §26.1-26.2).
+ *   - Memory safety does not depend on the data: an expert id outside [0, E) routes nowhere
+ *     (the pages write -1 for "no expert"), a row index outside the source range selects a
+ *     zero row (permute) or no term (combine). Expert ids in one row of topk_idx must be
+ *     distinct for the pages' routing map to be defined; if they repeat, slots of the same
+ *     expert are ordered by slot.
+ *   - The library holds no global state; calls on different streams may run concurrently as
+ *     long as they do not write the same memory.
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_HIP = 3
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Upper limits of the kernels. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char *moe_status_string(moe_status s);
+
+/* Expert capacity, [Scratch] §18: ceil(tokens * top_k / num_experts * capacity_factor) with the
+ * capacity factor given as the exact fraction cf_num / cf_den (1.25 = 5/4), computed in
+ * integers on the host. 1024 tokens, top_k 2, 8 experts, 5/4 -> 320.
+ * Returns -1 for tokens < 0, top_k < 1, num_experts < 1, cf_num < 0, cf_den < 1 or a result
+ * that does not fit in int32. */
+int64_t moe_expert_capacity(int64_t tokens, int32_t top_k, int32_t num_experts,
+                            int32_t cf_num, int32_t cf_den);
+
+/* Top-k routing, [Scratch] §3 and §27: for each token t the K experts with the largest logits,
+ * then a softmax over those K logits only.
+ *   logits   [T, E] float32, finite.
+ *   topk_idx [T, K] int32 out: slot k is the k-th expert in the order (logit descending,
+ *            expert id ascending); equal logits (+0 and -0 are equal) go to the lower id.
+ *   topk_w   [T, K] float32 out: w_k = exp(s_k - s_0) / sum_j exp(s_j - s_0), evaluated in
+ *            double (the router softmax is precision sensitive, [Scratch] §26.7) and rounded
+ *            once to float32; the sum runs in slot order.
+ * Requires 1 <= K <= E, E <= MOE_MAX_EXPERTS, K <= MOE_MAX_TOPK. */
+moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
+                          int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/* The dispatch "handle" ([Combine] §3: computed once by dispatch, reused by combine).
+ * All members are caller-owned device arrays, written by moe_build_index.
+ * R = T*K in the standard and group modes, R = E*capacity in drop-and-pad mode. */
+typedef struct moe_index {
+    int32_t *counts;         /* [E] rows routed to each expert, before capacity ([Megatron] §1.2
+                                num_tokens_per_expert). Required. */
+    int32_t *group_list;     /* [E] inclusive running sum of counts ([Scratch] §7:
+                                [3,2,4] -> [3,5,9]; expert e owns rows
+                                [group_list[e]-counts[e], group_list[e])). Required. */
+    int32_t *kept_counts;    /* [E] min(counts, capacity) in drop-and-pad mode, counts
+                                otherwise. May be NULL. */
+    int32_t *sorted_indices; /* [R] source token of each expert-major row ([Megatron] §1.1,
+                                masked_select over the transposed routing map): experts in
+                                ascending order, tokens ascending inside an expert. Padding and
+                                unused rows hold -1. Required. */
+    int32_t *row_of;         /* [T, K] expert-major row of slot (t,k), -1 if the slot routes
+                                nowhere or was dropped (the saved mapping that makes the permute
+                                invertible, [Scratch] §26.5). Required. */
+    float *permuted_probs;   /* [R] topk_w of the slot in each row ([Megatron] §1.1 step 4),
+                                0 on padding/unused rows, 1 if topk_w is NULL. May be NULL. */
+    /* group mode only (group_size > 0), else ignored; all required in group mode: */
+    int32_t *slot_of;        /* [T, G] slot of (token t, group g) in the send-once list, -1 if
+                                token t uses no expert of group g ([CANN] §1(1)). */
+    int32_t *gsrc;           /* [T*min(K,G)] source token of each group slot, groups ascending
+                                then tokens ascending; only the first n_slots entries are
+                                written. */
+    int32_t *esrc;           /* [R] group slot feeding each expert-major row; -1 on unused
+                                rows. */
+    int32_t *group_counts;   /* [G] slots per group. */
+    int32_t *n_slots;        /* [1] number of group slots M_g (the caller reads it back if it
+                                needs the exact size; gsrc may be sized by the upper bound). */
+} moe_index;
+
+/* Bytes of device workspace that moe_build_index needs for these sizes (the caller allocates
+ * it, any alignment of at least 256 bytes). */
+moe_status moe_build_index_workspace_size(int64_t T, int32_t K, int32_t E, int32_t group_size,
+                                          size_t *bytes);
+
+/* Builds the expert-major index from the routing result ([Megatron] §1.1; [Scratch] §6, §7,
+ * §11-13, §16).
+ *   topk_idx [T, K] int32 expert ids (-1 or any id outside [0, E) = no expert).
+ *   topk_w   [T, K] float32 or NULL (then permuted_probs holds 1 on routed rows).
+ *   capacity > 0 selects drop-and-pad ([Scratch] §18, §26.6): expert e owns rows
+ *            [e*capacity, (e+1)*capacity); the p-th token of expert e (tokens in ascending
+ *            order) is kept at row e*capacity + p iff p < capacity, later ones are dropped
+ *            (row_of = -1) and the rest of the expert's rows are padding.
+ *   group_size > 0 selects group mode ([CANN] §1(1)): experts e form G = E / group_size
+ *            contiguous groups g = e / group_size, and slot_of/gsrc/esrc/group_counts/n_slots
+ *            are written. capacity > 0 together with group_size > 0 is MOE_ERR_UNSUPPORTED.
+ * The build is deterministic: no position depends on the timing of atomics. */
+moe_status moe_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K,
+                           int32_t E, int32_t capacity, int32_t group_size,
+                           const moe_index *out, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Row gather ([Megatron] §1.1 step 5, permuted_input = tokens.index_select(0, sorted_indices);
+ * [Scratch] §12, permuted_tokens = tokens[permute_indices]):
+ *   dst[i, :] = src[src_row[i], :] copied bit for bit, for i in [0, N); a src_row outside
+ *   [0, src_rows) (the -1 of padding rows) writes a row of zeros.
+ *   src [src_rows, H] of dtype dt, src_row [N] int32, dst [N, H] of dtype dt.
+ * Used for the standard dispatch (src_row = sorted_indices, N = R), drop-and-pad (which also
+ * zero-fills the padding rows) and the two stages of the group dispatch (src_row = gsrc, then
+ * esrc). */
+moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
+                       const int32_t *src_row, int64_t N, void *dst, hipStream_t stream);
+
+/* Unpermute + weighted top-k merge ([Combine] §1: out[t] = sum over the token's top-k experts
+ * of probs[t,e] * expert_e(x[t]); [Scratch] §13, §16):
+ *   out[t, :] = sum_{k = 0..K-1, row_of[t,k] in [0, y_rows)} w[t,k] * y[row_of[t,k], :]
+ * with a float32 accumulator starting at +0 and one fused multiply-add per term in slot order
+ * k = 0, 1, ..., K-1 (deterministic: no atomics, no reordering), then stored as float32 or
+ * rounded to bf16 (nearest, ties to even).
+ *   y      [y_rows, H] expert outputs in expert-major order (dtype y_dt).
+ *   row_of [T, K] int32 (moe_index.row_of).
+ *   w      [T, K] float32, or NULL for unit weights (the pure-add combine, [Combine] §3).
+ *   out    [T, H] dtype out_dt.
+ * K may be up to 1024 here: the group-mode final sum calls it with y = partials,
+ * row_of = slot_of, w = NULL and K = G. */
+moe_status moe_unpermute_combine(const void *y, moe_dtype y_dt, int64_t y_rows, int64_t H,
+                                 const int32_t *row_of, const float *w, int64_t T, int32_t K,
+                                 void *out, moe_dtype out_dt, hipStream_t stream);
+
+/* Local pre-combine per group ([CANN] §1(2): the outputs of a token's experts on the same rank
+ * are merged with their weights before leaving the rank; here a group of group_size experts
+ * stands for a rank). For every (t, g) with s = slot_of[t*G + g] in [0, slots_cap):
+ *   partials[s, :] = sum_{k: topk_idx[t,k] in group g, row_of[t,k] in [0, y_rows)}
+ *                    w[t,k] * y[row_of[t,k], :]
+ * float32, fused multiply-add in slot order, an empty sum being +0. With slot_of from
+ * moe_build_index the partials are stored compactly ([n_slots, H], one row per (token,
+ * group) that exists); a slot_of numbering every (t, g) gives the dense [T, G, H] layout.
+ * Rows of partials not named by slot_of are left untouched.
+ *   y [y_rows, H] (y_dt), row_of/topk_idx/w [T, K], slot_of [T, G], partials [slots_cap, H]
+ *   float32. w may be NULL (unit weights). */
+moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, int64_t H,
+                                const int32_t *row_of, const float *w, const int32_t *topk_idx,
+                                int64_t T, int32_t K, int32_t E, int32_t group_size,
+                                const int32_t *slot_of, int64_t slots_cap, float *partials,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DISPATCH_H */

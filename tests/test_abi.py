@@ -1,0 +1,88 @@
+"""The C-ABI library loads on a machine without a GPU and exports every symbol the header
+declares; host-only entry points and argument validation (which returns before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, load_golden
+
+HEADER = os.path.join(ROOT, "include", "moe_dispatch.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def capi():
+    from unpermute_combine_amd import _capi
+    return _capi
+
+
+def test_header_declares_the_five_operations():
+    names = declared_functions()
+    for op in ("moe_route_topk", "moe_build_index", "moe_permute", "moe_unpermute_combine",
+               "moe_group_precombine"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(capi):
+    lib = capi.lib()
+    names = declared_functions()
+    assert set(names) == set(capi.SIGNATURES)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(capi):
+    assert capi.status_string(0) == "ok"
+    assert "invalid" in capi.status_string(1)
+    assert capi.status_string(99) == "unknown status"
+
+
+def test_library_capacity_matches_the_pages_example(capi):
+    g = load_golden("capacity_example.json")
+    lib = capi.lib()
+    assert lib.moe_expert_capacity(g["tokens_per_rank"], g["top_k"], g["num_experts"], 5, 4) == g["capacity"]
+    assert lib.moe_expert_capacity(8192, 8, 128, 5, 4) == 640
+    assert lib.moe_expert_capacity(-1, 8, 128, 5, 4) == -1
+    assert lib.moe_expert_capacity(8, 0, 128, 5, 4) == -1
+
+
+def test_workspace_size_and_limits(capi):
+    lib = capi.lib()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_build_index_workspace_size(16384, 8, 256, 0, ctypes.byref(n)) == capi.MOE_OK
+    assert n.value >= 256 * 4
+    assert lib.moe_build_index_workspace_size(16, 8, 4, 0, ctypes.byref(n)) == capi.MOE_ERR_INVALID  # K > E
+    assert lib.moe_build_index_workspace_size(16, 2, 2048, 0, ctypes.byref(n)) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_build_index_workspace_size(16, 2, 12, 5, ctypes.byref(n)) == capi.MOE_ERR_INVALID
+    assert lib.moe_build_index_workspace_size(0, 2, 8, 0, ctypes.byref(n)) == capi.MOE_OK
+
+
+def test_argument_errors_return_before_any_launch(capi):
+    lib = capi.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert lib.moe_route_topk(fake, 4, 8, 9, fake, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_route_topk(fake, 4, 2048, 2, fake, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(fake, 4, 64, 33, fake, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(None, 4, 8, 2, fake, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == capi.MOE_OK  # empty: no-op
+    assert lib.moe_permute(fake, 4, 0, 1, fake, 4, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute(fake, 4, 8, 7, fake, 4, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute(None, 0, 8, 1, None, 0, None, None) == capi.MOE_OK
+    assert lib.moe_unpermute_combine(fake, 1, 4, 8, fake, None, 2, 0, fake, 1, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_unpermute_combine(fake, 1, 4, 8, fake, None, 2, 2000, fake, 1, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(fake, 1, 4, 8, None, None, 2, 2, fake, 1, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 3, fake, 4, fake, None) == \
+        capi.MOE_ERR_INVALID
+    ix = capi.MoeIndexStruct()
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 4, 2, ctypes.byref(ix), fake, 1 << 20, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # drop-and-pad with groups
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, ctypes.byref(ix), fake, 1 << 20, None) == \
+        capi.MOE_ERR_INVALID  # null outputs
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, None, fake, 1 << 20, None) == capi.MOE_ERR_INVALID

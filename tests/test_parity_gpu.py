@@ -1,0 +1,339 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Small cases span several tiles and ragged tails; edge cases cover empty inputs, experts and
+groups with no tokens, slots that route nowhere, out-of-range ids and rows, capacities below
+and above the largest count; the five named workloads run at full size through the same
+entry points and launch configuration that bench.py times, with index arrays compared in full
+and permuted / combined rows compared on a sample the oracle computes row by row.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from oracle.compare import assert_combined, assert_exact, assert_rel_f32, exact_fraction
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import unpermute_combine_amd as mod
+    mod.lib()  # the HIP library must be there: no fallback
+    return mod
+
+
+DEV = "cuda:0"
+
+
+def dev(a: np.ndarray):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def say(*args):
+    print(*args, flush=True)
+
+
+# ------------------------------------------------------------------ routing
+
+
+def tie_logits(key, T, E):
+    g = np.random.default_rng([*key, 99])
+    v = (g.integers(-6, 7, size=(T, E)) * 0.25).astype(np.float32)
+    v[g.random((T, E)) < 0.1] = -0.0
+    return v
+
+
+@pytest.mark.parametrize("T,E,K,kind", [
+    (1, 1, 1, "normal"), (37, 8, 2, "normal"), (1030, 64, 2, "normal"), (999, 256, 8, "zipf"),
+    (130, 33, 5, "ties"), (77, 1000, 32, "normal"), (500, 1024, 8, "ties"), (64, 64, 32, "ties"),
+    (301, 65, 1, "normal"), (200, 128, 8, "ties")])
+def test_route_topk(m, T, E, K, kind):
+    say(f"route_topk T={T} E={E} K={K} {kind}")
+    key = wl.case_key(20, T, E, K)
+    if kind == "ties":
+        logits = tie_logits(key, T, E)
+    else:
+        logits = wl.router_logits(key, T, E, zipf_s=1.2 if kind == "zipf" else None)
+    want_i, want_w = oracle.route_topk(logits, K)
+    gi, gw = m.route_topk(dev(logits), K)
+    torch.cuda.synchronize()
+    assert_exact(host(gi), want_i, "topk_idx")
+    assert_rel_f32(host(gw), want_w, "topk_w")
+
+
+def test_route_topk_empty(m):
+    gi, gw = m.route_topk(torch.empty((0, 8), dtype=torch.float32, device=DEV), 2)
+    torch.cuda.synchronize()
+    assert gi.shape == (0, 2) and gw.shape == (0, 2)
+
+
+# ------------------------------------------------------------------ index build
+
+
+def ids_case(key, T, E, K, p_missing=0.1, junk=False):
+    ids = wl.random_topk_ids(key, T, E, K, p_missing=p_missing)
+    if junk and T > 3:
+        ids[1, 0] = E + 5  # out of range: routes nowhere on both sides
+        ids[2, -1] = -7
+    return ids
+
+
+def check_index(m, ids, w, E, cap=0, gs=0):
+    want = oracle.build_index(ids, w, E, capacity=cap, group_size=gs)
+    ix = m.build_index(dev(ids), None if w is None else dev(w), E, capacity=cap, group_size=gs)
+    torch.cuda.synchronize()
+    for name in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs"):
+        assert_exact(host(getattr(ix, name)), want[name], name)
+    if gs > 0:
+        n = int(host(ix.n_slots)[0])
+        assert n == int(want["n_slots"][0])
+        assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
+        for name in ("slot_of", "esrc", "group_counts"):
+            assert_exact(host(getattr(ix, name)), want[name], name)
+    return ix, want
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 1, 1), (5, 3, 2), (300, 8, 2), (4099, 64, 8), (2000, 256, 8),
+                                   (1500, 1024, 32), (700, 40, 7), (9000, 128, 4)])
+@pytest.mark.parametrize("weighted", [True, False])
+def test_build_index_standard(m, T, E, K, weighted):
+    say(f"build_index standard T={T} E={E} K={K} weighted={weighted}")
+    key = wl.case_key(21, T, E, K)
+    ids = ids_case(key, T, E, K, junk=True)
+    w = wl.random_weights(key, T, K) if weighted else None
+    check_index(m, ids, w, E)
+
+
+def test_build_index_skewed_with_empty_experts(m):
+    T, E, K = 3000, 256, 8
+    logits = wl.router_logits(wl.case_key(22), T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    ix, want = check_index(m, idx, w, E)
+    assert (want["counts"] == 0).any()
+
+
+@pytest.mark.parametrize("T,E,K,cap", [(300, 8, 2, 3), (4099, 64, 8, 40), (2000, 128, 8, 200),
+                                       (1000, 16, 4, 1000), (50, 1024, 8, 1), (1, 4, 2, 5)])
+def test_build_index_drop_and_pad(m, T, E, K, cap):
+    say(f"build_index drop T={T} E={E} K={K} cap={cap}")
+    key = wl.case_key(23, T, E, K)
+    logits = wl.router_logits(key, T, E, zipf_s=1.0)
+    idx, w = oracle.route_topk(logits, K)
+    idx[0, -1] = -1
+    check_index(m, idx, w, E, cap=cap)
+
+
+@pytest.mark.parametrize("T,E,K,gs", [(300, 8, 2, 2), (4099, 64, 8, 8), (2000, 256, 8, 8), (500, 32, 8, 32),
+                                      (700, 96, 6, 1), (1000, 1024, 8, 32), (3, 4, 2, 2)])
+def test_build_index_groups(m, T, E, K, gs):
+    say(f"build_index group T={T} E={E} K={K} gs={gs}")
+    key = wl.case_key(24, T, E, K)
+    logits = wl.router_logits(key, T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    idx[min(1, T - 1), 0] = -1
+    check_index(m, idx, w, E, gs=gs)
+
+
+@pytest.mark.parametrize("cap,gs", [(0, 0), (4, 0), (0, 2)])
+def test_build_index_no_tokens(m, cap, gs):
+    ids = np.zeros((0, 2), np.int32)
+    check_index(m, ids, None, 8, cap=cap, gs=gs)
+
+
+# ------------------------------------------------------------------ permute
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H", [1, 3, 8, 64, 1000, 7168, 4095])
+def test_permute(m, dtype, H):
+    say(f"permute {dtype} H={H}")
+    key = wl.case_key(25, H)
+    src_rows = 301
+    x = wl.hidden_states(key, src_rows, H, dtype)
+    g = np.random.default_rng([*key, 1])
+    src_row = g.integers(-3, src_rows + 3, size=1234).astype(np.int32)  # includes -1.. and >= rows
+    src_row[:4] = [0, src_rows - 1, -1, src_rows]
+    want = oracle.permute(x, src_row)
+    got = host(m.permute(dev(x), dev(src_row)))
+    assert_exact(got, want, "permuted rows")
+
+
+def test_permute_empty_source_gives_zero_rows(m):
+    x = np.zeros((0, 16), np.uint16)
+    src_row = np.asarray([-1, 0, 3], np.int32)
+    got = host(m.permute(dev(x), dev(src_row)))
+    assert (got == 0).all() and got.shape == (3, 16)
+
+
+# ------------------------------------------------------------------ combine
+
+
+@pytest.mark.parametrize("ydt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
+@pytest.mark.parametrize("H,K,T", [(1, 1, 10), (5, 2, 33), (512, 2, 1024), (7168, 8, 130), (1000, 8, 77),
+                                   (64, 32, 200), (24, 256, 40)])
+@pytest.mark.parametrize("weighted", [True, False])
+def test_unpermute_combine(m, ydt, odt, H, K, T, weighted):
+    say(f"combine y={ydt} out={odt} H={H} K={K} T={T} weighted={weighted}")
+    key = wl.case_key(26, H, K, T)
+    y_rows = T * K + 5
+    y = wl.expert_outputs(key, y_rows, H, ydt)
+    g = np.random.default_rng([*key, 2])
+    row_of = g.permutation(y_rows)[: T * K].astype(np.int32).reshape(T, K)
+    row_of[g.random((T, K)) < 0.15] = -1
+    row_of[0, 0] = y_rows + 2  # out of range: no term
+    w = wl.random_weights(key, T, K) if weighted else None
+    out_np = np.uint16 if odt == "bf16" else np.float32
+    want = oracle.unpermute_combine(y, row_of, w, out_np)
+    got = host(m.unpermute_combine(dev(y), dev(row_of), None if w is None else dev(w),
+                                   out_dtype=torch.bfloat16 if odt == "bf16" else torch.float32))
+    assert_combined(got, want, "combined")
+    assert exact_fraction(got, want) == 1.0
+
+
+def test_combine_no_tokens(m):
+    out = m.unpermute_combine(torch.zeros((4, 8), dtype=torch.bfloat16, device=DEV),
+                              torch.zeros((0, 2), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8)
+
+
+# ------------------------------------------------------------------ group pre-combine
+
+
+@pytest.mark.parametrize("T,E,K,gs,H,ydt", [(300, 8, 2, 2, 64, "bf16"), (513, 64, 8, 8, 1000, "bf16"),
+                                            (200, 256, 8, 8, 7168, "bf16"), (100, 32, 4, 4, 5, "f32"),
+                                            (150, 16, 8, 16, 24, "bf16")])
+@pytest.mark.parametrize("layout", ["compact", "dense"])
+def test_group_precombine_and_final_sum(m, T, E, K, gs, H, ydt, layout):
+    say(f"precombine T={T} E={E} K={K} gs={gs} H={H} {ydt} {layout}")
+    key = wl.case_key(27, T, E, K, gs, H)
+    logits = wl.router_logits(key, T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    want_ix = oracle.build_index(idx, w, E, group_size=gs)
+    G = E // gs
+    if layout == "compact":
+        slot_of = want_ix["slot_of"]
+        cap = int(want_ix["n_slots"][0])
+    else:
+        slot_of = np.arange(T * G, dtype=np.int32).reshape(T, G)
+        cap = T * G
+    y = wl.expert_outputs(key, T * K, H, ydt)
+    want_p = oracle.group_precombine(y, want_ix["row_of"], w, idx, E, gs, slot_of, cap)
+    got_p = host(m.group_precombine(dev(y), dev(want_ix["row_of"]), dev(w), dev(idx), E, gs, dev(slot_of),
+                                    slots_cap=cap))
+    assert_combined(got_p, want_p, "partials")
+    assert exact_fraction(got_p, want_p) == 1.0
+    want_o = oracle.unpermute_combine(want_p, slot_of, None, np.uint16)
+    got_o = host(m.unpermute_combine(dev(want_p), dev(slot_of), None, out_dtype=torch.bfloat16))
+    assert_combined(got_o, want_o, "final sum")
+
+
+# ------------------------------------------------------------------ the five workloads at full size
+
+
+def sample_rows(n, count, seed):
+    g = np.random.default_rng(seed)
+    s = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, size=min(count, n))]))
+    return s.astype(np.int64)
+
+
+def run_workload(m, cfg_id):
+    """Runs route -> index -> permute -> (pre-)combine on the GPU and checks every stage."""
+    c = wl.WORKLOADS[cfg_id]
+    T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
+    key = wl.workload_key(cfg_id)
+    say(f"workload {cfg_id}: {c['name']}")
+    logits = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])
+    x = wl.hidden_states(key, T, H, dt)
+    cap = oracle.capacity(T, K, E, *c["cf"]) if c["cf"] else 0
+    assert cap == (m.expert_capacity(T, K, E, *c["cf"]) if c["cf"] else 0)
+    gs = c["group_size"]
+
+    want_i, want_w = oracle.route_topk(logits, K)
+    gi, gw = m.route_topk(dev(logits), K)
+    assert_exact(host(gi), want_i, "topk_idx")
+    assert_rel_f32(host(gw), want_w, "topk_w")
+    # the same weight bits on both sides from here on
+    w_np = host(gw)
+    ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs)
+    want = oracle.build_index(want_i, w_np, E, capacity=cap, group_size=gs)
+    for name in ("counts", "group_list", "sorted_indices", "row_of", "permuted_probs"):
+        assert_exact(host(getattr(ix, name)), want[name], name)
+    rows = ix.rows
+    xd = dev(x)
+    if gs > 0:
+        n = int(host(ix.n_slots)[0])
+        assert n == int(want["n_slots"][0])
+        assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
+        assert_exact(host(ix.esrc), want["esrc"], "esrc")
+        assert_exact(host(ix.slot_of), want["slot_of"], "slot_of")
+        gbuf = m.permute(xd, ix.gsrc[:n])
+        xp = m.permute(gbuf, ix.esrc)
+    else:
+        xp = m.permute(xd, ix.sorted_indices)
+    torch.cuda.synchronize()
+    rs = sample_rows(rows, 3000, cfg_id)
+    assert_exact(host(xp[torch.from_numpy(rs).to(DEV)]), oracle.permute(x, want["sorted_indices"][rs]),
+                 "permuted rows (sample)")
+    del xd
+
+    if c["identity_experts"]:
+        y_np = oracle.permute(x, want["sorted_indices"])
+        yd = xp
+    else:
+        y_np = wl.expert_outputs(key, rows, H, dt)
+        yd = dev(y_np)
+    out_np = np.uint16 if dt == "bf16" else np.float32
+    ts = sample_rows(T, 1500, 100 + cfg_id)
+    tsd = torch.from_numpy(ts).to(DEV)
+    if gs > 0:
+        n = int(host(ix.n_slots)[0])
+        part = m.group_precombine(yd, ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=n)
+        out = m.unpermute_combine(part, ix.slot_of, None, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        slot_rows = want["slot_of"][ts]
+        want_p = oracle.group_precombine(y_np, want["row_of"][ts], w_np[ts], want_i[ts], E, gs,
+                                         np.where(slot_rows >= 0, np.arange(slot_rows.size).reshape(slot_rows.shape),
+                                                  -1).astype(np.int32), slot_rows.size)
+        got_p = host(part[torch.from_numpy(np.maximum(slot_rows.reshape(-1), 0)).to(DEV)])
+        present = slot_rows.reshape(-1) >= 0
+        assert_combined(got_p[present], want_p[present], "partials (sample)")
+        local_slot = np.where(slot_rows >= 0, np.arange(slot_rows.size).reshape(slot_rows.shape), -1)
+        want_o = oracle.unpermute_combine(want_p, local_slot.astype(np.int32), None, np.uint16)
+    else:
+        out = m.unpermute_combine(yd, ix.row_of, gw, out_dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+        torch.cuda.synchronize()
+        want_o = oracle.unpermute_combine(y_np, want["row_of"][ts], w_np[ts], out_np)
+    got_o = host(out[tsd])
+    assert_combined(got_o, want_o, "combined (sample)")
+    say(f"workload {cfg_id}: combined exact share {exact_fraction(got_o, want_o):.6f}")
+    if c["identity_experts"]:
+        rel = np.abs(host(out).astype(np.float64) - x) / np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+        assert rel.max() <= 1e-6
+    return out
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_workload_full_size(m, cfg_id):
+    run_workload(m, cfg_id)
+    torch.cuda.empty_cache()
+
+
+def test_pipeline_is_deterministic(m):
+    """No atomics decide positions or sums: two runs give identical bits."""
+    a = host(run_workload(m, 2))
+    b = host(run_workload(m, 2))
+    assert np.array_equal(a, b)

@@ -1,0 +1,13 @@
+"""MI355X (gfx950) MoE token dispatch / unpermute-combine.
+
+Top-k routing with a softmax over the selected logits, the expert histogram with its running
+sum (group_list), the stable expert-major permute, the weighted unpermute-combine and the
+per-group local pre-combine, as hand-written HIP kernels behind a C ABI
+(``include/moe_dispatch.h``, ``libmoe_dispatch.so``). This package is the torch binding.
+"""
+from .ops import (MoeIndex, alloc_index, build_index, expert_capacity, group_precombine, permute,
+                  route_topk, unpermute_combine, workspace_bytes)
+from ._capi import MoeError, lib
+
+__all__ = ["MoeIndex", "MoeError", "alloc_index", "build_index", "expert_capacity", "group_precombine",
+           "lib", "permute", "route_topk", "unpermute_combine", "workspace_bytes"]

@@ -1,0 +1,102 @@
+// Row gather: dst[i] = src[src_row[i]] bit for bit, a zero row when src_row[i] is out of range.
+// [Megatron] §1.1 step 5 (permuted_input = tokens.index_select(0, sorted_indices));
+// [Scratch] §12 (permuted_tokens = tokens[permute_indices]); padded expert buffers are zero
+// ([Scratch] §18 drop-and-pad).
+//
+// Pure HBM traffic: one wavefront copies one row with 16-byte accesses (1 KiB per wave
+// instruction), UNROLL loads in flight per lane before the matching stores. Rows whose size is
+// not a multiple of 16 bytes (or unaligned bases) take an element-wise path.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // 4 wavefronts, one row each
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_vec16_kernel(
+    const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
+    int64_t N, char *__restrict__ dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x / kWave);
+    if (i >= N)
+        return;
+    const int32_t s = src_row[i];
+    const int64_t row_bytes = nvec * 16;
+    char *d = dst + i * row_bytes;
+    if (s < 0 || s >= src_rows) {
+        const u32x4 z{0u, 0u, 0u, 0u};
+        for (int64_t v = lane; v < nvec; v += kWave)
+            st16(d + v * 16, z);
+        return;
+    }
+    const char *p = src + static_cast<int64_t>(s) * row_bytes;
+    int64_t v = lane;
+    for (; v + (kUnroll - 1) * kWave < nvec; v += kUnroll * kWave) {
+        u32x4 r[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            r[u] = ld16(p + (v + u * kWave) * 16);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            st16(d + (v + u * kWave) * 16, r[u]);
+    }
+    for (; v < nvec; v += kWave)
+        st16(d + v * 16, ld16(p + v * 16));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
+    const T *__restrict__ src, int64_t src_rows, int64_t H, const int32_t *__restrict__ src_row,
+    int64_t N, T *__restrict__ dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x / kWave);
+    if (i >= N)
+        return;
+    const int32_t s = src_row[i];
+    T *d = dst + i * H;
+    if (s < 0 || s >= src_rows) {
+        for (int64_t h = lane; h < H; h += kWave)
+            d[h] = T(0);
+        return;
+    }
+    const T *p = src + static_cast<int64_t>(s) * H;
+    for (int64_t h = lane; h < H; h += kWave)
+        d[h] = p[h];
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
+                                  const int32_t *src_row, int64_t N, void *dst, hipStream_t stream)
+{
+    using namespace moe;
+    if (src_rows < 0 || H < 1 || N < 0 || (dt != MOE_F32 && dt != MOE_BF16))
+        return MOE_ERR_INVALID;
+    if (N == 0)
+        return MOE_OK;
+    if (!src_row || !dst || (src_rows > 0 && !src))
+        return MOE_ERR_INVALID;
+    const int64_t blocks = ceil_div(N, kRowsPerBlock);
+    if (blocks > 0x7fffffff)
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t esz = dt == MOE_F32 ? 4 : 2;
+    const int64_t row_bytes = H * esz;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kRowsPerBlock * kWave);
+    if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
+        hipLaunchKernelGGL(permute_vec16_kernel, grid, block, 0, stream, static_cast<const char *>(src),
+                           src_rows, row_bytes / 16, src_row, N, static_cast<char *>(dst));
+    } else if (esz == 4) {
+        hipLaunchKernelGGL(permute_elem_kernel<uint32_t>, grid, block, 0, stream,
+                           static_cast<const uint32_t *>(src), src_rows, H, src_row, N,
+                           static_cast<uint32_t *>(dst));
+    } else {
+        hipLaunchKernelGGL(permute_elem_kernel<uint16_t>, grid, block, 0, stream,
+                           static_cast<const uint16_t *>(src), src_rows, H, src_row, N,
+                           static_cast<uint16_t *>(dst));
+    }
+    return launch_status();
+}

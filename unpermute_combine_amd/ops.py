@@ -1,0 +1,220 @@
+"""Torch-facing binding of the MoE dispatch / combine C ABI.
+
+Argument marshalling only: tensors are checked (device, dtype, shape, contiguity), their
+device pointers and the current HIP stream are handed to libmoe_dispatch.so, and every step
+of the computation runs in the gfx950 kernels. Calls are asynchronous on
+``torch.cuda.current_stream()``. There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _capi
+from ._capi import MOE_BF16, MOE_F32, check, lib
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _hidden_dt(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def expert_capacity(tokens: int, top_k: int, num_experts: int, cf_num: int = 5, cf_den: int = 4) -> int:
+    """ceil(tokens * top_k / num_experts * cf_num / cf_den), computed exactly on the host."""
+    v = lib().moe_expert_capacity(tokens, top_k, num_experts, cf_num, cf_den)
+    if v < 0:
+        raise ValueError("invalid capacity arguments")
+    return int(v)
+
+
+def route_topk(logits: torch.Tensor, k: int, out=None):
+    """Top-k experts per token (ties -> lower id) and softmax over the k selected logits.
+
+    Returns (topk_idx int32 [T, k], topk_w float32 [T, k])."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if out is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    else:
+        idx, w = out
+        _need(idx, "topk_idx", torch.int32, 2)
+        _need(w, "topk_w", torch.float32, 2)
+        if tuple(idx.shape) != (T, k) or tuple(w.shape) != (T, k):
+            raise ValueError("output shapes must be [T, k]")
+    check("moe_route_topk", lib().moe_route_topk(_p(logits), T, E, k, _p(idx), _p(w), _stream()))
+    return idx, w
+
+
+@dataclass
+class MoeIndex:
+    """The dispatch "handle": built once by build_index, reused by permute and combine."""
+    T: int
+    K: int
+    E: int
+    capacity: int
+    group_size: int
+    counts: torch.Tensor
+    group_list: torch.Tensor
+    kept_counts: torch.Tensor
+    sorted_indices: torch.Tensor
+    row_of: torch.Tensor
+    permuted_probs: torch.Tensor
+    slot_of: Optional[torch.Tensor] = None
+    gsrc: Optional[torch.Tensor] = None
+    esrc: Optional[torch.Tensor] = None
+    group_counts: Optional[torch.Tensor] = None
+    n_slots: Optional[torch.Tensor] = None
+    workspace: Optional[torch.Tensor] = None
+
+    @property
+    def rows(self) -> int:
+        """Rows of the expert-major buffers: T*K, or E*capacity in drop-and-pad mode."""
+        return self.E * self.capacity if self.capacity > 0 else self.T * self.K
+
+    @property
+    def num_groups(self) -> int:
+        return self.E // self.group_size if self.group_size > 0 else 0
+
+    def struct(self) -> _capi.MoeIndexStruct:
+        return _capi.MoeIndexStruct(*[None if t is None else t.data_ptr() for t in (
+            self.counts, self.group_list, self.kept_counts, self.sorted_indices, self.row_of,
+            self.permuted_probs, self.slot_of, self.gsrc, self.esrc, self.group_counts, self.n_slots)])
+
+
+def workspace_bytes(T: int, K: int, E: int, group_size: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    check("moe_build_index_workspace_size",
+          lib().moe_build_index_workspace_size(T, K, E, group_size, ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_index(T: int, K: int, E: int, capacity: int = 0, group_size: int = 0, device="cuda") -> MoeIndex:
+    i32 = dict(dtype=torch.int32, device=device)
+    rows = E * capacity if capacity > 0 else T * K
+    ix = MoeIndex(
+        T=T, K=K, E=E, capacity=capacity, group_size=group_size,
+        counts=torch.empty(E, **i32), group_list=torch.empty(E, **i32), kept_counts=torch.empty(E, **i32),
+        sorted_indices=torch.empty(rows, **i32), row_of=torch.empty((T, K), **i32),
+        permuted_probs=torch.empty(rows, dtype=torch.float32, device=device))
+    if group_size > 0:
+        G = E // group_size
+        ix.slot_of = torch.empty((T, G), **i32)
+        ix.gsrc = torch.empty(T * min(K, G), **i32)
+        ix.esrc = torch.empty(rows, **i32)
+        ix.group_counts = torch.empty(G, **i32)
+        ix.n_slots = torch.empty(1, **i32)
+    ws = workspace_bytes(T, K, E, group_size)
+    ix.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+    return ix
+
+
+def build_index(topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor], num_experts: int,
+                capacity: int = 0, group_size: int = 0, out: Optional[MoeIndex] = None) -> MoeIndex:
+    """Expert-major index of the routing result (sorted_indices, row_of, counts, group_list, ...)."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    T, K = topk_idx.shape
+    if topk_w is not None:
+        _need(topk_w, "topk_w", torch.float32, 2)
+        if tuple(topk_w.shape) != (T, K):
+            raise ValueError("topk_w must have the shape of topk_idx")
+    ix = out if out is not None else alloc_index(T, K, num_experts, capacity, group_size, topk_idx.device)
+    if (ix.T, ix.K, ix.E, ix.capacity, ix.group_size) != (T, K, num_experts, capacity, group_size):
+        raise ValueError("preallocated index was made for other sizes")
+    s = ix.struct()
+    ws = ix.workspace
+    check("moe_build_index", lib().moe_build_index(
+        _p(topk_idx), _p(topk_w), T, K, num_experts, capacity, group_size, ctypes.byref(s),
+        _p(ws), ws.numel(), _stream()))
+    return ix
+
+
+def permute(src: torch.Tensor, src_row: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[i] = src[src_row[i]] bit for bit; an out-of-range src_row (e.g. -1) gives a zero row."""
+    _need(src, "src", None, 2)
+    dt = _hidden_dt(src, "src")
+    _need(src_row, "src_row", torch.int32, 1)
+    N = src_row.shape[0]
+    H = src.shape[1]
+    if out is None:
+        out = torch.empty((N, H), dtype=src.dtype, device=src.device)
+    _need(out, "out", src.dtype, 2)
+    if tuple(out.shape) != (N, H):
+        raise ValueError(f"out must be [{N}, {H}]")
+    check("moe_permute", lib().moe_permute(_p(src), src.shape[0], H, dt, _p(src_row), N, _p(out), _stream()))
+    return out
+
+
+def unpermute_combine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = sum_k weights[t,k] * y[row_of[t,k]] (float32 FMA chain in k order)."""
+    _need(y, "y", None, 2)
+    y_dt = _hidden_dt(y, "y")
+    _need(row_of, "row_of", torch.int32, 2)
+    T, K = row_of.shape
+    H = y.shape[1]
+    if weights is not None:
+        _need(weights, "weights", torch.float32, 2)
+        if tuple(weights.shape) != (T, K):
+            raise ValueError("weights must have the shape of row_of")
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype or y.dtype, device=y.device)
+    _need(out, "out", None, 2)
+    out_dt = _hidden_dt(out, "out")
+    if tuple(out.shape) != (T, H):
+        raise ValueError(f"out must be [{T}, {H}]")
+    check("moe_unpermute_combine", lib().moe_unpermute_combine(
+        _p(y), y_dt, y.shape[0], H, _p(row_of), _p(weights), T, K, _p(out), out_dt, _stream()))
+    return out
+
+
+def group_precombine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[torch.Tensor],
+                     topk_idx: torch.Tensor, num_experts: int, group_size: int, slot_of: torch.Tensor,
+                     slots_cap: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-(token, group) weighted partial sums (float32) stored at row slot_of[t, g]."""
+    _need(y, "y", None, 2)
+    y_dt = _hidden_dt(y, "y")
+    _need(row_of, "row_of", torch.int32, 2)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    _need(slot_of, "slot_of", torch.int32, 2)
+    T, K = row_of.shape
+    H = y.shape[1]
+    if weights is not None:
+        _need(weights, "weights", torch.float32, 2)
+    if out is None:
+        if slots_cap is None:
+            raise ValueError("give slots_cap or out")
+        out = torch.empty((slots_cap, H), dtype=torch.float32, device=y.device)
+    _need(out, "out", torch.float32, 2)
+    check("moe_group_precombine", lib().moe_group_precombine(
+        _p(y), y_dt, y.shape[0], H, _p(row_of), _p(weights), _p(topk_idx), T, K, num_experts, group_size,
+        _p(slot_of), out.shape[0], _p(out), _stream()))
+    return out
