@@ -29,7 +29,7 @@ KERNEL_SOURCES = {
     "permute": ["unpermute_combine_amd/csrc/permute.hip", "unpermute_combine_amd/csrc/moe_common.h"],
     "combine": ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csrc/moe_common.h"],
 }
-KERNEL_SYMBOLS = {"permute": "permute_vec16_kernel", "combine": "combine_kernel"}
+KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine_kernel"}
 
 
 def log(*a):
@@ -157,10 +157,10 @@ def main():
         mark(2)
         if gs:
             n = int(ix.n_slots.item())  # the group count is only known on the device
-            m.permute(x, ix.gsrc[:n], out=gbuf[:n])
+            m.permute_scatter(x, ix.slot_of, n, out=gbuf[:n])
             m.permute(gbuf[:n], ix.esrc, out=xp)
         else:
-            m.permute(x, ix.sorted_indices, out=xp)
+            m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=xp)
         mark(3)
         src = xp if y is None else y
         if gs:

@@ -138,9 +138,23 @@ moe_status moe_build_index(const int32_t *topk_idx, const float *topk_w, int64_t
  *   src [src_rows, H] of dtype dt, src_row [N] int32, dst [N, H] of dtype dt.
  * Used for the standard dispatch (src_row = sorted_indices, N = R), drop-and-pad (which also
  * zero-fills the padding rows) and the two stages of the group dispatch (src_row = gsrc, then
- * esrc). */
+ * esrc). moe_permute_scatter below computes the same rows reading each source row once. */
 moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
                        const int32_t *src_row, int64_t N, void *dst, hipStream_t stream);
+
+/* The same row copy as moe_permute, taken source-major: each source row is read once and
+ * written to every destination that names it, instead of being read again for each destination
+ * (with top-k routing a token row feeds K expert rows, [Scratch] §4).
+ *   dst_of  [src_rows, J] int32: dst[dst_of[t*J + j], :] = src[t, :] for every entry in [0, N);
+ *           other entries (-1) are skipped. J <= 64.
+ *   src_row [N] int32 or NULL: rows i with src_row[i] outside [0, src_rows) are written as zeros
+ *           (the padding rows of drop-and-pad); NULL writes no zero rows.
+ * When dst_of is the inverse of src_row -- row_of and sorted_indices of one moe_index are -- the
+ * result is bit for bit that of moe_permute(src, src_rows, H, dt, src_row, N, dst). Every
+ * destination row must be named at most once; rows named by neither map are left untouched. */
+moe_status moe_permute_scatter(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
+                               const int32_t *dst_of, int32_t J, const int32_t *src_row, int64_t N,
+                               void *dst, hipStream_t stream);
 
 /* Unpermute + weighted top-k merge ([Combine] §1: out[t] = sum over the token's top-k experts
  * of probs[t,e] * expert_e(x[t]); [Scratch] §13, §16):

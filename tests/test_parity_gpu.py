@@ -107,7 +107,8 @@ def check_index(m, ids, w, E, cap=0, gs=0):
 
 
 @pytest.mark.parametrize("T,E,K", [(1, 1, 1), (5, 3, 2), (300, 8, 2), (4099, 64, 8), (2000, 256, 8),
-                                   (1500, 1024, 32), (700, 40, 7), (9000, 128, 4)])
+                                   (1500, 1024, 32), (700, 40, 7), (9000, 128, 4), (50000, 64, 8),
+                                   (33333, 130, 6)])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_build_index_standard(m, T, E, K, weighted):
     say(f"build_index standard T={T} E={E} K={K} weighted={weighted}")
@@ -126,7 +127,7 @@ def test_build_index_skewed_with_empty_experts(m):
 
 
 @pytest.mark.parametrize("T,E,K,cap", [(300, 8, 2, 3), (4099, 64, 8, 40), (2000, 128, 8, 200),
-                                       (1000, 16, 4, 1000), (50, 1024, 8, 1), (1, 4, 2, 5)])
+                                       (1000, 16, 4, 1000), (50, 1024, 8, 1), (1, 4, 2, 5), (40000, 96, 8, 2000)])
 def test_build_index_drop_and_pad(m, T, E, K, cap):
     say(f"build_index drop T={T} E={E} K={K} cap={cap}")
     key = wl.case_key(23, T, E, K)
@@ -137,7 +138,8 @@ def test_build_index_drop_and_pad(m, T, E, K, cap):
 
 
 @pytest.mark.parametrize("T,E,K,gs", [(300, 8, 2, 2), (4099, 64, 8, 8), (2000, 256, 8, 8), (500, 32, 8, 32),
-                                      (700, 96, 6, 1), (1000, 1024, 8, 32), (3, 4, 2, 2)])
+                                      (700, 96, 6, 1), (1000, 1024, 8, 32), (3, 4, 2, 2), (50000, 64, 6, 8),
+                                      (20000, 36, 5, 3)])
 def test_build_index_groups(m, T, E, K, gs):
     say(f"build_index group T={T} E={E} K={K} gs={gs}")
     key = wl.case_key(24, T, E, K)
@@ -176,6 +178,48 @@ def test_permute_empty_source_gives_zero_rows(m):
     src_row = np.asarray([-1, 0, 3], np.int32)
     got = host(m.permute(dev(x), dev(src_row)))
     assert (got == 0).all() and got.shape == (3, 16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H,T,E,K,mode", [(7168, 600, 64, 8, "standard"), (1000, 300, 16, 4, "drop"),
+                                          (3, 257, 8, 2, "standard"), (4096, 513, 32, 8, "drop"),
+                                          (64, 100, 8, 2, "missing"), (24, 90, 12, 6, "group")])
+def test_permute_scatter_matches_gather(m, dtype, H, T, E, K, mode):
+    """Source-major permute with the index's inverse maps equals the pages' gather, bit for bit."""
+    say(f"permute_scatter {dtype} H={H} T={T} E={E} K={K} {mode}")
+    key = wl.case_key(28, H, T, E, K)
+    logits = wl.router_logits(key, T, E, zipf_s=1.0)
+    idx, w = oracle.route_topk(logits, K)
+    if mode == "missing":
+        idx[::3, -1] = -1
+    cap = oracle.capacity(T, K, E, 1, 2) if mode == "drop" else 0
+    gs = 3 if mode == "group" else 0
+    ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs)
+    x = wl.hidden_states(key, T, H, dtype)
+    want = oracle.permute(x, ix["sorted_indices"])
+    xd = dev(x)
+    got = host(m.permute_scatter(xd, dev(ix["row_of"]), len(ix["sorted_indices"]), src_row=dev(ix["sorted_indices"])))
+    assert_exact(got, want, "scatter rows")
+    if mode == "group":  # stage 1 of the group dispatch: one copy per (token, group)
+        n = int(ix["n_slots"][0])
+        got1 = host(m.permute_scatter(xd, dev(ix["slot_of"]), n))
+        assert_exact(got1, oracle.permute(x, ix["gsrc"]), "group slots")
+
+
+def test_permute_scatter_leaves_unnamed_rows(m):
+    x = wl.hidden_states(wl.case_key(29), 10, 16, "bf16")
+    dst_of = np.full((10, 2), -1, np.int32)
+    dst_of[3, 1] = 5
+    dst_of[7, 0] = 0
+    out = dev(np.full((8, 16), 0x1234, np.uint16))
+    m.permute_scatter(dev(x), dev(dst_of), 8, out=out)
+    got = host(out)
+    assert np.array_equal(got[5], x[3]) and np.array_equal(got[0], x[7])
+    assert (got[[1, 2, 3, 4, 6, 7]] == 0x1234).all()
+    src_row = np.asarray([7, -1, 99, -1, -1, 3, -1, -1], np.int32)
+    m.permute_scatter(dev(x), dev(dst_of), 8, src_row=dev(src_row), out=out)
+    got = host(out)
+    assert (got[[1, 2, 3, 4, 6, 7]] == 0).all()
 
 
 # ------------------------------------------------------------------ combine
@@ -280,10 +324,11 @@ def run_workload(m, cfg_id):
         assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
         assert_exact(host(ix.esrc), want["esrc"], "esrc")
         assert_exact(host(ix.slot_of), want["slot_of"], "slot_of")
-        gbuf = m.permute(xd, ix.gsrc[:n])
+        gbuf = m.permute_scatter(xd, ix.slot_of, n)
+        assert_exact(host(gbuf), host(m.permute(xd, ix.gsrc[:n])), "group slots: scatter vs gather")
         xp = m.permute(gbuf, ix.esrc)
     else:
-        xp = m.permute(xd, ix.sorted_indices)
+        xp = m.permute_scatter(xd, ix.row_of, rows, src_row=ix.sorted_indices)
     torch.cuda.synchronize()
     rs = sample_rows(rows, 3000, cfg_id)
     assert_exact(host(xp[torch.from_numpy(rs).to(DEV)]), oracle.permute(x, want["sorted_indices"][rs]),

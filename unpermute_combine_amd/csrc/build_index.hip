@@ -6,16 +6,22 @@
 // gives permuted_probs; [Scratch] §7 ("从零理解 MoE 算子") gives group_list as the running sum
 // of the per-expert counts. Ordering the slots i = t*K + k by (expert, i) is exactly that list.
 //
-// gfx950 design (three launches, plus one in group mode):
-//   1. hist   one workgroup per tile of whole tokens: per-tile expert histogram (and group
-//             histogram of the first slot of each (token, group)) with LDS atomics -- only the
-//             counts, never positions, come from atomics, so the result is deterministic.
-//   2. scan   one workgroup: exclusive scan of the [key][tile] histograms in key-major order,
-//             giving every (key, tile) its first row; counts, group_list, capacity bookkeeping,
-//             padding and unused rows.
+// gfx950 design. A dependent global-memory round trip costs microseconds here, so every pass
+// issues its loads together, stores whole cache lines, and orders loads before stores (on gfx9
+// the vector-memory counter retires loads and stores in issue order, so a load issued after a
+// store cannot be waited for without waiting for the store too). Three launches, plus one in
+// group mode:
+//   1. hist   one workgroup per tile of whole tokens: the tile's expert histogram (and the
+//             group histogram of each token's first slot in a group) with LDS atomics -- only
+//             counts come from atomics, never positions, so the result is deterministic -- and
+//             one coalesced row hist[tile][0..E) per tile.
+//   2. scan   one workgroup: lanes own 4 consecutive keys, wavefronts own ranges of tiles; the
+//             per-wave partial sums meet in LDS, giving each (tile, key) its first row inside
+//             the key; a block scan over the key totals gives each key's first row. Also
+//             counts, group_list, capacity bookkeeping, padding and unused rows.
 //   3. rank   one wavefront per tile walks its slots 64 at a time in slot order. Lanes with
 //             the same key find each other with one ballot per key bit (a match-any built from
-//             ballots), their stable rank is popcount(peers & lanes_below), and the last peer
+//             ballots); their stable rank is popcount(peers & lanes_below) and the last peer
 //             advances the key's running row counter in LDS.
 //   4. esrc   (group mode) expert-major row -> group slot.
 // The drop-and-pad capacity rule ([Scratch] §18, §26.6) and the group (send once per rank)
@@ -27,15 +33,25 @@
 namespace moe {
 namespace {
 
+constexpr int kMaxTiles = 128;      // tiles grow with T so that there are never more
+constexpr int kScanThreads = 1024;  // the scan workgroup: 16 wavefronts
+constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kKeysPerChunk = 4 * kWave;                                  // 4 keys per lane
+constexpr int kTilesPerWave = (kMaxTiles + kScanWaves - 1) / kScanWaves;  // 8
+constexpr int kRankBatch = 8;  // 64-slot groups whose loads a rank wave issues together
+
 struct IndexArgs {
     const int32_t *topk_idx;
     const float *topk_w;
     int64_t T;
     int32_t K, E, cap, gs, G;
+    int32_t Ep, Gp;  // row strides of the histograms (E, G rounded up to a multiple of 4)
     int32_t tile_tokens, ntiles;
     int32_t ebits, gbits;
-    int32_t *hist_e;  // [E][ntiles] -> exclusive bases after the scan
-    int32_t *hist_g;  // [G][ntiles]
+    int32_t *hist_e;  // [ntiles][Ep] tile counts -> first row of (tile, expert) inside the expert
+    int32_t *hist_g;  // [ntiles][Gp] the same for group slots
+    int32_t *seg_e;   // [E] first row of each expert
+    int32_t *seg_g;   // [G] first slot of each group
     moe_index ix;
 };
 
@@ -52,13 +68,15 @@ __device__ __forceinline__ bool group_leader(const int32_t *ids, int k, int g, i
     return true;
 }
 
+// ---------------------------------------------------------------- 1. per-tile histograms
 __global__ __launch_bounds__(256) void hist_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
-    int32_t *he = sh;
-    int32_t *hg = sh + a.E;
+    int32_t *he = sh;         // [Ep]
+    int32_t *hg = sh + a.Ep;  // [Gp]
     const int tile = blockIdx.x;
-    for (int i = threadIdx.x; i < a.E + (a.gs > 0 ? a.G : 0); i += blockDim.x)
+    const int nsh = a.Ep + (a.gs > 0 ? a.Gp : 0);
+    for (int i = threadIdx.x; i < nsh; i += blockDim.x)
         sh[i] = 0;
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(tile) * a.tile_tokens;
@@ -82,67 +100,138 @@ __global__ __launch_bounds__(256) void hist_kernel(IndexArgs a)
             a.ix.slot_of[i] = -1;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < a.E; e += blockDim.x)
-        a.hist_e[static_cast<int64_t>(e) * a.ntiles + tile] = he[e];
-    if (a.gs > 0)
-        for (int g = threadIdx.x; g < a.G; g += blockDim.x)
-            a.hist_g[static_cast<int64_t>(g) * a.ntiles + tile] = hg[g];
+    int32_t *row = a.hist_e + static_cast<int64_t>(tile) * a.Ep;
+    for (int e = threadIdx.x; e < a.Ep; e += blockDim.x)
+        row[e] = he[e];
+    if (a.gs > 0) {
+        int32_t *rowg = a.hist_g + static_cast<int64_t>(tile) * a.Gp;
+        for (int g = threadIdx.x; g < a.Gp; g += blockDim.x)
+            rowg[g] = hg[g];
+    }
 }
 
-constexpr int kScanThreads = 1024;
+// ---------------------------------------------------------------- 2. scan
+struct ScanShared {
+    int32_t part[kScanWaves][kKeysPerChunk];  // per-wave partial sums -> per-wave prefixes
+    int32_t tot[MOE_MAX_EXPERTS];
+    int32_t seg[MOE_MAX_EXPERTS];
+    int32_t waves[kWave + 1];
+};
 
-// In-place exclusive scan of n ints by one workgroup; returns the total to every thread.
-__device__ int64_t block_exclusive_scan(int32_t *v, int64_t n, int32_t *sh_sums)
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v)
 {
-    const int tid = threadIdx.x;
-    const int64_t per = (n + kScanThreads - 1) / kScanThreads;
-    const int64_t lo = min(n, tid * per), hi = min(n, lo + per);
-    int32_t sum = 0;
-    for (int64_t i = lo; i < hi; ++i)
-        sum += v[i];
-    sh_sums[tid] = sum;
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(v, off, kWave);
+        if (lane >= off)
+            v += u;
+    }
+    return v;
+}
+
+// Exclusive scan of one value per thread over the workgroup; *total gets the sum.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *sh_waves, int32_t *total)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int32_t inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1)
+        sh_waves[wave] = inc;
     __syncthreads();
-    // Hillis-Steele over the 1024 strip sums
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        const int32_t add = tid >= off ? sh_sums[tid - off] : 0;
-        __syncthreads();
-        sh_sums[tid] += add;
-        __syncthreads();
+    if (wave == 0) {
+        const int32_t w = lane < kScanWaves ? sh_waves[lane] : 0;
+        const int32_t winc = wave_inclusive_scan(w);
+        if (lane < kScanWaves)
+            sh_waves[lane] = winc - w;
+        if (lane == kScanWaves - 1)
+            sh_waves[kWave] = winc;
     }
-    const int32_t total = sh_sums[kScanThreads - 1];
-    int32_t run = sh_sums[tid] - sum;  // exclusive prefix of this strip
-    for (int64_t i = lo; i < hi; ++i) {
-        const int32_t c = v[i];
-        v[i] = run;
-        run += c;
+    __syncthreads();
+    const int32_t r = sh_waves[wave] + inc - v;
+    *total = sh_waves[kWave];
+    __syncthreads();
+    return r;
+}
+
+// hist [ntiles][stride] (stride a multiple of 4, 16-byte aligned rows) holds tile counts; on
+// return it holds, for every (tile, key), the first row of that tile inside the key, sh.tot the
+// key totals and sh.seg each key's first row. Returns the grand total.
+__device__ __forceinline__ int32_t scan_tiles(int32_t *hist, int nkeys, int stride, int ntiles, ScanShared &sh)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int tpw = (ntiles + kScanWaves - 1) / kScanWaves;  // <= kTilesPerWave
+    const int j0 = wave * tpw;
+    for (int kc = 0; kc < nkeys; kc += kKeysPerChunk) {
+        const int key = kc + 4 * lane;  // this lane's 4 keys: key .. key+3
+        const bool mine = key < stride;
+        u32x4 c[kTilesPerWave];
+#pragma unroll
+        for (int j = 0; j < kTilesPerWave; ++j) {
+            const int tile = j0 + j;
+            c[j] = (j < tpw && tile < ntiles && mine) ? ld16(hist + static_cast<int64_t>(tile) * stride + key)
+                                                      : u32x4{0u, 0u, 0u, 0u};
+        }
+        u32x4 s{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kTilesPerWave; ++j) {
+            s.x += c[j].x;
+            s.y += c[j].y;
+            s.z += c[j].z;
+            s.w += c[j].w;
+        }
+        sh.part[wave][4 * lane + 0] = static_cast<int32_t>(s.x);
+        sh.part[wave][4 * lane + 1] = static_cast<int32_t>(s.y);
+        sh.part[wave][4 * lane + 2] = static_cast<int32_t>(s.z);
+        sh.part[wave][4 * lane + 3] = static_cast<int32_t>(s.w);
+        __syncthreads();
+        if (threadIdx.x < kKeysPerChunk) {  // one thread per key: prefix over the waves
+            int32_t run = 0;
+            for (int w = 0; w < kScanWaves; ++w) {
+                const int32_t v = sh.part[w][threadIdx.x];
+                sh.part[w][threadIdx.x] = run;
+                run += v;
+            }
+            if (kc + static_cast<int>(threadIdx.x) < nkeys)
+                sh.tot[kc + threadIdx.x] = run;
+        }
+        __syncthreads();
+        u32x4 run{static_cast<uint32_t>(sh.part[wave][4 * lane + 0]), static_cast<uint32_t>(sh.part[wave][4 * lane + 1]),
+                  static_cast<uint32_t>(sh.part[wave][4 * lane + 2]), static_cast<uint32_t>(sh.part[wave][4 * lane + 3])};
+#pragma unroll
+        for (int j = 0; j < kTilesPerWave; ++j) {
+            const int tile = j0 + j;
+            if (j < tpw && tile < ntiles && mine)
+                st16(hist + static_cast<int64_t>(tile) * stride + key, run);
+            run.x += c[j].x;
+            run.y += c[j].y;
+            run.z += c[j].z;
+            run.w += c[j].w;
+        }
+        __syncthreads();  // sh.part is reused by the next chunk of keys
     }
+    int32_t total;
+    const int32_t v = static_cast<int>(threadIdx.x) < nkeys ? sh.tot[threadIdx.x] : 0;
+    const int32_t ex = block_exclusive_scan(v, sh.waves, &total);
+    if (static_cast<int>(threadIdx.x) < nkeys)
+        sh.seg[threadIdx.x] = ex;
     __syncthreads();
     return total;
 }
 
-// First row of key `key` after the scan (its tile-0 base); `total` past the last key.
-__device__ __forceinline__ int32_t key_start(const int32_t *bases, int key, int nkeys, int ntiles,
-                                             int32_t total)
-{
-    if (ntiles == 0)
-        return 0;
-    return key < nkeys ? bases[static_cast<int64_t>(key) * ntiles] : total;
-}
-
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(IndexArgs a)
 {
-    __shared__ int32_t sums[kScanThreads];
+    __shared__ ScanShared sh;
     const int tid = threadIdx.x;
     const int64_t R = a.cap > 0 ? static_cast<int64_t>(a.E) * a.cap : a.T * a.K;
-    const int32_t total = static_cast<int32_t>(
-        block_exclusive_scan(a.hist_e, static_cast<int64_t>(a.E) * a.ntiles, sums));
-    __threadfence_block();
+    const int32_t total = scan_tiles(a.hist_e, a.E, a.Ep, a.ntiles, sh);
     for (int e = tid; e < a.E; e += kScanThreads) {
-        const int32_t start = key_start(a.hist_e, e, a.E, a.ntiles, total);
-        const int32_t end = key_start(a.hist_e, e + 1, a.E, a.ntiles, total);
-        const int32_t cnt = end - start;
+        const int32_t cnt = sh.tot[e];
+        const int32_t start = sh.seg[e];
+        a.seg_e[e] = start;
         a.ix.counts[e] = cnt;
-        a.ix.group_list[e] = end;
+        a.ix.group_list[e] = start + cnt;
         if (a.ix.kept_counts)
             a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
     }
@@ -151,9 +240,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(IndexArgs a)
         for (int64_t r = tid; r < R; r += kScanThreads) {
             const int e = static_cast<int>(r / a.cap);
             const int p = static_cast<int>(r - static_cast<int64_t>(e) * a.cap);
-            const int32_t start = key_start(a.hist_e, e, a.E, a.ntiles, total);
-            const int32_t end = key_start(a.hist_e, e + 1, a.E, a.ntiles, total);
-            if (p >= min(end - start, a.cap)) {
+            if (p >= min(sh.tot[e], a.cap)) {
                 a.ix.sorted_indices[r] = -1;
                 if (a.ix.permuted_probs)
                     a.ix.permuted_probs[r] = 0.0f;
@@ -170,19 +257,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(IndexArgs a)
         }
     }
     if (a.gs > 0) {
-        __syncthreads();
-        const int32_t m = static_cast<int32_t>(
-            block_exclusive_scan(a.hist_g, static_cast<int64_t>(a.G) * a.ntiles, sums));
+        __syncthreads();  // sh is reused for the group keys
+        const int32_t m = scan_tiles(a.hist_g, a.G, a.Gp, a.ntiles, sh);
         for (int g = tid; g < a.G; g += kScanThreads) {
-            const int32_t start = key_start(a.hist_g, g, a.G, a.ntiles, m);
-            const int32_t end = key_start(a.hist_g, g + 1, a.G, a.ntiles, m);
-            a.ix.group_counts[g] = end - start;
+            a.seg_g[g] = sh.seg[g];
+            a.ix.group_counts[g] = sh.tot[g];
         }
         if (tid == 0)
             a.ix.n_slots[0] = m;
     }
 }
 
+// ---------------------------------------------------------------- 3. stable ranks
 // Bitwise match-any over the low `bits` bits of key among the lanes in `active`.
 __device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t active)
 {
@@ -197,75 +283,132 @@ __device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t acti
 
 __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(m); }
 
-__global__ __launch_bounds__(64) void rank_kernel(IndexArgs a)
+__global__ __launch_bounds__(kWave) void rank_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
-    int32_t *run_e = sh;         // next row of each expert in this tile
-    int32_t *run_g = sh + a.E;   // next slot of each group in this tile
+    int32_t *run_e = sh;           // [E] next row of each expert in this tile
+    int32_t *seg_e = run_e + a.E;  // [E] first row of each expert
+    int32_t *run_g = seg_e + a.E;  // [G] next slot of each group in this tile
+    int32_t *ids = run_g + a.G;    // [kRankBatch * 64] expert ids of the current batch
     const int tile = blockIdx.x;
     const int lane = threadIdx.x;
-    for (int e = lane; e < a.E; e += kWave)
-        run_e[e] = a.hist_e[static_cast<int64_t>(e) * a.ntiles + tile];
-    if (a.gs > 0)
+    const int32_t *hrow = a.hist_e + static_cast<int64_t>(tile) * a.Ep;
+    for (int e = lane; e < a.E; e += kWave) {
+        const int32_t s = a.seg_e[e];
+        seg_e[e] = s;
+        run_e[e] = s + hrow[e];
+    }
+    if (a.gs > 0) {
+        const int32_t *hrowg = a.hist_g + static_cast<int64_t>(tile) * a.Gp;
         for (int g = lane; g < a.G; g += kWave)
-            run_g[g] = a.hist_g[static_cast<int64_t>(g) * a.ntiles + tile];
-    __syncthreads();
+            run_g[g] = a.seg_g[g] + hrowg[g];
+    }
 
     const int64_t t0 = static_cast<int64_t>(tile) * a.tile_tokens;
     const int64_t t1 = min(a.T, t0 + a.tile_tokens);
     const int64_t s0 = t0 * a.K, s1 = t1 * a.K;
     const uint64_t below = lanemask_lt();
-    for (int64_t base = s0; base < s1; base += kWave) {
-        const int64_t i = base + lane;
-        const bool in = i < s1;
-        const int e = in ? a.topk_idx[i] : -1;
-        const bool ok = valid_expert(e, a.E);
-        const int64_t t = i / a.K;
-        const int k = static_cast<int>(i - t * a.K);
-
-        // ---- expert-major row
-        const uint64_t pe = match_peers(e, a.ebits, __ballot(ok));
-        int32_t row = -1;
-        if (ok) {
-            const int32_t r = run_e[e] + __popcll(pe & below);
-            row = r;
-            if (a.cap > 0) {
-                const int32_t seg = a.hist_e[static_cast<int64_t>(e) * a.ntiles];  // expert's first row
-                const int32_t p = r - seg;
-                row = p < a.cap ? e * a.cap + p : -1;
+    const bool want_w = a.ix.permuted_probs && a.topk_w;
+    constexpr int kSpan = kRankBatch * kWave;
+    // the loads of a batch of 8 x 64 slots are issued together, and before the previous
+    // batch's stores
+    int e_nx[kRankBatch];
+    float w_nx[kRankBatch];
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) {
+        const int64_t i = s0 + b * kWave + lane;
+        e_nx[b] = i < s1 ? a.topk_idx[i] : -1;
+        w_nx[b] = want_w && i < s1 ? a.topk_w[i] : 1.0f;
+    }
+    for (int64_t base0 = s0; base0 < s1; base0 += kSpan) {
+        int e_cur[kRankBatch];
+        float w_cur[kRankBatch];
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b) {
+            e_cur[b] = e_nx[b];
+            w_cur[b] = w_nx[b];
+        }
+        if (base0 + kSpan < s1) {
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b) {
+                const int64_t i = base0 + kSpan + b * kWave + lane;
+                e_nx[b] = i < s1 ? a.topk_idx[i] : -1;
+                w_nx[b] = want_w && i < s1 ? a.topk_w[i] : 1.0f;
             }
         }
-        __builtin_amdgcn_wave_barrier();
-        if (ok && lane == last_lane(pe))
-            run_e[e] += __popcll(pe);
-        if (in)
-            a.ix.row_of[i] = row;
-        if (row >= 0) {
-            a.ix.sorted_indices[row] = static_cast<int32_t>(t);
-            if (a.ix.permuted_probs)
-                a.ix.permuted_probs[row] = a.topk_w ? a.topk_w[i] : 1.0f;
-        }
-
-        // ---- group slots: one per (token, group), listed group by group, tokens ascending
-        if (a.gs > 0) {
-            const int g = ok ? e / a.gs : -1;
-            const bool lead = ok && group_leader(a.topk_idx + t * a.K, k, g, a.E, a.gs);
-            const uint64_t pg = match_peers(g, a.gbits, __ballot(lead));
-            int32_t slot = -1;
-            if (lead)
-                slot = run_g[g] + __popcll(pg & below);
+        if (a.gs > 0) {  // the batch's ids, for the first-slot-in-group test
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                ids[b * kWave + lane] = e_cur[b];
             __builtin_amdgcn_wave_barrier();
-            if (lead && lane == last_lane(pg))
-                run_g[g] += __popcll(pg);
-            if (lead) {
-                a.ix.slot_of[t * a.G + g] = slot;
-                a.ix.gsrc[slot] = static_cast<int32_t>(t);
+        }
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b) {
+            if (base0 + b * kWave >= s1)
+                break;
+            const int64_t i = base0 + b * kWave + lane;
+            const bool in = i < s1;
+            const int e = e_cur[b];
+            const bool ok = in && valid_expert(e, a.E);
+            const int64_t t = i / a.K;
+            const int k = static_cast<int>(i - t * a.K);
+
+            // ---- expert-major row
+            const uint64_t pe = match_peers(e, a.ebits, __ballot(ok));
+            int32_t row = -1;
+            if (ok) {
+                const int32_t r = run_e[e] + __popcll(pe & below);
+                row = r;
+                if (a.cap > 0) {
+                    const int32_t p = r - seg_e[e];  // position inside the expert
+                    row = p < a.cap ? e * a.cap + p : -1;
+                }
             }
+            __builtin_amdgcn_wave_barrier();
+            if (ok && lane == last_lane(pe))
+                run_e[e] += __popcll(pe);
+            if (in)
+                a.ix.row_of[i] = row;
+            if (row >= 0) {
+                a.ix.sorted_indices[row] = static_cast<int32_t>(t);
+                if (a.ix.permuted_probs)
+                    a.ix.permuted_probs[row] = w_cur[b];
+            }
+
+            // ---- group slots: one per (token, group), listed group by group, tokens ascending
+            if (a.gs > 0) {
+                const int g = ok ? e / a.gs : -1;
+                bool lead = ok;
+                if (ok) {
+                    // earlier slots of the token: in this batch (LDS), or -- only when K does
+                    // not divide the batch size -- just before it
+                    const int64_t first = i - k;
+                    for (int j = 0; j < k; ++j) {
+                        const int64_t q = first + j;
+                        const int ej = q >= base0 ? ids[q - base0] : a.topk_idx[q];
+                        if (valid_expert(ej, a.E) && ej / a.gs == g)
+                            lead = false;
+                    }
+                }
+                const uint64_t pg = match_peers(g, a.gbits, __ballot(lead));
+                int32_t slot = -1;
+                if (lead)
+                    slot = run_g[g] + __popcll(pg & below);
+                __builtin_amdgcn_wave_barrier();
+                if (lead && lane == last_lane(pg))
+                    run_g[g] += __popcll(pg);
+                if (lead) {
+                    a.ix.slot_of[t * a.G + g] = slot;
+                    a.ix.gsrc[slot] = static_cast<int32_t>(t);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
         }
         __builtin_amdgcn_wave_barrier();
     }
 }
 
+// ---------------------------------------------------------------- 4. group mode: esrc
 __global__ __launch_bounds__(256) void esrc_kernel(IndexArgs a)
 {
     const int64_t n = a.T * a.K;
@@ -288,23 +431,28 @@ int bits_for(int n)  // bits needed to tell apart the keys 0..n-1
     return b;
 }
 
+int round4(int n) { return (n + 3) & ~3; }
+
 struct Plan {
     int32_t tile_tokens, ntiles;
-    size_t ws_e, ws_g;  // bytes of the two histogram arrays
+    size_t ws_hist_e, ws_e;  // bytes of the expert tile counts, and of those plus the expert starts
+    size_t ws_hist_g, ws_g;  // the same for groups
 };
 
-// Tiles hold whole tokens (so a token's group-leader test stays inside one tile), at least
-// ~512 slots each and at most 256 tiles, which keeps the single-workgroup scan short.
+// Tiles hold whole tokens (so a token's group test stays inside one tile), at least ~512 slots
+// each and at most kMaxTiles of them.
 Plan make_plan(int64_t T, int32_t K, int32_t E, int32_t G)
 {
     Plan p{};
     int64_t tt = ceil_div(512, K);
-    tt = std::max<int64_t>(tt, ceil_div(T, 256));
+    tt = std::max<int64_t>(tt, ceil_div(T, kMaxTiles));
     p.tile_tokens = static_cast<int32_t>(std::min<int64_t>(tt, 0x7fffffff));
     p.ntiles = static_cast<int32_t>(T == 0 ? 0 : ceil_div(T, p.tile_tokens));
     auto al = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
-    p.ws_e = al(sizeof(int32_t) * static_cast<size_t>(E) * p.ntiles);
-    p.ws_g = G > 0 ? al(sizeof(int32_t) * static_cast<size_t>(G) * p.ntiles) : 0;
+    p.ws_hist_e = al(sizeof(int32_t) * static_cast<size_t>(round4(E)) * p.ntiles);
+    p.ws_e = p.ws_hist_e + al(sizeof(int32_t) * static_cast<size_t>(E));
+    p.ws_hist_g = G > 0 ? al(sizeof(int32_t) * static_cast<size_t>(round4(G)) * p.ntiles) : 0;
+    p.ws_g = G > 0 ? p.ws_hist_g + al(sizeof(int32_t) * static_cast<size_t>(G)) : 0;
     return p;
 }
 
@@ -363,7 +511,9 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     if (T > 0 && !topk_idx)
         return MOE_ERR_INVALID;
     const Plan p = make_plan(T, K, E, G);
-    if (p.ntiles > 0 && (!workspace || workspace_bytes < p.ws_e + p.ws_g))
+    if (p.ntiles > kMaxTiles)
+        return MOE_ERR_UNSUPPORTED;  // cannot happen: tiles grow with T to stay within the limit
+    if (!workspace || workspace_bytes < p.ws_e + p.ws_g || !aligned16(workspace))
         return MOE_ERR_INVALID;
 
     IndexArgs a{};
@@ -375,12 +525,17 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     a.cap = capacity > 0 ? capacity : 0;
     a.gs = group_size > 0 ? group_size : 0;
     a.G = G;
+    a.Ep = round4(E);
+    a.Gp = round4(G);
     a.tile_tokens = p.tile_tokens;
     a.ntiles = p.ntiles;
     a.ebits = bits_for(E);
     a.gbits = bits_for(G);
-    a.hist_e = static_cast<int32_t *>(workspace);
-    a.hist_g = G > 0 ? reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + p.ws_e) : nullptr;
+    char *ws = static_cast<char *>(workspace);
+    a.hist_e = reinterpret_cast<int32_t *>(ws);
+    a.seg_e = reinterpret_cast<int32_t *>(ws + p.ws_hist_e);
+    a.hist_g = G > 0 ? reinterpret_cast<int32_t *>(ws + p.ws_e) : nullptr;
+    a.seg_g = G > 0 ? reinterpret_cast<int32_t *>(ws + p.ws_e + p.ws_hist_g) : nullptr;
     a.ix = *out;
 
     if (T == 0) {
@@ -389,14 +544,15 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
         return launch_status();
     }
 
-    const size_t lds_keys = sizeof(int32_t) * (static_cast<size_t>(E) + G);
-    hipLaunchKernelGGL(hist_kernel, dim3(p.ntiles), dim3(256), lds_keys, stream, a);
+    const size_t lds_hist = sizeof(int32_t) * (static_cast<size_t>(a.Ep) + (G > 0 ? a.Gp : 0));
+    hipLaunchKernelGGL(hist_kernel, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
-    hipLaunchKernelGGL(rank_kernel, dim3(p.ntiles), dim3(kWave), lds_keys, stream, a);
+    const size_t lds_rank = sizeof(int32_t) * (2 * static_cast<size_t>(E) + G + kRankBatch * kWave);
+    hipLaunchKernelGGL(rank_kernel, dim3(p.ntiles), dim3(kWave), lds_rank, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
     if (G > 0) {

@@ -9,14 +9,18 @@
 // one token: it compacts the token's valid (row, weight) pairs into LDS in slot order, then
 // every thread owns 8 consecutive hidden elements at a time, issues the 16-byte loads of all
 // the token's rows before the fused multiply-adds (which run in slot order, float32, from +0),
-// and writes 8 outputs with one 16-byte (bf16) or two (float32) stores. Each y row is read once;
-// each out row written once.
+// and writes 8 outputs with one 16-byte (bf16) or two (float32) stores. Each y row is read once
+// and each out row written once, both with nontemporal hints (streamed data: no reuse to keep
+// in L2 / MALL, which measurably raises the read rate on MI355X).
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
 constexpr int kMaxCombineK = 1024;
+constexpr int kMaxThreads = 1024;  // largest workgroup block_threads() picks
 constexpr int kBatch = 8;  // rows whose loads are issued together
 
 // ---------------------------------------------------------------- 8-element vector access
@@ -27,7 +31,7 @@ template <>
 struct Vec8Load<uint16_t> {  // bf16: one 16-byte load
     __device__ static void load(const uint16_t *p, float (&v)[8])
     {
-        const u32x4 q = ld16(p);
+        const u32x4 q = ld16_stream(p);
         v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
         v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
@@ -39,7 +43,7 @@ template <>
 struct Vec8Load<float> {  // float32: two 16-byte loads
     __device__ static void load(const float *p, float (&v)[8])
     {
-        const u32x4 a = ld16(p), b = ld16(p + 4);
+        const u32x4 a = ld16_stream(p), b = ld16_stream(p + 4);
         v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
         v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
         v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
@@ -49,14 +53,14 @@ struct Vec8Load<float> {  // float32: two 16-byte loads
 
 __device__ __forceinline__ void store8(uint16_t *p, const float (&a)[8])
 {
-    st16(p, u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
-                  pack_bf16x2(a[6], a[7])});
+    st16_stream(p, u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
+                         pack_bf16x2(a[6], a[7])});
 }
 
 __device__ __forceinline__ void store8(float *p, const float (&a)[8])
 {
-    st16(p, u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])});
-    st16(p + 4, u32x4{__float_as_uint(a[4]), __float_as_uint(a[5]), __float_as_uint(a[6]), __float_as_uint(a[7])});
+    st16_stream(p, u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])});
+    st16_stream(p + 4, u32x4{__float_as_uint(a[4]), __float_as_uint(a[5]), __float_as_uint(a[6]), __float_as_uint(a[7])});
 }
 
 __device__ __forceinline__ float load1(const uint16_t *p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
@@ -119,7 +123,7 @@ __device__ int compact_rows(const int32_t *rows_in, const float *w_in, int K, in
 }
 
 template <typename Y, typename O, bool VEC>
-__global__ __launch_bounds__(256) void combine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
+__global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
                                                       const int32_t *__restrict__ row_of,
                                                       const float *__restrict__ w, int K,
                                                       O *__restrict__ out)
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const Y *__restrict__ y, i
 
 // ---------------------------------------------------------------- group pre-combine
 template <typename Y, bool VEC>
-__global__ __launch_bounds__(256) void precombine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
+__global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
                                                          const int32_t *__restrict__ row_of,
                                                          const float *__restrict__ w,
                                                          const int32_t *__restrict__ topk_idx, int K,
@@ -226,13 +230,13 @@ __global__ __launch_bounds__(256) void precombine_kernel(const Y *__restrict__ y
     }
 }
 
+// Threads per token: about two 8-element chunks per thread, whole wavefronts, at most 1024
+// (H = 7168 -> 448 threads, two chunks each).
 int block_threads(int64_t nchunk)
 {
-    if (nchunk >= 768)
-        return 256;
-    if (nchunk >= 192)
-        return 128;
-    return 64;
+    const int64_t half = (nchunk + 1) / 2;
+    const int64_t waves = std::min<int64_t>(kMaxThreads / kWave, std::max<int64_t>(1, (half + kWave - 1) / kWave));
+    return static_cast<int>(waves * kWave);
 }
 
 template <typename Y, typename O>

@@ -3,9 +3,14 @@
 // [Scratch] §12 (permuted_tokens = tokens[permute_indices]); padded expert buffers are zero
 // ([Scratch] §18 drop-and-pad).
 //
-// Pure HBM traffic: one wavefront copies one row with 16-byte accesses (1 KiB per wave
-// instruction), UNROLL loads in flight per lane before the matching stores. Rows whose size is
-// not a multiple of 16 bytes (or unaligned bases) take an element-wise path.
+// Pure HBM traffic. Two forms with identical results:
+//   moe_permute          gather: one wavefront per destination row, 16-byte accesses (1 KiB per
+//                        wave instruction), kUnroll loads in flight per lane. A source row that
+//                        several destinations name is read again for each of them.
+//   moe_permute_scatter  source-major: one workgroup per source row reads it once and writes it
+//                        to all its destinations (the inverse map, e.g. row_of), so x is read
+//                        once instead of K times; zero rows come from the gather map.
+// Rows whose size is not a multiple of 16 bytes (or unaligned bases) take element-wise paths.
 #include "moe_common.h"
 
 namespace moe {
@@ -67,8 +72,140 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
         d[h] = p[h];
 }
 
+// ---------------------------------------------------------------- source-major form
+// One workgroup per source row: the row is read once (kScatterUnroll 16-byte vectors per thread
+// in flight) and written to each of its destinations; the destinations sit in lanes 0..J-1 of
+// every wave and are walked in lane order with readlane, so the loop is uniform. Extra
+// workgroups after the source rows write the zero rows: each wave checks 16 entries of
+// src_row and zero-fills those outside [0, src_rows).
+constexpr int kScatterThreads = 256;
+constexpr int kScatterUnroll = 4;
+constexpr int kZeroRowsPerWave = 16;
+constexpr int kMaxScatterDests = 64;
+
+__global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
+    const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ dst_of, int J,
+    const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row_bytes = nvec * 16;
+    if (static_cast<int64_t>(blockIdx.x) >= src_rows) {
+        // zero rows of the gather map
+        const int64_t first = (static_cast<int64_t>(blockIdx.x) - src_rows) * (kScatterThreads / kWave) * kZeroRowsPerWave +
+                              static_cast<int64_t>(threadIdx.x / kWave) * kZeroRowsPerWave;
+        const int64_t i = first + lane;
+        const bool zero = lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+        uint64_t m = __ballot(zero);
+        const u32x4 z{0u, 0u, 0u, 0u};
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            char *d = dst + (first + j) * row_bytes;
+            for (int64_t v = lane; v < nvec; v += kWave)
+                st16(d + v * 16, z);
+        }
+        return;
+    }
+    const int64_t t = blockIdx.x;
+    const int32_t my = lane < J ? dst_of[t * J + lane] : -1;
+    const uint64_t mask = __ballot(my >= 0 && my < N);
+    if (mask == 0)
+        return;
+    const char *p = src + t * row_bytes;
+    for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += kScatterThreads * kScatterUnroll) {
+        u32x4 r[kScatterUnroll];
+#pragma unroll
+        for (int u = 0; u < kScatterUnroll; ++u) {
+            const int64_t v = v0 + u * kScatterThreads;
+            if (v < nvec)
+                r[u] = ld16(p + v * 16);
+        }
+        uint64_t m = mask;
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            char *q = dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * row_bytes;
+#pragma unroll
+            for (int u = 0; u < kScatterUnroll; ++u) {
+                const int64_t v = v0 + u * kScatterThreads;
+                if (v < nvec)
+                    st16(q + v * 16, r[u]);
+            }
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kScatterThreads) void permute_scatter_elem_kernel(
+    const T *__restrict__ src, int64_t src_rows, int64_t H, const int32_t *__restrict__ dst_of, int J,
+    const int32_t *__restrict__ src_row, int64_t N, T *__restrict__ dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (static_cast<int64_t>(blockIdx.x) >= src_rows) {
+        const int64_t first = (static_cast<int64_t>(blockIdx.x) - src_rows) * (kScatterThreads / kWave) * kZeroRowsPerWave +
+                              static_cast<int64_t>(threadIdx.x / kWave) * kZeroRowsPerWave;
+        const int64_t i = first + lane;
+        const bool zero = lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+        uint64_t m = __ballot(zero);
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            T *d = dst + (first + j) * H;
+            for (int64_t h = lane; h < H; h += kWave)
+                d[h] = T(0);
+        }
+        return;
+    }
+    const int64_t t = blockIdx.x;
+    const int32_t my = lane < J ? dst_of[t * J + lane] : -1;
+    uint64_t m = __ballot(my >= 0 && my < N);
+    const T *p = src + t * H;
+    while (m) {
+        const int j = __builtin_ctzll(m);
+        m &= m - 1;
+        T *q = dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * H;
+        for (int64_t h = threadIdx.x; h < H; h += kScatterThreads)
+            q[h] = p[h];
+    }
+}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
+                                          const int32_t *dst_of, int32_t J, const int32_t *src_row, int64_t N,
+                                          void *dst, hipStream_t stream)
+{
+    using namespace moe;
+    if (src_rows < 0 || H < 1 || N < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16))
+        return MOE_ERR_INVALID;
+    if (J > kMaxScatterDests)
+        return MOE_ERR_UNSUPPORTED;
+    if (N == 0 || (src_rows == 0 && !src_row))
+        return MOE_OK;
+    if (!dst || (src_rows > 0 && (!src || !dst_of)))
+        return MOE_ERR_INVALID;
+    const int64_t zero_blocks = src_row ? ceil_div(N, (kScatterThreads / kWave) * kZeroRowsPerWave) : 0;
+    const int64_t blocks = src_rows + zero_blocks;
+    if (blocks > 0x7fffffff)
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t esz = dt == MOE_F32 ? 4 : 2;
+    const int64_t row_bytes = H * esz;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kScatterThreads);
+    if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
+        hipLaunchKernelGGL(permute_scatter_vec16_kernel, grid, block, 0, stream, static_cast<const char *>(src),
+                           src_rows, row_bytes / 16, dst_of, J, src_row, N, static_cast<char *>(dst));
+    } else if (esz == 4) {
+        hipLaunchKernelGGL(permute_scatter_elem_kernel<uint32_t>, grid, block, 0, stream,
+                           static_cast<const uint32_t *>(src), src_rows, H, dst_of, J, src_row, N,
+                           static_cast<uint32_t *>(dst));
+    } else {
+        hipLaunchKernelGGL(permute_scatter_elem_kernel<uint16_t>, grid, block, 0, stream,
+                           static_cast<const uint16_t *>(src), src_rows, H, dst_of, J, src_row, N,
+                           static_cast<uint16_t *>(dst));
+    }
+    return launch_status();
+}
 
 extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
                                   const int32_t *src_row, int64_t N, void *dst, hipStream_t stream)

@@ -2,101 +2,160 @@
 // ("从零理解 MoE 算子：路由、专家并行与 Token 重排"): topk over router_logits, then softmax of the
 // K selected scores.
 //
-// One wavefront per token. Lane l holds the logits of experts l, l+64, l+128, ... as 64-bit
-// keys (order-preserving image of the float in the high word, ~id in the low word), so that
-// one unsigned max picks the larger logit and, on a tie, the lower id. Each of the K rounds is
-// a wave-wide max (shuffle butterfly); only the winning lane rescans its own keys. The softmax
-// runs in double on lanes 0..K-1 and sums in slot order.
+// gfx950 design: 16 lanes per token, 4 tokens per wavefront. Lane l of a token's 16-lane row
+// holds the logits of experts l, l+16, l+32, ... and keeps the best of its own still-unselected
+// experts. A key orders (logit descending, expert id ascending): high word an order-preserving
+// image of the float, low word ~id. Each of the K rounds is a 16-lane all-reduce of the keys
+// made of four DPP steps (row_mirror, row_half_mirror, quad xor 2, quad xor 1) -- plain VALU
+// instructions, no LDS round trip -- after which only the lane that owned the winner rescans
+// its keys. The softmax runs in double; the K exponentials meet in LDS and every lane sums them
+// in slot order.
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint64_t score_key(float s, int e)
+constexpr int kLanesPerToken = 16;
+constexpr int kRouteThreads = 256;
+constexpr int kTokensPerBlock = kRouteThreads / kLanesPerToken;  // 16
+constexpr int kSlotRegs = (MOE_MAX_TOPK + kLanesPerToken - 1) / kLanesPerToken;  // slots per lane
+
+// DPP controls (gfx9 encoding)
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppQuadXor2 = 0x4e;  // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xb1;  // quad_perm [1,0,3,2]
+
+__device__ __forceinline__ uint32_t orderable(float s)
 {
     if (s == 0.0f)
         s = 0.0f;  // -0 and +0 compare equal: same key, so the lower id wins
-    uint32_t u = __float_as_uint(s);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(0xffffffffu - static_cast<uint32_t>(e));
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // > 0 for every non-NaN float
 }
 
-__device__ __forceinline__ float key_score(uint64_t key)
+__device__ __forceinline__ float from_orderable(uint32_t u)
 {
-    uint32_t u = static_cast<uint32_t>(key >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-    return __uint_as_float(u);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-__device__ __forceinline__ int key_id(uint64_t key)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
 {
-    return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+template <int CTRL>
+__device__ __forceinline__ void max_step(uint32_t &hi, uint32_t &lo)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-        uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-        uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    const uint32_t ohi = dpp<CTRL>(hi);
+    const uint32_t olo = dpp<CTRL>(lo);
+    const bool gt = ohi > hi || (ohi == hi && olo > lo);
+    hi = gt ? ohi : hi;
+    lo = gt ? olo : lo;
 }
 
-template <int NJ>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
-                                                         int E, int K, int32_t *__restrict__ topk_idx,
-                                                         float *__restrict__ topk_w)
+// Largest (hi, lo) of the 16 lanes of this lane's row, in every lane of the row.
+__device__ __forceinline__ void row_max(uint32_t &hi, uint32_t &lo)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
-    if (t >= T)
-        return;  // uniform per wave
+    max_step<kDppRowMirror>(hi, lo);
+    max_step<kDppRowHalfMirror>(hi, lo);
+    max_step<kDppQuadXor2>(hi, lo);
+    max_step<kDppQuadXor1>(hi, lo);
+}
+
+template <int J>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
+                                                                   int E, int K, int32_t *__restrict__ topk_idx,
+                                                                   float *__restrict__ topk_w)
+{
+    __shared__ double ex_sh[kTokensPerBlock][MOE_MAX_TOPK];
+    const int sub = threadIdx.x & (kLanesPerToken - 1);
+    const int tok = threadIdx.x / kLanesPerToken;  // token of this row inside the block
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + tok;
+    const bool live = t < T;  // rows past T take part in the DPP steps with empty keys
     const float *row = logits + t * E;
 
-    uint64_t key[NJ];
+    uint32_t u[J];  // orderable logits of experts sub + 16 j; 0 = absent or already selected
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int e = lane + j * kWave;
-        key[j] = e < E ? score_key(row[e], e) : 0ull;  // 0 is below every real key
+    for (int j = 0; j < J; ++j) {
+        const int e = sub + kLanesPerToken * j;
+        u[j] = (live && e < E) ? orderable(row[e]) : 0u;
     }
-    uint64_t best = 0;
+    // this lane's best: strict > over ascending j keeps the lowest id among equal logits
+    uint32_t bu = 0;
+    int bj = 0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-        best = key[j] > best ? key[j] : best;
+    for (int j = 0; j < J; ++j)
+        if (u[j] > bu) {
+            bu = u[j];
+            bj = j;
+        }
 
-    uint64_t mine = 0;  // lane k keeps the key of slot k
-    float s0 = 0.0f;
+    uint32_t slot_u[kSlotRegs];
+    int slot_e[kSlotRegs];
+#pragma unroll
+    for (int q = 0; q < kSlotRegs; ++q) {
+        slot_u[q] = 0;
+        slot_e[q] = 0;
+    }
+    uint32_t s0u = 0;
     for (int k = 0; k < K; ++k) {
-        const uint64_t win = wave_max_u64(best);
+        uint32_t hi = bu;
+        uint32_t lo = bu ? 0xffffffffu - static_cast<uint32_t>(sub + kLanesPerToken * bj) : 0u;
+        row_max(hi, lo);
+        const int win = static_cast<int>(0xffffffffu - lo);  // winning expert id of this row
         if (k == 0)
-            s0 = key_score(win);
-        if (lane == k)
-            mine = win;
-        if (best == win) {  // exactly one lane: ids are unique
+            s0u = hi;
+        if (sub == (k & (kLanesPerToken - 1))) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                key[j] = key[j] == win ? 0ull : key[j];
-            best = 0;
+            for (int q = 0; q < kSlotRegs; ++q)
+                if (q == k / kLanesPerToken) {
+                    slot_u[q] = hi;
+                    slot_e[q] = win;
+                }
+        }
+        if (hi != 0 && sub == (win & (kLanesPerToken - 1))) {  // the owner drops it and rescans
+            const int wj = win / kLanesPerToken;
+            bu = 0;
+            bj = 0;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                best = key[j] > best ? key[j] : best;
+            for (int j = 0; j < J; ++j) {
+                if (j == wj)
+                    u[j] = 0;
+                if (u[j] > bu) {
+                    bu = u[j];
+                    bj = j;
+                }
+            }
         }
     }
 
-    const bool has = lane < K;
-    double ex = has ? exp(static_cast<double>(key_score(mine)) - static_cast<double>(s0)) : 0.0;
-    double z = 0.0;
-    for (int k = 0; k < K; ++k) {
-        const uint32_t lo = __shfl(static_cast<uint32_t>(__double_as_longlong(ex)), k, kWave);
-        const uint32_t hi = __shfl(static_cast<uint32_t>(__double_as_longlong(ex) >> 32), k, kWave);
-        z += __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+    // softmax over the K selected logits, in double, summed in slot order
+    const double s0 = static_cast<double>(from_orderable(s0u));
+    double ex[kSlotRegs];
+#pragma unroll
+    for (int q = 0; q < kSlotRegs; ++q) {
+        const int k = sub + kLanesPerToken * q;
+        ex[q] = 0.0;
+        if (k < K) {
+            ex[q] = exp(static_cast<double>(from_orderable(slot_u[q])) - s0);
+            ex_sh[tok][k] = ex[q];
+        }
     }
-    if (has) {
-        topk_idx[t * K + lane] = key_id(mine);
-        topk_w[t * K + lane] = static_cast<float>(ex / z);
+    __builtin_amdgcn_wave_barrier();
+    double z = 0.0;
+    for (int k = 0; k < K; ++k)
+        z += ex_sh[tok][k];
+    if (live) {
+#pragma unroll
+        for (int q = 0; q < kSlotRegs; ++q) {
+            const int k = sub + kLanesPerToken * q;
+            if (k < K) {
+                topk_idx[t * K + k] = slot_e[q];
+                topk_w[t * K + k] = static_cast<float>(ex[q] / z);
+            }
+        }
     }
 }
 
@@ -115,13 +174,11 @@ extern "C" moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, 
         return MOE_OK;
     if (!logits || !topk_idx || !topk_w)
         return MOE_ERR_INVALID;
-    constexpr int kThreads = 256;
-    constexpr int kTokensPerBlock = kThreads / kWave;
     const int64_t blocks = ceil_div(T, kTokensPerBlock);
     if (blocks > 0x7fffffff)
         return MOE_ERR_UNSUPPORTED;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-    const int nj = static_cast<int>(ceil_div(E, kWave));
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kRouteThreads);
+    const int nj = static_cast<int>(ceil_div(E, kLanesPerToken));
     if (nj <= 1)
         hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
     else if (nj <= 2)
@@ -130,7 +187,11 @@ extern "C" moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, 
         hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
     else if (nj <= 8)
         hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
-    else
+    else if (nj <= 16)
         hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+    else if (nj <= 32)
+        hipLaunchKernelGGL(route_topk_kernel<32>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+    else
+        hipLaunchKernelGGL(route_topk_kernel<64>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
     return launch_status();
 }

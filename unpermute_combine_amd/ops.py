@@ -173,6 +173,32 @@ def permute(src: torch.Tensor, src_row: torch.Tensor, out: Optional[torch.Tensor
     return out
 
 
+def permute_scatter(src: torch.Tensor, dst_of: torch.Tensor, num_rows: int,
+                    src_row: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Source-major permute: out[dst_of[t, j]] = src[t]; rows with src_row[i] out of range are zeros.
+
+    With dst_of = index.row_of and src_row = index.sorted_indices this equals
+    permute(src, index.sorted_indices), reading every source row once."""
+    _need(src, "src", None, 2)
+    dt = _hidden_dt(src, "src")
+    _need(dst_of, "dst_of", torch.int32, 2)
+    if dst_of.shape[0] != src.shape[0]:
+        raise ValueError("dst_of must have one row per source row")
+    if src_row is not None:
+        _need(src_row, "src_row", torch.int32, 1)
+        if src_row.shape[0] != num_rows:
+            raise ValueError("src_row must have num_rows entries")
+    H = src.shape[1]
+    if out is None:
+        out = torch.empty((num_rows, H), dtype=src.dtype, device=src.device)
+    _need(out, "out", src.dtype, 2)
+    if tuple(out.shape) != (num_rows, H):
+        raise ValueError(f"out must be [{num_rows}, {H}]")
+    check("moe_permute_scatter", lib().moe_permute_scatter(
+        _p(src), src.shape[0], H, dt, _p(dst_of), dst_of.shape[1], _p(src_row), num_rows, _p(out), _stream()))
+    return out
+
+
 def unpermute_combine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[torch.Tensor] = None,
                       out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[t] = sum_k weights[t,k] * y[row_of[t,k]] (float32 FMA chain in k order)."""
