@@ -10,8 +10,9 @@
 // every thread owns 8 consecutive hidden elements at a time, issues the 16-byte loads of all
 // the token's rows before the fused multiply-adds (which run in slot order, float32, from +0),
 // and writes 8 outputs with one 16-byte (bf16) or two (float32) stores. Each y row is read once
-// and each out row written once, both with nontemporal hints (streamed data: no reuse to keep
-// in L2 / MALL, which measurably raises the read rate on MI355X).
+// and each out row written once, both with streaming cache policies (no reuse to keep in L2 /
+// MALL, which measurably raises the read rate on MI355X); y rows are read through buffer
+// resources, which give the sc0|nt policy and a hardware bounds check.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -24,32 +25,47 @@ constexpr int kMaxThreads = 1024;  // largest workgroup block_threads() picks
 constexpr int kBatch = 8;  // rows whose loads are issued together
 
 // ---------------------------------------------------------------- 8-element vector access
+// Raw 16-byte vectors of one 8-element chunk: one for bf16, two for float32.
 template <typename Y>
-struct Vec8Load;
+struct Chunk;
 
 template <>
-struct Vec8Load<uint16_t> {  // bf16: one 16-byte load
-    __device__ static void load(const uint16_t *p, float (&v)[8])
+struct Chunk<uint16_t> {
+    static constexpr int kVecs = 1;
+    __device__ static void widen(const u32x4 (&q)[1], float (&v)[8])
     {
-        const u32x4 q = ld16_stream(p);
-        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
-        v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
-        v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+        v[0] = bf16_lo(q[0].x); v[1] = bf16_hi(q[0].x);
+        v[2] = bf16_lo(q[0].y); v[3] = bf16_hi(q[0].y);
+        v[4] = bf16_lo(q[0].z); v[5] = bf16_hi(q[0].z);
+        v[6] = bf16_lo(q[0].w); v[7] = bf16_hi(q[0].w);
     }
 };
 
 template <>
-struct Vec8Load<float> {  // float32: two 16-byte loads
-    __device__ static void load(const float *p, float (&v)[8])
+struct Chunk<float> {
+    static constexpr int kVecs = 2;
+    __device__ static void widen(const u32x4 (&q)[2], float (&v)[8])
     {
-        const u32x4 a = ld16_stream(p), b = ld16_stream(p + 4);
-        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
-        v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-        v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
-        v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+        v[0] = __uint_as_float(q[0].x); v[1] = __uint_as_float(q[0].y);
+        v[2] = __uint_as_float(q[0].z); v[3] = __uint_as_float(q[0].w);
+        v[4] = __uint_as_float(q[1].x); v[5] = __uint_as_float(q[1].y);
+        v[6] = __uint_as_float(q[1].z); v[7] = __uint_as_float(q[1].w);
     }
 };
+
+// Loads chunk `col8` (8 elements) of row `row` of y; a negative row gives zeros without a
+// memory access (a zero-size buffer resource).
+template <typename Y>
+__device__ __forceinline__ void load_chunk(const Y *__restrict__ y, int64_t H, int32_t row, int64_t col8,
+                                           u32x4 (&q)[Chunk<Y>::kVecs])
+{
+    const uint32_t row_bytes = static_cast<uint32_t>(H * sizeof(Y));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(y + static_cast<int64_t>(row < 0 ? 0 : row) * H, row < 0 ? 0u : row_bytes);
+    const uint32_t off = static_cast<uint32_t>(col8 * 8 * sizeof(Y));
+#pragma unroll
+    for (int i = 0; i < Chunk<Y>::kVecs; ++i)
+        q[i] = ld16_buf<kPolicyStreamLoad>(r, off + 16 * i);
+}
 
 __device__ __forceinline__ void store8(uint16_t *p, const float (&a)[8])
 {
@@ -68,33 +84,39 @@ __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ void store1(uint16_t *p, float a) { *p = static_cast<uint16_t>(f32_to_bf16_bits(a)); }
 __device__ __forceinline__ void store1(float *p, float a) { *p = a; }
 
-// acc = fma(w, y[rows[j]], acc) for j = 0..n-1 in order, 8 elements at column c8*8.
-template <typename Y, bool VEC>
-__device__ __forceinline__ void accumulate(const Y *__restrict__ y, int64_t H, const int32_t *rows,
-                                           const float *ws, int n, int64_t col, float (&acc)[8])
+// One batch of up to kBatch terms, acc = fma(w[u], y[row[u]], acc) in order u = 0, 1, ...; a
+// negative row is an absent term: it loads nothing (zero-size resource) and its FMA result is
+// discarded, so no branch splits the batch and all its loads are in flight before the first FMA.
+template <typename Y>
+__device__ __forceinline__ void fma_batch(const Y *__restrict__ y, int64_t H, const int32_t (&row)[kBatch],
+                                          const float (&w)[kBatch], int64_t col8, float (&acc)[8])
 {
-    for (int j0 = 0; j0 < n; j0 += kBatch) {
-        float v[kBatch][8];
+    u32x4 q[kBatch][Chunk<Y>::kVecs];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            if (j0 + u < n) {
-                const Y *p = y + static_cast<int64_t>(rows[j0 + u]) * H + col;
-                if constexpr (VEC) {
-                    Vec8Load<Y>::load(p, v[u]);
-                } else {
-                    v[u][0] = load1(p);
-                }
-            }
+    for (int u = 0; u < kBatch; ++u)
+        load_chunk<Y>(y, H, row[u], col8, q[u]);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const bool live = row[u] >= 0;
+        float v[8];
+        Chunk<Y>::widen(q[u], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r = __builtin_fmaf(w[u], v[e], acc[e]);
+            acc[e] = live ? r : acc[e];
         }
+    }
+}
+
+// Terms j0 .. j0+kBatch-1 of the compacted list (LDS) into registers; uniform across the block.
+__device__ __forceinline__ void batch_terms(const int32_t *rows, const float *ws, int n, int j0,
+                                            int32_t (&row)[kBatch], float (&w)[kBatch])
+{
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            if (j0 + u < n) {
-                const float w = ws[j0 + u];
-#pragma unroll
-                for (int q = 0; q < (VEC ? 8 : 1); ++q)
-                    acc[q] = __builtin_fmaf(w, v[u][q], acc[q]);
-            }
-        }
+    for (int u = 0; u < kBatch; ++u) {
+        const bool live = j0 + u < n;
+        row[u] = live ? __builtin_amdgcn_readfirstlane(rows[j0 + u]) : -1;
+        w[u] = live ? ws[j0 + u] : 0.0f;
     }
 }
 
@@ -136,16 +158,29 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
         compact_rows(row_of + t * K, w ? w + t * K : nullptr, K, y_rows, rows, ws, &n_sh);
     __syncthreads();
     const int n = n_sh;
-    constexpr int kE = VEC ? 8 : 1;
-    const int64_t nchunk = H / kE;
     O *o = out + t * H;
-    for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        accumulate<Y, VEC>(y, H, rows, ws, n, c * kE, acc);
-        if constexpr (VEC)
-            store8(o + c * kE, acc);
-        else
-            store1(o + c, acc[0]);
+    if constexpr (VEC) {
+        int32_t row0[kBatch];  // the first batch of terms stays in registers for every chunk
+        float w0[kBatch];
+        batch_terms(rows, ws, n, 0, row0, w0);
+        for (int64_t c = threadIdx.x; c < H / 8; c += blockDim.x) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            fma_batch<Y>(y, H, row0, w0, c, acc);
+            for (int j0 = kBatch; j0 < n; j0 += kBatch) {
+                int32_t row[kBatch];
+                float w[kBatch];
+                batch_terms(rows, ws, n, j0, row, w);
+                fma_batch<Y>(y, H, row, w, c, acc);
+            }
+            store8(o + c * 8, acc);
+        }
+    } else {
+        for (int64_t h = threadIdx.x; h < H; h += blockDim.x) {
+            float acc = 0.0f;
+            for (int j = 0; j < n; ++j)
+                acc = __builtin_fmaf(ws[j], load1(y + static_cast<int64_t>(rows[j]) * H + h), acc);
+            store1(o + h, acc);
+        }
     }
 }
 
@@ -202,23 +237,23 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
         for (int64_t c = tid; c < nchunk; c += blockDim.x) {
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < K; k0 += kBatch) {
-                float v[kBatch][8];
+                if constexpr (VEC) {
+                    int32_t row[kBatch];
+                    float w[kBatch];
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    if (k0 + u < K && grp[k0 + u] == g) {
-                        const Y *p = y + static_cast<int64_t>(rows[k0 + u]) * H + c * kE;
-                        if constexpr (VEC)
-                            Vec8Load<Y>::load(p, v[u]);
-                        else
-                            v[u][0] = load1(p);
+                    for (int u = 0; u < kBatch; ++u) {
+                        const bool member = k0 + u < K && grp[k0 + u] == g;
+                        row[u] = member ? __builtin_amdgcn_readfirstlane(rows[k0 + u]) : -1;
+                        w[u] = member ? ws[k0 + u] : 0.0f;
                     }
-                }
+                    fma_batch<Y>(y, H, row, w, c, acc);
+                } else {
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    if (k0 + u < K && grp[k0 + u] == g) {
-#pragma unroll
-                        for (int q = 0; q < kE; ++q)
-                            acc[q] = __builtin_fmaf(ws[k0 + u], v[u][q], acc[q]);
+                    for (int u = 0; u < kBatch; ++u) {
+                        const bool member = k0 + u < K && grp[k0 + u] == g;
+                        const float v = member ? load1(y + static_cast<int64_t>(rows[k0 + u]) * H + c) : 0.0f;
+                        const float r = __builtin_fmaf(member ? ws[k0 + u] : 0.0f, v, acc[0]);
+                        acc[0] = member ? r : acc[0];
                     }
                 }
             }

@@ -10,7 +10,8 @@
 //   moe_permute_scatter  source-major: one workgroup per source row reads it once and writes it
 //                        to all its destinations (the inverse map, e.g. row_of), so x is read
 //                        once instead of K times; zero rows come from the gather map.
-// Rows whose size is not a multiple of 16 bytes (or unaligned bases) take element-wise paths.
+// Destination rows are written with agent-scope streaming stores (see kPolicyStreamStore). Rows
+// whose size is not a multiple of 16 bytes (or unaligned bases) take element-wise paths.
 #include "moe_common.h"
 
 namespace moe {
@@ -24,16 +25,17 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_vec16_kernel(
     int64_t N, char *__restrict__ dst)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x / kWave);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock +
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     if (i >= N)
         return;
     const int32_t s = src_row[i];
     const int64_t row_bytes = nvec * 16;
-    char *d = dst + i * row_bytes;
+    const __amdgpu_buffer_rsrc_t d = make_rsrc(dst + i * row_bytes, static_cast<uint32_t>(row_bytes));
     if (s < 0 || s >= src_rows) {
         const u32x4 z{0u, 0u, 0u, 0u};
         for (int64_t v = lane; v < nvec; v += kWave)
-            st16(d + v * 16, z);
+            st16_buf<kPolicyStreamStore>(d, static_cast<uint32_t>(v * 16), z);
         return;
     }
     const char *p = src + static_cast<int64_t>(s) * row_bytes;
@@ -45,10 +47,10 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_vec16_kernel(
             r[u] = ld16(p + (v + u * kWave) * 16);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            st16(d + (v + u * kWave) * 16, r[u]);
+            st16_buf<kPolicyStreamStore>(d, static_cast<uint32_t>((v + u * kWave) * 16), r[u]);
     }
     for (; v < nvec; v += kWave)
-        st16(d + v * 16, ld16(p + v * 16));
+        st16_buf<kPolicyStreamStore>(d, static_cast<uint32_t>(v * 16), ld16(p + v * 16));
 }
 
 template <typename T>
@@ -92,7 +94,8 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     if (static_cast<int64_t>(blockIdx.x) >= src_rows) {
         // zero rows of the gather map
         const int64_t first = (static_cast<int64_t>(blockIdx.x) - src_rows) * (kScatterThreads / kWave) * kZeroRowsPerWave +
-                              static_cast<int64_t>(threadIdx.x / kWave) * kZeroRowsPerWave;
+                              static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave))) *
+                                  kZeroRowsPerWave;
         const int64_t i = first + lane;
         const bool zero = lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
         uint64_t m = __ballot(zero);
@@ -100,9 +103,9 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
         while (m) {
             const int j = __builtin_ctzll(m);
             m &= m - 1;
-            char *d = dst + (first + j) * row_bytes;
+            const __amdgpu_buffer_rsrc_t d = make_rsrc(dst + (first + j) * row_bytes, static_cast<uint32_t>(row_bytes));
             for (int64_t v = lane; v < nvec; v += kWave)
-                st16(d + v * 16, z);
+                st16_buf<kPolicyStreamStore>(d, static_cast<uint32_t>(v * 16), z);
         }
         return;
     }
@@ -124,12 +127,13 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
         while (m) {
             const int j = __builtin_ctzll(m);
             m &= m - 1;
-            char *q = dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * row_bytes;
+            const __amdgpu_buffer_rsrc_t q = make_rsrc(
+                dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * row_bytes, static_cast<uint32_t>(row_bytes));
 #pragma unroll
             for (int u = 0; u < kScatterUnroll; ++u) {
                 const int64_t v = v0 + u * kScatterThreads;
                 if (v < nvec)
-                    st16(q + v * 16, r[u]);
+                    st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r[u]);
             }
         }
     }
