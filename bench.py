@@ -155,17 +155,18 @@ def main():
         mark(1)
         m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix)
         mark(2)
+        # group mode: the number of group slots is only known on the device; every call below
+        # is bounded by its upper bound T*min(K,G) instead, so the step never waits for the host
         if gs:
-            n = int(ix.n_slots.item())  # the group count is only known on the device
-            m.permute_scatter(x, ix.slot_of, n, out=gbuf[:n])
-            m.permute(gbuf[:n], ix.esrc, out=xp)
+            m.permute_scatter(x, ix.slot_of, gbuf.shape[0], out=gbuf)
+            m.permute(gbuf, ix.esrc, out=xp)
         else:
             m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=xp)
         mark(3)
         src = xp if y is None else y
         if gs:
-            m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part[:n])
-            m.unpermute_combine(part[:n], ix.slot_of, None, out=out)
+            m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)
+            m.unpermute_combine(part, ix.slot_of, None, out=out)
         else:
             m.unpermute_combine(src, ix.row_of, gw, out=out)
         mark(4)

@@ -18,11 +18,13 @@
 //   2. scan   one workgroup: lanes own 4 consecutive keys, wavefronts own ranges of tiles; the
 //             per-wave partial sums meet in LDS, giving each (tile, key) its first row inside
 //             the key; a block scan over the key totals gives each key's first row. Also
-//             counts, group_list, capacity bookkeeping, padding and unused rows.
-//   3. rank   one wavefront per tile walks its slots 64 at a time in slot order. Lanes with
-//             the same key find each other with one ballot per key bit (a match-any built from
-//             ballots); their stable rank is popcount(peers & lanes_below) and the last peer
-//             advances the key's running row counter in LDS.
+//             counts, group_list and the capacity bookkeeping.
+//   3. rank   one workgroup per tile, its tokens split over 4 wavefronts (per-wave counts and
+//             a prefix over the waves in LDS); each wavefront walks its slots 64 at a time in
+//             slot order. Lanes with the same key find each other with one ballot per key bit
+//             (a match-any built from ballots); their stable rank is popcount(peers &
+//             lanes_below) and the last peer advances the key's running row counter in LDS.
+//             The workgroups then write the padding or unused rows together.
 //   4. esrc   (group mode) expert-major row -> group slot.
 // The drop-and-pad capacity rule ([Scratch] §18, §26.6) and the group (send once per rank)
 // slots ([CANN] §1(1)) are applied inside the same passes.
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(IndexArgs a)
     __shared__ ScanShared sh;
     const int tid = threadIdx.x;
     const int64_t R = a.cap > 0 ? static_cast<int64_t>(a.E) * a.cap : a.T * a.K;
-    const int32_t total = scan_tiles(a.hist_e, a.E, a.Ep, a.ntiles, sh);
+    scan_tiles(a.hist_e, a.E, a.Ep, a.ntiles, sh);
     for (int e = tid; e < a.E; e += kScanThreads) {
         const int32_t cnt = sh.tot[e];
         const int32_t start = sh.seg[e];
@@ -235,25 +237,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(IndexArgs a)
         if (a.ix.kept_counts)
             a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
     }
-    if (a.cap > 0) {
-        // padding rows of every expert: p >= min(count, cap)
+    if (a.ntiles == 0 && a.cap > 0) {
+        // no tokens: every row of every expert is padding (otherwise the rank kernel writes it)
         for (int64_t r = tid; r < R; r += kScanThreads) {
-            const int e = static_cast<int>(r / a.cap);
-            const int p = static_cast<int>(r - static_cast<int64_t>(e) * a.cap);
-            if (p >= min(sh.tot[e], a.cap)) {
-                a.ix.sorted_indices[r] = -1;
-                if (a.ix.permuted_probs)
-                    a.ix.permuted_probs[r] = 0.0f;
-            }
-        }
-    } else {
-        // rows after the last routed slot are unused
-        for (int64_t r = total + tid; r < R; r += kScanThreads) {
             a.ix.sorted_indices[r] = -1;
             if (a.ix.permuted_probs)
                 a.ix.permuted_probs[r] = 0.0f;
-            if (a.gs > 0)
-                a.ix.esrc[r] = -1;
         }
     }
     if (a.gs > 0) {
@@ -283,42 +272,145 @@ __device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t acti
 
 __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(m); }
 
-__global__ __launch_bounds__(kWave) void rank_kernel(IndexArgs a)
+constexpr int kRankWaves = 4;  // a tile's tokens are split across 4 wavefronts
+constexpr int kRankThreads = kRankWaves * kWave;
+constexpr int kSpan = kRankBatch * kWave;  // slots whose loads a wavefront issues together
+
+// True when slot i = (t, k) is the first of token t's slots in group g. The token's earlier
+// slots are in `ids` (the current batch, starting at slot base0) or, when the token straddles
+// the batch start, just before it.
+__device__ __forceinline__ bool first_in_group(const IndexArgs &a, int64_t i, int k, int g, int64_t base0,
+                                               const int32_t *ids)
+{
+    bool lead = true;
+    for (int j = 1; j <= k; ++j) {
+        const int64_t q = i - j;
+        const int ej = q >= base0 ? ids[q - base0] : a.topk_idx[q];
+        if (valid_expert(ej, a.E) && ej / a.gs == g)
+            lead = false;
+    }
+    return lead;
+}
+
+__device__ __forceinline__ void load_batch(const IndexArgs &a, int64_t base0, int64_t s1, bool want_w,
+                                           int (&e)[kRankBatch], float (&w)[kRankBatch])
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) {
+        const int64_t i = base0 + b * kWave + lane;
+        e[b] = i < s1 ? a.topk_idx[i] : -1;
+        w[b] = want_w && i < s1 ? a.topk_w[i] : 1.0f;
+    }
+}
+
+// One workgroup per tile, kRankWaves wavefronts, each owning a contiguous quarter of the tile's
+// tokens (whole tokens). Phase A: every wave counts its slots per expert (and its first-in-group
+// slots per group) in LDS. Phase B: per key, a prefix over the waves starting at the tile's
+// first row of the key. Phase C: every wave walks its slots in order, 64 at a time, and ranks
+// them against its own running counters. Finally the workgroups together write the padding
+// (drop-and-pad) or unused rows.
+__global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
-    int32_t *run_e = sh;           // [E] next row of each expert in this tile
-    int32_t *seg_e = run_e + a.E;  // [E] first row of each expert
-    int32_t *run_g = seg_e + a.E;  // [G] next slot of each group in this tile
-    int32_t *ids = run_g + a.G;    // [kRankBatch * 64] expert ids of the current batch
+    int32_t *cnt_e = sh;                        // [kRankWaves][E] counts -> next row of the wave
+    int32_t *cnt_g = cnt_e + kRankWaves * a.E;  // [kRankWaves][G]
+    int32_t *seg_e = cnt_g + kRankWaves * a.G;  // [E] first row of each expert
+    int32_t *ids_all = seg_e + a.E;             // [kRankWaves][kSpan] expert ids of each wave's batch
     const int tile = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int32_t *hrow = a.hist_e + static_cast<int64_t>(tile) * a.Ep;
-    for (int e = lane; e < a.E; e += kWave) {
-        const int32_t s = a.seg_e[e];
-        seg_e[e] = s;
-        run_e[e] = s + hrow[e];
-    }
-    if (a.gs > 0) {
-        const int32_t *hrowg = a.hist_g + static_cast<int64_t>(tile) * a.Gp;
-        for (int g = lane; g < a.G; g += kWave)
-            run_g[g] = a.seg_g[g] + hrowg[g];
-    }
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    int32_t *cw_e = cnt_e + wave * a.E;
+    int32_t *cw_g = cnt_g + wave * a.G;
+    int32_t *ids = ids_all + wave * kSpan;
+    for (int i = tid; i < kRankWaves * (a.E + a.G); i += kRankThreads)
+        sh[i] = 0;
+    for (int e = tid; e < a.E; e += kRankThreads)
+        seg_e[e] = a.seg_e[e];
 
-    const int64_t t0 = static_cast<int64_t>(tile) * a.tile_tokens;
-    const int64_t t1 = min(a.T, t0 + a.tile_tokens);
+    // this wave's tokens and slots
+    const int64_t tile_t0 = static_cast<int64_t>(tile) * a.tile_tokens;
+    const int64_t tile_t1 = min(a.T, tile_t0 + a.tile_tokens);
+    const int64_t per = (a.tile_tokens + kRankWaves - 1) / kRankWaves;
+    const int64_t t0 = min(tile_t1, tile_t0 + wave * per);
+    const int64_t t1 = min(tile_t1, t0 + per);
     const int64_t s0 = t0 * a.K, s1 = t1 * a.K;
-    const uint64_t below = lanemask_lt();
     const bool want_w = a.ix.permuted_probs && a.topk_w;
-    constexpr int kSpan = kRankBatch * kWave;
-    // the loads of a batch of 8 x 64 slots are issued together, and before the previous
-    // batch's stores
+    int e_first[kRankBatch];
+    float w_first[kRankBatch];
+    load_batch(a, s0, s1, want_w, e_first, w_first);
+    __syncthreads();
+
+    // ---- phase A: per-wave counts
+    for (int64_t base0 = s0; base0 < s1; base0 += kSpan) {
+        int e_b[kRankBatch];
+        float w_b[kRankBatch];
+        if (base0 == s0) {
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                e_b[b] = e_first[b];
+        } else {
+            load_batch(a, base0, s1, false, e_b, w_b);
+        }
+        if (a.gs > 0) {
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b)
+                ids[b * kWave + lane] = e_b[b];
+            __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b) {
+            const int64_t i = base0 + b * kWave + lane;
+            const int e = e_b[b];
+            if (i >= s1 || !valid_expert(e, a.E))
+                continue;
+            atomicAdd(&cw_e[e], 1);
+            if (a.gs > 0) {
+                const int64_t t = i / a.K;
+                const int k = static_cast<int>(i - t * a.K);
+                const int g = e / a.gs;
+                if (first_in_group(a, i, k, g, base0, ids))
+                    atomicAdd(&cw_g[g], 1);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+
+    // ---- phase B: each wave's first row per key
+    {
+        const int32_t *hrow = a.hist_e + static_cast<int64_t>(tile) * a.Ep;
+        for (int e = tid; e < a.E; e += kRankThreads) {
+            int32_t run = seg_e[e] + hrow[e];
+            for (int w = 0; w < kRankWaves; ++w) {
+                const int32_t c = cnt_e[w * a.E + e];
+                cnt_e[w * a.E + e] = run;
+                run += c;
+            }
+        }
+        if (a.gs > 0) {
+            const int32_t *hrowg = a.hist_g + static_cast<int64_t>(tile) * a.Gp;
+            for (int g = tid; g < a.G; g += kRankThreads) {
+                int32_t run = a.seg_g[g] + hrowg[g];
+                for (int w = 0; w < kRankWaves; ++w) {
+                    const int32_t c = cnt_g[w * a.G + g];
+                    cnt_g[w * a.G + g] = run;
+                    run += c;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase C: stable ranks
+    const uint64_t below = lanemask_lt();
     int e_nx[kRankBatch];
     float w_nx[kRankBatch];
 #pragma unroll
     for (int b = 0; b < kRankBatch; ++b) {
-        const int64_t i = s0 + b * kWave + lane;
-        e_nx[b] = i < s1 ? a.topk_idx[i] : -1;
-        w_nx[b] = want_w && i < s1 ? a.topk_w[i] : 1.0f;
+        e_nx[b] = e_first[b];
+        w_nx[b] = w_first[b];
     }
     for (int64_t base0 = s0; base0 < s1; base0 += kSpan) {
         int e_cur[kRankBatch];
@@ -328,15 +420,9 @@ __global__ __launch_bounds__(kWave) void rank_kernel(IndexArgs a)
             e_cur[b] = e_nx[b];
             w_cur[b] = w_nx[b];
         }
-        if (base0 + kSpan < s1) {
-#pragma unroll
-            for (int b = 0; b < kRankBatch; ++b) {
-                const int64_t i = base0 + kSpan + b * kWave + lane;
-                e_nx[b] = i < s1 ? a.topk_idx[i] : -1;
-                w_nx[b] = want_w && i < s1 ? a.topk_w[i] : 1.0f;
-            }
-        }
-        if (a.gs > 0) {  // the batch's ids, for the first-slot-in-group test
+        if (base0 + kSpan < s1)  // next batch in flight, issued before this batch's stores
+            load_batch(a, base0 + kSpan, s1, want_w, e_nx, w_nx);
+        if (a.gs > 0) {
 #pragma unroll
             for (int b = 0; b < kRankBatch; ++b)
                 ids[b * kWave + lane] = e_cur[b];
@@ -353,11 +439,11 @@ __global__ __launch_bounds__(kWave) void rank_kernel(IndexArgs a)
             const int64_t t = i / a.K;
             const int k = static_cast<int>(i - t * a.K);
 
-            // ---- expert-major row
+            // expert-major row
             const uint64_t pe = match_peers(e, a.ebits, __ballot(ok));
             int32_t row = -1;
             if (ok) {
-                const int32_t r = run_e[e] + __popcll(pe & below);
+                const int32_t r = cw_e[e] + __popcll(pe & below);
                 row = r;
                 if (a.cap > 0) {
                     const int32_t p = r - seg_e[e];  // position inside the expert
@@ -366,7 +452,7 @@ __global__ __launch_bounds__(kWave) void rank_kernel(IndexArgs a)
             }
             __builtin_amdgcn_wave_barrier();
             if (ok && lane == last_lane(pe))
-                run_e[e] += __popcll(pe);
+                cw_e[e] += __popcll(pe);
             if (in)
                 a.ix.row_of[i] = row;
             if (row >= 0) {
@@ -375,28 +461,17 @@ __global__ __launch_bounds__(kWave) void rank_kernel(IndexArgs a)
                     a.ix.permuted_probs[row] = w_cur[b];
             }
 
-            // ---- group slots: one per (token, group), listed group by group, tokens ascending
+            // group slots: one per (token, group), listed group by group, tokens ascending
             if (a.gs > 0) {
                 const int g = ok ? e / a.gs : -1;
-                bool lead = ok;
-                if (ok) {
-                    // earlier slots of the token: in this batch (LDS), or -- only when K does
-                    // not divide the batch size -- just before it
-                    const int64_t first = i - k;
-                    for (int j = 0; j < k; ++j) {
-                        const int64_t q = first + j;
-                        const int ej = q >= base0 ? ids[q - base0] : a.topk_idx[q];
-                        if (valid_expert(ej, a.E) && ej / a.gs == g)
-                            lead = false;
-                    }
-                }
+                const bool lead = ok && first_in_group(a, i, k, g, base0, ids);
                 const uint64_t pg = match_peers(g, a.gbits, __ballot(lead));
                 int32_t slot = -1;
                 if (lead)
-                    slot = run_g[g] + __popcll(pg & below);
+                    slot = cw_g[g] + __popcll(pg & below);
                 __builtin_amdgcn_wave_barrier();
                 if (lead && lane == last_lane(pg))
-                    run_g[g] += __popcll(pg);
+                    cw_g[g] += __popcll(pg);
                 if (lead) {
                     a.ix.slot_of[t * a.G + g] = slot;
                     a.ix.gsrc[slot] = static_cast<int32_t>(t);
@@ -405,6 +480,35 @@ __global__ __launch_bounds__(kWave) void rank_kernel(IndexArgs a)
             __builtin_amdgcn_wave_barrier();
         }
         __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- padding rows (drop-and-pad) or rows after the last routed slot
+    __syncthreads();
+    int32_t *cnt = cnt_e;  // reused: per-expert counts
+    for (int e = tid; e < a.E; e += kRankThreads)
+        cnt[e] = a.ix.counts[e];
+    __syncthreads();
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kRankThreads;
+    if (a.cap > 0) {
+        const int64_t R = static_cast<int64_t>(a.E) * a.cap;
+        for (int64_t r = static_cast<int64_t>(tile) * kRankThreads + tid; r < R; r += stride) {
+            const int e = static_cast<int>(r / a.cap);
+            const int p = static_cast<int>(r - static_cast<int64_t>(e) * a.cap);
+            if (p >= min(cnt[e], a.cap)) {
+                a.ix.sorted_indices[r] = -1;
+                if (a.ix.permuted_probs)
+                    a.ix.permuted_probs[r] = 0.0f;
+            }
+        }
+    } else {
+        const int64_t total = static_cast<int64_t>(seg_e[a.E - 1]) + cnt[a.E - 1];
+        for (int64_t r = total + static_cast<int64_t>(tile) * kRankThreads + tid; r < a.T * a.K; r += stride) {
+            a.ix.sorted_indices[r] = -1;
+            if (a.ix.permuted_probs)
+                a.ix.permuted_probs[r] = 0.0f;
+            if (a.gs > 0)
+                a.ix.esrc[r] = -1;
+        }
     }
 }
 
@@ -551,8 +655,9 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
-    const size_t lds_rank = sizeof(int32_t) * (2 * static_cast<size_t>(E) + G + kRankBatch * kWave);
-    hipLaunchKernelGGL(rank_kernel, dim3(p.ntiles), dim3(kWave), lds_rank, stream, a);
+    const size_t lds_rank =
+        sizeof(int32_t) * (static_cast<size_t>(kRankWaves) * (E + G) + E + static_cast<size_t>(kRankWaves) * kSpan);
+    hipLaunchKernelGGL(rank_kernel, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
     if (G > 0) {

@@ -22,7 +22,8 @@ namespace {
 
 constexpr int kMaxCombineK = 1024;
 constexpr int kMaxThreads = 1024;  // largest workgroup block_threads() picks
-constexpr int kBatch = 8;  // rows whose loads are issued together
+constexpr int kBatch = 8;     // rows whose loads are issued together
+constexpr int kFewTerms = 4;  // tokens with at most this many terms take the two-chunk path
 
 // ---------------------------------------------------------------- 8-element vector access
 // Raw 16-byte vectors of one 8-element chunk: one for bf16, two for float32.
@@ -108,6 +109,36 @@ __device__ __forceinline__ void fma_batch(const Y *__restrict__ y, int64_t H, co
     }
 }
 
+// Two chunks (c, c2) of the same (at most kFewTerms) terms with all their loads in flight before
+// the first FMA; row1 marks the terms of chunk c2 (negative: nothing to load).
+template <typename Y>
+__device__ __forceinline__ void fma_few2(const Y *__restrict__ y, int64_t H, const int32_t (&row)[kBatch],
+                                         const int32_t (&row1)[kBatch], const float (&w)[kBatch], int64_t c,
+                                         int64_t c2, float (&acc)[8], float (&acc2)[8])
+{
+    u32x4 q[kFewTerms][Chunk<Y>::kVecs];
+    u32x4 q2[kFewTerms][Chunk<Y>::kVecs];
+#pragma unroll
+    for (int u = 0; u < kFewTerms; ++u) {
+        load_chunk<Y>(y, H, row[u], c, q[u]);
+        load_chunk<Y>(y, H, row1[u], c2, q2[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kFewTerms; ++u) {
+        const bool live = row[u] >= 0;
+        float v[8], v2[8];
+        Chunk<Y>::widen(q[u], v);
+        Chunk<Y>::widen(q2[u], v2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r = __builtin_fmaf(w[u], v[e], acc[e]);
+            acc[e] = live ? r : acc[e];
+            const float r2 = __builtin_fmaf(w[u], v2[e], acc2[e]);
+            acc2[e] = live ? r2 : acc2[e];
+        }
+    }
+}
+
 // Terms j0 .. j0+kBatch-1 of the compacted list (LDS) into registers; uniform across the block.
 __device__ __forceinline__ void batch_terms(const int32_t *rows, const float *ws, int n, int j0,
                                             int32_t (&row)[kBatch], float (&w)[kBatch])
@@ -163,16 +194,37 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
         int32_t row0[kBatch];  // the first batch of terms stays in registers for every chunk
         float w0[kBatch];
         batch_terms(rows, ws, n, 0, row0, w0);
-        for (int64_t c = threadIdx.x; c < H / 8; c += blockDim.x) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            fma_batch<Y>(y, H, row0, w0, c, acc);
-            for (int j0 = kBatch; j0 < n; j0 += kBatch) {
-                int32_t row[kBatch];
-                float w[kBatch];
-                batch_terms(rows, ws, n, j0, row, w);
-                fma_batch<Y>(y, H, row, w, c, acc);
+        const int64_t nchunk = H / 8;
+        if (n > kFewTerms) {
+            // many terms: one chunk per thread, the token's rows read whole and at once
+            for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
+                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                fma_batch<Y>(y, H, row0, w0, c, acc);
+                for (int j0 = kBatch; j0 < n; j0 += kBatch) {
+                    int32_t row[kBatch];
+                    float w[kBatch];
+                    batch_terms(rows, ws, n, j0, row, w);
+                    fma_batch<Y>(y, H, row, w, c, acc);
+                }
+                store8(o + c * 8, acc);
             }
-            store8(o + c * 8, acc);
+        } else {
+            // few terms (n <= kFewTerms): half the threads take two chunks each, with the loads
+            // of both in flight together; the other half has nothing to do
+            const int64_t half = (nchunk + 1) / 2;
+            for (int64_t c = threadIdx.x; c < half; c += blockDim.x) {
+                const int64_t c2 = c + half;
+                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                float acc2[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                int32_t row1[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    row1[u] = c2 < nchunk ? row0[u] : -1;
+                fma_few2<Y>(y, H, row0, row1, w0, c, c2, acc, acc2);
+                store8(o + c * 8, acc);
+                if (c2 < nchunk)
+                    store8(o + c2 * 8, acc2);
+            }
         }
     } else {
         for (int64_t h = threadIdx.x; h < H; h += blockDim.x) {
@@ -265,12 +317,14 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
     }
 }
 
-// Threads per token: about two 8-element chunks per thread, whole wavefronts, at most 1024
-// (H = 7168 -> 448 threads, two chunks each).
-int block_threads(int64_t nchunk)
+// Threads per workgroup: one per `cpt` 8-element chunks, whole wavefronts, at most 1024.
+// Measured on MI355X: a token with 8 terms at H = 7168 combines fastest with one chunk per
+// thread (361 us vs 372 us with two per launch of the bf16 combine), tokens with few terms
+// (K = 2, drop-and-pad, the per-group partials) with two chunks per thread.
+int block_threads(int64_t nchunk, int cpt)
 {
-    const int64_t half = (nchunk + 1) / 2;
-    const int64_t waves = std::min<int64_t>(kMaxThreads / kWave, std::max<int64_t>(1, (half + kWave - 1) / kWave));
+    const int64_t per = (nchunk + cpt - 1) / cpt;
+    const int64_t waves = std::min<int64_t>(kMaxThreads / kWave, std::max<int64_t>(1, (per + kWave - 1) / kWave));
     return static_cast<int>(waves * kWave);
 }
 
@@ -280,7 +334,7 @@ moe_status launch_combine(const void *y, int64_t y_rows, int64_t H, const int32_
 {
     const bool vec = H % 8 == 0 && aligned16(out) && (y_rows == 0 || aligned16(y));
     const int64_t nchunk = vec ? H / 8 : H;
-    const dim3 grid(static_cast<unsigned>(T)), block(block_threads(nchunk));
+    const dim3 grid(static_cast<unsigned>(T)), block(block_threads(nchunk, 1));
     if (vec)
         hipLaunchKernelGGL((combine_kernel<Y, O, true>), grid, block, 0, stream, static_cast<const Y *>(y),
                            y_rows, H, row_of, w, K, static_cast<O *>(out));
@@ -297,7 +351,7 @@ moe_status launch_precombine(const void *y, int64_t y_rows, int64_t H, const int
 {
     const bool vec = H % 8 == 0 && aligned16(partials) && (y_rows == 0 || aligned16(y));
     const int64_t nchunk = vec ? H / 8 : H;
-    const dim3 grid(static_cast<unsigned>(T)), block(block_threads(nchunk));
+    const dim3 grid(static_cast<unsigned>(T)), block(block_threads(nchunk, 2));
     const int G = E / gs;
     if (vec)
         hipLaunchKernelGGL((precombine_kernel<Y, true>), grid, block, 0, stream, static_cast<const Y *>(y),
