@@ -30,7 +30,18 @@ def _load():
     src = os.path.join(os.path.dirname(path), "moe_oracle.c")
     if not os.path.exists(path) or os.path.getmtime(src) > os.path.getmtime(path):
         _build()
-    lib = ctypes.CDLL(path)
+    _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
+
+def use_library(path):
+    """Test hook: route every call to the oracle library at `path` (None restores the default).
+    The mutation tests use it to check that the pins catch deliberately broken oracles."""
+    global _lib
+    _lib = None if path is None else _declare(ctypes.CDLL(path))
+
+
+def _declare(lib):
     P = ctypes.c_void_p
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     lib.oracle_capacity.argtypes = [i64, i32, i32, i32, i32]
@@ -47,7 +58,6 @@ def _load():
     lib.oracle_unpermute_combine.restype = ctypes.c_int
     lib.oracle_group_precombine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, i32, P, i64, P]
     lib.oracle_group_precombine.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 
@@ -72,6 +82,14 @@ def _dt_of(a: np.ndarray) -> int:
     raise TypeError(f"hidden tensors must be float32 or uint16 (bf16 bits), got {a.dtype}")
 
 
+def _poisoned(shape, dtype) -> np.ndarray:
+    """Output buffer pre-filled with a NaN pattern, so that an entry the oracle forgets to write
+    shows up in the pins instead of passing as a fresh page's zeros."""
+    a = np.empty(shape, dtype)
+    a.view(np.uint8)[...] = 0xFF
+    return a
+
+
 def capacity(tokens: int, top_k: int, num_experts: int, cf_num: int, cf_den: int) -> int:
     """Expert capacity ceil(tokens*top_k/num_experts*cf), cf = cf_num/cf_den, exact."""
     v = _load().oracle_capacity(tokens, top_k, num_experts, cf_num, cf_den)
@@ -88,8 +106,8 @@ def route_topk(logits: np.ndarray, K: int):
     """Top-K experts per token (ties -> lower id) and softmax over the K selected logits."""
     logits = _c(logits, np.float32)
     T, E = logits.shape
-    idx = np.empty((T, K), np.int32)
-    w = np.empty((T, K), np.float32)
+    idx = np.full((T, K), -7, np.int32)
+    w = np.full((T, K), np.nan, np.float32)
     _check(_load().oracle_route_topk(_ptr(logits), T, E, K, _ptr(idx), _ptr(w)), "route_topk")
     return idx, w
 
@@ -137,7 +155,7 @@ def permute(src: np.ndarray, src_row: np.ndarray) -> np.ndarray:
     _dt_of(src)
     src_rows, H = src.shape
     src_row = _c(src_row, np.int32).reshape(-1)
-    dst = np.empty((src_row.shape[0], H), src.dtype)
+    dst = _poisoned((src_row.shape[0], H), src.dtype)
     rc = _load().oracle_permute(_ptr(src), src_rows, H, src.dtype.itemsize, _ptr(src_row),
                                 src_row.shape[0], _ptr(dst))
     _check(rc, "permute")
@@ -152,7 +170,7 @@ def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype) -> np.nda
     row_of = _c(row_of, np.int32)
     T, K = row_of.shape
     w = None if w is None else _c(w, np.float32).reshape(T, K)
-    out = np.empty((T, H), out_dtype)
+    out = _poisoned((T, H), out_dtype)
     out_dt = _dt_of(out)
     rc = _load().oracle_unpermute_combine(_ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
                                           T, K, _ptr(out), out_dt)

@@ -14,7 +14,7 @@ import oracle
 import workloads as wl
 
 
-def brute_index(ids, E, cap=0, gs=0):
+def brute_index(ids, E, cap=0, gs=0, w=None):
     T, K = ids.shape
     slots = sorted((int(ids[t, k]), t, k) for t in range(T) for k in range(K)
                    if 0 <= ids[t, k] < E)
@@ -36,8 +36,12 @@ def brute_index(ids, E, cap=0, gs=0):
         for r, (e, t, k) in enumerate(slots):
             sorted_idx[r] = t
             row_of[t, k] = r
+    probs = np.zeros(len(sorted_idx), np.float32)
+    for e, t, k in slots:
+        if row_of[t, k] >= 0:
+            probs[row_of[t, k]] = 1.0 if w is None else w[t, k]
     out = dict(counts=counts, group_list=gl, sorted_indices=sorted_idx.tolist(),
-               row_of=row_of.tolist())
+               row_of=row_of.tolist(), permuted_probs=probs)
     if gs > 0:
         G = E // gs
         pairs = sorted({(e // gs, t) for e, t, _ in slots})
@@ -70,23 +74,27 @@ def routing(draw, max_t=12, max_e=9, max_k=4, allow_missing=True):
 
 
 @settings(max_examples=300, deadline=None)
-@given(routing())
-def test_index_matches_tuple_sort(case):
+@given(routing(), st.booleans())
+def test_index_matches_tuple_sort(case, weighted):
     ids, E = case
-    ix = oracle.build_index(ids, None, E)
-    bf = brute_index(ids, E)
+    w = np.random.default_rng(ids.size).random(ids.shape).astype(np.float32) if weighted else None
+    ix = oracle.build_index(ids, w, E)
+    bf = brute_index(ids, E, w=w)
     assert ix["counts"].tolist() == bf["counts"]
     assert ix["group_list"].tolist() == bf["group_list"]
     assert ix["sorted_indices"].tolist() == bf["sorted_indices"]
     assert ix["row_of"].tolist() == bf["row_of"]
+    assert np.array_equal(ix["permuted_probs"], bf["permuted_probs"])
 
 
 @settings(max_examples=200, deadline=None)
 @given(routing(), st.integers(1, 5))
 def test_drop_and_pad_matches_tuple_sort(case, cap):
     ids, E = case
-    ix = oracle.build_index(ids, None, E, capacity=cap)
-    bf = brute_index(ids, E, cap=cap)
+    w = np.random.default_rng(ids.size + 1).random(ids.shape).astype(np.float32)
+    ix = oracle.build_index(ids, w, E, capacity=cap)
+    bf = brute_index(ids, E, cap=cap, w=w)
+    assert np.array_equal(ix["permuted_probs"], bf["permuted_probs"])
     assert ix["counts"].tolist() == bf["counts"]
     assert ix["sorted_indices"].tolist() == bf["sorted_indices"]
     assert ix["row_of"].tolist() == bf["row_of"]
