@@ -75,13 +75,14 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
 }
 
 // ---------------------------------------------------------------- source-major form
-// One workgroup per source row: the row is read once (kScatterUnroll 16-byte vectors per thread
-// in flight) and written to each of its destinations; the destinations sit in lanes 0..J-1 of
-// every wave and are walked in lane order with readlane, so the loop is uniform. Extra
-// workgroups after the source rows write the zero rows: each wave checks 16 entries of
-// src_row and zero-fills those outside [0, src_rows).
+// One wavefront per (source row, 1 KiB slice of it): each lane loads one 16-byte vector of the
+// row once and stores it to every destination; the destinations sit in lanes 0..J-1 and are
+// walked in lane order with readlane, so the loop is uniform. Waves past the last source row
+// write the zero rows: each checks kZeroRowsPerWave entries of src_row and zero-fills those
+// outside [0, src_rows). Measured at T16384 H7168 K8 bf16: 339 us per launch (6.2 TB/s) with
+// slices, 350 us with one 256-thread workgroup per row.
 constexpr int kScatterThreads = 256;
-constexpr int kScatterUnroll = 4;
+constexpr int kScatterWaves = kScatterThreads / kWave;
 constexpr int kZeroRowsPerWave = 16;
 constexpr int kMaxScatterDests = 64;
 
@@ -91,13 +92,15 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
-    if (static_cast<int64_t>(blockIdx.x) >= src_rows) {
+    const int64_t wpr = (nvec + kWave - 1) / kWave;  // waves per source row
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterWaves +
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+    const int64_t copy_waves = src_rows * wpr;
+    if (gw >= copy_waves) {
         // zero rows of the gather map
-        const int64_t first = (static_cast<int64_t>(blockIdx.x) - src_rows) * (kScatterThreads / kWave) * kZeroRowsPerWave +
-                              static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave))) *
-                                  kZeroRowsPerWave;
+        const int64_t first = (gw - copy_waves) * kZeroRowsPerWave;
         const int64_t i = first + lane;
-        const bool zero = lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+        const bool zero = src_row && lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
         uint64_t m = __ballot(zero);
         const u32x4 z{0u, 0u, 0u, 0u};
         while (m) {
@@ -109,33 +112,22 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
         }
         return;
     }
-    const int64_t t = blockIdx.x;
+    const int64_t t = gw / wpr;
+    const int64_t v = (gw - t * wpr) * kWave + lane;  // this lane's vector of the row
     const int32_t my = lane < J ? dst_of[t * J + lane] : -1;
-    const uint64_t mask = __ballot(my >= 0 && my < N);
-    if (mask == 0)
+    uint64_t m = __ballot(my >= 0 && my < N);
+    if (m == 0)
         return;
-    const char *p = src + t * row_bytes;
-    for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += kScatterThreads * kScatterUnroll) {
-        u32x4 r[kScatterUnroll];
-#pragma unroll
-        for (int u = 0; u < kScatterUnroll; ++u) {
-            const int64_t v = v0 + u * kScatterThreads;
-            if (v < nvec)
-                r[u] = ld16(p + v * 16);
-        }
-        uint64_t m = mask;
-        while (m) {
-            const int j = __builtin_ctzll(m);
-            m &= m - 1;
-            const __amdgpu_buffer_rsrc_t q = make_rsrc(
-                dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * row_bytes, static_cast<uint32_t>(row_bytes));
-#pragma unroll
-            for (int u = 0; u < kScatterUnroll; ++u) {
-                const int64_t v = v0 + u * kScatterThreads;
-                if (v < nvec)
-                    st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r[u]);
-            }
-        }
+    u32x4 r{0u, 0u, 0u, 0u};
+    if (v < nvec)
+        r = ld16(src + t * row_bytes + v * 16);
+    while (m) {
+        const int j = __builtin_ctzll(m);
+        m &= m - 1;
+        const __amdgpu_buffer_rsrc_t q = make_rsrc(
+            dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * row_bytes, static_cast<uint32_t>(row_bytes));
+        if (v < nvec)
+            st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r);
     }
 }
 
@@ -189,17 +181,27 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
         return MOE_OK;
     if (!dst || (src_rows > 0 && (!src || !dst_of)))
         return MOE_ERR_INVALID;
-    const int64_t zero_blocks = src_row ? ceil_div(N, (kScatterThreads / kWave) * kZeroRowsPerWave) : 0;
-    const int64_t blocks = src_rows + zero_blocks;
-    if (blocks > 0x7fffffff)
-        return MOE_ERR_UNSUPPORTED;
     const int64_t esz = dt == MOE_F32 ? 4 : 2;
     const int64_t row_bytes = H * esz;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kScatterThreads);
+    if (row_bytes > 0x7fffffffLL)
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t zero_waves = src_row ? ceil_div(N, kZeroRowsPerWave) : 0;
     if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
-        hipLaunchKernelGGL(permute_scatter_vec16_kernel, grid, block, 0, stream, static_cast<const char *>(src),
-                           src_rows, row_bytes / 16, dst_of, J, src_row, N, static_cast<char *>(dst));
-    } else if (esz == 4) {
+        const int64_t nvec = row_bytes / 16;
+        const int64_t waves = src_rows * ceil_div(nvec, kWave) + zero_waves;
+        const int64_t blocks = ceil_div(waves, kScatterWaves);
+        if (blocks > 0x7fffffff)
+            return MOE_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(permute_scatter_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0,
+                           stream, static_cast<const char *>(src), src_rows, nvec, dst_of, J, src_row, N,
+                           static_cast<char *>(dst));
+        return launch_status();
+    }
+    const int64_t blocks = src_rows + ceil_div(zero_waves, kScatterWaves);
+    if (blocks > 0x7fffffff)
+        return MOE_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kScatterThreads);
+    if (esz == 4) {
         hipLaunchKernelGGL(permute_scatter_elem_kernel<uint32_t>, grid, block, 0, stream,
                            static_cast<const uint32_t *>(src), src_rows, H, dst_of, J, src_row, N,
                            static_cast<uint32_t *>(dst));
