@@ -7,9 +7,10 @@ unpermute_combine (expert outputs back to token order, weighted). In group mode 
 the two-stage dedup dispatch and the combine is the per-group pre-combine plus the final sum.
 
 Prints ONE JSON line. `value` is the whole step's algorithmic bytes (each stage's minimal HBM
-traffic, computed from the actual routing) divided by the measured step time. `roofline`
-describes the dominant kernel (permute or combine) with its own HIP-event time; `cpu_baseline`
-is the CPU oracle on the same workload on this host.
+traffic, computed from the actual routing) divided by the measured step time. Every kernel call
+is bracketed by HIP events on the launch stream (`kernel_us`; `stage_us` sums them per stage);
+`roofline` describes the dominant HBM-bound kernel with its own event time; `cpu_baseline` is the
+CPU oracle on the same workload on this host.
 """
 from __future__ import annotations
 
@@ -25,11 +26,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 METRIC = "permute+combine effective HBM GB/s (% of peak) and routed tokens/s"
-KERNEL_SOURCES = {
-    "permute": ["unpermute_combine_amd/csrc/permute.hip", "unpermute_combine_amd/csrc/moe_common.h"],
-    "combine": ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csrc/moe_common.h"],
-}
-KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine_kernel"}
+_PERMUTE_SRC = ["unpermute_combine_amd/csrc/permute.hip", "unpermute_combine_amd/csrc/moe_common.h"]
+_COMBINE_SRC = ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csrc/moe_common.h"]
+# HBM-bound kernel calls of a step: sources (for the PMC summaries' digest) and kernel symbol.
+# Standard and drop-and-pad steps run `permute` and `combine`; group-mode steps run the two
+# dispatch stages (send: one copy per token and group; receive: group slots to expert-major
+# rows), the per-group pre-combine and the final sum over groups.
+KERNEL_SOURCES = {"permute": _PERMUTE_SRC, "combine": _COMBINE_SRC, "dispatch_send": _PERMUTE_SRC,
+                  "dispatch_recv": _PERMUTE_SRC, "precombine": _COMBINE_SRC, "final_sum": _COMBINE_SRC}
+KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine_kernel",
+                  "dispatch_send": "permute_scatter_vec16_kernel", "dispatch_recv": "permute_grouped_vec16_kernel",
+                  "precombine": "precombine_kernel", "final_sum": "combine_kernel"}
 
 
 def log(*a):
@@ -144,38 +151,36 @@ def main():
     gbuf = torch.empty((T * min(K, G), H), dtype=tdt, device="cuda") if gs else None
     part = torch.empty((T * min(K, G), H), dtype=torch.float32, device="cuda") if gs else None
 
-    stages = ["route", "index", "permute", "combine"]
+    # the step's calls in order: (kernel name, stage, call)
+    calls = [("route", "route", lambda: m.route_topk(logits, K, out=(gi, gw))),
+             ("index", "index", lambda: m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix))]
+    src = xp if y is None else y
+    if gs:
+        # the number of group slots is only known on the device; every call is bounded by its
+        # upper bound T*min(K,G) instead, so the step never waits for the host
+        calls += [("dispatch_send", "permute", lambda: m.permute_scatter(x, ix.slot_of, gbuf.shape[0], out=gbuf)),
+                  ("dispatch_recv", "permute", lambda: m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=xp)),
+                  ("precombine", "combine",
+                   lambda: m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)),
+                  ("final_sum", "combine", lambda: m.unpermute_combine(part, ix.slot_of, None, out=out))]
+    else:
+        calls += [("permute", "permute",
+                   lambda: m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=xp)),
+                  ("combine", "combine", lambda: m.unpermute_combine(src, ix.row_of, gw, out=out))]
 
     def step(ev=None):
-        def mark(i):
+        for i, (_, _, call) in enumerate(calls):
             if ev is not None:
                 ev[i].record()
-        mark(0)
-        m.route_topk(logits, K, out=(gi, gw))
-        mark(1)
-        m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix)
-        mark(2)
-        # group mode: the number of group slots is only known on the device; every call below
-        # is bounded by its upper bound T*min(K,G) instead, so the step never waits for the host
-        if gs:
-            m.permute_scatter(x, ix.slot_of, gbuf.shape[0], out=gbuf)
-            m.permute(gbuf, ix.esrc, out=xp)
-        else:
-            m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=xp)
-        mark(3)
-        src = xp if y is None else y
-        if gs:
-            m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)
-            m.unpermute_combine(part, ix.slot_of, None, out=out)
-        else:
-            m.unpermute_combine(src, ix.row_of, gw, out=out)
-        mark(4)
+            call()
+        if ev is not None:
+            ev[len(calls)].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -183,38 +188,46 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
+    kernel_us = {}
+    for i, (name, _, _) in enumerate(calls):
+        kernel_us[name] = float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.steps)]))
     stage_us = {}
-    for i, name in enumerate(stages):
-        d = [evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.steps)]
-        stage_us[name] = float(np.mean(d))
+    for name, stage, _ in calls:
+        stage_us[stage] = stage_us.get(stage, 0.0) + kernel_us[name]
 
     # ---- algorithmic bytes from the actual routing
     row_of = ix.row_of.cpu().numpy()
     counts = ix.counts.cpu().numpy()
     valid = int((row_of >= 0).sum())  # rows the combine reads
     routed = int((row_of >= 0).any(axis=1).sum()) if K else 0  # distinct source rows the permute reads
-    bytes_route = T * E * 4 + T * K * 8
-    bytes_index = T * K * 8 + rows * 8 + T * K * 4 + E * 4 * 3
+    kbytes = {"route": T * E * 4 + T * K * 8,
+              "index": T * K * 8 + rows * 8 + T * K * 4 + E * 4 * 3}
     if gs:
         n = int(ix.n_slots.item())
-        bytes_permute = (routed * H * b + n * 4 + n * H * b) + (n * H * b + rows * 4 + rows * H * b)
-        bytes_combine = (valid * H * b + 2 * T * K * 4 + n * H * 4) + (n * H * 4 + T * G * 4 + T * H * b)
+        kbytes.update(dispatch_send=routed * H * b + n * 4 + n * H * b,
+                      dispatch_recv=n * H * b + rows * 4 + rows * H * b,
+                      precombine=valid * H * b + 2 * T * K * 4 + n * H * 4,
+                      final_sum=n * H * 4 + T * G * 4 + T * H * b)
     else:
-        bytes_permute = routed * H * b + rows * 4 + rows * H * b
-        bytes_combine = valid * H * b + 2 * T * K * 4 + T * H * b
-    step_bytes = bytes_route + bytes_index + bytes_permute + bytes_combine
+        kbytes.update(permute=routed * H * b + rows * 4 + rows * H * b,
+                      combine=valid * H * b + 2 * T * K * 4 + T * H * b)
+    stage_bytes = {}
+    for name, stage, _ in calls:
+        stage_bytes[stage] = stage_bytes.get(stage, 0) + kbytes[name]
+    step_bytes = sum(kbytes.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     routed_per_s = T * K / (ms_per_step * 1e-3)
 
-    per_kernel = {"permute": (bytes_permute, stage_us["permute"]), "combine": (bytes_combine, stage_us["combine"])}
-    dom = max(per_kernel, key=lambda k: per_kernel[k][1])
-    dbytes, dus = per_kernel[dom]
-    achieved = dbytes / (dus * 1e-6) / 1e9
-    traffic = read_traffic(dom, cid) if not gs else None
+    def gbs(nbytes, us):
+        return round(nbytes / (us * 1e-6) / 1e9, 1)
+
+    hbm_kernels = [name for name, stage, _ in calls if stage in ("permute", "combine")]
+    dom = max(hbm_kernels, key=lambda k: kernel_us[k])
+    achieved = kbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": KERNEL_SYMBOLS[dom], "algorithmic_bytes_per_launch": dbytes,
-                "avg_launch_us": round(dus, 2)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dom, cid),
+                "kernel": KERNEL_SYMBOLS[dom], "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
+                "avg_launch_us": round(kernel_us[dom], 2)}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -225,8 +238,10 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "routed_tokens_per_s": round(routed_per_s, 1),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "stage_gbs": {"permute": round(bytes_permute / (stage_us["permute"] * 1e-6) / 1e9, 1),
-                      "combine": round(bytes_combine / (stage_us["combine"] * 1e-6) / 1e9, 1)},
+        "stage_gbs": {k: gbs(stage_bytes[k], stage_us[k]) for k in ("permute", "combine")},
+        "kernel_us": {k: round(v, 2) for k, v in kernel_us.items()},
+        "kernel_gbs": {k: gbs(kbytes[k], kernel_us[k]) for k in hbm_kernels},
+        "kernel_bytes": kbytes,
         "max_expert_count": int(counts.max()), "empty_experts": int((counts == 0).sum()),
         "roofline": roofline,
     }

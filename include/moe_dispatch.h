@@ -16,8 +16,9 @@
  *     null stream) and return. Results are visible to later work on the same stream.
  *   - Argument errors are reported synchronously, before anything is launched:
  *     MOE_ERR_INVALID (null pointer where data is needed, negative size, K < 1, K > E,
- *     H < 1, group size not dividing E, ...) or MOE_ERR_UNSUPPORTED (E > 1024, K > 32, or a
- *     combination the call does not implement). MOE_ERR_HIP means a launch failed.
+ *     H < 1, group size not dividing E, ...) or MOE_ERR_UNSUPPORTED (E > 1024, K > 32, a
+ *     hidden row longer than 2^31 - 1 bytes, more than 2^31 - 1 tokens, or a combination the
+ *     call does not implement). MOE_ERR_HIP means a launch failed.
  *   - A size of zero tokens / rows is valid and launches nothing (an empty rank or an expert
  *     with no tokens must work, [Scratch] §26.1-26.2).
  *   - Memory safety does not depend on the data: an expert id outside [0, E) routes nowhere
@@ -155,6 +156,26 @@ moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, moe_dtype d
 moe_status moe_permute_scatter(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
                                const int32_t *dst_of, int32_t J, const int32_t *src_row, int64_t N,
                                void *dst, hipStream_t stream);
+
+/* The row gather of moe_permute, worked through in groups of destination rows: the result is
+ * defined by the gather map alone,
+ *   dst[r, :] = src[src_row[r], :]   (bit for bit) for every r listed in dst_of,
+ *   dst[r, :] = 0                     for every r in [0, N) with src_row[r] outside [0, src_rows),
+ * and dst_of only decides which rows are copied together: within one group (a row of dst_of),
+ * a source row named by several destinations is read once. This is the receive side of the
+ * send-once-per-rank dispatch ([CANN] §1(1)) put back in expert-major order ([Scratch] §11-12,
+ * rank-major to expert-major): src = the group buffer, src_row = moe_index.esrc, dst_of =
+ * moe_index.row_of (one group per token, J = K), where each group slot feeds every expert of
+ * its group that the token chose.
+ *   src     [src_rows, H] (dt); src_row [N] int32 (required); dst [N, H] (dt).
+ *   dst_of  [M, J] int32 destination rows, J <= 64; entries outside [0, N) are ignored. A row
+ *           may be listed more than once (each copy writes the same bytes); rows with a valid
+ *           src_row that dst_of never lists are left untouched.
+ * With dst_of = the inverse of src_row (every row listed), the result equals
+ * moe_permute(src, src_rows, H, dt, src_row, N, dst) bit for bit. */
+moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
+                               const int32_t *src_row, int64_t N, const int32_t *dst_of, int64_t M,
+                               int32_t J, void *dst, hipStream_t stream);
 
 /* Unpermute + weighted top-k merge ([Combine] §1: out[t] = sum over the token's top-k experts
  * of probs[t,e] * expert_e(x[t]); [Scratch] §13, §16):

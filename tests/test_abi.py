@@ -80,6 +80,21 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_unpermute_combine(fake, 1, 4, 8, None, None, 2, 2, fake, 1, None) == capi.MOE_ERR_INVALID
     assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 3, fake, 4, fake, None) == \
         capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, 2, 65, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, None, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, None, 2, 2, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, -1, 2, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped(None, 0, 8, 1, None, 0, None, 0, 2, None, None) == capi.MOE_OK
+    # hidden rows longer than 2^31 - 1 bytes are refused (buffer resources address a row in 32 bits)
+    big = 1 << 30
+    assert lib.moe_permute(fake, 4, big, 1, fake, 4, fake, None) == capi.MOE_ERR_UNSUPPORTED  # bf16: 2 GiB rows
+    assert lib.moe_permute(fake, 4, big // 2, 0, fake, 4, fake, None) == capi.MOE_ERR_UNSUPPORTED  # f32
+    assert lib.moe_permute_scatter(fake, 4, big, 1, fake, 2, None, 8, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_grouped(fake, 4, big, 1, fake, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(fake, 1, 4, big // 2, fake, None, 2, 2, fake, 0, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # float32 output rows of 2 GiB
+    assert lib.moe_group_precombine(fake, 1, 4, big // 2, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # float32 partial rows of 2 GiB
     ix = capi.MoeIndexStruct()
     assert lib.moe_build_index(fake, None, 4, 2, 8, 4, 2, ctypes.byref(ix), fake, 1 << 20, None) == \
         capi.MOE_ERR_UNSUPPORTED  # drop-and-pad with groups

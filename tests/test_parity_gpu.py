@@ -222,6 +222,75 @@ def test_permute_scatter_leaves_unnamed_rows(m):
     assert (got[[1, 2, 3, 4, 6, 7]] == 0).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H,T,E,K,gs", [(7168, 300, 64, 8, 8), (1000, 513, 32, 8, 4), (3, 200, 16, 4, 4),
+                                        (4096, 257, 256, 8, 32), (24, 90, 12, 6, 3), (520, 128, 8, 8, 8)])
+def test_permute_grouped_group_receive(m, dtype, H, T, E, K, gs):
+    """Receive side of the group dispatch: group slots to expert-major rows, one group per token;
+    bit for bit the pages' gather (oracle permute of the group buffer by esrc) and the flat permute."""
+    say(f"permute_grouped {dtype} H={H} T={T} E={E} K={K} gs={gs}")
+    key = wl.case_key(30, H, T, E, K, gs)
+    logits = wl.router_logits(key, T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    idx[::5, -1] = -1  # some slots route nowhere: unused tail rows are zero
+    ix = oracle.build_index(idx, w, E, group_size=gs)
+    x = wl.hidden_states(key, T, H, dtype)
+    gbuf = oracle.permute(x, ix["gsrc"])
+    want = oracle.permute(gbuf, ix["esrc"])
+    assert np.array_equal(want, oracle.permute(x, ix["sorted_indices"]))
+    got = host(m.permute_grouped(dev(gbuf), dev(ix["esrc"]), dev(ix["row_of"])))
+    assert_exact(got, want, "expert-major rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H,J", [(1, 1), (8, 3), (1000, 8), (7168, 16), (4095, 64), (64, 64)])
+def test_permute_grouped_random_maps(m, dtype, H, J):
+    """Arbitrary groups: shared sources inside a group, repeated rows, out-of-range entries;
+    listed rows and zero rows as the oracle's gather, unlisted rows untouched."""
+    say(f"permute_grouped random {dtype} H={H} J={J}")
+    key = wl.case_key(31, H, J)
+    g = np.random.default_rng([*key, 3])
+    src_rows, N = 97, 700
+    x = wl.hidden_states(key, src_rows, H, dtype)
+    src_row = g.integers(0, src_rows, size=N).astype(np.int32)
+    src_row[g.random(N) < 0.1] = -1
+    src_row[:3] = [src_rows, -5, src_rows - 1]
+    rows = g.permutation(N + 40)  # entries >= N are outside [0, N): ignored
+    M = (len(rows) * 3 // 4 + J - 1) // J
+    dst_of = np.full(M * J, -1, np.int64)
+    dst_of[: len(rows) * 3 // 4] = rows[: len(rows) * 3 // 4]
+    dst_of = dst_of.reshape(M, J)
+    dst_of[g.random((M, J)) < 0.05] = -3
+    if J > 1:
+        dst_of[0, 1] = dst_of[0, 0]  # a row listed twice
+    for i in range(0, M, 7):  # rows of one group naming one source
+        live = dst_of[i][(dst_of[i] >= 0) & (dst_of[i] < N)]
+        src_row[live] = src_row[live[0]] if len(live) else 0
+    dst_of = dst_of.astype(np.int32)
+    listed = np.zeros(N, bool)
+    listed[dst_of[(dst_of >= 0) & (dst_of < N)]] = True
+    zero = (src_row < 0) | (src_row >= src_rows)
+    want = oracle.permute(x, src_row)
+    poison = np.full((N, H), 0x3F01 if dtype == "bf16" else 0x7FC00001, np.uint16 if dtype == "bf16" else np.uint32)
+    out = dev(poison.view(np.float32) if dtype == "f32" else poison)
+    m.permute_grouped(dev(x), dev(src_row), dev(dst_of), out=out)
+    got = host(out)
+    if dtype == "f32":
+        got, want, poison = got.view(np.uint32), want.view(np.uint32), poison
+    sel = listed | zero
+    assert_exact(got[sel], want[sel], "listed and zero rows")
+    assert np.array_equal(got[~sel], poison[~sel]), "rows never listed must be left untouched"
+
+
+def test_permute_grouped_without_groups_writes_zero_rows(m):
+    x = wl.hidden_states(wl.case_key(32), 4, 16, "bf16")
+    src_row = np.asarray([-1, 2, 9, -1], np.int32)
+    out = dev(np.full((4, 16), 0x1234, np.uint16))
+    m.permute_grouped(dev(x), dev(src_row), dev(np.zeros((0, 4), np.int32)), out=out)
+    got = host(out)
+    assert (got[[0, 2, 3]] == 0).all() and (got[1] == 0x1234).all()
+
+
 # ------------------------------------------------------------------ combine
 
 
@@ -257,15 +326,23 @@ def test_combine_no_tokens(m):
 # ------------------------------------------------------------------ group pre-combine
 
 
-@pytest.mark.parametrize("T,E,K,gs,H,ydt", [(300, 8, 2, 2, 64, "bf16"), (513, 64, 8, 8, 1000, "bf16"),
-                                            (200, 256, 8, 8, 7168, "bf16"), (100, 32, 4, 4, 5, "f32"),
-                                            (150, 16, 8, 16, 24, "bf16")])
+@pytest.mark.parametrize("T,E,K,gs,H,ydt,holes", [
+    (300, 8, 2, 2, 64, "bf16", False), (513, 64, 8, 8, 1000, "bf16", False),
+    (200, 256, 8, 8, 7168, "bf16", False), (100, 32, 4, 4, 5, "f32", False),
+    (150, 16, 8, 16, 24, "bf16", False),
+    (200, 64, 16, 8, 1000, "bf16", False),   # K > 8: member rows loaded per (group, slot)
+    (64, 64, 32, 4, 520, "f32", False),      # K = 32, float32 rows, a ragged 512-element unit
+    (90, 64, 8, 8, 7168, "f32", False),
+    (400, 64, 8, 8, 1000, "bf16", True),     # some slots route nowhere (id -1)
+    (150, 64, 16, 4, 1000, "bf16", True)])
 @pytest.mark.parametrize("layout", ["compact", "dense"])
-def test_group_precombine_and_final_sum(m, T, E, K, gs, H, ydt, layout):
-    say(f"precombine T={T} E={E} K={K} gs={gs} H={H} {ydt} {layout}")
+def test_group_precombine_and_final_sum(m, T, E, K, gs, H, ydt, holes, layout):
+    say(f"precombine T={T} E={E} K={K} gs={gs} H={H} {ydt} holes={holes} {layout}")
     key = wl.case_key(27, T, E, K, gs, H)
     logits = wl.router_logits(key, T, E, zipf_s=1.2)
     idx, w = oracle.route_topk(logits, K)
+    if holes:
+        idx[np.random.default_rng([*key, 9]).random((T, K)) < 0.2] = -1
     want_ix = oracle.build_index(idx, w, E, group_size=gs)
     G = E // gs
     if layout == "compact":
@@ -324,9 +401,11 @@ def run_workload(m, cfg_id):
         assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
         assert_exact(host(ix.esrc), want["esrc"], "esrc")
         assert_exact(host(ix.slot_of), want["slot_of"], "slot_of")
-        gbuf = m.permute_scatter(xd, ix.slot_of, n)
-        assert_exact(host(gbuf), host(m.permute(xd, ix.gsrc[:n])), "group slots: scatter vs gather")
-        xp = m.permute(gbuf, ix.esrc)
+        # as bench.py launches it: the group buffer sized by the bound T*min(K,G), not by n
+        gbuf = m.permute_scatter(xd, ix.slot_of, T * min(K, E // gs))
+        assert_exact(host(gbuf[:n]), host(m.permute(xd, ix.gsrc[:n])), "group slots: scatter vs gather")
+        xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of)
+        assert_exact(host(xp), host(m.permute(gbuf, ix.esrc)), "receive side: grouped vs gather")
     else:
         xp = m.permute_scatter(xd, ix.row_of, rows, src_row=ix.sorted_indices)
     torch.cuda.synchronize()

@@ -13,6 +13,14 @@
 // and each out row written once, both with streaming cache policies (no reuse to keep in L2 /
 // MALL, which measurably raises the read rate on MI355X); y rows are read through buffer
 // resources, which give the sc0|nt policy and a hardware bounds check.
+//
+// Rows with 4-byte elements (float32 inputs or outputs: the pre-combine's partials, the group
+// final sum) use a split lane layout instead: per 512-element unit of a row, lane j of a
+// wavefront owns elements 4j..4j+3 and 256+4j..256+4j+3, so every load or store instruction of
+// the wavefront covers one contiguous span (1 KiB of float32, 512 B of bf16). With 8 consecutive
+// elements per lane a 32-byte float32 chunk takes two 16-byte instructions that each touch only
+// half of every 128-byte line; on MI355X that ran the pre-combine ~12% and the final sum ~15%
+// slower.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -26,7 +34,7 @@ constexpr int kBatch = 8;     // rows whose loads are issued together
 constexpr int kFewTerms = 4;  // tokens with at most this many terms take the two-chunk path
 
 // ---------------------------------------------------------------- 8-element vector access
-// Raw 16-byte vectors of one 8-element chunk: one for bf16, two for float32.
+// Raw 16-byte vector of one 8-element bf16 chunk (rows with 4-byte elements take the split layout).
 template <typename Y>
 struct Chunk;
 
@@ -39,18 +47,6 @@ struct Chunk<uint16_t> {
         v[2] = bf16_lo(q[0].y); v[3] = bf16_hi(q[0].y);
         v[4] = bf16_lo(q[0].z); v[5] = bf16_hi(q[0].z);
         v[6] = bf16_lo(q[0].w); v[7] = bf16_hi(q[0].w);
-    }
-};
-
-template <>
-struct Chunk<float> {
-    static constexpr int kVecs = 2;
-    __device__ static void widen(const u32x4 (&q)[2], float (&v)[8])
-    {
-        v[0] = __uint_as_float(q[0].x); v[1] = __uint_as_float(q[0].y);
-        v[2] = __uint_as_float(q[0].z); v[3] = __uint_as_float(q[0].w);
-        v[4] = __uint_as_float(q[1].x); v[5] = __uint_as_float(q[1].y);
-        v[6] = __uint_as_float(q[1].z); v[7] = __uint_as_float(q[1].w);
     }
 };
 
@@ -72,12 +68,6 @@ __device__ __forceinline__ void store8(uint16_t *p, const float (&a)[8])
 {
     st16_stream(p, u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
                          pack_bf16x2(a[6], a[7])});
-}
-
-__device__ __forceinline__ void store8(float *p, const float (&a)[8])
-{
-    st16_stream(p, u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])});
-    st16_stream(p + 4, u32x4{__float_as_uint(a[4]), __float_as_uint(a[5]), __float_as_uint(a[6]), __float_as_uint(a[7])});
 }
 
 __device__ __forceinline__ float load1(const uint16_t *p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
@@ -175,6 +165,106 @@ __device__ int compact_rows(const int32_t *rows_in, const float *w_in, int K, in
     return n;
 }
 
+// ---------------------------------------------------------------- split layout (4-byte rows)
+constexpr int kUnit = 512;  // elements per wavefront and unit: two halves of 64 lanes x 4
+
+// Four consecutive elements as loaded: 8 bytes of bf16 or 16 bytes of float32.
+template <typename Y>
+struct Part;
+
+template <>
+struct Part<uint16_t> {
+    uint32_t a, b;
+    __device__ static Part load(__amdgpu_buffer_rsrc_t r, int64_t e)
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(e * 2), 0, kPolicyStreamLoad);
+        return Part{static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1])};
+    }
+    __device__ void widen(float *v) const
+    {
+        v[0] = bf16_lo(a); v[1] = bf16_hi(a); v[2] = bf16_lo(b); v[3] = bf16_hi(b);
+    }
+};
+
+template <>
+struct Part<float> {
+    u32x4 q;
+    __device__ static Part load(__amdgpu_buffer_rsrc_t r, int64_t e)
+    {
+        return Part{ld16_buf<kPolicyStreamLoad>(r, static_cast<uint32_t>(e * 4))};
+    }
+    __device__ void widen(float *v) const
+    {
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+    }
+};
+
+// Both parts (elements e0.. and e0+256..) of a row; a negative row loads nothing (zero-size
+// resource) and reads as zeros; elements past H read as zeros (the resource's bound).
+template <typename Y>
+__device__ __forceinline__ void load_parts(const Y *__restrict__ y, int64_t H, int32_t row, int64_t e0, Part<Y> (&q)[2])
+{
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(y + static_cast<int64_t>(row < 0 ? 0 : row) * H, row < 0 ? 0u : static_cast<uint32_t>(H * sizeof(Y)));
+    q[0] = Part<Y>::load(r, e0);
+    q[1] = Part<Y>::load(r, e0 + kUnit / 2);
+}
+
+// acc = fma(w[u], value, acc) over the batch in order u = 0, 1, ... for the terms selected by
+// `take[u]` (all loads issued first, absent terms discarded by a select, as in fma_batch).
+template <typename Y>
+__device__ __forceinline__ void fma_parts(const Part<Y> (&q)[kBatch][2], const float (&w)[kBatch],
+                                          const bool (&take)[kBatch], float (&acc)[8])
+{
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        float v[8];
+        q[u][0].widen(v);
+        q[u][1].widen(v + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r = __builtin_fmaf(w[u], v[e], acc[e]);
+            acc[e] = take[u] ? r : acc[e];
+        }
+    }
+}
+
+template <typename Y>
+__device__ __forceinline__ void fma_batch_split(const Y *__restrict__ y, int64_t H, const int32_t (&row)[kBatch],
+                                                const float (&w)[kBatch], int64_t e0, float (&acc)[8])
+{
+    Part<Y> q[kBatch][2];
+    bool take[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        load_parts<Y>(y, H, row[u], e0, q[u]);
+        take[u] = row[u] >= 0;
+    }
+    fma_parts<Y>(q, w, take, acc);
+}
+
+// Stores the 8 results of one lane at elements e0.. and e0+256.. of row `o` (stores past the
+// resource's size, i.e. past H, are dropped by the hardware).
+__device__ __forceinline__ void store_parts(__amdgpu_buffer_rsrc_t o, int64_t e0, const float (&a)[8], uint16_t *)
+{
+    __attribute__((ext_vector_type(2))) unsigned int lo = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    __attribute__((ext_vector_type(2))) unsigned int hi = {pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
+    __builtin_amdgcn_raw_buffer_store_b64(lo, o, static_cast<int>(e0 * 2), 0, kPolicyNontemporal);
+    __builtin_amdgcn_raw_buffer_store_b64(hi, o, static_cast<int>((e0 + kUnit / 2) * 2), 0, kPolicyNontemporal);
+}
+
+__device__ __forceinline__ void store_parts(__amdgpu_buffer_rsrc_t o, int64_t e0, const float (&a)[8], float *)
+{
+    st16_buf<kPolicyNontemporal>(o, static_cast<uint32_t>(e0 * 4),
+                u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])});
+    st16_buf<kPolicyNontemporal>(o, static_cast<uint32_t>((e0 + kUnit / 2) * 4),
+                u32x4{__float_as_uint(a[4]), __float_as_uint(a[5]), __float_as_uint(a[6]), __float_as_uint(a[7])});
+}
+
+template <typename Y, typename O>
+constexpr bool kSplit = sizeof(Y) == 4 || sizeof(O) == 4;
+
 template <typename Y, typename O, bool VEC>
 __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
                                                       const int32_t *__restrict__ row_of,
@@ -190,7 +280,23 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
     __syncthreads();
     const int n = n_sh;
     O *o = out + t * H;
-    if constexpr (VEC) {
+    if constexpr (VEC && kSplit<Y, O>) {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int nwaves = blockDim.x / kWave;
+        const int64_t units = ceil_div(H, kUnit);
+        const __amdgpu_buffer_rsrc_t orr = make_rsrc(o, static_cast<uint32_t>(H * sizeof(O)));
+        for (int64_t un = threadIdx.x / kWave; un < units; un += nwaves) {
+            const int64_t e0 = un * kUnit + 4 * lane;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int j0 = 0; j0 < n; j0 += kBatch) {
+                int32_t row[kBatch];
+                float w[kBatch];
+                batch_terms(rows, ws, n, j0, row, w);
+                fma_batch_split<Y>(y, H, row, w, e0, acc);
+            }
+            store_parts(orr, e0, acc, o);
+        }
+    } else if constexpr (VEC) {
         int32_t row0[kBatch];  // the first batch of terms stays in registers for every chunk
         float w0[kBatch];
         batch_terms(rows, ws, n, 0, row0, w0);
@@ -281,38 +387,79 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
     }
     __syncthreads();
     const int n_items = n_items_sh;
-    constexpr int kE = VEC ? 8 : 1;
-    const int64_t nchunk = H / kE;
-    for (int it = 0; it < n_items; ++it) {
-        const int g = item_g[it];
-        float *o = partials + static_cast<int64_t>(item_s[it]) * H;
-        for (int64_t c = tid; c < nchunk; c += blockDim.x) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < K; k0 += kBatch) {
-                if constexpr (VEC) {
-                    int32_t row[kBatch];
-                    float w[kBatch];
+    if constexpr (VEC) {
+        const int lane = tid & (kWave - 1);
+        const int nwaves = blockDim.x / kWave;
+        const int64_t units = ceil_div(H, kUnit);
+        if (K <= kBatch) {
+            // every slot of the token in one batch: its rows are loaded once per unit and each
+            // (group, slot) partial is reduced from registers
+            int32_t row[kBatch];
+            float wv[kBatch];
+            int32_t gk[kBatch];
 #pragma unroll
-                    for (int u = 0; u < kBatch; ++u) {
-                        const bool member = k0 + u < K && grp[k0 + u] == g;
-                        row[u] = member ? __builtin_amdgcn_readfirstlane(rows[k0 + u]) : -1;
-                        w[u] = member ? ws[k0 + u] : 0.0f;
-                    }
-                    fma_batch<Y>(y, H, row, w, c, acc);
-                } else {
+            for (int u = 0; u < kBatch; ++u) {
+                const bool live = u < K && grp[u] >= 0;
+                row[u] = live ? __builtin_amdgcn_readfirstlane(rows[u]) : -1;
+                wv[u] = live ? ws[u] : 0.0f;
+                gk[u] = live ? grp[u] : -1;
+            }
+            for (int64_t un = tid / kWave; un < units; un += nwaves) {
+                const int64_t e0 = un * kUnit + 4 * lane;
+                Part<Y> q[kBatch][2];
 #pragma unroll
-                    for (int u = 0; u < kBatch; ++u) {
-                        const bool member = k0 + u < K && grp[k0 + u] == g;
-                        const float v = member ? load1(y + static_cast<int64_t>(rows[k0 + u]) * H + c) : 0.0f;
-                        const float r = __builtin_fmaf(member ? ws[k0 + u] : 0.0f, v, acc[0]);
-                        acc[0] = member ? r : acc[0];
-                    }
+                for (int u = 0; u < kBatch; ++u)
+                    load_parts<Y>(y, H, row[u], e0, q[u]);
+                for (int it = 0; it < n_items; ++it) {
+                    const int g = item_g[it];
+                    bool take[kBatch];
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u)
+                        take[u] = gk[u] == g;
+                    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    fma_parts<Y>(q, wv, take, acc);
+                    const int32_t s = __builtin_amdgcn_readfirstlane(item_s[it]);
+                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * 4)), e0,
+                                acc, partials);
                 }
             }
-            if constexpr (VEC)
-                store8(o + c * kE, acc);
-            else
-                store1(o + c, acc[0]);
+        } else {
+            for (int64_t un = tid / kWave; un < units; un += nwaves) {
+                const int64_t e0 = un * kUnit + 4 * lane;
+                for (int it = 0; it < n_items; ++it) {
+                    const int g = item_g[it];
+                    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    for (int k0 = 0; k0 < K; k0 += kBatch) {
+                        int32_t row[kBatch];
+                        float w[kBatch];
+#pragma unroll
+                        for (int u = 0; u < kBatch; ++u) {
+                            const bool member = k0 + u < K && grp[k0 + u] == g;
+                            row[u] = member ? __builtin_amdgcn_readfirstlane(rows[k0 + u]) : -1;
+                            w[u] = member ? ws[k0 + u] : 0.0f;
+                        }
+                        fma_batch_split<Y>(y, H, row, w, e0, acc);
+                    }
+                    const int32_t s = __builtin_amdgcn_readfirstlane(item_s[it]);
+                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * 4)), e0,
+                                acc, partials);
+                }
+            }
+        }
+    } else {
+        for (int it = 0; it < n_items; ++it) {
+            const int g = item_g[it];
+            float *o = partials + static_cast<int64_t>(item_s[it]) * H;
+            for (int64_t h = tid; h < H; h += blockDim.x) {
+                float acc = 0.0f;
+                for (int k = 0; k < K; ++k) {
+                    const bool member = grp[k] == g;
+                    const float v = member ? load1(y + static_cast<int64_t>(rows[k]) * H + h) : 0.0f;
+                    const float r = __builtin_fmaf(member ? ws[k] : 0.0f, v, acc);
+                    acc = member ? r : acc;
+                }
+                store1(o + h, acc);
+            }
         }
     }
 }
@@ -328,13 +475,20 @@ int block_threads(int64_t nchunk, int cpt)
     return static_cast<int>(waves * kWave);
 }
 
+// Threads per workgroup of the split layout: one wavefront per 512-element unit, at most 1024.
+int split_threads(int64_t H)
+{
+    return static_cast<int>(std::min<int64_t>(kMaxThreads / kWave, ceil_div(H, kUnit)) * kWave);
+}
+
 template <typename Y, typename O>
 moe_status launch_combine(const void *y, int64_t y_rows, int64_t H, const int32_t *row_of, const float *w,
                           int64_t T, int K, void *out, hipStream_t stream)
 {
     const bool vec = H % 8 == 0 && aligned16(out) && (y_rows == 0 || aligned16(y));
     const int64_t nchunk = vec ? H / 8 : H;
-    const dim3 grid(static_cast<unsigned>(T)), block(block_threads(nchunk, 1));
+    const dim3 grid(static_cast<unsigned>(T)),
+        block(vec && kSplit<Y, O> ? split_threads(H) : block_threads(nchunk, 1));
     if (vec)
         hipLaunchKernelGGL((combine_kernel<Y, O, true>), grid, block, 0, stream, static_cast<const Y *>(y),
                            y_rows, H, row_of, w, K, static_cast<O *>(out));
@@ -350,8 +504,7 @@ moe_status launch_precombine(const void *y, int64_t y_rows, int64_t H, const int
                              const int32_t *slot_of, int64_t slots_cap, float *partials, hipStream_t stream)
 {
     const bool vec = H % 8 == 0 && aligned16(partials) && (y_rows == 0 || aligned16(y));
-    const int64_t nchunk = vec ? H / 8 : H;
-    const dim3 grid(static_cast<unsigned>(T)), block(block_threads(nchunk, 2));
+    const dim3 grid(static_cast<unsigned>(T)), block(vec ? split_threads(H) : block_threads(H, 2));
     const int G = E / gs;
     if (vec)
         hipLaunchKernelGGL((precombine_kernel<Y, true>), grid, block, 0, stream, static_cast<const Y *>(y),
@@ -379,7 +532,7 @@ extern "C" moe_status moe_unpermute_combine(const void *y, moe_dtype y_dt, int64
         return MOE_OK;
     if (!row_of || !out || (y_rows > 0 && !y))
         return MOE_ERR_INVALID;
-    if (T > 0x7fffffff)
+    if (T > 0x7fffffff || H * ((y_dt == MOE_F32 || out_dt == MOE_F32) ? 4 : 2) > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
     if (y_dt == MOE_BF16)
         return out_dt == MOE_BF16 ? launch_combine<uint16_t, uint16_t>(y, y_rows, H, row_of, w, T, K, out, stream)
@@ -404,7 +557,7 @@ extern "C" moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_
         return MOE_OK;
     if (!row_of || !topk_idx || !slot_of || (slots_cap > 0 && !partials) || (y_rows > 0 && !y))
         return MOE_ERR_INVALID;
-    if (T > 0x7fffffff)
+    if (T > 0x7fffffff || H * 4 > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
     if (y_dt == MOE_BF16)
         return launch_precombine<uint16_t>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size, slot_of,

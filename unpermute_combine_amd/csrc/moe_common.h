@@ -71,9 +71,12 @@ __device__ __forceinline__ void st16_stream(void *p, const u32x4 &v)
 // Policy bits of the aux operand: 1 = sc0, 2 = nt (streaming), 16 = sc1.
 //   kPolicyStreamStore = sc1|nt: agent-scope streaming store, written through the per-XCD L2
 //                        (measured: the expert-major permute writes at ~6.0 TB/s instead of ~5.4);
-//   kPolicyStreamLoad  = sc0|nt: streaming load of data read exactly once.
+//   kPolicyStreamLoad  = sc0|nt: streaming load of data read exactly once;
+//   kPolicyNontemporal = nt: streaming store at the default scope (the combine's and the
+//                        pre-combine's outputs, where sc1 measured no faster).
 constexpr int kPolicyStreamLoad = 1 | 2;
 constexpr int kPolicyStreamStore = 16 | 2;
+constexpr int kPolicyNontemporal = 2;
 constexpr int kRsrcWord3 = 0x00020000;  // dword 3 of the resource: 32-bit data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -109,6 +112,6 @@ inline moe_status launch_status()
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace moe

@@ -7,9 +7,13 @@
 //   moe_permute          gather: one wavefront per destination row, 16-byte accesses (1 KiB per
 //                        wave instruction), kUnroll loads in flight per lane. A source row that
 //                        several destinations name is read again for each of them.
-//   moe_permute_scatter  source-major: one workgroup per source row reads it once and writes it
-//                        to all its destinations (the inverse map, e.g. row_of), so x is read
-//                        once instead of K times; zero rows come from the gather map.
+//   moe_permute_scatter  source-major: one wavefront per (source row, 1 KiB slice) reads it once
+//                        and writes it to all its destinations (the inverse map, e.g. row_of),
+//                        so x is read once instead of K times; zero rows come from the gather map.
+//   moe_permute_grouped  the gather's map, worked through in groups of destination rows (e.g.
+//                        row_of, one group per token): a source row that several rows of one
+//                        group name is read once for all of them. The receive side of the group
+//                        dispatch uses it: a group slot feeds up to group_size expert rows.
 // Destination rows are written with agent-scope streaming stores (see kPolicyStreamStore). Rows
 // whose size is not a multiple of 16 bytes (or unaligned bases) take element-wise paths.
 #include "moe_common.h"
@@ -86,6 +90,26 @@ constexpr int kScatterWaves = kScatterThreads / kWave;
 constexpr int kZeroRowsPerWave = 16;
 constexpr int kMaxScatterDests = 64;
 
+// Zero-fills rows first .. first+kZeroRowsPerWave-1 whose src_row entry is outside [0, src_rows)
+// (one wavefront; no-op without a gather map).
+__device__ __forceinline__ void zero_rows_wave(int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
+                                               int64_t N, int64_t first, char *__restrict__ dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row_bytes = nvec * 16;
+    const int64_t i = first + lane;
+    const bool zero = src_row && lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+    uint64_t m = __ballot(zero);
+    const u32x4 z{0u, 0u, 0u, 0u};
+    while (m) {
+        const int j = __builtin_ctzll(m);
+        m &= m - 1;
+        const __amdgpu_buffer_rsrc_t d = make_rsrc(dst + (first + j) * row_bytes, static_cast<uint32_t>(row_bytes));
+        for (int64_t v = lane; v < nvec; v += kWave)
+            st16_buf<kPolicyStreamStore>(d, static_cast<uint32_t>(v * 16), z);
+    }
+}
+
 __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ dst_of, int J,
     const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst)
@@ -97,19 +121,7 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = src_rows * wpr;
     if (gw >= copy_waves) {
-        // zero rows of the gather map
-        const int64_t first = (gw - copy_waves) * kZeroRowsPerWave;
-        const int64_t i = first + lane;
-        const bool zero = src_row && lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
-        uint64_t m = __ballot(zero);
-        const u32x4 z{0u, 0u, 0u, 0u};
-        while (m) {
-            const int j = __builtin_ctzll(m);
-            m &= m - 1;
-            const __amdgpu_buffer_rsrc_t d = make_rsrc(dst + (first + j) * row_bytes, static_cast<uint32_t>(row_bytes));
-            for (int64_t v = lane; v < nvec; v += kWave)
-                st16_buf<kPolicyStreamStore>(d, static_cast<uint32_t>(v * 16), z);
-        }
+        zero_rows_wave(src_rows, nvec, src_row, N, (gw - copy_waves) * kZeroRowsPerWave, dst);
         return;
     }
     const int64_t t = gw / wpr;
@@ -162,6 +174,110 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_elem_kernel(
         T *q = dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * H;
         for (int64_t h = threadIdx.x; h < H; h += kScatterThreads)
             q[h] = p[h];
+    }
+}
+
+// ---------------------------------------------------------------- grouped gather
+// One wavefront per (group of destination rows, 1 KiB slice): lanes 0..J-1 hold the group's
+// destination rows and, one dependent load later, their source rows src_row[d]. The distinct
+// source rows are taken kGroupLoads at a time: their slices are loaded first (all in flight
+// together; gfx9 completes vector-memory operations in order, so a load issued after a store
+// would wait for it), then stored to every destination of the group that names them. Waves past
+// the last group write the zero rows, as in the source-major form.
+constexpr int kGroupLoads = 4;
+
+__global__ __launch_bounds__(kScatterThreads) void permute_grouped_vec16_kernel(
+    const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
+    const int32_t *__restrict__ dst_of, int64_t M, int J, int64_t N, char *__restrict__ dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row_bytes = nvec * 16;
+    const int64_t wpr = (nvec + kWave - 1) / kWave;
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterWaves +
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+    const int64_t copy_waves = M * wpr;
+    if (gw >= copy_waves) {
+        zero_rows_wave(src_rows, nvec, src_row, N, (gw - copy_waves) * kZeroRowsPerWave, dst);
+        return;
+    }
+    const int64_t g = gw / wpr;
+    const int64_t v = (gw - g * wpr) * kWave + lane;
+    const int32_t d = lane < J ? dst_of[g * J + lane] : -1;
+    const bool dv = d >= 0 && d < N;
+    const int32_t sr = dv ? src_row[d] : -1;
+    const bool ok = dv && sr >= 0 && sr < src_rows;
+    uint64_t m = __ballot(ok);
+    while (m) {
+        int32_t sb[kGroupLoads];
+        uint64_t pb[kGroupLoads];
+#pragma unroll
+        for (int u = 0; u < kGroupLoads; ++u) {
+            sb[u] = -1;
+            pb[u] = 0;
+            if (m) {
+                sb[u] = __builtin_amdgcn_readlane(sr, __builtin_ctzll(m));
+                pb[u] = __ballot(sr == sb[u]) & m;  // lanes naming this source (valid ones only)
+                m &= ~pb[u];
+            }
+        }
+        u32x4 r[kGroupLoads];
+#pragma unroll
+        for (int u = 0; u < kGroupLoads; ++u) {
+            r[u] = u32x4{0u, 0u, 0u, 0u};
+            if (sb[u] >= 0 && v < nvec)
+                r[u] = ld16(src + static_cast<int64_t>(sb[u]) * row_bytes + v * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kGroupLoads; ++u) {
+            uint64_t p = pb[u];
+            while (p) {
+                const int j = __builtin_ctzll(p);
+                p &= p - 1;
+                const __amdgpu_buffer_rsrc_t q = make_rsrc(
+                    dst + static_cast<int64_t>(__builtin_amdgcn_readlane(d, j)) * row_bytes, static_cast<uint32_t>(row_bytes));
+                if (v < nvec)
+                    st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r[u]);
+            }
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kScatterThreads) void permute_grouped_elem_kernel(
+    const T *__restrict__ src, int64_t src_rows, int64_t H, const int32_t *__restrict__ src_row,
+    const int32_t *__restrict__ dst_of, int64_t M, int J, int64_t N, T *__restrict__ dst)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (static_cast<int64_t>(blockIdx.x) >= M) {
+        const int64_t first = (static_cast<int64_t>(blockIdx.x) - M) * kScatterWaves * kZeroRowsPerWave +
+                              static_cast<int64_t>(threadIdx.x / kWave) * kZeroRowsPerWave;
+        const int64_t i = first + lane;
+        const bool zero = lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+        uint64_t m = __ballot(zero);
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            T *q = dst + (first + j) * H;
+            for (int64_t h = lane; h < H; h += kWave)
+                q[h] = T(0);
+        }
+        return;
+    }
+    const int64_t g = blockIdx.x;
+    for (int j0 = 0; j0 < J; j0 += kWave) {  // every wave walks the same entries
+        const int j = j0 + lane;
+        const int32_t d = j < J ? dst_of[g * J + j] : -1;
+        const bool dv = d >= 0 && d < N;
+        const int32_t sr = dv ? src_row[d] : -1;
+        uint64_t m = __ballot(dv && sr >= 0 && sr < src_rows);
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const T *p = src + static_cast<int64_t>(__builtin_amdgcn_readlane(sr, k)) * H;
+            T *q = dst + static_cast<int64_t>(__builtin_amdgcn_readlane(d, k)) * H;
+            for (int64_t h = threadIdx.x; h < H; h += kScatterThreads)
+                q[h] = p[h];
+        }
     }
 }
 
@@ -224,10 +340,10 @@ extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, 
     if (!src_row || !dst || (src_rows > 0 && !src))
         return MOE_ERR_INVALID;
     const int64_t blocks = ceil_div(N, kRowsPerBlock);
-    if (blocks > 0x7fffffff)
-        return MOE_ERR_UNSUPPORTED;
     const int64_t esz = dt == MOE_F32 ? 4 : 2;
     const int64_t row_bytes = H * esz;
+    if (blocks > 0x7fffffff || row_bytes > 0x7fffffffLL)
+        return MOE_ERR_UNSUPPORTED;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kRowsPerBlock * kWave);
     if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
         hipLaunchKernelGGL(permute_vec16_kernel, grid, block, 0, stream, static_cast<const char *>(src),
@@ -239,6 +355,50 @@ extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, 
     } else {
         hipLaunchKernelGGL(permute_elem_kernel<uint16_t>, grid, block, 0, stream,
                            static_cast<const uint16_t *>(src), src_rows, H, src_row, N,
+                           static_cast<uint16_t *>(dst));
+    }
+    return launch_status();
+}
+
+extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
+                                          const int32_t *src_row, int64_t N, const int32_t *dst_of, int64_t M,
+                                          int32_t J, void *dst, hipStream_t stream)
+{
+    using namespace moe;
+    if (src_rows < 0 || H < 1 || N < 0 || M < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16))
+        return MOE_ERR_INVALID;
+    if (J > kMaxScatterDests)
+        return MOE_ERR_UNSUPPORTED;
+    if (N == 0)
+        return MOE_OK;
+    if (!src_row || !dst || (M > 0 && !dst_of) || (src_rows > 0 && !src))
+        return MOE_ERR_INVALID;
+    const int64_t esz = dt == MOE_F32 ? 4 : 2;
+    const int64_t row_bytes = H * esz;
+    if (row_bytes > 0x7fffffffLL)
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t zero_waves = ceil_div(N, kZeroRowsPerWave);
+    if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
+        const int64_t nvec = row_bytes / 16;
+        const int64_t blocks = ceil_div(M * ceil_div(nvec, kWave) + zero_waves, kScatterWaves);
+        if (blocks > 0x7fffffff)
+            return MOE_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(permute_grouped_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0,
+                           stream, static_cast<const char *>(src), src_rows, nvec, src_row, dst_of, M, J, N,
+                           static_cast<char *>(dst));
+        return launch_status();
+    }
+    const int64_t blocks = M + ceil_div(zero_waves, kScatterWaves);
+    if (blocks > 0x7fffffff)
+        return MOE_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kScatterThreads);
+    if (esz == 4) {
+        hipLaunchKernelGGL(permute_grouped_elem_kernel<uint32_t>, grid, block, 0, stream,
+                           static_cast<const uint32_t *>(src), src_rows, H, src_row, dst_of, M, J, N,
+                           static_cast<uint32_t *>(dst));
+    } else {
+        hipLaunchKernelGGL(permute_grouped_elem_kernel<uint16_t>, grid, block, 0, stream,
+                           static_cast<const uint16_t *>(src), src_rows, H, src_row, dst_of, M, J, N,
                            static_cast<uint16_t *>(dst));
     }
     return launch_status();

@@ -199,6 +199,30 @@ def permute_scatter(src: torch.Tensor, dst_of: torch.Tensor, num_rows: int,
     return out
 
 
+def permute_grouped(src: torch.Tensor, src_row: torch.Tensor, dst_of: torch.Tensor,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The gather out[r] = src[src_row[r]] (zero rows where src_row is out of range), done in the
+    groups of destination rows that dst_of [M, J] lists; a source row named by several rows of
+    one group is read once. Rows with a valid src_row that dst_of never lists are not written.
+
+    The group dispatch's receive side: permute_grouped(group_buffer, index.esrc, index.row_of)."""
+    _need(src, "src", None, 2)
+    dt = _hidden_dt(src, "src")
+    _need(src_row, "src_row", torch.int32, 1)
+    _need(dst_of, "dst_of", torch.int32, 2)
+    N = src_row.shape[0]
+    H = src.shape[1]
+    if out is None:
+        out = torch.empty((N, H), dtype=src.dtype, device=src.device)
+    _need(out, "out", src.dtype, 2)
+    if tuple(out.shape) != (N, H):
+        raise ValueError(f"out must be [{N}, {H}]")
+    check("moe_permute_grouped", lib().moe_permute_grouped(
+        _p(src), src.shape[0], H, dt, _p(src_row), N, _p(dst_of), dst_of.shape[0], dst_of.shape[1], _p(out),
+        _stream()))
+    return out
+
+
 def unpermute_combine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[torch.Tensor] = None,
                       out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[t] = sum_k weights[t,k] * y[row_of[t,k]] (float32 FMA chain in k order)."""
