@@ -57,6 +57,10 @@ def _declare(lib):
     lib.oracle_unpermute_combine.argtypes = [P, i32, i64, i64, P, P, i64, i32, P, i32]
     lib.oracle_unpermute_combine.restype = ctypes.c_int
     lib.oracle_group_precombine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, i32, P, i64, P]
+    lib.oracle_combine_backward.argtypes = [P, i32, P, i32, i64, i64, P, P, i64, i32, P, i32, P]
+    lib.oracle_combine_backward.restype = ctypes.c_int
+    lib.oracle_route_topk_backward.argtypes = [P, P, P, i64, i32, i32, P]
+    lib.oracle_route_topk_backward.restype = ctypes.c_int
     lib.oracle_group_precombine.restype = ctypes.c_int
     return lib
 
@@ -195,3 +199,35 @@ def group_precombine(y: np.ndarray, row_of, w, topk_idx, E: int, group_size: int
                                          slots_cap, _ptr(partials))
     _check(rc, "group_precombine")
     return partials
+
+
+def combine_backward(dout: np.ndarray, y: np.ndarray, row_of: np.ndarray, w, dy_dtype, want_dw: bool = True):
+    """Backward of the weighted combine: dy[row_of[t,k]] = w[t,k] * dout[t] (zero elsewhere),
+    dw[t,k] = <dout[t], y[row_of[t,k]]> (double sum, rounded to float32). Returns (dy, dw|None)."""
+    dout = np.ascontiguousarray(dout)
+    dout_dt = _dt_of(dout)
+    y = np.ascontiguousarray(y)
+    y_dt = _dt_of(y)
+    y_rows, H = y.shape
+    row_of = _c(row_of, np.int32)
+    T, K = row_of.shape
+    assert dout.shape == (T, H)
+    w = None if w is None else _c(w, np.float32).reshape(T, K)
+    dy = _poisoned((y_rows, H), dy_dtype)
+    dw = np.full((T, K), np.nan, np.float32) if want_dw else None
+    rc = _load().oracle_combine_backward(_ptr(dout), dout_dt, _ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
+                                         T, K, _ptr(dy), _dt_of(dy), _ptr(dw))
+    _check(rc, "combine_backward")
+    return dy, dw
+
+
+def route_topk_backward(topk_idx: np.ndarray, topk_w: np.ndarray, d_topk_w: np.ndarray, E: int) -> np.ndarray:
+    """Gradient of the logits through the softmax over the K selected logits (zero elsewhere)."""
+    topk_idx = _c(topk_idx, np.int32)
+    T, K = topk_idx.shape
+    topk_w = _c(topk_w, np.float32).reshape(T, K)
+    d_topk_w = _c(d_topk_w, np.float32).reshape(T, K)
+    d_logits = np.full((T, E), np.nan, np.float32)
+    rc = _load().oracle_route_topk_backward(_ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w), T, E, K, _ptr(d_logits))
+    _check(rc, "route_topk_backward")
+    return d_logits

@@ -389,3 +389,84 @@ int oracle_group_precombine(const void *y, int32_t y_dt, int64_t y_rows, int64_t
     }
     return ORC_OK;
 }
+
+/* ---------------------------------------------------------------- backward ------------ */
+
+/* Backward of the weighted unpermute-combine. [Combine] §4: the path is linear in the expert
+ * outputs, so its backward is the transposed map -- the backward of the combine is a dispatch
+ * of the output gradient back to the expert rows (§4.1, and the forward/backward table of
+ * §4.2) -- and the router gradient reaches only the selected slots (§6, the closing
+ * pseudo-code). With the weights applied in the combine, out[t] = sum_k w[t,k] y[row_of[t,k]]:
+ *   dy[r, :] = w[t,k] * dout[t, :] for every (t, k) whose r = row_of[t,k] is in [0, y_rows)
+ *              (a float32 product, stored as float32 or rounded to bf16); every other row of dy
+ *              fed no output and is zero. A row is named by at most one (t, k) (precondition);
+ *   dw[t, k] = sum_h dout[t,h] * y[r,h] for a valid r, else 0 -- the dot product summed in
+ *              double and rounded once to float32.
+ * w == NULL is the pure-add combine: dy[r] = dout[t]. dw may be NULL (not computed). */
+int oracle_combine_backward(const void *dout, int32_t dout_dt, const void *y, int32_t y_dt, int64_t y_rows,
+                            int64_t H, const int32_t *row_of, const float *w, int64_t T, int32_t K,
+                            void *dy, int32_t dy_dt, float *dw)
+{
+    if (y_rows < 0 || H < 1 || T < 0 || K < 1 || (dout_dt != 0 && dout_dt != 1) || (y_dt != 0 && y_dt != 1) ||
+        (dy_dt != 0 && dy_dt != 1) || (T > 0 && (!row_of || !dout)) || (y_rows > 0 && (!dy || (dw && !y))))
+        return ORC_INVALID;
+    for (int64_t r = 0; r < y_rows; ++r)
+        for (int64_t h = 0; h < H; ++h)
+            store_elem(dy, dy_dt, r * H + h, 0.0f);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t r = row_of[t * K + k];
+            if (r < 0 || r >= y_rows) {
+                if (dw)
+                    dw[t * K + k] = 0.0f;
+                continue;
+            }
+            float wk = w ? w[t * K + k] : 1.0f;
+            for (int64_t h = 0; h < H; ++h)
+                store_elem(dy, dy_dt, (int64_t)r * H + h, wk * load_elem(dout, dout_dt, t * H + h));
+            if (dw) {
+                double s = 0.0;
+                for (int64_t h = 0; h < H; ++h)
+                    s += (double)load_elem(dout, dout_dt, t * H + h) * (double)load_elem(y, y_dt, (int64_t)r * H + h);
+                dw[t * K + k] = (float)s;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Backward of route_topk's softmax over the K selected logits ([Scratch] §3 and §27: the
+ * softmax runs over the selected scores; [Combine] §6: only the selected experts carry router
+ * gradient -- the top-k selection itself is piecewise constant). With w = topk_w (the forward's
+ * output, all K slots taking part in the softmax) and g = d_topk_w, the softmax Jacobian
+ * dw_k/ds_j = w_k (delta_kj - w_j) gives
+ *   d_logits[t, topk_idx[t,k]] += w[t,k] * (g[t,k] - sum_j w[t,j] g[t,j])
+ * in double, slots in order k = 0..K-1, the sum over j in slot order; each entry is rounded
+ * once to float32; logits outside the selection get 0, slots with an id outside [0, E) give
+ * nothing. */
+int oracle_route_topk_backward(const int32_t *topk_idx, const float *topk_w, const float *d_topk_w, int64_t T,
+                               int32_t E, int32_t K, float *d_logits)
+{
+    if (T < 0 || E < 1 || K < 1 || K > E || (T > 0 && (!topk_idx || !topk_w || !d_topk_w || !d_logits)))
+        return ORC_INVALID;
+    double *acc = (double *)malloc(sizeof(double) * (size_t)E);
+    if (!acc)
+        return ORC_INVALID;
+    for (int64_t t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int32_t j = 0; j < K; ++j)
+            s += (double)topk_w[t * K + j] * (double)d_topk_w[t * K + j];
+        for (int32_t e = 0; e < E; ++e)
+            acc[e] = 0.0;
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = topk_idx[t * K + k];
+            if (e < 0 || e >= E)
+                continue;
+            acc[e] += (double)topk_w[t * K + k] * ((double)d_topk_w[t * K + k] - s);
+        }
+        for (int32_t e = 0; e < E; ++e)
+            d_logits[t * E + e] = (float)acc[e];
+    }
+    free(acc);
+    return ORC_OK;
+}

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from oracle.build import SRC
+import test_oracle_backward as bw
 import test_oracle_bruteforce as bf
 import test_oracle_pins as pins
 
@@ -54,6 +55,18 @@ MUTANTS = [
     ("pre-combine mixes groups", "if (e < 0 || e >= E || e / group_size != g || r < 0 || r >= y_rows)",
      "if (e < 0 || e >= E || r < 0 || r >= y_rows)"),
     ("capacity rounds down", "    return (num + den - 1) / den;", "    return num / den;"),
+    ("combine backward ignores the weight",
+     "store_elem(dy, dy_dt, (int64_t)r * H + h, wk * load_elem(dout, dout_dt, t * H + h));",
+     "store_elem(dy, dy_dt, (int64_t)r * H + h, load_elem(dout, dout_dt, t * H + h));"),
+    ("combine backward leaves unnamed rows unwritten",
+     "    for (int64_t r = 0; r < y_rows; ++r)\n        for (int64_t h = 0; h < H; ++h)\n            store_elem(dy, dy_dt, r * H + h, 0.0f);",
+     "    (void)0;"),
+    ("weight gradient dots with the next row",
+     "* (double)load_elem(y, y_dt, (int64_t)r * H + h);",
+     "* (double)load_elem(y, y_dt, (int64_t)((r + 1) % y_rows) * H + h);"),
+    ("router gradient drops the mean term", "((double)d_topk_w[t * K + k] - s)", "((double)d_topk_w[t * K + k])"),
+    ("router gradient sign flipped", "((double)d_topk_w[t * K + k] - s)", "(s - (double)d_topk_w[t * K + k])"),
+    ("router gradient uses slot 0's weight", "acc[e] += (double)topk_w[t * K + k] *", "acc[e] += (double)topk_w[t * K] *"),
 ]
 
 
@@ -85,6 +98,12 @@ def _pins():
         _combine_exact_bound,
         _precombine_exact_bound,
         _route_brute_force,
+        lambda: bw.test_combine_backward_matches_autograd("f32", "f32", True, "drop"),
+        lambda: bw.test_combine_backward_matches_autograd("bf16", "bf16", True, "holes"),
+        lambda: bw.test_combine_backward_matches_autograd("f32", "f32", False, "standard"),
+        bw.test_dispatch_backward_is_the_unit_weight_combine,
+        bw.test_route_backward_matches_autograd_and_finite_differences,
+        bw.test_route_backward_closed_forms,
     ]
     return checks
 
