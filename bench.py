@@ -32,11 +32,20 @@ _COMBINE_SRC = ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd
 # Standard and drop-and-pad steps run `permute` and `combine`; group-mode steps run the two
 # dispatch stages (send: one copy per token and group; receive: group slots to expert-major
 # rows), the per-group pre-combine and the final sum over groups.
+# With --backward the step is the backward of the path on one saved forward index: the combine's
+# backward (expert-row gradient and weight gradient), the dispatch's backward (the unit-weight
+# combine of the expert-row gradient; in group mode the unit-weight pre-combine, then the final
+# sum) and the router softmax's backward.
 KERNEL_SOURCES = {"permute": _PERMUTE_SRC, "combine": _COMBINE_SRC, "dispatch_send": _PERMUTE_SRC,
-                  "dispatch_recv": _PERMUTE_SRC, "precombine": _COMBINE_SRC, "final_sum": _COMBINE_SRC}
+                  "dispatch_recv": _PERMUTE_SRC, "precombine": _COMBINE_SRC, "final_sum": _COMBINE_SRC,
+                  "combine_bwd": _COMBINE_SRC, "dispatch_bwd": _COMBINE_SRC, "dispatch_bwd_recv": _COMBINE_SRC,
+                  "dispatch_bwd_send": _COMBINE_SRC}
 KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine_kernel",
                   "dispatch_send": "permute_scatter_vec16_kernel", "dispatch_recv": "permute_grouped_vec16_kernel",
-                  "precombine": "precombine_kernel", "final_sum": "combine_kernel"}
+                  "precombine": "precombine_kernel", "final_sum": "combine_kernel",
+                  "combine_bwd": "combine_backward_kernel", "dispatch_bwd": "combine_kernel",
+                  "dispatch_bwd_recv": "precombine_kernel", "dispatch_bwd_send": "combine_kernel"}
+METRIC_BACKWARD = "backward of permute+combine (and router softmax) effective HBM GB/s (% of peak)"
 
 
 def log(*a):
@@ -50,6 +59,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=3, help="named workload id (see workloads.py)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (for scaling PMC byte counters)")
     return p.parse_args()
@@ -155,7 +166,29 @@ def main():
     calls = [("route", "route", lambda: m.route_topk(logits, K, out=(gi, gw))),
              ("index", "index", lambda: m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix))]
     src = xp if y is None else y
-    if gs:
+    if args.backward:
+        # one forward pass (not timed) leaves the saved state the backward consumes
+        for _, _, call in calls:
+            call()
+        if y is None:
+            m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=xp)
+        dout = to_dev(torch, wl.expert_outputs((*key, 7), T, H, dt))
+        dxp = to_dev(torch, wl.expert_outputs((*key, 8), rows, H, dt))
+        dy = torch.empty((rows, H), dtype=tdt, device="cuda")
+        dw = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        dx = torch.empty((T, H), dtype=tdt, device="cuda")
+        dlog = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        calls = [("combine_bwd", "combine_bwd",
+                  lambda: m.unpermute_combine_backward(dout, src, ix.row_of, gw, src_row=ix.sorted_indices,
+                                                       out=(dy, dw)))]
+        if gs:
+            calls += [("dispatch_bwd_recv", "dispatch_bwd",
+                       lambda: m.group_precombine(dxp, ix.row_of, None, gi, E, gs, ix.slot_of, out=part)),
+                      ("dispatch_bwd_send", "dispatch_bwd", lambda: m.unpermute_combine(part, ix.slot_of, None, out=dx))]
+        else:
+            calls += [("dispatch_bwd", "dispatch_bwd", lambda: m.unpermute_combine(dxp, ix.row_of, None, out=dx))]
+        calls += [("route_bwd", "route_bwd", lambda: m.route_topk_backward(gi, gw, dw, E, out=dlog))]
+    elif gs:
         # the number of group slots is only known on the device; every call is bounded by its
         # upper bound T*min(K,G) instead, so the step never waits for the host
         calls += [("dispatch_send", "permute", lambda: m.permute_scatter(x, ix.slot_of, gbuf.shape[0], out=gbuf)),
@@ -202,7 +235,16 @@ def main():
     routed = int((row_of >= 0).any(axis=1).sum()) if K else 0  # distinct source rows the permute reads
     kbytes = {"route": T * E * 4 + T * K * 8,
               "index": T * K * 8 + rows * 8 + T * K * 4 + E * 4 * 3}
-    if gs:
+    if args.backward:
+        kbytes = {"combine_bwd": T * H * b + valid * H * b + rows * H * b + T * K * 8 + rows * 4 + T * K * 4,
+                  "route_bwd": T * K * 12 + T * E * 4}
+        if gs:
+            n = int(ix.n_slots.item())
+            kbytes.update(dispatch_bwd_recv=valid * H * b + 2 * T * K * 4 + n * H * 4,
+                          dispatch_bwd_send=n * H * 4 + T * G * 4 + T * H * b)
+        else:
+            kbytes.update(dispatch_bwd=valid * H * b + T * K * 4 + T * H * b)
+    elif gs:
         n = int(ix.n_slots.item())
         kbytes.update(dispatch_send=routed * H * b + n * 4 + n * H * b,
                       dispatch_recv=n * H * b + rows * 4 + rows * H * b,
@@ -221,7 +263,8 @@ def main():
     def gbs(nbytes, us):
         return round(nbytes / (us * 1e-6) / 1e9, 1)
 
-    hbm_kernels = [name for name, stage, _ in calls if stage in ("permute", "combine")]
+    hbm_stages = ("permute", "combine", "combine_bwd", "dispatch_bwd")
+    hbm_kernels = [name for name, stage, _ in calls if stage in hbm_stages]
     dom = max(hbm_kernels, key=lambda k: kernel_us[k])
     achieved = kbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -230,7 +273,7 @@ def main():
                 "avg_launch_us": round(kernel_us[dom], 2)}
 
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_BACKWARD if args.backward else METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": c["name"], "T": T, "H": H, "E": E, "K": K, "capacity": cap,
@@ -238,15 +281,20 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "routed_tokens_per_s": round(routed_per_s, 1),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "stage_gbs": {k: gbs(stage_bytes[k], stage_us[k]) for k in ("permute", "combine")},
+        "stage_gbs": {k: gbs(stage_bytes[k], stage_us[k]) for k in stage_us if k in hbm_stages},
         "kernel_us": {k: round(v, 2) for k, v in kernel_us.items()},
         "kernel_gbs": {k: gbs(kbytes[k], kernel_us[k]) for k in hbm_kernels},
         "kernel_bytes": kbytes,
         "max_expert_count": int(counts.max()), "empty_experts": int((counts == 0).sum()),
         "roofline": roofline,
     }
+    if args.backward:
+        result["pass"] = "backward"
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes)
+        if args.backward:
+            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, step_bytes)
+        else:
+            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes)
     print(json.dumps(result), flush=True)
 
 
@@ -282,6 +330,39 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes):
             "sample": f"the whole workload ({c['name']}), one pass, best of 2, single thread",
             "seconds_per_pass": round(best, 3),
             "routed_tokens_per_s": round(T * K / best, 1)}
+
+
+def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, step_bytes):
+    """The CPU oracle's backward (single thread) on the same saved forward state, 2 passes."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    T, H, E, K, gs = c["T"], c["H"], c["E"], c["K"], c["group_size"]
+    out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
+    idx, w = oracle.route_topk(logits_np, K)
+    ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs)
+    rows = len(ix["sorted_indices"])
+    y = oracle.permute(x_np, ix["sorted_indices"]) if y_np is None else y_np
+    dout = wl.expert_outputs((*key, 7), T, H, c["dtype"])
+    dxp = wl.expert_outputs((*key, 8), rows, H, c["dtype"])
+    best = None
+    for _ in range(2):
+        t0 = time.perf_counter()
+        _, dw = oracle.combine_backward(dout, y, ix["row_of"], w, out_dt)
+        if gs:
+            n = int(ix["n_slots"][0])
+            part = oracle.group_precombine(dxp, ix["row_of"], None, idx, E, gs, ix["slot_of"], n)
+            oracle.unpermute_combine(part, ix["slot_of"], None, out_dt)
+        else:
+            oracle.unpermute_combine(dxp, ix["row_of"], None, out_dt)
+        oracle.route_topk_backward(idx, w, dw, E)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return {"value": round(step_bytes / best / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole backward of the workload ({c['name']}), one pass, best of 2, single thread",
+            "seconds_per_pass": round(best, 3)}
 
 
 if __name__ == "__main__":

@@ -210,6 +210,37 @@ moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, i
                                 const int32_t *slot_of, int64_t slots_cap, float *partials,
                                 hipStream_t stream);
 
+/* Backward of moe_unpermute_combine ([Combine] §4: the combine is linear in the expert outputs,
+ * so its backward is the transposed map -- a dispatch of the output gradient back to the expert
+ * rows -- and the router gradient reaches only the selected slots):
+ *   dy[row_of[t,k], :] = w[t,k] * dout[t, :]   (float32 product, stored as dy_dt)
+ *   dw[t, k] = sum_h dout[t,h] * y[row_of[t,k], h]   (float32, summed in a fixed order: each
+ *              thread's chunks in order, a butterfly over the wavefront, the wavefronts in
+ *              order; 0 for a slot whose row is outside [0, y_rows))
+ * and, when src_row is given, every row r of dy with src_row[r] outside [0, T) is written as
+ * zeros (rows that fed no output: padding, the unused tail). Each row of dy must be named by at
+ * most one slot; other rows are left untouched.
+ *   dout [T, H] (dout_dt); y [y_rows, H] (y_dt; may be NULL when dw is NULL); row_of, w [T, K]
+ *   (w NULL: unit weights, dy = dout); src_row [y_rows] (moe_index.sorted_indices) or NULL;
+ *   dy [y_rows, H] (dy_dt); dw [T, K] float32 or NULL (not computed).
+ * The backward of the dispatch needs no call of its own ([Combine] §4.1): it is the unit-weight
+ * combine of the expert-row gradient, moe_unpermute_combine(dxp, ..., row_of, NULL, ...); in
+ * group mode moe_group_precombine with w = NULL followed by the final sum over groups. */
+moe_status moe_unpermute_combine_backward(const void *dout, moe_dtype dout_dt, const void *y, moe_dtype y_dt,
+                                          int64_t y_rows, int64_t H, const int32_t *row_of, const float *w,
+                                          int64_t T, int32_t K, const int32_t *src_row, void *dy, moe_dtype dy_dt,
+                                          float *dw, hipStream_t stream);
+
+/* Backward of moe_route_topk's softmax over the K selected logits ([Scratch] §3, §27: the
+ * softmax runs over the selected scores; [Combine] §6: only the selected experts carry router
+ * gradient, the selection itself being piecewise constant). With w = topk_w, g = d_topk_w:
+ *   d_logits[t, topk_idx[t,k]] += w[t,k] * (g[t,k] - sum_j w[t,j] g[t,j])
+ * in double (the sum over j in slot order, the slots in order), rounded once to float32; every
+ * other logit of the row gets 0. Slots with an id outside [0, E) give nothing.
+ *   topk_idx, topk_w, d_topk_w [T, K]; d_logits [T, E] float32, every entry written. */
+moe_status moe_route_topk_backward(const int32_t *topk_idx, const float *topk_w, const float *d_topk_w, int64_t T,
+                                   int32_t E, int32_t K, float *d_logits, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

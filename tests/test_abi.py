@@ -85,6 +85,20 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, None, 2, 2, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, -1, 2, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute_grouped(None, 0, 8, 1, None, 0, None, 0, 2, None, None) == capi.MOE_OK
+    assert lib.moe_route_topk_backward(fake, fake, fake, 4, 8, 9, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_route_topk_backward(fake, fake, fake, 4, 2048, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk_backward(fake, None, fake, 4, 8, 2, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_route_topk_backward(None, None, None, 0, 8, 2, None, None) == capi.MOE_OK
+    assert lib.moe_unpermute_combine_backward(fake, 1, fake, 1, 4, 8, fake, None, 2, 2000, None, fake, 1, None,
+                                              None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine_backward(None, 1, fake, 1, 4, 8, fake, None, 2, 2, None, fake, 1, None,
+                                              None) == capi.MOE_ERR_INVALID
+    assert lib.moe_unpermute_combine_backward(fake, 1, None, 1, 4, 8, fake, None, 2, 2, None, fake, 1, fake,
+                                              None) == capi.MOE_ERR_INVALID  # dw needs y
+    assert lib.moe_unpermute_combine_backward(fake, 7, fake, 1, 4, 8, fake, None, 2, 2, None, fake, 1, None,
+                                              None) == capi.MOE_ERR_INVALID
+    assert lib.moe_unpermute_combine_backward(None, 1, None, 1, 4, 8, None, None, 0, 2, None, None, 1, None,
+                                              None) == capi.MOE_OK  # no tokens, no gather map: nothing to do
     # hidden rows longer than 2^31 - 1 bytes are refused (buffer resources address a row in 32 bits)
     big = 1 << 30
     assert lib.moe_permute(fake, 4, big, 1, fake, 4, fake, None) == capi.MOE_ERR_UNSUPPORTED  # bf16: 2 GiB rows

@@ -461,3 +461,144 @@ def test_pipeline_is_deterministic(m):
     a = host(run_workload(m, 2))
     b = host(run_workload(m, 2))
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ backward
+
+
+def _dw_bound(dout, y, row_of, H):
+    """Error bound of the kernel's fixed-order float32 dot: at most ceil(H/64) + 30 roundings
+    along any product's path (per-lane chain, wavefront butterfly, wavefronts), each at most
+    2^-24 of the sum of |products|; plus the oracle's own rounding to float32."""
+    d = np.abs(wl.bf16_bits_to_f32(dout) if dout.dtype == np.uint16 else dout).astype(np.float64)
+    yy = np.abs(wl.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y).astype(np.float64)
+    mag = np.einsum("th,tkh->tk", d, yy[np.clip(row_of, 0, len(yy) - 1)])
+    mag[(row_of < 0) | (row_of >= len(yy))] = 0.0
+    return (-(-H // 64) + 30) * 2.0 ** -24 * mag + 2.0 ** -130
+
+
+def _check_dw(got, want, bound):
+    diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    assert (diff <= bound + 2.0 ** -24 * np.abs(want.astype(np.float64))).all(), float((diff - bound).max())
+
+
+@pytest.mark.parametrize("dts", [("bf16", "bf16", "bf16"), ("f32", "f32", "f32"), ("bf16", "bf16", "f32"),
+                                 ("f32", "bf16", "bf16")])
+@pytest.mark.parametrize("H,T,E,K,mode", [(7168, 130, 64, 8, "standard"), (1000, 200, 16, 4, "drop"),
+                                          (5, 90, 8, 2, "holes"), (520, 150, 32, 8, "holes"), (8, 300, 8, 2, "drop"),
+                                          (4096, 64, 128, 16, "standard")])
+@pytest.mark.parametrize("weighted", [True, False])
+def test_combine_backward(m, dts, H, T, E, K, mode, weighted):
+    ddt, ydt, dydt = dts
+    say(f"combine_backward dout={ddt} y={ydt} dy={dydt} H={H} T={T} E={E} K={K} {mode} weighted={weighted}")
+    key = wl.case_key(33, H, T, E, K)
+    logits = wl.router_logits(key, T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    if mode == "holes":
+        idx[np.random.default_rng([*key, 4]).random((T, K)) < 0.2] = -1
+    cap = oracle.capacity(T, K, E, 1, 2) if mode == "drop" else 0
+    ix = oracle.build_index(idx, w, E, capacity=cap)
+    rows = len(ix["sorted_indices"])
+    y = wl.expert_outputs(key, rows, H, ydt)
+    dout = wl.expert_outputs((*key, 1), T, H, ddt)
+    ww = w if weighted else None
+    dy_np = np.uint16 if dydt == "bf16" else np.float32
+    want_dy, want_dw = oracle.combine_backward(dout, y, ix["row_of"], ww, dy_np)
+    dy, dw = m.unpermute_combine_backward(dev(dout), dev(y), dev(ix["row_of"]), None if ww is None else dev(ww),
+                                          src_row=dev(ix["sorted_indices"]),
+                                          dy_dtype=torch.bfloat16 if dydt == "bf16" else torch.float32)
+    assert_exact(host(dy), want_dy, "dy")
+    _check_dw(host(dw), want_dw, _dw_bound(dout, y, ix["row_of"], H))
+    assert (host(dw)[ix["row_of"] < 0] == 0).all()
+
+
+def test_combine_backward_without_dw_and_without_zero_rows(m):
+    key = wl.case_key(34)
+    T, K, H, rows = 50, 2, 64, 130
+    row_of = np.random.default_rng(1).permutation(rows)[: T * K].astype(np.int32).reshape(T, K)
+    dout = wl.expert_outputs(key, T, H, "bf16")
+    want_dy, _ = oracle.combine_backward(dout, np.zeros((rows, H), np.uint16), row_of, None, np.uint16, want_dw=False)
+    out = dev(np.full((rows, H), 0x1234, np.uint16))
+    dy, dw = m.unpermute_combine_backward(dev(dout), None, dev(row_of), num_rows=rows, want_dw=False,
+                                          out=(out, None))
+    assert dw is None
+    got = host(dy)
+    named = np.zeros(rows, bool)
+    named[row_of.reshape(-1)] = True
+    assert_exact(got[named], want_dy[named], "named rows")
+    assert (got[~named] == 0x1234).all()  # no gather map: other rows untouched
+
+
+@pytest.mark.parametrize("T,E,K,holes", [(1, 8, 1, False), (333, 64, 8, False), (1000, 256, 8, True),
+                                         (77, 1000, 32, False), (50, 5, 5, True), (513, 128, 2, False)])
+def test_route_topk_backward(m, T, E, K, holes):
+    say(f"route_backward T={T} E={E} K={K} holes={holes}")
+    key = wl.case_key(35, T, E, K)
+    logits = wl.router_logits(key, T, E, zipf_s=1.0)
+    idx, w = oracle.route_topk(logits, K)
+    if holes:
+        idx[np.random.default_rng([*key, 2]).random((T, K)) < 0.2] = -1
+    g = wl.random_weights((*key, 3), T, K) - 0.5
+    want = oracle.route_topk_backward(idx, w, g, E)
+    got = host(m.route_topk_backward(dev(idx), dev(w), dev(g), E))
+    assert_exact(got, want, "d_logits")
+
+
+def test_backward_no_tokens(m):
+    d = m.route_topk_backward(torch.zeros((0, 2), dtype=torch.int32, device=DEV),
+                              torch.zeros((0, 2), dtype=torch.float32, device=DEV),
+                              torch.zeros((0, 2), dtype=torch.float32, device=DEV), 8)
+    torch.cuda.synchronize()
+    assert d.shape == (0, 8)
+    # no tokens but a gather map: every row of dy fed nothing and is zero
+    dy, dw = m.unpermute_combine_backward(torch.zeros((0, 16), dtype=torch.bfloat16, device=DEV),
+                                          torch.ones((5, 16), dtype=torch.bfloat16, device=DEV),
+                                          torch.zeros((0, 2), dtype=torch.int32, device=DEV),
+                                          src_row=torch.full((5,), -1, dtype=torch.int32, device=DEV),
+                                          out=(torch.ones((5, 16), dtype=torch.bfloat16, device=DEV), None))
+    assert (host(dy) == 0).all() and dw.shape == (0, 2)
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3, 5])
+def test_backward_workload(m, cfg_id):
+    """Backward at the named workloads' full size, in the launch configuration bench.py --backward
+    times: sampled tokens against the oracle (their dy rows bit for bit, their dw within the
+    bound), every padding row zero, and the dispatch backward against the oracle's combine."""
+    c = wl.WORKLOADS[cfg_id]
+    T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
+    say(f"backward workload {cfg_id}: {c['name']}")
+    key = wl.workload_key(cfg_id)
+    cap = oracle.capacity(T, K, E, *c["cf"]) if c["cf"] else 0
+    logits = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])
+    idx, w = m.route_topk(dev(logits), K)
+    ix = m.build_index(idx, w, E, capacity=cap)
+    rows = ix.rows
+    y = wl.expert_outputs(key, rows, H, dt)
+    dout = wl.expert_outputs((*key, 7), T, H, dt)
+    dxp = wl.expert_outputs((*key, 8), rows, H, dt)
+    dy, dw = m.unpermute_combine_backward(dev(dout), dev(y), ix.row_of, w, src_row=ix.sorted_indices)
+    dx = m.unpermute_combine(dev(dxp), ix.row_of)
+    dlog = m.route_topk_backward(idx, w, dw, E)
+    torch.cuda.synchronize()
+    row_of, w_np, idx_np = host(ix.row_of), host(w), host(idx)
+    src = host(ix.sorted_indices)
+    ts = sample_rows(T, 600, cfg_id)
+    sub = row_of[ts]
+    used = np.unique(sub[sub >= 0])
+    remap = np.full(rows, -1, np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    sub_local = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
+    want_dy, want_dw = oracle.combine_backward(dout[ts], y[used], sub_local, w_np[ts],
+                                               np.uint16 if dt == "bf16" else np.float32)
+    got_dy = host(dy[torch.from_numpy(used).to(DEV)])
+    assert_exact(got_dy, want_dy, "dy rows of the sampled tokens")
+    dw_np = host(dw)
+    _check_dw(dw_np[ts], want_dw, _dw_bound(dout[ts], y[used], sub_local, H))
+    pad = np.flatnonzero(src < 0)
+    if len(pad):
+        pr = pad[sample_rows(len(pad), 500, cfg_id + 1)]
+        assert (host(dy[torch.from_numpy(pr).to(DEV)]) == 0).all(), "padding rows of dy must be zero"
+    want_dx = oracle.unpermute_combine(dxp, row_of[ts], None, np.uint16 if dt == "bf16" else np.float32)
+    assert_exact(host(dx[torch.from_numpy(ts).to(DEV)]), want_dx, "dispatch backward (sampled tokens)")
+    want_dl = oracle.route_topk_backward(idx_np, w_np, dw_np, E)
+    assert_exact(host(dlog), want_dl, "router gradient")

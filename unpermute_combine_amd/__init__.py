@@ -6,8 +6,10 @@ per-group local pre-combine, as hand-written HIP kernels behind a C ABI
 (``include/moe_dispatch.h``, ``libmoe_dispatch.so``). This package is the torch binding.
 """
 from .ops import (MoeIndex, alloc_index, build_index, expert_capacity, group_precombine, permute,
-                  permute_grouped, permute_scatter, route_topk, unpermute_combine, workspace_bytes)
+                  permute_grouped, permute_scatter, route_topk, route_topk_backward, unpermute_combine,
+                  unpermute_combine_backward, workspace_bytes)
 from ._capi import MoeError, lib
 
 __all__ = ["MoeIndex", "MoeError", "alloc_index", "build_index", "expert_capacity", "group_precombine",
-           "lib", "permute", "permute_grouped", "permute_scatter", "route_topk", "unpermute_combine", "workspace_bytes"]
+           "lib", "permute", "permute_grouped", "permute_scatter", "route_topk", "route_topk_backward",
+           "unpermute_combine", "unpermute_combine_backward", "workspace_bytes"]

@@ -31,6 +31,9 @@ SIGNATURES = {
     "moe_permute": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _P]),
     "moe_permute_scatter": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i32, _P, _i64, _P, _P]),
     "moe_permute_grouped": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _i64, _i32, _P, _P]),
+    "moe_unpermute_combine_backward": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, _i64, _i64, _P, _P, _i64,
+                                                      _i32, _P, _P, ctypes.c_int, _P, _P]),
+    "moe_route_topk_backward": (ctypes.c_int, [_P, _P, _P, _i64, _i32, _i32, _P, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _P, _P, _i64, _i32, _P,
                                              ctypes.c_int, _P]),
     "moe_group_precombine": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _P, _P, _P, _i64, _i32, _i32,

@@ -464,6 +464,198 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
     }
 }
 
+// ---------------------------------------------------------------- combine backward
+// [Combine] §4: the combine is linear in the expert outputs, so its backward is the transposed
+// map -- a dispatch of the output gradient back to the expert rows, scaled by the weights -- and
+// the weights' gradient is a row dot product:
+//   dy[row_of[t,k]] = w[t,k] * dout[t]      (float32 product, stored as float32 or bf16)
+//   dw[t,k]         = <dout[t], y[row_of[t,k]]>
+// One workgroup per token. Each thread owns 8 elements at a time (chunk layout for bf16-only
+// rows, split layout as soon as one side is float32): it loads its part of dout[t] once, and per
+// batch of 8 slots the same part of their y rows (all loads in flight together), stores w*dout to
+// each dy row and accumulates one partial dot per slot. The partial dots are reduced in a fixed
+// order -- per lane over its chunks in order, each chunk's 8 products in order, then a butterfly
+// over the wavefront (xor 32, 16, ..., 1; lane 0's value), then the wavefronts in order -- so the
+// result is deterministic. An absent slot (row outside [0, y_rows)) has a zero-size resource: its
+// loads read 0 and its stores are dropped, and its dw is 0. Workgroups past the last token zero
+// the rows of dy that the gather map src_row leaves without a source (padding rows).
+constexpr int kBwdZeroRowsPerWave = 16;
+
+template <bool SPLIT>
+__device__ __forceinline__ int64_t chunk_e0(int64_t c)
+{
+    return SPLIT ? (c / kWave) * kUnit + 4 * (c % kWave) : 8 * c;
+}
+
+template <typename X, bool SPLIT>
+__device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, int64_t e0, float (&v)[8])
+{
+    if constexpr (SPLIT) {
+        const Part<X> a = Part<X>::load(r, e0);
+        const Part<X> b = Part<X>::load(r, e0 + kUnit / 2);
+        a.widen(v);
+        b.widen(v + 4);
+    } else {
+        const u32x4 q[1] = {ld16_buf<kPolicyStreamLoad>(r, static_cast<uint32_t>(e0 * 2))};
+        Chunk<uint16_t>::widen(q, v);
+    }
+}
+
+template <typename X, bool SPLIT>
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, int64_t e0, const float (&a)[8])
+{
+    if constexpr (SPLIT) {
+        store_parts(r, e0, a, static_cast<X *>(nullptr));
+    } else {
+        st16_buf<kPolicyStreamStore>(r, static_cast<uint32_t>(e0 * 2),
+                                     u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
+                                           pack_bf16x2(a[6], a[7])});
+    }
+}
+
+// Sums p[u] over the workgroup (fixed order, see above) and lets threads u < n write
+// dw[u] (0 for an absent slot). Ends with a barrier, so `red` can be reused.
+__device__ __forceinline__ void reduce_dots(float (&p)[kBatch], float (*red)[kBatch], int n, const int32_t *rows,
+                                            int64_t y_rows, float *dw)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+        for (int m = kWave / 2; m >= 1; m >>= 1)
+            p[u] += __shfl_xor(p[u], m);
+    if (lane == 0)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            red[wave][u] = p[u];
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) < n) {
+        float s = 0.0f;
+        for (int q = 0; q < static_cast<int>(blockDim.x / kWave); ++q)
+            s += red[q][threadIdx.x];
+        const int32_t r = rows[threadIdx.x];
+        dw[threadIdx.x] = (r >= 0 && r < y_rows) ? s : 0.0f;
+    }
+    __syncthreads();
+}
+
+template <typename D, typename Y, typename DY, bool SPLIT>
+__global__ __launch_bounds__(kMaxThreads) void combine_backward_kernel(
+    const D *__restrict__ dout, const Y *__restrict__ y, int64_t y_rows, int64_t H, const int32_t *__restrict__ row_of,
+    const float *__restrict__ w, int K, int64_t T, const int32_t *__restrict__ src_row, DY *__restrict__ dy,
+    float *__restrict__ dw)
+{
+    __shared__ float red[kMaxThreads / kWave][kBatch];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nwaves = blockDim.x / kWave;
+    const uint32_t dy_bytes = static_cast<uint32_t>(H * sizeof(DY));
+    const int64_t t = blockIdx.x;
+    if (t >= T) {
+        const int64_t first = ((t - T) * nwaves + threadIdx.x / kWave) * kBwdZeroRowsPerWave;
+        const int64_t i = first + lane;
+        const bool zero = lane < kBwdZeroRowsPerWave && i < y_rows && (src_row[i] < 0 || src_row[i] >= T);
+        uint64_t m = __ballot(zero);
+        const u32x4 z{0u, 0u, 0u, 0u};
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            const __amdgpu_buffer_rsrc_t d = make_rsrc(dy + (first + j) * H, dy_bytes);
+            for (uint32_t off = lane * 16u; off < dy_bytes; off += kWave * 16u)
+                st16_buf<kPolicyStreamStore>(d, off, z);
+        }
+        return;
+    }
+    const int64_t nchunk = SPLIT ? ceil_div(H, kUnit) * kWave : H / 8;
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout + t * H, static_cast<uint32_t>(H * sizeof(D)));
+    const uint32_t y_bytes = static_cast<uint32_t>(H * sizeof(Y));
+    for (int k0 = 0; k0 < K; k0 += kBatch) {
+        int32_t rb[kBatch];
+        float wb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int k = k0 + u;
+            const int32_t r = k < K ? row_of[t * K + k] : -1;
+            rb[u] = (r >= 0 && r < y_rows) ? r : -1;
+            wb[u] = (k < K && w) ? w[t * K + k] : 1.0f;
+        }
+        float p[kBatch] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
+            const int64_t e0 = chunk_e0<SPLIT>(c);
+            float d[8];
+            load8<D, SPLIT>(dr, e0, d);
+            if (dw) {
+                float yv[kBatch][8];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    load8<Y, SPLIT>(make_rsrc(y + static_cast<int64_t>(rb[u] < 0 ? 0 : rb[u]) * H, rb[u] < 0 ? 0u : y_bytes),
+                                    e0, yv[u]);
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        p[u] = __builtin_fmaf(d[e], yv[u][e], p[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[e] = wb[u] * d[e];
+                store8<DY, SPLIT>(make_rsrc(dy + static_cast<int64_t>(rb[u] < 0 ? 0 : rb[u]) * H, rb[u] < 0 ? 0u : dy_bytes),
+                                  e0, o);
+            }
+        }
+        if (dw)
+            reduce_dots(p, red, K - k0 < kBatch ? K - k0 : kBatch, row_of + t * K + k0, y_rows, dw + t * K + k0);
+    }
+}
+
+// Element-wise form (H not a multiple of 8, or unaligned rows): same arithmetic, one element
+// per thread at a time, the dot reduced as above.
+template <typename D, typename Y, typename DY>
+__global__ __launch_bounds__(kMaxThreads) void combine_backward_scalar_kernel(
+    const D *__restrict__ dout, const Y *__restrict__ y, int64_t y_rows, int64_t H, const int32_t *__restrict__ row_of,
+    const float *__restrict__ w, int K, int64_t T, const int32_t *__restrict__ src_row, DY *__restrict__ dy,
+    float *__restrict__ dw)
+{
+    __shared__ float red[kMaxThreads / kWave][kBatch];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nwaves = blockDim.x / kWave;
+    const int64_t t = blockIdx.x;
+    if (t >= T) {
+        const int64_t first = ((t - T) * nwaves + threadIdx.x / kWave) * kBwdZeroRowsPerWave;
+        const int64_t i = first + lane;
+        const bool zero = lane < kBwdZeroRowsPerWave && i < y_rows && (src_row[i] < 0 || src_row[i] >= T);
+        uint64_t m = __ballot(zero);
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            for (int64_t h = lane; h < H; h += kWave)
+                store1(dy + (first + j) * H + h, 0.0f);
+        }
+        return;
+    }
+    for (int k0 = 0; k0 < K; k0 += kBatch) {
+        float p[kBatch] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int k = k0 + u;
+            const int32_t r = k < K ? row_of[t * K + k] : -1;
+            if (r < 0 || r >= y_rows)
+                continue;
+            const float wk = w ? w[t * K + k] : 1.0f;
+            for (int64_t h = threadIdx.x; h < H; h += blockDim.x) {
+                const float d = load1(dout + t * H + h);
+                store1(dy + static_cast<int64_t>(r) * H + h, wk * d);
+                if (dw)
+                    p[u] = __builtin_fmaf(d, load1(y + static_cast<int64_t>(r) * H + h), p[u]);
+            }
+        }
+        if (dw)
+            reduce_dots(p, red, K - k0 < kBatch ? K - k0 : kBatch, row_of + t * K + k0, y_rows, dw + t * K + k0);
+    }
+}
+
 // Threads per workgroup: one per `cpt` 8-element chunks, whole wavefronts, at most 1024.
 // Measured on MI355X: a token with 8 terms at H = 7168 combines fastest with one chunk per
 // thread (361 us vs 372 us with two per launch of the bf16 combine), tokens with few terms
@@ -515,6 +707,42 @@ moe_status launch_precombine(const void *y, int64_t y_rows, int64_t H, const int
     return launch_status();
 }
 
+template <typename D, typename Y, typename DY>
+moe_status launch_combine_backward(const void *dout, const void *y, int64_t y_rows, int64_t H, const int32_t *row_of,
+                                   const float *w, int64_t T, int K, const int32_t *src_row, void *dy, float *dw,
+                                   hipStream_t stream)
+{
+    constexpr bool split = sizeof(D) == 4 || sizeof(Y) == 4 || sizeof(DY) == 4;
+    const bool vec = H % 8 == 0 && (T == 0 || aligned16(dout)) && (y_rows == 0 || aligned16(dy)) &&
+                     (!dw || y_rows == 0 || aligned16(y));
+    const int threads = vec ? (split ? split_threads(H) : block_threads(H / 8, 1)) : block_threads(H, 1);
+    const int64_t zero_blocks = src_row ? ceil_div(ceil_div(y_rows, kBwdZeroRowsPerWave), threads / kWave) : 0;
+    const int64_t blocks = T + zero_blocks;
+    if (blocks > 0x7fffffff)
+        return MOE_ERR_UNSUPPORTED;
+    if (blocks == 0)
+        return MOE_OK;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
+    if (vec)
+        hipLaunchKernelGGL((combine_backward_kernel<D, Y, DY, split>), grid, block, 0, stream, static_cast<const D *>(dout),
+                           static_cast<const Y *>(y), y_rows, H, row_of, w, K, T, src_row, static_cast<DY *>(dy), dw);
+    else
+        hipLaunchKernelGGL((combine_backward_scalar_kernel<D, Y, DY>), grid, block, 0, stream,
+                           static_cast<const D *>(dout), static_cast<const Y *>(y), y_rows, H, row_of, w, K, T, src_row,
+                           static_cast<DY *>(dy), dw);
+    return launch_status();
+}
+
+template <typename D, typename Y>
+moe_status launch_combine_backward_dy(moe_dtype dy_dt, const void *dout, const void *y, int64_t y_rows, int64_t H,
+                                      const int32_t *row_of, const float *w, int64_t T, int K, const int32_t *src_row,
+                                      void *dy, float *dw, hipStream_t stream)
+{
+    return dy_dt == MOE_BF16
+               ? launch_combine_backward<D, Y, uint16_t>(dout, y, y_rows, H, row_of, w, T, K, src_row, dy, dw, stream)
+               : launch_combine_backward<D, Y, float>(dout, y, y_rows, H, row_of, w, T, K, src_row, dy, dw, stream);
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -564,4 +792,34 @@ extern "C" moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_
                                            slots_cap, partials, stream);
     return launch_precombine<float>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size, slot_of, slots_cap,
                                     partials, stream);
+}
+
+extern "C" moe_status moe_unpermute_combine_backward(const void *dout, moe_dtype dout_dt, const void *y, moe_dtype y_dt,
+                                                     int64_t y_rows, int64_t H, const int32_t *row_of, const float *w,
+                                                     int64_t T, int32_t K, const int32_t *src_row, void *dy,
+                                                     moe_dtype dy_dt, float *dw, hipStream_t stream)
+{
+    using namespace moe;
+    auto dt_ok = [](moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; };
+    if (y_rows < 0 || H < 1 || T < 0 || K < 1 || !dt_ok(dout_dt) || !dt_ok(y_dt) || !dt_ok(dy_dt))
+        return MOE_ERR_INVALID;
+    if (K > kMaxCombineK)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0 && (y_rows == 0 || !src_row))
+        return MOE_OK;
+    if ((T > 0 && (!row_of || !dout)) || (y_rows > 0 && !dy) || (dw && y_rows > 0 && !y))
+        return MOE_ERR_INVALID;
+    if (T > 0x7fffffff || H * 4 > 0x7fffffffLL)
+        return MOE_ERR_UNSUPPORTED;
+    if (dout_dt == MOE_BF16)
+        return y_dt == MOE_BF16
+                   ? launch_combine_backward_dy<uint16_t, uint16_t>(dy_dt, dout, y, y_rows, H, row_of, w, T, K, src_row, dy,
+                                                                    dw, stream)
+                   : launch_combine_backward_dy<uint16_t, float>(dy_dt, dout, y, y_rows, H, row_of, w, T, K, src_row, dy,
+                                                                 dw, stream);
+    return y_dt == MOE_BF16
+               ? launch_combine_backward_dy<float, uint16_t>(dy_dt, dout, y, y_rows, H, row_of, w, T, K, src_row, dy, dw,
+                                                             stream)
+               : launch_combine_backward_dy<float, float>(dy_dt, dout, y, y_rows, H, row_of, w, T, K, src_row, dy, dw,
+                                                          stream);
 }

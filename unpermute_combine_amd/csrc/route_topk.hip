@@ -159,6 +159,47 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
     }
 }
 
+// ---------------------------------------------------------------- backward
+// Gradient of the logits through the softmax over the K selected logits ([Scratch] §3/§27: the
+// softmax runs over the selected scores; [Combine] §6: only the selected experts carry router
+// gradient, the selection itself being piecewise constant). With w = topk_w and g = d_topk_w:
+//   d_logits[t, topk_idx[t,k]] += w[t,k] * (g[t,k] - sum_j w[t,j] g[t,j])
+// in double -- the sum over j in slot order, the slots in order -- rounded once to float32; every
+// other logit gets 0. One wavefront per token: lanes 0..K-1 hold the slots, every lane forms the
+// same sum from them with readlane, and each lane writes whole positions of the row (no two
+// lanes write one entry).
+constexpr int kBwdTokensPerBlock = kRouteThreads / kWave;
+
+__global__ __launch_bounds__(kRouteThreads) void route_topk_backward_kernel(
+    const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, const float *__restrict__ d_topk_w, int64_t T,
+    int E, int K, float *__restrict__ d_logits)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kBwdTokensPerBlock +
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+    if (t >= T)
+        return;
+    const bool mine = lane < K;
+    const int32_t id = mine ? topk_idx[t * K + lane] : -1;
+    const float wk = mine ? topk_w[t * K + lane] : 0.0f;
+    const float gk = mine ? d_topk_w[t * K + lane] : 0.0f;
+    double s = 0.0;
+    for (int j = 0; j < K; ++j)
+        s += static_cast<double>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j))) *
+             static_cast<double>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(gk), j)));
+    for (int e = lane; e < E; e += kWave) {
+        double v = 0.0;
+        for (int k = 0; k < K; ++k) {
+            if (__builtin_amdgcn_readlane(id, k) != e)
+                continue;
+            const double w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), k));
+            const double g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gk), k));
+            v += w1 * (g1 - s);
+        }
+        d_logits[t * E + e] = static_cast<float>(v);
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -193,5 +234,25 @@ extern "C" moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, 
         hipLaunchKernelGGL(route_topk_kernel<32>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
     else
         hipLaunchKernelGGL(route_topk_kernel<64>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+    return launch_status();
+}
+
+extern "C" moe_status moe_route_topk_backward(const int32_t *topk_idx, const float *topk_w, const float *d_topk_w,
+                                              int64_t T, int32_t E, int32_t K, float *d_logits, hipStream_t stream)
+{
+    using namespace moe;
+    if (T < 0 || E < 1 || K < 1 || K > E)
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_OK;
+    if (!topk_idx || !topk_w || !d_topk_w || !d_logits)
+        return MOE_ERR_INVALID;
+    const int64_t blocks = ceil_div(T, kBwdTokensPerBlock);
+    if (blocks > 0x7fffffff)
+        return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(route_topk_backward_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRouteThreads), 0, stream,
+                       topk_idx, topk_w, d_topk_w, T, E, K, d_logits);
     return launch_status();
 }

@@ -268,3 +268,81 @@ def group_precombine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[to
         _p(y), y_dt, y.shape[0], H, _p(row_of), _p(weights), _p(topk_idx), T, K, num_experts, group_size,
         _p(slot_of), out.shape[0], _p(out), _stream()))
     return out
+
+
+# ---------------------------------------------------------------- backward
+
+
+def unpermute_combine_backward(dout: torch.Tensor, y: Optional[torch.Tensor], row_of: torch.Tensor,
+                               weights: Optional[torch.Tensor] = None, src_row: Optional[torch.Tensor] = None,
+                               num_rows: Optional[int] = None, want_dw: bool = True,
+                               dy_dtype: Optional[torch.dtype] = None, out=None):
+    """Backward of unpermute_combine: dy[row_of[t,k]] = weights[t,k] * dout[t] (rows with
+    src_row out of range are zeros), dw[t,k] = <dout[t], y[row_of[t,k]]>. Returns (dy, dw|None).
+
+    The dispatch's backward is unpermute_combine(dxp, row_of) (unit weights)."""
+    _need(dout, "dout", None, 2)
+    dout_dt = _hidden_dt(dout, "dout")
+    _need(row_of, "row_of", torch.int32, 2)
+    T, K = row_of.shape
+    H = dout.shape[1]
+    if dout.shape[0] != T:
+        raise ValueError("dout must have one row per token of row_of")
+    if y is not None:
+        _need(y, "y", None, 2)
+        if y.shape[1] != H:
+            raise ValueError("y and dout must have the same hidden size")
+    elif want_dw:
+        raise ValueError("dw needs y")
+    rows = num_rows if num_rows is not None else (y.shape[0] if y is not None else None)
+    if rows is None:
+        raise ValueError("num_rows is needed without y")
+    if y is not None and y.shape[0] != rows:
+        raise ValueError("y must have num_rows rows")
+    y_dt = _hidden_dt(y, "y") if y is not None else dout_dt
+    if weights is not None:
+        _need(weights, "weights", torch.float32, 2)
+        if tuple(weights.shape) != (T, K):
+            raise ValueError("weights must be [T, K]")
+    if src_row is not None:
+        _need(src_row, "src_row", torch.int32, 1)
+        if src_row.shape[0] != rows:
+            raise ValueError("src_row must have num_rows entries")
+    ddt = dy_dtype or (y.dtype if y is not None else dout.dtype)
+    dy, dw = (None, None) if out is None else out
+    if dy is None:
+        dy = torch.empty((rows, H), dtype=ddt, device=dout.device)
+    _need(dy, "dy", ddt, 2)
+    if tuple(dy.shape) != (rows, H):
+        raise ValueError(f"dy must be [{rows}, {H}]")
+    if want_dw:
+        if dw is None:
+            dw = torch.empty((T, K), dtype=torch.float32, device=dout.device)
+        _need(dw, "dw", torch.float32, 2)
+        if tuple(dw.shape) != (T, K):
+            raise ValueError("dw must be [T, K]")
+    else:
+        dw = None
+    check("moe_unpermute_combine_backward", lib().moe_unpermute_combine_backward(
+        _p(dout), dout_dt, _p(y), y_dt, rows, H, _p(row_of), _p(weights), T, K, _p(src_row), _p(dy),
+        _DT[ddt], _p(dw), _stream()))
+    return dy, dw
+
+
+def route_topk_backward(topk_idx: torch.Tensor, topk_w: torch.Tensor, d_topk_w: torch.Tensor, num_experts: int,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the router logits through the softmax over the K selected logits."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _need(d_topk_w, "d_topk_w", torch.float32, 2)
+    T, K = topk_idx.shape
+    if tuple(topk_w.shape) != (T, K) or tuple(d_topk_w.shape) != (T, K):
+        raise ValueError("topk_w and d_topk_w must be [T, K]")
+    if out is None:
+        out = torch.empty((T, num_experts), dtype=torch.float32, device=topk_idx.device)
+    _need(out, "out", torch.float32, 2)
+    if tuple(out.shape) != (T, num_experts):
+        raise ValueError(f"out must be [{T}, {num_experts}]")
+    check("moe_route_topk_backward", lib().moe_route_topk_backward(
+        _p(topk_idx), _p(topk_w), _p(d_topk_w), T, num_experts, K, _p(out), _stream()))
+    return out
