@@ -215,8 +215,8 @@ moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, i
  * rows -- and the router gradient reaches only the selected slots):
  *   dy[row_of[t,k], :] = w[t,k] * dout[t, :]   (float32 product, stored as dy_dt)
  *   dw[t, k] = sum_h dout[t,h] * y[row_of[t,k], h]   (float32, summed in a fixed order: each
- *              thread's chunks in order, a butterfly over the wavefront, the wavefronts in
- *              order; 0 for a slot whose row is outside [0, y_rows))
+ *              thread's elements in order, a reduce-scatter butterfly over the wavefront, the
+ *              wavefronts in order; 0 for a slot whose row is outside [0, y_rows))
  * and, when src_row is given, every row r of dy with src_row[r] outside [0, T) is written as
  * zeros (rows that fed no output: padding, the unused tail). Each row of dy must be named by at
  * most one slot; other rows are left untouched.
