@@ -74,9 +74,10 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: int):
+def read_traffic(kernel: str, workload: int, backward: bool = False):
     """HBM bytes per launch from a committed PMC summary; None if absent or stale."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_SYMBOLS[kernel]}__workload{workload}__pmc.txt")
+    tag = f"workload{workload}_bwd" if backward else f"workload{workload}"
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_SYMBOLS[kernel]}__{tag}__pmc.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -268,7 +269,7 @@ def main():
     dom = max(hbm_kernels, key=lambda k: kernel_us[k])
     achieved = kbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dom, cid),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dom, cid, args.backward),
                 "kernel": KERNEL_SYMBOLS[dom], "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kernel_us[dom], 2)}
 
