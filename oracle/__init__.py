@@ -50,7 +50,7 @@ def _declare(lib):
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
     lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
     lib.oracle_route_topk.restype = ctypes.c_int
-    lib.oracle_build_index.argtypes = [P, P, i64, i32, i32, i32, i32] + [P] * 11
+    lib.oracle_build_index.argtypes = [P, P, i64, i32, i32, i32, i32, i32] + [P] * 11
     lib.oracle_build_index.restype = ctypes.c_int
     lib.oracle_permute.argtypes = [P, i64, i64, i32, P, i64, P]
     lib.oracle_permute.restype = ctypes.c_int
@@ -116,12 +116,20 @@ def route_topk(logits: np.ndarray, K: int):
     return idx, w
 
 
-def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_size: int = 0):
+def index_rows(T: int, K: int, E: int, capacity: int = 0, alignment: int = 0) -> int:
+    """Rows of the expert-major buffer: E*cap with a capacity, T*K + E*(A-1) with alignment A."""
+    if capacity > 0:
+        return E * capacity
+    return T * K + (E * (alignment - 1) if alignment > 1 else 0)
+
+
+def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_size: int = 0,
+                alignment: int = 0):
     """Expert-major index (the dispatch "handle"). Returns a dict of numpy arrays."""
     topk_idx = _c(topk_idx, np.int32)
     T, K = topk_idx.shape
     w = None if topk_w is None else _c(topk_w, np.float32)
-    rows = E * capacity if capacity > 0 else T * K
+    rows = index_rows(T, K, E, capacity, alignment)
     out = dict(
         counts=np.zeros(E, np.int32),
         group_list=np.zeros(E, np.int32),
@@ -142,7 +150,7 @@ def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_s
         )
         g_arrays = [out["slot_of"], out["gsrc"], out["esrc"], out["group_counts"], out["n_slots"]]
     rc = _load().oracle_build_index(
-        _ptr(topk_idx), _ptr(w), T, K, E, capacity, group_size,
+        _ptr(topk_idx), _ptr(w), T, K, E, capacity, group_size, alignment,
         _ptr(out["counts"]), _ptr(out["group_list"]), _ptr(out["kept_counts"]),
         _ptr(out["sorted_indices"]), _ptr(out["row_of"]), _ptr(out["permuted_probs"]),
         *[_ptr(a) for a in g_arrays])
@@ -154,7 +162,8 @@ def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_s
 
 
 def permute(src: np.ndarray, src_row: np.ndarray) -> np.ndarray:
-    """dst[i] = src[src_row[i]] bitwise; rows outside [0, len(src)) give zeros."""
+    """dst[i] = src[src_row[i]] bitwise; rows outside [0, len(src)) give zeros, except -2
+    (unused slack), which leaves the row as it is (here: the NaN poison)."""
     src = np.ascontiguousarray(src)
     _dt_of(src)
     src_rows, H = src.shape

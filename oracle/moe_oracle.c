@@ -163,8 +163,15 @@ int oracle_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
  * [e*cap, (e+1)*cap); the p-th token of expert e in the scan (p from 0) is kept at row
  * e*cap + p when p < cap and dropped otherwise (row_of = -1, it adds nothing in the combine);
  * rows past min(counts[e], cap) are padding: sorted_indices = -1, permuted_probs = 0.
- * kept_counts[e] = min(counts[e], cap). Without capacity, when some slots route nowhere the
- * rows after the last routed one are unused and hold -1 / 0 the same way.
+ * kept_counts[e] = min(counts[e], cap).
+ * Expert alignment (alignment A > 1, no capacity), [Combine] §6 (dispatch(..., expert_alignment=
+ * 128)) and the per-expert receive counts that DeepEP aligns before publishing them: expert e's
+ * segment is rounded up to ceil(counts[e]/A)*A rows, its tokens first (in the same order), then
+ * padding rows (sorted_indices = -1, permuted_probs = 0); group_list is the running sum of the
+ * aligned lengths, so every segment starts at a multiple of A. The buffer holds
+ * R = T*K + E*(A-1) rows, the most the aligned segments can need.
+ * Rows after the last segment (in the aligned layout, or when slots route nowhere) are unused
+ * slack: sorted_indices = -2, permuted_probs = 0 (no permute writes them).
  * Group mode (group_size > 0), [CANN] §1(1): experts form contiguous groups
  * g = e / group_size (a group stands for a rank); a token is sent once per group it uses.
  * The group slots are listed group by group, tokens ascending, in gsrc; slot_of[t,g] is the
@@ -172,7 +179,7 @@ int oracle_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
  * expert-major row r (the copy inside the group to each expert's input).
  * Drop-and-pad together with group mode is not supported. */
 int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K,
-                       int32_t E, int32_t capacity, int32_t group_size,
+                       int32_t E, int32_t capacity, int32_t group_size, int32_t alignment,
                        int32_t *counts, int32_t *group_list, int32_t *kept_counts,
                        int32_t *sorted_indices, int32_t *row_of, float *permuted_probs,
                        int32_t *slot_of, int32_t *gsrc, int32_t *esrc, int32_t *group_counts,
@@ -181,8 +188,10 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
     if (T < 0 || K < 1 || E < 1 || !counts || !group_list || !sorted_indices || !row_of ||
         (T > 0 && !topk_idx))
         return ORC_INVALID;
-    if (capacity > 0 && group_size > 0)
+    if (capacity > 0 && (group_size > 0 || alignment > 1))
         return ORC_UNSUPPORTED;
+    int64_t A = alignment > 1 ? alignment : 1;
+    int64_t R = capacity > 0 ? (int64_t)E * capacity : T * K + (int64_t)E * (A - 1);
     if (group_size > 0 && (E % group_size != 0 || !slot_of || !gsrc || !esrc ||
                            !group_counts || !n_slots))
         return ORC_INVALID;
@@ -193,6 +202,7 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
     /* masked_select over the [E][T][K] map, row-major */
     int64_t r = 0;
     for (int32_t e = 0; e < E; ++e) {
+        int64_t start = r;
         int64_t p = 0; /* position inside expert e's segment */
         for (int64_t t = 0; t < T; ++t) {
             for (int32_t k = 0; k < K; ++k) {
@@ -217,11 +227,19 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
             }
         }
         counts[e] = (int32_t)p;
+        if (capacity == 0) {
+            /* rows up to the aligned end of the segment are padding */
+            for (int64_t end = start + (p + A - 1) / A * A; r < end; ++r) {
+                sorted_indices[r] = -1;
+                if (permuted_probs)
+                    permuted_probs[r] = 0.0f;
+            }
+        }
     }
 
     int64_t run = 0;
     for (int32_t e = 0; e < E; ++e) {
-        run += counts[e];
+        run += capacity > 0 ? counts[e] : (counts[e] + A - 1) / A * A;
         group_list[e] = (int32_t)run;
     }
 
@@ -241,9 +259,9 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
         if (kept_counts)
             for (int32_t e = 0; e < E; ++e)
                 kept_counts[e] = counts[e];
-        /* slots that route nowhere leave rows [r, T*K) unused: -1 and probability 0 */
-        for (int64_t q = r; q < T * K; ++q) {
-            sorted_indices[q] = -1;
+        /* rows after the last segment are unused slack */
+        for (int64_t q = r; q < R; ++q) {
+            sorted_indices[q] = -2;
             if (permuted_probs)
                 permuted_probs[q] = 0.0f;
         }
@@ -273,9 +291,10 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
             group_counts[g] = (int32_t)cnt;
         }
         *n_slots = (int32_t)m;
-        /* expert-major row r holds token sorted_indices[r] for expert e(r); unused rows -1 */
-        for (int64_t q = 0; q < T * K; ++q)
-            esrc[q] = -1;
+        /* expert-major row r holds token sorted_indices[r] for expert e(r); padding rows -1,
+           unused slack -2 */
+        for (int64_t q = 0; q < R; ++q)
+            esrc[q] = q < r ? -1 : -2;
         for (int64_t t = 0; t < T; ++t)
             for (int32_t k = 0; k < K; ++k) {
                 int32_t e = topk_idx[t * K + k];
@@ -293,7 +312,8 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
 /* [Megatron] §1.1 step 5 (permuted_input = tokens.index_select(0, sorted_indices)) and
  * [Scratch] §12 (permuted_tokens = tokens[permute_indices]): row i of the output is a bitwise
  * copy of source row src_row[i]. A src_row outside [0, src_rows) (the padding rows of the
- * drop-and-pad layout carry -1) gives a row of zeros ([Scratch] §18 padded expert buffers).
+ * drop-and-pad and aligned layouts carry -1) gives a row of zeros ([Scratch] §18 padded expert
+ * buffers); src_row = -2 marks unused slack, a row that is left as it is.
  * elem_bytes is the size of one hidden element (4 or 2). */
 int oracle_permute(const void *src, int64_t src_rows, int64_t H, int32_t elem_bytes,
                    const int32_t *src_row, int64_t N, void *dst)
@@ -307,7 +327,7 @@ int oracle_permute(const void *src, int64_t src_rows, int64_t H, int32_t elem_by
         int32_t s = src_row[i];
         if (s >= 0 && s < src_rows)
             memcpy(d, (const unsigned char *)src + (size_t)s * row_bytes, row_bytes);
-        else
+        else if (s != -2)
             memset(d, 0, row_bytes);
     }
     return ORC_OK;

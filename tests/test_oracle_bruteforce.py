@@ -14,16 +14,20 @@ import oracle
 import workloads as wl
 
 
-def brute_index(ids, E, cap=0, gs=0, w=None):
+def brute_index(ids, E, cap=0, gs=0, w=None, align=0):
+    """The index by sorting (expert, token, slot) tuples and laying the segments out directly:
+    drop-and-pad rows e*cap + p; otherwise segments back to back, each rounded up to a multiple
+    of `align` (padding rows -1), rows after the last segment -2 (unused slack)."""
     T, K = ids.shape
     slots = sorted((int(ids[t, k]), t, k) for t in range(T) for k in range(K)
                    if 0 <= ids[t, k] < E)
     counts = [0] * E
     for e, _, _ in slots:
         counts[e] += 1
-    gl = list(accumulate(counts))
+    A = align if align > 1 else 1
     row_of = -np.ones((T, K), np.int64)
     if cap > 0:
+        gl = list(accumulate(counts))
         sorted_idx = -np.ones(E * cap, np.int64)
         pos = [0] * E
         for e, t, k in slots:
@@ -31,11 +35,19 @@ def brute_index(ids, E, cap=0, gs=0, w=None):
                 sorted_idx[e * cap + pos[e]] = t
                 row_of[t, k] = e * cap + pos[e]
             pos[e] += 1
+        total = E * cap
     else:
-        sorted_idx = -np.ones(T * K, np.int64)
-        for r, (e, t, k) in enumerate(slots):
-            sorted_idx[r] = t
-            row_of[t, k] = r
+        seglen = [-(-c // A) * A for c in counts]
+        gl = list(accumulate(seglen))
+        starts = [g - n for g, n in zip(gl, seglen)]
+        total = gl[-1] if E else 0
+        sorted_idx = np.full(T * K + E * (A - 1), -2, np.int64)
+        sorted_idx[:total] = -1
+        pos = [0] * E
+        for e, t, k in slots:
+            sorted_idx[starts[e] + pos[e]] = t
+            row_of[t, k] = starts[e] + pos[e]
+            pos[e] += 1
     probs = np.zeros(len(sorted_idx), np.float32)
     for e, t, k in slots:
         if row_of[t, k] >= 0:
@@ -48,7 +60,7 @@ def brute_index(ids, E, cap=0, gs=0, w=None):
         slot_of = -np.ones((T, G), np.int64)
         for m, (g, t) in enumerate(pairs):
             slot_of[t, g] = m
-        esrc = -np.ones(T * K, np.int64)
+        esrc = np.where(np.arange(len(sorted_idx)) < total, -1, -2)
         for e, t, k in slots:
             esrc[row_of[t, k]] = slot_of[t, e // gs]
         out.update(gsrc=[t for _, t in pairs], slot_of=slot_of.tolist(),
@@ -116,6 +128,42 @@ def test_group_mode_matches_pair_sort(case, gs):
     assert ix["esrc"].tolist() == bf["esrc"]
     assert int(ix["n_slots"][0]) == bf["n_slots"]
     assert ix["group_counts"].tolist() == bf["group_counts"]
+
+
+@settings(max_examples=200, deadline=None)
+@given(routing(max_e=8), st.sampled_from([2, 3, 4, 8, 128]), st.sampled_from([0, 1, 2, 4]))
+def test_aligned_index_matches_tuple_sort(case, align, gs):
+    ids, E = case
+    if gs and E % gs:
+        gs = 1
+    w = np.random.default_rng(ids.size + 2).random(ids.shape).astype(np.float32)
+    ix = oracle.build_index(ids, w, E, group_size=gs, alignment=align)
+    bf = brute_index(ids, E, gs=gs, w=w, align=align)
+    assert ix["counts"].tolist() == bf["counts"]
+    assert ix["group_list"].tolist() == bf["group_list"]
+    assert ix["sorted_indices"].tolist() == bf["sorted_indices"]
+    assert ix["row_of"].tolist() == bf["row_of"]
+    assert np.array_equal(ix["permuted_probs"], bf["permuted_probs"])
+    if gs:
+        assert ix["esrc"].tolist() == bf["esrc"]
+        assert ix["gsrc"].tolist() == bf["gsrc"]
+    gl = np.concatenate([[0], ix["group_list"]])
+    assert (gl % align == 0).all()  # every segment starts (and ends) at a multiple of the alignment
+    assert (np.diff(gl) - ix["counts"] >= 0).all() and (np.diff(gl) - ix["counts"] < align).all()
+
+
+def test_aligned_hand_example():
+    """[Scratch] §7's counts [3,2,4] laid out with alignment 4 (derived by hand): segments of 4,
+    4 and 4 rows, padding rows -1, the slack after the last segment -2."""
+    ids = np.array([[0], [0], [1], [0], [1], [2], [2], [2], [2]], np.int32)
+    ix = oracle.build_index(ids, None, 3, alignment=4)
+    assert ix["counts"].tolist() == [3, 2, 4]
+    assert ix["group_list"].tolist() == [4, 8, 12]
+    assert ix["sorted_indices"].tolist() == [0, 1, 3, -1, 2, 4, -1, -1, 5, 6, 7, 8] + [-2] * 6
+    assert ix["row_of"].reshape(-1).tolist() == [0, 1, 4, 2, 5, 8, 9, 10, 11]
+    x = np.arange(9 * 2, dtype=np.float32).reshape(9, 2) + 1
+    xp = oracle.permute(x, ix["sorted_indices"])
+    assert (xp[[3, 6, 7]] == 0).all() and np.isnan(xp[12:]).all()  # padding zero, slack untouched
 
 
 def test_group_mode_hand_example():

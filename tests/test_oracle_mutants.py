@@ -23,8 +23,14 @@ MUTANTS = [
      "topk_w[t * K + k] = (float)(ex[0] / z);"),
     ("softmax sum skips the first slot", "            z += ex[k];", "            if (k > 0) z += ex[k];"),
     ("softmax sign flipped", "ex[k] = exp((double)s[idx[k]] - m);", "ex[k] = exp(m - (double)s[idx[k]]);"),
-    ("group_list exclusive instead of inclusive", "        run += counts[e];\n        group_list[e] = (int32_t)run;",
-     "        group_list[e] = (int32_t)run;\n        run += counts[e];"),
+    ("group_list exclusive instead of inclusive",
+     "        run += capacity > 0 ? counts[e] : (counts[e] + A - 1) / A * A;\n        group_list[e] = (int32_t)run;",
+     "        group_list[e] = (int32_t)run;\n        run += capacity > 0 ? counts[e] : (counts[e] + A - 1) / A * A;"),
+    ("group_list ignores the alignment", "        run += capacity > 0 ? counts[e] : (counts[e] + A - 1) / A * A;",
+     "        run += counts[e];"),
+    ("aligned segments get no padding rows", "for (int64_t end = start + (p + A - 1) / A * A; r < end; ++r)",
+     "for (int64_t end = start + p; r < end; ++r)"),
+    ("unused slack marked as padding", "            sorted_indices[q] = -2;", "            sorted_indices[q] = -1;"),
     ("tokens scanned in descending order", "        for (int64_t t = 0; t < T; ++t) {\n            for (int32_t k = 0; k < K; ++k) {\n                if (topk_idx[t * K + k] != e)",
      "        for (int64_t t = T - 1; t >= 0; --t) {\n            for (int32_t k = 0; k < K; ++k) {\n                if (topk_idx[t * K + k] != e)"),
     ("row_of stored transposed", "                    row_of[t * K + k] = (int32_t)r;", "                    row_of[k * T + t] = (int32_t)r;"),
@@ -41,7 +47,8 @@ MUTANTS = [
      "esrc[row] = slot_of[t * G + e % G];"),
     ("permute copies the next row", "memcpy(d, (const unsigned char *)src + (size_t)s * row_bytes, row_bytes);",
      "memcpy(d, (const unsigned char *)src + (size_t)(s + 1 < src_rows ? s + 1 : s) * row_bytes, row_bytes);"),
-    ("permute leaves padding rows unwritten", "        else\n            memset(d, 0, row_bytes);", "        else\n            (void)0;"),
+    ("permute leaves padding rows unwritten", "        else if (s != -2)\n            memset(d, 0, row_bytes);",
+     "        else\n            (void)0;"),
     ("combine drops the accumulator", "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            store_elem(out, out_dt, t * H + h, acc);",
      "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), 0.0f);\n            }\n            store_elem(out, out_dt, t * H + h, acc);"),
     ("combine skips slot 0", "            for (int32_t k = 0; k < K; ++k) {\n                int32_t r = row_of[t * K + k];\n                if (r < 0 || r >= y_rows)\n                    continue;\n                float wk",
@@ -89,6 +96,7 @@ def _pins():
         pins.test_route_weights_form_distribution,
         pins.test_bf16_rounding_of_oracle,
         bf.test_group_mode_hand_example,
+        bf.test_aligned_hand_example,
         bf.test_identity_experts_reproduce_x,
         bf.test_k1_unit_weight_combine_is_bitwise_unpermute,
         bf.test_permute_zero_rows_and_bitwise_copy,
@@ -141,9 +149,10 @@ def _index_brute_force():
         ids = np.argsort(g.random((T, E)), axis=1)[:, :K].astype(np.int32)
         ids[g.random((T, K)) < 0.15] = -1
         w = g.random((T, K)).astype(np.float32)
-        for cap, gs in ((0, 0), (int(g.integers(1, 4)), 0), (0, [d for d in range(1, E + 1) if E % d == 0][-2 if E > 1 else 0])):
-            ix = oracle.build_index(ids, w, E, capacity=cap, group_size=gs)
-            want = bf.brute_index(ids, E, cap=cap, gs=gs, w=w)
+        divisor = [d for d in range(1, E + 1) if E % d == 0][-2 if E > 1 else 0]
+        for cap, gs, al in ((0, 0, 0), (int(g.integers(1, 4)), 0, 0), (0, divisor, 0), (0, 0, 4), (0, divisor, 3)):
+            ix = oracle.build_index(ids, w, E, capacity=cap, group_size=gs, alignment=al)
+            want = bf.brute_index(ids, E, cap=cap, gs=gs, w=w, align=al)
             assert np.array_equal(ix["permuted_probs"], want["permuted_probs"])
             assert ix["counts"].tolist() == want["counts"]
             assert ix["group_list"].tolist() == want["group_list"]

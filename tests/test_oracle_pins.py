@@ -41,7 +41,7 @@ def test_megatron_routing_map_example():
     ix = oracle.build_index(ids, None, E)
     R = len(g["sorted_indices"])
     assert ix["sorted_indices"][:R].tolist() == g["sorted_indices"]
-    assert ix["sorted_indices"][R:].tolist() == [-1] * (ids.size - R)
+    assert ix["sorted_indices"][R:].tolist() == [-2] * (ids.size - R)  # unused slack after the last segment
     assert ix["counts"].tolist() == [len(r) for r in g["expert_receives"]]
     # every routed (token, expert) pair finds its own token at its row
     for t in range(ids.shape[0]):
