@@ -59,6 +59,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=3, help="named workload id (see workloads.py)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--alignment", type=int, default=0,
+                   help="round every expert segment up to a multiple of this many rows (padding rows)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
@@ -146,7 +148,8 @@ def main():
     t0 = time.time()
     logits_np = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])
     x_np = wl.hidden_states(key, T, H, dt)
-    rows = E * cap if cap > 0 else T * K
+    align = args.alignment if args.alignment > 1 else 0
+    rows = m.index_rows(T, K, E, cap, align)
     y_np = None if c["identity_experts"] else wl.expert_outputs(key, rows, H, dt)
     logits = to_dev(torch, logits_np)
     x = to_dev(torch, x_np)
@@ -156,7 +159,7 @@ def main():
     # preallocated outputs: nothing is allocated inside the timed region
     gi = torch.empty((T, K), dtype=torch.int32, device="cuda")
     gw = torch.empty((T, K), dtype=torch.float32, device="cuda")
-    ix = m.alloc_index(T, K, E, cap, gs)
+    ix = m.alloc_index(T, K, E, cap, gs, alignment=align)
     xp = torch.empty((rows, H), dtype=tdt, device="cuda")
     out = torch.empty((T, H), dtype=tdt, device="cuda")
     G = E // gs if gs else 0
@@ -165,7 +168,8 @@ def main():
 
     # the step's calls in order: (kernel name, stage, call)
     calls = [("route", "route", lambda: m.route_topk(logits, K, out=(gi, gw))),
-             ("index", "index", lambda: m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix))]
+             ("index", "index", lambda: m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix,
+                                                      alignment=align))]
     src = xp if y is None else y
     if args.backward:
         # one forward pass (not timed) leaves the saved state the backward consumes
@@ -233,11 +237,12 @@ def main():
     row_of = ix.row_of.cpu().numpy()
     counts = ix.counts.cpu().numpy()
     valid = int((row_of >= 0).sum())  # rows the combine reads
+    used = int((ix.sorted_indices != -2).sum().item())  # rows written (the slack after the last segment is not)
     routed = int((row_of >= 0).any(axis=1).sum()) if K else 0  # distinct source rows the permute reads
     kbytes = {"route": T * E * 4 + T * K * 8,
               "index": T * K * 8 + rows * 8 + T * K * 4 + E * 4 * 3}
     if args.backward:
-        kbytes = {"combine_bwd": T * H * b + valid * H * b + rows * H * b + T * K * 8 + rows * 4 + T * K * 4,
+        kbytes = {"combine_bwd": T * H * b + valid * H * b + used * H * b + T * K * 8 + rows * 4 + T * K * 4,
                   "route_bwd": T * K * 12 + T * E * 4}
         if gs:
             n = int(ix.n_slots.item())
@@ -248,11 +253,11 @@ def main():
     elif gs:
         n = int(ix.n_slots.item())
         kbytes.update(dispatch_send=routed * H * b + n * 4 + n * H * b,
-                      dispatch_recv=n * H * b + rows * 4 + rows * H * b,
+                      dispatch_recv=n * H * b + rows * 4 + used * H * b,
                       precombine=valid * H * b + 2 * T * K * 4 + n * H * 4,
                       final_sum=n * H * 4 + T * G * 4 + T * H * b)
     else:
-        kbytes.update(permute=routed * H * b + rows * 4 + rows * H * b,
+        kbytes.update(permute=routed * H * b + rows * 4 + used * H * b,
                       combine=valid * H * b + 2 * T * K * 4 + T * H * b)
     stage_bytes = {}
     for name, stage, _ in calls:
@@ -277,7 +282,8 @@ def main():
         "metric": METRIC_BACKWARD if args.backward else METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
-        "config": {"workload": c["name"], "T": T, "H": H, "E": E, "K": K, "capacity": cap,
+        "config": {"workload": c["name"] + (f" align{align}" if align else ""), "T": T, "H": H, "E": E, "K": K,
+                   "capacity": cap, "alignment": align,
                    "group_size": gs, "zipf_s": c["zipf_s"], "seed_key": list(key)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "routed_tokens_per_s": round(routed_per_s, 1),
@@ -293,13 +299,13 @@ def main():
         result["pass"] = "backward"
     if not args.no_cpu_baseline:
         if args.backward:
-            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, step_bytes)
+            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, step_bytes)
         else:
-            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes)
+            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, step_bytes)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes):
+def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, step_bytes):
     """The CPU oracle as it stands (single thread) over the same whole workload, 2 passes."""
     import numpy as np
 
@@ -311,7 +317,7 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes):
     for _ in range(2):
         t0 = time.perf_counter()
         idx, w = oracle.route_topk(logits_np, K)
-        ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs)
+        ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
         if gs:
             gbuf = oracle.permute(x_np, ix["gsrc"])
             xp = oracle.permute(gbuf, ix["esrc"])
@@ -333,7 +339,7 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, step_bytes):
             "routed_tokens_per_s": round(T * K / best, 1)}
 
 
-def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, step_bytes):
+def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, step_bytes):
     """The CPU oracle's backward (single thread) on the same saved forward state, 2 passes."""
     import numpy as np
 
@@ -343,7 +349,7 @@ def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, step_bytes):
     T, H, E, K, gs = c["T"], c["H"], c["E"], c["K"], c["group_size"]
     out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
     idx, w = oracle.route_topk(logits_np, K)
-    ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs)
+    ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
     rows = len(ix["sorted_indices"])
     y = oracle.permute(x_np, ix["sorted_indices"]) if y_np is None else y_np
     dout = wl.expert_outputs((*key, 7), T, H, c["dtype"])

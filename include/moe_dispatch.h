@@ -54,6 +54,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
 
+/* Markers in gather maps (sorted_indices, esrc): a padding row, written as zeros by the
+ * permutes; and an unused row after the last expert segment (buffer slack when the buffer is
+ * sized by an upper bound), which no call writes. */
+#define MOE_ROW_PAD (-1)
+#define MOE_ROW_UNUSED (-2)
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char *moe_status_string(moe_status s);
 
@@ -79,19 +85,24 @@ moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
 
 /* The dispatch "handle" ([Combine] §3: computed once by dispatch, reused by combine).
  * All members are caller-owned device arrays, written by moe_build_index.
- * R = T*K in the standard and group modes, R = E*capacity in drop-and-pad mode. */
+ * R = moe_index_rows(...): T*K in the standard and group modes, E*capacity in drop-and-pad
+ * mode, T*K + E*(alignment-1) with expert alignment. */
 typedef struct moe_index {
     int32_t *counts;         /* [E] rows routed to each expert, before capacity ([Megatron] §1.2
                                 num_tokens_per_expert). Required. */
     int32_t *group_list;     /* [E] inclusive running sum of counts ([Scratch] §7:
                                 [3,2,4] -> [3,5,9]; expert e owns rows
-                                [group_list[e]-counts[e], group_list[e])). Required. */
+                                [group_list[e]-counts[e], group_list[e])); with expert
+                                alignment A the running sum of the aligned lengths
+                                ceil(counts/A)*A (expert e's segment ends at group_list[e], its
+                                tokens come first, then padding rows). Required. */
     int32_t *kept_counts;    /* [E] min(counts, capacity) in drop-and-pad mode, counts
                                 otherwise. May be NULL. */
     int32_t *sorted_indices; /* [R] source token of each expert-major row ([Megatron] §1.1,
                                 masked_select over the transposed routing map): experts in
-                                ascending order, tokens ascending inside an expert. Padding and
-                                unused rows hold -1. Required. */
+                                ascending order, tokens ascending inside an expert. Padding
+                                rows hold MOE_ROW_PAD (-1), rows after the last segment
+                                MOE_ROW_UNUSED (-2). Required. */
     int32_t *row_of;         /* [T, K] expert-major row of slot (t,k), -1 if the slot routes
                                 nowhere or was dropped (the saved mapping that makes the permute
                                 invertible, [Scratch] §26.5). Required. */
@@ -103,12 +114,18 @@ typedef struct moe_index {
     int32_t *gsrc;           /* [T*min(K,G)] source token of each group slot, groups ascending
                                 then tokens ascending; only the first n_slots entries are
                                 written. */
-    int32_t *esrc;           /* [R] group slot feeding each expert-major row; -1 on unused
-                                rows. */
+    int32_t *esrc;           /* [R] group slot feeding each expert-major row; MOE_ROW_PAD on
+                                padding rows, MOE_ROW_UNUSED after the last segment. */
     int32_t *group_counts;   /* [G] slots per group. */
     int32_t *n_slots;        /* [1] number of group slots M_g (the caller reads it back if it
                                 needs the exact size; gsrc may be sized by the upper bound). */
 } moe_index;
+
+/* Rows R of the expert-major arrays (sorted_indices, permuted_probs, esrc) and buffers for
+ * these sizes: E*capacity with capacity > 0, else T*K + E*(alignment-1) (alignment <= 1: T*K),
+ * the most that the segments rounded up to a multiple of the alignment can need. Returns -1 for
+ * invalid sizes, capacity together with alignment > 1, or R above 2^31 - 1. */
+int64_t moe_index_rows(int64_t T, int32_t K, int32_t E, int32_t capacity, int32_t alignment);
 
 /* Bytes of device workspace that moe_build_index needs for these sizes (the caller allocates
  * it, any alignment of at least 256 bytes). */
@@ -126,16 +143,23 @@ moe_status moe_build_index_workspace_size(int64_t T, int32_t K, int32_t E, int32
  *   group_size > 0 selects group mode ([CANN] §1(1)): experts e form G = E / group_size
  *            contiguous groups g = e / group_size, and slot_of/gsrc/esrc/group_counts/n_slots
  *            are written. capacity > 0 together with group_size > 0 is MOE_ERR_UNSUPPORTED.
- * The build is deterministic: no position depends on the timing of atomics. */
+ *   alignment > 1 selects expert alignment ([Combine] §6, dispatch(..., expert_alignment=128)):
+ *            each expert segment is rounded up to a multiple of the alignment, its tokens first
+ *            and MOE_ROW_PAD rows after them, so that every segment of the grouped GEMM input
+ *            starts at a multiple of the alignment; group_list follows the aligned segments.
+ *            Not with capacity (MOE_ERR_UNSUPPORTED); 0 or 1 means none.
+ * Rows after the last segment are MOE_ROW_UNUSED. The build is deterministic: no position
+ * depends on the timing of atomics. */
 moe_status moe_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K,
-                           int32_t E, int32_t capacity, int32_t group_size,
+                           int32_t E, int32_t capacity, int32_t group_size, int32_t alignment,
                            const moe_index *out, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
 /* Row gather ([Megatron] §1.1 step 5, permuted_input = tokens.index_select(0, sorted_indices);
  * [Scratch] §12, permuted_tokens = tokens[permute_indices]):
  *   dst[i, :] = src[src_row[i], :] copied bit for bit, for i in [0, N); a src_row outside
- *   [0, src_rows) (the -1 of padding rows) writes a row of zeros.
+ *   [0, src_rows) (MOE_ROW_PAD of padding rows) writes a row of zeros, except MOE_ROW_UNUSED,
+ *   which leaves row i untouched (this holds for every call that takes a gather map).
  *   src [src_rows, H] of dtype dt, src_row [N] int32, dst [N, H] of dtype dt.
  * Used for the standard dispatch (src_row = sorted_indices, N = R), drop-and-pad (which also
  * zero-fills the padding rows) and the two stages of the group dispatch (src_row = gsrc, then
@@ -218,8 +242,8 @@ moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, i
  *              thread's elements in order, a reduce-scatter butterfly over the wavefront, the
  *              wavefronts in order; 0 for a slot whose row is outside [0, y_rows))
  * and, when src_row is given, every row r of dy with src_row[r] outside [0, T) is written as
- * zeros (rows that fed no output: padding, the unused tail). Each row of dy must be named by at
- * most one slot; other rows are left untouched.
+ * zeros (padding rows, which fed no output) -- except MOE_ROW_UNUSED rows. Each row of dy must be
+ * named by at most one slot; other rows are left untouched.
  *   dout [T, H] (dout_dt); y [y_rows, H] (y_dt; may be NULL when dw is NULL); row_of, w [T, K]
  *   (w NULL: unit weights, dy = dout); src_row [y_rows] (moe_index.sorted_indices) or NULL;
  *   dy [y_rows, H] (dy_dt); dw [T, K] float32 or NULL (not computed).

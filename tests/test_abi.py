@@ -110,8 +110,18 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_group_precombine(fake, 1, 4, big // 2, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, None) == \
         capi.MOE_ERR_UNSUPPORTED  # float32 partial rows of 2 GiB
     ix = capi.MoeIndexStruct()
-    assert lib.moe_build_index(fake, None, 4, 2, 8, 4, 2, ctypes.byref(ix), fake, 1 << 20, None) == \
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 4, 2, 0, ctypes.byref(ix), fake, 1 << 20, None) == \
         capi.MOE_ERR_UNSUPPORTED  # drop-and-pad with groups
-    assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, ctypes.byref(ix), fake, 1 << 20, None) == \
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, 0, ctypes.byref(ix), fake, 1 << 20, None) == \
         capi.MOE_ERR_INVALID  # null outputs
-    assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, None, fake, 1 << 20, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, 0, None, fake, 1 << 20, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 4, 0, 128, ctypes.byref(ix), fake, 1 << 20, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # drop-and-pad with alignment
+    assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, -3, ctypes.byref(ix), fake, 1 << 20, None) == \
+        capi.MOE_ERR_INVALID
+    # rows of the expert-major arrays
+    assert lib.moe_index_rows(16384, 8, 256, 0, 0) == 16384 * 8
+    assert lib.moe_index_rows(16384, 8, 256, 0, 128) == 16384 * 8 + 256 * 127
+    assert lib.moe_index_rows(8192, 8, 128, 640, 0) == 128 * 640
+    assert lib.moe_index_rows(8192, 8, 128, 640, 128) == -1
+    assert lib.moe_index_rows(1 << 30, 8, 8, 0, 0) == -1

@@ -91,9 +91,9 @@ def ids_case(key, T, E, K, p_missing=0.1, junk=False):
     return ids
 
 
-def check_index(m, ids, w, E, cap=0, gs=0):
-    want = oracle.build_index(ids, w, E, capacity=cap, group_size=gs)
-    ix = m.build_index(dev(ids), None if w is None else dev(w), E, capacity=cap, group_size=gs)
+def check_index(m, ids, w, E, cap=0, gs=0, align=0):
+    want = oracle.build_index(ids, w, E, capacity=cap, group_size=gs, alignment=align)
+    ix = m.build_index(dev(ids), None if w is None else dev(w), E, capacity=cap, group_size=gs, alignment=align)
     torch.cuda.synchronize()
     for name in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs"):
         assert_exact(host(getattr(ix, name)), want[name], name)
@@ -149,10 +149,26 @@ def test_build_index_groups(m, T, E, K, gs):
     check_index(m, idx, w, E, gs=gs)
 
 
-@pytest.mark.parametrize("cap,gs", [(0, 0), (4, 0), (0, 2)])
-def test_build_index_no_tokens(m, cap, gs):
+@pytest.mark.parametrize("cap,gs,align", [(0, 0, 0), (4, 0, 0), (0, 2, 0), (0, 0, 128), (0, 2, 4)])
+def test_build_index_no_tokens(m, cap, gs, align):
     ids = np.zeros((0, 2), np.int32)
-    check_index(m, ids, None, 8, cap=cap, gs=gs)
+    check_index(m, ids, None, 8, cap=cap, gs=gs, align=align)
+
+
+@pytest.mark.parametrize("T,E,K,align,gs", [(300, 8, 2, 128, 0), (4099, 64, 8, 128, 0), (2000, 256, 8, 128, 0),
+                                            (700, 40, 7, 3, 0), (50000, 64, 8, 16, 0), (1, 4, 2, 8, 0),
+                                            (2000, 256, 8, 128, 8), (500, 32, 8, 5, 4), (1500, 1024, 32, 2, 0)])
+def test_build_index_aligned(m, T, E, K, align, gs):
+    """Expert alignment: segments rounded up to a multiple of the alignment, padding rows -1,
+    the slack after the last segment -2, with skewed routing (empty experts) and holes."""
+    say(f"build_index aligned T={T} E={E} K={K} align={align} gs={gs}")
+    key = wl.case_key(36, T, E, K, align)
+    logits = wl.router_logits(key, T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    idx[::7, -1] = -1
+    ix, want = check_index(m, idx, w, E, gs=gs, align=align)
+    gl = np.concatenate([[0], want["group_list"]])
+    assert (gl % align == 0).all()
 
 
 # ------------------------------------------------------------------ permute
@@ -168,9 +184,15 @@ def test_permute(m, dtype, H):
     g = np.random.default_rng([*key, 1])
     src_row = g.integers(-3, src_rows + 3, size=1234).astype(np.int32)  # includes -1.. and >= rows
     src_row[:4] = [0, src_rows - 1, -1, src_rows]
+    src_row[4] = -2  # unused slack: left untouched
     want = oracle.permute(x, src_row)
-    got = host(m.permute(dev(x), dev(src_row)))
-    assert_exact(got, want, "permuted rows")
+    out = dev(np.full((len(src_row), H), 0x7F81 if dtype == "bf16" else 0x7F800001,
+                      np.uint16 if dtype == "bf16" else np.uint32).view(np.uint16 if dtype == "bf16" else np.float32))
+    got = host(m.permute(dev(x), dev(src_row), out=out))
+    live = src_row != -2
+    assert_exact(got[live], want[live], "permuted rows")
+    assert (got[~live].view(np.uint16 if dtype == "bf16" else np.uint32) ==
+            (0x7F81 if dtype == "bf16" else 0x7F800001)).all(), "unused rows must be left untouched"
 
 
 def test_permute_empty_source_gives_zero_rows(m):
@@ -199,7 +221,8 @@ def test_permute_scatter_matches_gather(m, dtype, H, T, E, K, mode):
     want = oracle.permute(x, ix["sorted_indices"])
     xd = dev(x)
     got = host(m.permute_scatter(xd, dev(ix["row_of"]), len(ix["sorted_indices"]), src_row=dev(ix["sorted_indices"])))
-    assert_exact(got, want, "scatter rows")
+    live = ix["sorted_indices"] != -2  # unused slack is not written
+    assert_exact(got[live], want[live], "scatter rows")
     if mode == "group":  # stage 1 of the group dispatch: one copy per (token, group)
         n = int(ix["n_slots"][0])
         got1 = host(m.permute_scatter(xd, dev(ix["slot_of"]), n))
@@ -237,9 +260,10 @@ def test_permute_grouped_group_receive(m, dtype, H, T, E, K, gs):
     x = wl.hidden_states(key, T, H, dtype)
     gbuf = oracle.permute(x, ix["gsrc"])
     want = oracle.permute(gbuf, ix["esrc"])
-    assert np.array_equal(want, oracle.permute(x, ix["sorted_indices"]))
+    live = ix["esrc"] != -2  # unused slack is not written
+    assert np.array_equal(want[live], oracle.permute(x, ix["sorted_indices"])[live])
     got = host(m.permute_grouped(dev(gbuf), dev(ix["esrc"]), dev(ix["row_of"])))
-    assert_exact(got, want, "expert-major rows")
+    assert_exact(got[live], want[live], "expert-major rows")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -289,6 +313,35 @@ def test_permute_grouped_without_groups_writes_zero_rows(m):
     m.permute_grouped(dev(x), dev(src_row), dev(np.zeros((0, 4), np.int32)), out=out)
     got = host(out)
     assert (got[[0, 2, 3]] == 0).all() and (got[1] == 0x1234).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H,T,E,K,align", [(7168, 600, 64, 8, 128), (1000, 300, 16, 4, 8), (3, 257, 8, 2, 4),
+                                           (520, 200, 32, 8, 16)])
+def test_permute_aligned(m, dtype, H, T, E, K, align):
+    """Aligned expert buffer: tokens bit for bit, padding rows zero, the slack after the last
+    segment untouched; the combine over the aligned rows equals the oracle's."""
+    say(f"permute aligned {dtype} H={H} T={T} E={E} K={K} align={align}")
+    key = wl.case_key(37, H, T, E, K, align)
+    logits = wl.router_logits(key, T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    idx[::9, 0] = -1
+    ix = oracle.build_index(idx, w, E, alignment=align)
+    si = ix["sorted_indices"]
+    x = wl.hidden_states(key, T, H, dtype)
+    want = oracle.permute(x, si)
+    pat = 0x7F81 if dtype == "bf16" else 0x7F800001
+    u = np.uint16 if dtype == "bf16" else np.uint32
+    out = dev(np.full((len(si), H), pat, u).view(np.uint16 if dtype == "bf16" else np.float32))
+    got = host(m.permute_scatter(dev(x), dev(ix["row_of"]), len(si), src_row=dev(si), out=out))
+    live = si != -2
+    assert_exact(got[live], want[live], "aligned rows")
+    assert (got[si == -1].view(u) == 0).all()
+    assert (got[~live].view(u) == pat).all(), "slack rows must be left untouched"
+    y = wl.expert_outputs(key, len(si), H, dtype)
+    out_np = np.uint16 if dtype == "bf16" else np.float32
+    assert_exact(host(m.unpermute_combine(dev(y), dev(ix["row_of"]), dev(w))),
+                 oracle.unpermute_combine(y, ix["row_of"], w, out_np), "combine over aligned rows")
 
 
 # ------------------------------------------------------------------ combine
@@ -371,8 +424,9 @@ def sample_rows(n, count, seed):
     return s.astype(np.int64)
 
 
-def run_workload(m, cfg_id):
-    """Runs route -> index -> permute -> (pre-)combine on the GPU and checks every stage."""
+def run_workload(m, cfg_id, align=0):
+    """Runs route -> index -> permute -> (pre-)combine on the GPU and checks every stage
+    (align > 1: the expert-aligned layout)."""
     c = wl.WORKLOADS[cfg_id]
     T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
     key = wl.workload_key(cfg_id)
@@ -389,8 +443,8 @@ def run_workload(m, cfg_id):
     assert_rel_f32(host(gw), want_w, "topk_w")
     # the same weight bits on both sides from here on
     w_np = host(gw)
-    ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs)
-    want = oracle.build_index(want_i, w_np, E, capacity=cap, group_size=gs)
+    ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs, alignment=align)
+    want = oracle.build_index(want_i, w_np, E, capacity=cap, group_size=gs, alignment=align)
     for name in ("counts", "group_list", "sorted_indices", "row_of", "permuted_probs"):
         assert_exact(host(getattr(ix, name)), want[name], name)
     rows = ix.rows
@@ -410,8 +464,13 @@ def run_workload(m, cfg_id):
         xp = m.permute_scatter(xd, ix.row_of, rows, src_row=ix.sorted_indices)
     torch.cuda.synchronize()
     rs = sample_rows(rows, 3000, cfg_id)
+    rs = rs[want["sorted_indices"][rs] != -2]  # unused slack is never written
     assert_exact(host(xp[torch.from_numpy(rs).to(DEV)]), oracle.permute(x, want["sorted_indices"][rs]),
                  "permuted rows (sample)")
+    pads = np.flatnonzero(want["sorted_indices"] == -1)
+    if len(pads):
+        pr = pads[sample_rows(len(pads), 1000, cfg_id + 7)]
+        assert (host(xp[torch.from_numpy(pr).to(DEV)]).view(np.uint16 if dt == "bf16" else np.uint32) == 0).all()
     del xd
 
     if c["identity_experts"]:
@@ -453,6 +512,14 @@ def run_workload(m, cfg_id):
 @pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
 def test_workload_full_size(m, cfg_id):
     run_workload(m, cfg_id)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg_id,align", [(3, 128), (2, 128), (4, 128)])
+def test_workload_aligned(m, cfg_id, align):
+    """The named workloads with every expert segment aligned to 128 rows, as bench.py --alignment
+    128 launches them."""
+    run_workload(m, cfg_id, align=align)
     torch.cuda.empty_cache()
 
 
@@ -507,7 +574,8 @@ def test_combine_backward(m, dts, H, T, E, K, mode, weighted):
     dy, dw = m.unpermute_combine_backward(dev(dout), dev(y), dev(ix["row_of"]), None if ww is None else dev(ww),
                                           src_row=dev(ix["sorted_indices"]),
                                           dy_dtype=torch.bfloat16 if dydt == "bf16" else torch.float32)
-    assert_exact(host(dy), want_dy, "dy")
+    live = ix["sorted_indices"] != -2  # unused slack is not written
+    assert_exact(host(dy)[live], want_dy[live], "dy")
     _check_dw(host(dw), want_dw, _dw_bound(dout, y, ix["row_of"], H))
     assert (host(dw)[ix["row_of"] < 0] == 0).all()
 
@@ -594,7 +662,7 @@ def test_backward_workload(m, cfg_id):
     assert_exact(got_dy, want_dy, "dy rows of the sampled tokens")
     dw_np = host(dw)
     _check_dw(dw_np[ts], want_dw, _dw_bound(dout[ts], y[used], sub_local, H))
-    pad = np.flatnonzero(src < 0)
+    pad = np.flatnonzero(src == -1)
     if len(pad):
         pr = pad[sample_rows(len(pad), 500, cfg_id + 1)]
         assert (host(dy[torch.from_numpy(pr).to(DEV)]) == 0).all(), "padding rows of dy must be zero"

@@ -26,8 +26,10 @@
 //             lanes_below) and the last peer advances the key's running row counter in LDS.
 //             The workgroups then write the padding or unused rows together.
 //   4. esrc   (group mode) expert-major row -> group slot.
-// The drop-and-pad capacity rule ([Scratch] §18, §26.6) and the group (send once per rank)
-// slots ([CANN] §1(1)) are applied inside the same passes.
+// The drop-and-pad capacity rule ([Scratch] §18, §26.6), the expert alignment ([Combine] §6:
+// segments rounded up to a multiple of A with padding rows, the segment starts being the scan of
+// the aligned lengths) and the group (send once per rank) slots ([CANN] §1(1)) are applied
+// inside the same passes. Rows after the last segment are unused slack (MOE_ROW_UNUSED).
 #include <algorithm>
 
 #include "moe_common.h"
@@ -47,6 +49,7 @@ struct IndexArgs {
     const float *topk_w;
     int64_t T;
     int32_t K, E, cap, gs, G;
+    int32_t align;   // expert alignment (1: none)
     int32_t Ep, Gp;  // row strides of the histograms (E, G rounded up to a multiple of 4)
     int32_t tile_tokens, ntiles;
     int32_t ebits, gbits;
@@ -58,6 +61,15 @@ struct IndexArgs {
 };
 
 __device__ __forceinline__ bool valid_expert(int e, int E) { return e >= 0 && e < E; }
+
+__host__ __device__ __forceinline__ int64_t round_up(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
+
+// Rows of the expert-major buffer: E*cap with a capacity, otherwise T*K plus the most the
+// aligned segments can add.
+__host__ __device__ __forceinline__ int64_t index_rows(int64_t T, int32_t K, int32_t E, int32_t cap, int32_t align)
+{
+    return cap > 0 ? static_cast<int64_t>(E) * cap : T * K + static_cast<int64_t>(E) * (align - 1);
+}
 
 // True if slot k of a token is the first of that token's slots in expert group g.
 __device__ __forceinline__ bool group_leader(const int32_t *ids, int k, int g, int E, int gs)
@@ -158,8 +170,10 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *sh_w
 
 // hist [ntiles][stride] (stride a multiple of 4, 16-byte aligned rows) holds tile counts; on
 // return it holds, for every (tile, key), the first row of that tile inside the key, sh.tot the
-// key totals and sh.seg each key's first row. Returns the grand total.
-__device__ __forceinline__ int32_t scan_tiles(int32_t *hist, int nkeys, int stride, int ntiles, ScanShared &sh)
+// key totals and sh.seg each key's first row, the keys' segments being their totals rounded up
+// to a multiple of `align`. Returns the grand total of the segments.
+__device__ __forceinline__ int32_t scan_tiles(int32_t *hist, int nkeys, int stride, int ntiles, int align,
+                                              ScanShared &sh)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -214,7 +228,7 @@ __device__ __forceinline__ int32_t scan_tiles(int32_t *hist, int nkeys, int stri
         __syncthreads();  // sh.part is reused by the next chunk of keys
     }
     int32_t total;
-    const int32_t v = static_cast<int>(threadIdx.x) < nkeys ? sh.tot[threadIdx.x] : 0;
+    const int32_t v = static_cast<int>(threadIdx.x) < nkeys ? static_cast<int32_t>(round_up(sh.tot[threadIdx.x], align)) : 0;
     const int32_t ex = block_exclusive_scan(v, sh.waves, &total);
     if (static_cast<int>(threadIdx.x) < nkeys)
         sh.seg[threadIdx.x] = ex;
@@ -226,28 +240,32 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(IndexArgs a)
 {
     __shared__ ScanShared sh;
     const int tid = threadIdx.x;
-    const int64_t R = a.cap > 0 ? static_cast<int64_t>(a.E) * a.cap : a.T * a.K;
-    scan_tiles(a.hist_e, a.E, a.Ep, a.ntiles, sh);
+    const int64_t R = index_rows(a.T, a.K, a.E, a.cap, a.align);
+    scan_tiles(a.hist_e, a.E, a.Ep, a.ntiles, a.cap > 0 ? 1 : a.align, sh);
     for (int e = tid; e < a.E; e += kScanThreads) {
         const int32_t cnt = sh.tot[e];
         const int32_t start = sh.seg[e];
         a.seg_e[e] = start;
         a.ix.counts[e] = cnt;
-        a.ix.group_list[e] = start + cnt;
+        a.ix.group_list[e] = start + (a.cap > 0 ? cnt : static_cast<int32_t>(round_up(cnt, a.align)));
         if (a.ix.kept_counts)
             a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
     }
-    if (a.ntiles == 0 && a.cap > 0) {
-        // no tokens: every row of every expert is padding (otherwise the rank kernel writes it)
+    if (a.ntiles == 0) {
+        // no tokens (otherwise the rank kernel writes these rows): every row of every expert is
+        // padding in drop-and-pad, every row is unused slack otherwise
+        const int32_t mark = a.cap > 0 ? MOE_ROW_PAD : MOE_ROW_UNUSED;
         for (int64_t r = tid; r < R; r += kScanThreads) {
-            a.ix.sorted_indices[r] = -1;
+            a.ix.sorted_indices[r] = mark;
             if (a.ix.permuted_probs)
                 a.ix.permuted_probs[r] = 0.0f;
+            if (a.gs > 0)
+                a.ix.esrc[r] = mark;
         }
     }
     if (a.gs > 0) {
         __syncthreads();  // sh is reused for the group keys
-        const int32_t m = scan_tiles(a.hist_g, a.G, a.Gp, a.ntiles, sh);
+        const int32_t m = scan_tiles(a.hist_g, a.G, a.Gp, a.ntiles, 1, sh);
         for (int g = tid; g < a.G; g += kScanThreads) {
             a.seg_g[g] = sh.seg[g];
             a.ix.group_counts[g] = sh.tot[g];
@@ -495,19 +513,37 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
             const int e = static_cast<int>(r / a.cap);
             const int p = static_cast<int>(r - static_cast<int64_t>(e) * a.cap);
             if (p >= min(cnt[e], a.cap)) {
-                a.ix.sorted_indices[r] = -1;
+                a.ix.sorted_indices[r] = MOE_ROW_PAD;
                 if (a.ix.permuted_probs)
                     a.ix.permuted_probs[r] = 0.0f;
             }
         }
     } else {
-        const int64_t total = static_cast<int64_t>(seg_e[a.E - 1]) + cnt[a.E - 1];
-        for (int64_t r = total + static_cast<int64_t>(tile) * kRankThreads + tid; r < a.T * a.K; r += stride) {
-            a.ix.sorted_indices[r] = -1;
+        const int A = a.align;
+        if (A > 1) {  // padding rows at the end of each aligned segment: (expert, p) pairs
+            const int64_t npad = static_cast<int64_t>(a.E) * (A - 1);
+            for (int64_t j = static_cast<int64_t>(tile) * kRankThreads + tid; j < npad; j += stride) {
+                const int e = static_cast<int>(j / (A - 1));
+                const int p = static_cast<int>(j - static_cast<int64_t>(e) * (A - 1));
+                const int32_t c = cnt[e];
+                if (p < round_up(c, A) - c) {
+                    const int64_t r = static_cast<int64_t>(seg_e[e]) + c + p;
+                    a.ix.sorted_indices[r] = MOE_ROW_PAD;
+                    if (a.ix.permuted_probs)
+                        a.ix.permuted_probs[r] = 0.0f;
+                    if (a.gs > 0)
+                        a.ix.esrc[r] = MOE_ROW_PAD;
+                }
+            }
+        }
+        const int64_t total = static_cast<int64_t>(seg_e[a.E - 1]) + round_up(cnt[a.E - 1], A);
+        const int64_t R = index_rows(a.T, a.K, a.E, 0, A);
+        for (int64_t r = total + static_cast<int64_t>(tile) * kRankThreads + tid; r < R; r += stride) {
+            a.ix.sorted_indices[r] = MOE_ROW_UNUSED;
             if (a.ix.permuted_probs)
                 a.ix.permuted_probs[r] = 0.0f;
             if (a.gs > 0)
-                a.ix.esrc[r] = -1;
+                a.ix.esrc[r] = MOE_ROW_UNUSED;
         }
     }
 }
@@ -590,27 +626,39 @@ extern "C" moe_status moe_build_index_workspace_size(int64_t T, int32_t K, int32
     return MOE_OK;
 }
 
+extern "C" int64_t moe_index_rows(int64_t T, int32_t K, int32_t E, int32_t capacity, int32_t alignment)
+{
+    using namespace moe;
+    if (T < 0 || K < 1 || E < 1 || alignment < 0 || (capacity > 0 && alignment > 1))
+        return -1;
+    const int64_t R = index_rows(T, K, E, capacity > 0 ? capacity : 0, alignment > 1 ? alignment : 1);
+    return R > 0x7fffffffLL ? -1 : R;
+}
+
 extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T,
                                       int32_t K, int32_t E, int32_t capacity, int32_t group_size,
-                                      const moe_index *out, void *workspace, size_t workspace_bytes,
-                                      hipStream_t stream)
+                                      int32_t alignment, const moe_index *out, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream)
 {
     using namespace moe;
     moe_status st = check_sizes(T, K, E, group_size);
     if (st != MOE_OK)
         return st;
-    if (capacity > 0 && group_size > 0)
+    if (alignment < 0)
+        return MOE_ERR_INVALID;
+    if (capacity > 0 && (group_size > 0 || alignment > 1))
         return MOE_ERR_UNSUPPORTED;
-    if (capacity > 0 && static_cast<int64_t>(E) * capacity > 0x7fffffffLL)
-        return MOE_ERR_UNSUPPORTED;
+    const int32_t A = alignment > 1 ? alignment : 1;
     // only the arrays that will be written must be present (empty tensors may come as NULL)
     const int32_t G = group_size > 0 ? E / group_size : 0;
-    const int64_t R = capacity > 0 ? static_cast<int64_t>(E) * capacity : T * K;
+    const int64_t R = index_rows(T, K, E, capacity > 0 ? capacity : 0, A);
+    if (R > 0x7fffffffLL)
+        return MOE_ERR_UNSUPPORTED;
     if (!out || !out->counts || !out->group_list || (R > 0 && !out->sorted_indices) ||
         (T > 0 && !out->row_of))
         return MOE_ERR_INVALID;
-    if (G > 0 && (!out->group_counts || !out->n_slots ||
-                  (T > 0 && (!out->slot_of || !out->gsrc || !out->esrc))))
+    if (G > 0 && (!out->group_counts || !out->n_slots || (T > 0 && (!out->slot_of || !out->gsrc)) ||
+                  (R > 0 && !out->esrc)))
         return MOE_ERR_INVALID;
     if (T > 0 && !topk_idx)
         return MOE_ERR_INVALID;
@@ -629,6 +677,7 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     a.cap = capacity > 0 ? capacity : 0;
     a.gs = group_size > 0 ? group_size : 0;
     a.G = G;
+    a.align = A;
     a.Ep = round4(E);
     a.Gp = round4(G);
     a.tile_tokens = p.tile_tokens;

@@ -570,7 +570,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_backward_kernel(
     if (t >= T) {
         const int64_t first = ((t - T) * nwaves + threadIdx.x / kWave) * kBwdZeroRowsPerWave;
         const int64_t i = first + lane;
-        const bool zero = lane < kBwdZeroRowsPerWave && i < y_rows && (src_row[i] < 0 || src_row[i] >= T);
+        const bool zero = lane < kBwdZeroRowsPerWave && i < y_rows && (src_row[i] < 0 || src_row[i] >= T) && src_row[i] != MOE_ROW_UNUSED;
         uint64_t m = __ballot(zero);
         const u32x4 z{0u, 0u, 0u, 0u};
         while (m) {
@@ -644,7 +644,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_backward_scalar_kernel(
     if (t >= T) {
         const int64_t first = ((t - T) * nwaves + threadIdx.x / kWave) * kBwdZeroRowsPerWave;
         const int64_t i = first + lane;
-        const bool zero = lane < kBwdZeroRowsPerWave && i < y_rows && (src_row[i] < 0 || src_row[i] >= T);
+        const bool zero = lane < kBwdZeroRowsPerWave && i < y_rows && (src_row[i] < 0 || src_row[i] >= T) && src_row[i] != MOE_ROW_UNUSED;
         uint64_t m = __ballot(zero);
         while (m) {
             const int j = __builtin_ctzll(m);

@@ -22,6 +22,13 @@ namespace moe {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // 4 wavefronts, one row each
+
+// A gather-map entry that asks for a zero row: outside [0, src_rows), but not the unused slack
+// after the last segment (MOE_ROW_UNUSED), which no permute writes.
+__device__ __forceinline__ bool zero_entry(int32_t s, int64_t src_rows)
+{
+    return (s < 0 || s >= src_rows) && s != MOE_ROW_UNUSED;
+}
 constexpr int kUnroll = 4;
 
 __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_vec16_kernel(
@@ -34,6 +41,8 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_vec16_kernel(
     if (i >= N)
         return;
     const int32_t s = src_row[i];
+    if (s == MOE_ROW_UNUSED)
+        return;
     const int64_t row_bytes = nvec * 16;
     const __amdgpu_buffer_rsrc_t d = make_rsrc(dst + i * row_bytes, static_cast<uint32_t>(row_bytes));
     if (s < 0 || s >= src_rows) {
@@ -67,6 +76,8 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
     if (i >= N)
         return;
     const int32_t s = src_row[i];
+    if (s == MOE_ROW_UNUSED)
+        return;
     T *d = dst + i * H;
     if (s < 0 || s >= src_rows) {
         for (int64_t h = lane; h < H; h += kWave)
@@ -81,24 +92,30 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
 // ---------------------------------------------------------------- source-major form
 // One wavefront per (source row, 1 KiB slice of it): each lane loads one 16-byte vector of the
 // row once and stores it to every destination; the destinations sit in lanes 0..J-1 and are
-// walked in lane order with readlane, so the loop is uniform. Waves past the last source row
-// write the zero rows: each checks kZeroRowsPerWave entries of src_row and zero-fills those
-// outside [0, src_rows). Measured at T16384 H7168 K8 bf16: 339 us per launch (6.2 TB/s) with
-// slices, 350 us with one 256-thread workgroup per row.
+// walked in lane order with readlane, so the loop is uniform. Other waves write the zero rows:
+// each checks `zr` entries of src_row and zero-fills those outside [0, src_rows). Measured at
+// T16384 H7168 K8 bf16: 339 us per launch (6.2 TB/s) with slices, 350 us with one 256-thread
+// workgroup per row. When the output has more rows than the map can name (N > src_rows * J:
+// drop-and-pad, aligned experts) padding is certain and its waves come first, 8 rows each,
+// so that they overlap the copies instead of trailing them (drop-and-pad at T8192 H4096 E128:
+// 134 -> 125 us); otherwise they come last, 16 rows each (putting them first cost the
+// unpadded case ~1%).
 constexpr int kScatterThreads = 256;
 constexpr int kScatterWaves = kScatterThreads / kWave;
 constexpr int kZeroRowsPerWave = 16;
+constexpr int kZeroRowsPerWaveFirst = 8;
 constexpr int kMaxScatterDests = 64;
 
-// Zero-fills rows first .. first+kZeroRowsPerWave-1 whose src_row entry is outside [0, src_rows)
-// (one wavefront; no-op without a gather map).
+// Zero-fills rows first .. first+zr-1 whose src_row entry asks for a zero row (one wavefront;
+// no-op without a gather map). zr <= 64.
 __device__ __forceinline__ void zero_rows_wave(int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
-                                               int64_t N, int64_t first, char *__restrict__ dst)
+                                               int64_t N, int64_t first, char *__restrict__ dst,
+                                               int zr = kZeroRowsPerWave)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
     const int64_t i = first + lane;
-    const bool zero = src_row && lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+    const bool zero = src_row && lane < zr && i < N && zero_entry(src_row[i], src_rows);
     uint64_t m = __ballot(zero);
     const u32x4 z{0u, 0u, 0u, 0u};
     while (m) {
@@ -112,7 +129,7 @@ __device__ __forceinline__ void zero_rows_wave(int64_t src_rows, int64_t nvec, c
 
 __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ dst_of, int J,
-    const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst)
+    const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst, int64_t zero_waves, bool zero_first)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
@@ -120,12 +137,19 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterWaves +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = src_rows * wpr;
-    if (gw >= copy_waves) {
-        zero_rows_wave(src_rows, nvec, src_row, N, (gw - copy_waves) * kZeroRowsPerWave, dst);
+    // wave index -> zero window or copy wave; the grid's last workgroup may hold up to 3 waves
+    // past both (zero windows past N check nothing, copy rows past src_rows return below)
+    const int64_t zw = zero_first ? gw : gw - copy_waves;
+    if (zero_first ? gw < zero_waves : gw >= copy_waves) {
+        const int zr = zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave;
+        zero_rows_wave(src_rows, nvec, src_row, N, zw * zr, dst, zr);
         return;
     }
-    const int64_t t = gw / wpr;
-    const int64_t v = (gw - t * wpr) * kWave + lane;  // this lane's vector of the row
+    const int64_t cw = zero_first ? gw - zero_waves : gw;
+    const int64_t t = cw / wpr;
+    if (t >= src_rows)
+        return;
+    const int64_t v = (cw - t * wpr) * kWave + lane;  // this lane's vector of the row
     const int32_t my = lane < J ? dst_of[t * J + lane] : -1;
     uint64_t m = __ballot(my >= 0 && my < N);
     if (m == 0)
@@ -153,7 +177,7 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_elem_kernel(
         const int64_t first = (static_cast<int64_t>(blockIdx.x) - src_rows) * (kScatterThreads / kWave) * kZeroRowsPerWave +
                               static_cast<int64_t>(threadIdx.x / kWave) * kZeroRowsPerWave;
         const int64_t i = first + lane;
-        const bool zero = lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+        const bool zero = lane < kZeroRowsPerWave && i < N && zero_entry(src_row[i], src_rows);
         uint64_t m = __ballot(zero);
         while (m) {
             const int j = __builtin_ctzll(m);
@@ -252,7 +276,7 @@ __global__ __launch_bounds__(kScatterThreads) void permute_grouped_elem_kernel(
         const int64_t first = (static_cast<int64_t>(blockIdx.x) - M) * kScatterWaves * kZeroRowsPerWave +
                               static_cast<int64_t>(threadIdx.x / kWave) * kZeroRowsPerWave;
         const int64_t i = first + lane;
-        const bool zero = lane < kZeroRowsPerWave && i < N && (src_row[i] < 0 || src_row[i] >= src_rows);
+        const bool zero = lane < kZeroRowsPerWave && i < N && zero_entry(src_row[i], src_rows);
         uint64_t m = __ballot(zero);
         while (m) {
             const int j = __builtin_ctzll(m);
@@ -304,13 +328,15 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
     const int64_t zero_waves = src_row ? ceil_div(N, kZeroRowsPerWave) : 0;
     if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
         const int64_t nvec = row_bytes / 16;
-        const int64_t waves = src_rows * ceil_div(nvec, kWave) + zero_waves;
+        const bool zero_first = src_row && N > src_rows * J;  // padding rows are certain
+        const int64_t zwaves = src_row ? ceil_div(N, zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave) : 0;
+        const int64_t waves = src_rows * ceil_div(nvec, kWave) + zwaves;
         const int64_t blocks = ceil_div(waves, kScatterWaves);
         if (blocks > 0x7fffffff)
             return MOE_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(permute_scatter_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0,
                            stream, static_cast<const char *>(src), src_rows, nvec, dst_of, J, src_row, N,
-                           static_cast<char *>(dst));
+                           static_cast<char *>(dst), zwaves, zero_first);
         return launch_status();
     }
     const int64_t blocks = src_rows + ceil_div(zero_waves, kScatterWaves);

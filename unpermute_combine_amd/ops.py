@@ -82,6 +82,7 @@ class MoeIndex:
     E: int
     capacity: int
     group_size: int
+    alignment: int
     counts: torch.Tensor
     group_list: torch.Tensor
     kept_counts: torch.Tensor
@@ -97,8 +98,9 @@ class MoeIndex:
 
     @property
     def rows(self) -> int:
-        """Rows of the expert-major buffers: T*K, or E*capacity in drop-and-pad mode."""
-        return self.E * self.capacity if self.capacity > 0 else self.T * self.K
+        """Rows of the expert-major buffers: T*K, E*capacity in drop-and-pad mode, or
+        T*K + E*(alignment-1) with expert alignment (rows after the last segment are unused)."""
+        return index_rows(self.T, self.K, self.E, self.capacity, self.alignment)
 
     @property
     def num_groups(self) -> int:
@@ -117,11 +119,20 @@ def workspace_bytes(T: int, K: int, E: int, group_size: int = 0) -> int:
     return int(n.value)
 
 
-def alloc_index(T: int, K: int, E: int, capacity: int = 0, group_size: int = 0, device="cuda") -> MoeIndex:
+def index_rows(T: int, K: int, E: int, capacity: int = 0, alignment: int = 0) -> int:
+    """Rows of the expert-major arrays for these sizes (moe_index_rows)."""
+    r = lib().moe_index_rows(T, K, E, capacity, alignment)
+    if r < 0:
+        raise ValueError("invalid index sizes (or capacity together with alignment)")
+    return int(r)
+
+
+def alloc_index(T: int, K: int, E: int, capacity: int = 0, group_size: int = 0, device="cuda",
+                alignment: int = 0) -> MoeIndex:
     i32 = dict(dtype=torch.int32, device=device)
-    rows = E * capacity if capacity > 0 else T * K
+    rows = index_rows(T, K, E, capacity, alignment)
     ix = MoeIndex(
-        T=T, K=K, E=E, capacity=capacity, group_size=group_size,
+        T=T, K=K, E=E, capacity=capacity, group_size=group_size, alignment=alignment,
         counts=torch.empty(E, **i32), group_list=torch.empty(E, **i32), kept_counts=torch.empty(E, **i32),
         sorted_indices=torch.empty(rows, **i32), row_of=torch.empty((T, K), **i32),
         permuted_probs=torch.empty(rows, dtype=torch.float32, device=device))
@@ -138,21 +149,25 @@ def alloc_index(T: int, K: int, E: int, capacity: int = 0, group_size: int = 0, 
 
 
 def build_index(topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor], num_experts: int,
-                capacity: int = 0, group_size: int = 0, out: Optional[MoeIndex] = None) -> MoeIndex:
-    """Expert-major index of the routing result (sorted_indices, row_of, counts, group_list, ...)."""
+                capacity: int = 0, group_size: int = 0, out: Optional[MoeIndex] = None,
+                alignment: int = 0) -> MoeIndex:
+    """Expert-major index of the routing result (sorted_indices, row_of, counts, group_list, ...);
+    alignment > 1 rounds every expert segment up to a multiple of it (padding rows)."""
     _need(topk_idx, "topk_idx", torch.int32, 2)
     T, K = topk_idx.shape
     if topk_w is not None:
         _need(topk_w, "topk_w", torch.float32, 2)
         if tuple(topk_w.shape) != (T, K):
             raise ValueError("topk_w must have the shape of topk_idx")
-    ix = out if out is not None else alloc_index(T, K, num_experts, capacity, group_size, topk_idx.device)
-    if (ix.T, ix.K, ix.E, ix.capacity, ix.group_size) != (T, K, num_experts, capacity, group_size):
+    ix = out if out is not None else alloc_index(T, K, num_experts, capacity, group_size, topk_idx.device,
+                                                 alignment)
+    if (ix.T, ix.K, ix.E, ix.capacity, ix.group_size, ix.alignment) != (T, K, num_experts, capacity, group_size,
+                                                                        alignment):
         raise ValueError("preallocated index was made for other sizes")
     s = ix.struct()
     ws = ix.workspace
     check("moe_build_index", lib().moe_build_index(
-        _p(topk_idx), _p(topk_w), T, K, num_experts, capacity, group_size, ctypes.byref(s),
+        _p(topk_idx), _p(topk_w), T, K, num_experts, capacity, group_size, alignment, ctypes.byref(s),
         _p(ws), ws.numel(), _stream()))
     return ix
 
