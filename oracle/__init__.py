@@ -57,6 +57,8 @@ def _declare(lib):
     lib.oracle_unpermute_combine.argtypes = [P, i32, i64, i64, P, P, i64, i32, P, i32]
     lib.oracle_unpermute_combine.restype = ctypes.c_int
     lib.oracle_group_precombine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, i32, P, i64, P]
+    lib.oracle_route_topk_grouped.argtypes = [P, i64, i32, i32, i32, i32, P, P]
+    lib.oracle_route_topk_grouped.restype = ctypes.c_int
     lib.oracle_combine_backward.argtypes = [P, i32, P, i32, i64, i64, P, P, i64, i32, P, i32, P]
     lib.oracle_combine_backward.restype = ctypes.c_int
     lib.oracle_route_topk_backward.argtypes = [P, P, P, i64, i32, i32, P]
@@ -121,6 +123,17 @@ def index_rows(T: int, K: int, E: int, capacity: int = 0, alignment: int = 0) ->
     if capacity > 0:
         return E * capacity
     return T * K + (E * (alignment - 1) if alignment > 1 else 0)
+
+
+def route_topk_grouped(logits: np.ndarray, K: int, group_size: int, topk_groups: int):
+    """Group-limited routing: the topk_groups groups with the best expert, then top-K inside them."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.full((T, K), -7, np.int32)
+    w = np.full((T, K), np.nan, np.float32)
+    _check(_load().oracle_route_topk_grouped(_ptr(logits), T, E, K, group_size, topk_groups, _ptr(idx), _ptr(w)),
+           "route_topk_grouped")
+    return idx, w
 
 
 def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_size: int = 0,

@@ -100,6 +100,32 @@ int64_t oracle_capacity(int64_t tokens, int32_t top_k, int32_t num_experts,
  *     double: w_k = exp(s_k - s_0) / sum_j exp(s_j - s_0) (s_0 is the largest selected logit),
  *     the sum taken in slot order, each weight rounded once to float.
  * Logits must be finite; E >= K. */
+/* The K best experts of one token among those not yet taken (taken[e] = 1 excludes e), slot k
+ * the k-th in the order (score descending, id ascending), and the softmax over their scores. */
+static void select_and_softmax(const float *s, int32_t E, int32_t K, unsigned char *taken, int32_t *idx,
+                               double *ex, float *w)
+{
+    for (int32_t k = 0; k < K; ++k) {
+        int32_t best = -1;
+        for (int32_t e = 0; e < E; ++e) {
+            if (taken[e])
+                continue;
+            if (best < 0 || s[e] > s[best]) /* strict: an equal score keeps the lower id */
+                best = e;
+        }
+        taken[best] = 1;
+        idx[k] = best;
+    }
+    double m = (double)s[idx[0]];
+    double z = 0.0;
+    for (int32_t k = 0; k < K; ++k) {
+        ex[k] = exp((double)s[idx[k]] - m);
+        z += ex[k];
+    }
+    for (int32_t k = 0; k < K; ++k)
+        w[k] = (float)(ex[k] / z);
+}
+
 int oracle_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
                       int32_t *topk_idx, float *topk_w)
 {
@@ -113,30 +139,71 @@ int oracle_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
         return ORC_INVALID;
     }
     for (int64_t t = 0; t < T; ++t) {
-        const float *s = logits + t * E;
-        int32_t *idx = topk_idx + t * K;
         memset(taken, 0, (size_t)E);
-        for (int32_t k = 0; k < K; ++k) {
-            int32_t best = -1;
-            for (int32_t e = 0; e < E; ++e) {
-                if (taken[e])
-                    continue;
-                if (best < 0 || s[e] > s[best]) /* strict: an equal score keeps the lower id */
-                    best = e;
-            }
-            taken[best] = 1;
-            idx[k] = best;
-        }
-        double m = (double)s[idx[0]];
-        double z = 0.0;
-        for (int32_t k = 0; k < K; ++k) {
-            ex[k] = exp((double)s[idx[k]] - m);
-            z += ex[k];
-        }
-        for (int32_t k = 0; k < K; ++k)
-            topk_w[t * K + k] = (float)(ex[k] / z);
+        select_and_softmax(logits + t * E, E, K, taken, topk_idx + t * K, ex, topk_w + t * K);
     }
     free(taken);
+    free(ex);
+    return ORC_OK;
+}
+
+/* Group-limited routing, [Scratch] §21: the experts are split into groups (here contiguous,
+ * g = e / group_size), the router first picks a few groups and then the top experts inside
+ * them, so that a token's experts sit in at most topk_groups groups (ranks).
+ * Reading of the open points (the page defines no group score):
+ *   - a group's score is the largest logit among its experts (so topk_groups = G is plain
+ *     routing, and the token's best expert is always kept);
+ *   - the topk_groups groups with the largest scores are taken, an equal score going to the
+ *     lower group id (+0 == -0 a tie);
+ *   - the K experts and their weights are then chosen exactly as in oracle_route_topk, among
+ *     the experts of the chosen groups only.
+ * Requires group_size dividing E, 1 <= topk_groups <= G and K <= topk_groups * group_size. */
+int oracle_route_topk_grouped(const float *logits, int64_t T, int32_t E, int32_t K, int32_t group_size,
+                              int32_t topk_groups, int32_t *topk_idx, float *topk_w)
+{
+    if (T < 0 || E < 1 || K < 1 || K > E || group_size < 1 || E % group_size != 0 || topk_groups < 1 ||
+        topk_groups > E / group_size || (int64_t)K > (int64_t)topk_groups * group_size ||
+        (T > 0 && (!logits || !topk_idx || !topk_w)))
+        return ORC_INVALID;
+    int32_t G = E / group_size;
+    unsigned char *taken = malloc((size_t)E);
+    unsigned char *chosen = malloc((size_t)G);
+    float *score = malloc(sizeof(float) * (size_t)G);
+    double *ex = malloc(sizeof(double) * (size_t)K);
+    if (!taken || !chosen || !score || !ex) {
+        free(taken);
+        free(chosen);
+        free(score);
+        free(ex);
+        return ORC_INVALID;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *s = logits + t * E;
+        for (int32_t g = 0; g < G; ++g) {
+            int32_t top = g * group_size;
+            for (int32_t e = g * group_size; e < (g + 1) * group_size; ++e)
+                if (s[e] > s[top])
+                    top = e;
+            score[g] = s[top];
+        }
+        memset(chosen, 0, (size_t)G);
+        for (int32_t m = 0; m < topk_groups; ++m) {
+            int32_t bg = -1;
+            for (int32_t g = 0; g < G; ++g) {
+                if (chosen[g])
+                    continue;
+                if (bg < 0 || score[g] > score[bg])
+                    bg = g;
+            }
+            chosen[bg] = 1;
+        }
+        for (int32_t e = 0; e < E; ++e)
+            taken[e] = chosen[e / group_size] ? 0 : 1;
+        select_and_softmax(s, E, K, taken, topk_idx + t * K, ex, topk_w + t * K);
+    }
+    free(taken);
+    free(chosen);
+    free(score);
     free(ex);
     return ORC_OK;
 }

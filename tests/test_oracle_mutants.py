@@ -15,13 +15,13 @@ import oracle
 from oracle.build import SRC
 import test_oracle_backward as bw
 import test_oracle_bruteforce as bf
+import test_oracle_grouped_route as gr
 import test_oracle_pins as pins
 
 MUTANTS = [
     ("ties go to the higher id", "if (best < 0 || s[e] > s[best])", "if (best < 0 || s[e] >= s[best])"),
-    ("softmax normalised over the wrong slot", "topk_w[t * K + k] = (float)(ex[k] / z);",
-     "topk_w[t * K + k] = (float)(ex[0] / z);"),
-    ("softmax sum skips the first slot", "            z += ex[k];", "            if (k > 0) z += ex[k];"),
+    ("softmax normalised over the wrong slot", "w[k] = (float)(ex[k] / z);", "w[k] = (float)(ex[0] / z);"),
+    ("softmax sum skips the first slot", "        z += ex[k];", "        if (k > 0) z += ex[k];"),
     ("softmax sign flipped", "ex[k] = exp((double)s[idx[k]] - m);", "ex[k] = exp(m - (double)s[idx[k]]);"),
     ("group_list exclusive instead of inclusive",
      "        run += capacity > 0 ? counts[e] : (counts[e] + A - 1) / A * A;\n        group_list[e] = (int32_t)run;",
@@ -62,6 +62,10 @@ MUTANTS = [
     ("pre-combine mixes groups", "if (e < 0 || e >= E || e / group_size != g || r < 0 || r >= y_rows)",
      "if (e < 0 || e >= E || r < 0 || r >= y_rows)"),
     ("capacity rounds down", "    return (num + den - 1) / den;", "    return num / den;"),
+    ("group score from the group's first expert", "                if (s[e] > s[top])\n                    top = e;",
+     "                if (0 && s[e] > s[top])\n                    top = e;"),
+    ("group ties go to the higher id", "if (bg < 0 || score[g] > score[bg])", "if (bg < 0 || score[g] >= score[bg])"),
+    ("experts outside the chosen groups allowed", "taken[e] = chosen[e / group_size] ? 0 : 1;", "taken[e] = 0;"),
     ("combine backward ignores the weight",
      "store_elem(dy, dy_dt, (int64_t)r * H + h, wk * load_elem(dout, dout_dt, t * H + h));",
      "store_elem(dy, dy_dt, (int64_t)r * H + h, load_elem(dout, dout_dt, t * H + h));"),
@@ -112,6 +116,10 @@ def _pins():
         bw.test_dispatch_backward_is_the_unit_weight_combine,
         bw.test_route_backward_matches_autograd_and_finite_differences,
         bw.test_route_backward_closed_forms,
+        gr.test_all_groups_allowed_is_plain_routing,
+        gr.test_single_expert_groups_is_plain_routing,
+        gr.test_k1_is_the_argmax,
+        gr.test_selection_is_the_optimal_one_fixed_cases,
     ]
     return checks
 
