@@ -61,6 +61,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--alignment", type=int, default=0,
                    help="round every expert segment up to a multiple of this many rows (padding rows)")
+    p.add_argument("--route-groups", type=int, default=0,
+                   help="group-limited routing: each token keeps this many of the workload's expert groups")
     p.add_argument("--backward", action="store_true",
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
@@ -167,7 +169,12 @@ def main():
     part = torch.empty((T * min(K, G), H), dtype=torch.float32, device="cuda") if gs else None
 
     # the step's calls in order: (kernel name, stage, call)
-    calls = [("route", "route", lambda: m.route_topk(logits, K, out=(gi, gw))),
+    rg = args.route_groups
+    if rg and not gs:
+        print("--route-groups needs a workload with expert groups (workload 4)", file=sys.stderr, flush=True)
+        sys.exit(2)
+    calls = [("route", "route", lambda: m.route_topk(logits, K, out=(gi, gw), group_size=gs if rg else 0,
+                                                     topk_groups=rg)),
              ("index", "index", lambda: m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix,
                                                       alignment=align))]
     src = xp if y is None else y
@@ -282,8 +289,8 @@ def main():
         "metric": METRIC_BACKWARD if args.backward else METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
-        "config": {"workload": c["name"] + (f" align{align}" if align else ""), "T": T, "H": H, "E": E, "K": K,
-                   "capacity": cap, "alignment": align,
+        "config": {"workload": c["name"] + (f" align{align}" if align else "") + (f" groups{rg}" if rg else ""),
+                   "T": T, "H": H, "E": E, "K": K, "capacity": cap, "alignment": align, "route_groups": rg,
                    "group_size": gs, "zipf_s": c["zipf_s"], "seed_key": list(key)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "routed_tokens_per_s": round(routed_per_s, 1),
@@ -299,13 +306,17 @@ def main():
         result["pass"] = "backward"
     if not args.no_cpu_baseline:
         if args.backward:
-            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, step_bytes)
+            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes)
         else:
-            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, step_bytes)
+            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, step_bytes):
+def _oracle_route(oracle, logits_np, K, gs, rg):
+    return oracle.route_topk_grouped(logits_np, K, gs, rg) if rg else oracle.route_topk(logits_np, K)
+
+
+def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes):
     """The CPU oracle as it stands (single thread) over the same whole workload, 2 passes."""
     import numpy as np
 
@@ -316,7 +327,7 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, step_bytes):
     best = None
     for _ in range(2):
         t0 = time.perf_counter()
-        idx, w = oracle.route_topk(logits_np, K)
+        idx, w = _oracle_route(oracle, logits_np, K, gs, rg)
         ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
         if gs:
             gbuf = oracle.permute(x_np, ix["gsrc"])
@@ -339,7 +350,7 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, step_bytes):
             "routed_tokens_per_s": round(T * K / best, 1)}
 
 
-def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, step_bytes):
+def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes):
     """The CPU oracle's backward (single thread) on the same saved forward state, 2 passes."""
     import numpy as np
 
@@ -348,7 +359,7 @@ def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, step_b
 
     T, H, E, K, gs = c["T"], c["H"], c["E"], c["K"], c["group_size"]
     out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
-    idx, w = oracle.route_topk(logits_np, K)
+    idx, w = _oracle_route(oracle, logits_np, K, gs, rg)
     ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
     rows = len(ix["sorted_indices"])
     y = oracle.permute(x_np, ix["sorted_indices"]) if y_np is None else y_np

@@ -83,6 +83,19 @@ int64_t moe_expert_capacity(int64_t tokens, int32_t top_k, int32_t num_experts,
 moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
                           int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
+/* Group-limited routing, [Scratch] §21: the experts form G = E / group_size contiguous groups
+ * (g = e / group_size; a group stands for a rank or node); the router first keeps the
+ * topk_groups groups with the best scores, then picks the top K experts among the experts of
+ * those groups only, and the weights are the softmax over the K selected logits exactly as in
+ * moe_route_topk. A group's score is its largest logit (the pages define no score: with the
+ * maximum, topk_groups = G is plain routing and the token's best expert is always kept); equal
+ * scores go to the lower group id. A token's K experts then lie in at most topk_groups groups,
+ * so the group dispatch sends each token at most topk_groups times.
+ * Requires group_size dividing E, 1 <= topk_groups <= G, K <= topk_groups * group_size
+ * (else MOE_ERR_INVALID) and G <= 256 (else MOE_ERR_UNSUPPORTED). */
+moe_status moe_route_topk_grouped(const float *logits, int64_t T, int32_t E, int32_t K, int32_t group_size,
+                                  int32_t topk_groups, int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
 /* The dispatch "handle" ([Combine] §3: computed once by dispatch, reused by combine).
  * All members are caller-owned device arrays, written by moe_build_index.
  * R = moe_index_rows(...): T*K in the standard and group modes, E*capacity in drop-and-pad

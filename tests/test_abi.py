@@ -72,6 +72,12 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_route_topk(fake, 4, 64, 33, fake, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_route_topk(None, 4, 8, 2, fake, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == capi.MOE_OK  # empty: no-op
+    assert lib.moe_route_topk_grouped(fake, 4, 16, 2, 3, 2, fake, fake, None) == capi.MOE_ERR_INVALID  # 3 does not divide 16
+    assert lib.moe_route_topk_grouped(fake, 4, 16, 2, 4, 5, fake, fake, None) == capi.MOE_ERR_INVALID  # 5 of 4 groups
+    assert lib.moe_route_topk_grouped(fake, 4, 16, 9, 4, 2, fake, fake, None) == capi.MOE_ERR_INVALID  # K > 2*4
+    assert lib.moe_route_topk_grouped(fake, 4, 16, 2, 4, 0, fake, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_route_topk_grouped(fake, 4, 1024, 2, 2, 4, fake, fake, None) == capi.MOE_ERR_UNSUPPORTED  # 512 groups
+    assert lib.moe_route_topk_grouped(None, 0, 16, 2, 4, 2, None, None, None) == capi.MOE_OK
     assert lib.moe_permute(fake, 4, 0, 1, fake, 4, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute(fake, 4, 8, 7, fake, 4, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute(None, 0, 8, 1, None, 0, None, None) == capi.MOE_OK

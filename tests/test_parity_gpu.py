@@ -74,6 +74,21 @@ def test_route_topk(m, T, E, K, kind):
     assert_rel_f32(host(gw), want_w, "topk_w")
 
 
+@pytest.mark.parametrize("T,E,K,gs,M", [(1000, 256, 8, 8, 4), (777, 64, 6, 8, 2), (500, 256, 8, 32, 1),
+                                        (300, 16, 4, 4, 4), (2000, 1024, 8, 16, 8), (400, 12, 3, 3, 2),
+                                        (64, 8, 8, 1, 8), (10, 256, 1, 8, 1), (333, 256, 32, 8, 4)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_topk_grouped(m, T, E, K, gs, M, ties):
+    say(f"route_topk grouped T={T} E={E} K={K} gs={gs} M={M} ties={ties}")
+    key = wl.case_key(38, T, E, K, gs, M)
+    logits = tie_logits(key, T, E) if ties else wl.router_logits(key, T, E, zipf_s=1.2)
+    want_i, want_w = oracle.route_topk_grouped(logits, K, gs, M)
+    gi, gw = m.route_topk(dev(logits), K, group_size=gs, topk_groups=M)
+    torch.cuda.synchronize()
+    assert_exact(host(gi), want_i, "topk_idx")
+    assert_rel_f32(host(gw), want_w, "topk_w")
+
+
 def test_route_topk_empty(m):
     gi, gw = m.route_topk(torch.empty((0, 8), dtype=torch.float32, device=DEV), 2)
     torch.cuda.synchronize()
@@ -424,9 +439,10 @@ def sample_rows(n, count, seed):
     return s.astype(np.int64)
 
 
-def run_workload(m, cfg_id, align=0):
+def run_workload(m, cfg_id, align=0, route_groups=0):
     """Runs route -> index -> permute -> (pre-)combine on the GPU and checks every stage
-    (align > 1: the expert-aligned layout)."""
+    (align > 1: the expert-aligned layout; route_groups > 0: group-limited routing over the
+    workload's expert groups, that many groups per token)."""
     c = wl.WORKLOADS[cfg_id]
     T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
     key = wl.workload_key(cfg_id)
@@ -437,8 +453,12 @@ def run_workload(m, cfg_id, align=0):
     assert cap == (m.expert_capacity(T, K, E, *c["cf"]) if c["cf"] else 0)
     gs = c["group_size"]
 
-    want_i, want_w = oracle.route_topk(logits, K)
-    gi, gw = m.route_topk(dev(logits), K)
+    if route_groups:
+        want_i, want_w = oracle.route_topk_grouped(logits, K, gs, route_groups)
+        gi, gw = m.route_topk(dev(logits), K, group_size=gs, topk_groups=route_groups)
+    else:
+        want_i, want_w = oracle.route_topk(logits, K)
+        gi, gw = m.route_topk(dev(logits), K)
     assert_exact(host(gi), want_i, "topk_idx")
     assert_rel_f32(host(gw), want_w, "topk_w")
     # the same weight bits on both sides from here on
@@ -512,6 +532,13 @@ def run_workload(m, cfg_id, align=0):
 @pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
 def test_workload_full_size(m, cfg_id):
     run_workload(m, cfg_id)
+    torch.cuda.empty_cache()
+
+
+def test_workload_group_limited_routing(m):
+    """Workload 4 with every token limited to 4 of its 32 expert groups, as bench.py
+    --route-groups 4 launches it."""
+    run_workload(m, 4, route_groups=4)
     torch.cuda.empty_cache()
 
 

@@ -25,6 +25,7 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_expert_capacity": (_i64, [_i64, _i32, _i32, _i32, _i32]),
     "moe_route_topk": (ctypes.c_int, [_P, _i64, _i32, _i32, _P, _P, _P]),
+    "moe_route_topk_grouped": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _i32, _P, _P, _P]),
     "moe_build_index_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_build_index": (ctypes.c_int, [_P, _P, _i64, _i32, _i32, _i32, _i32, _i32,
                                        ctypes.POINTER(MoeIndexStruct), _P, ctypes.c_size_t, _P]),

@@ -10,6 +10,12 @@
 // instructions, no LDS round trip -- after which only the lane that owned the winner rescans
 // its keys. The softmax runs in double; the K exponentials meet in LDS and every lane sums them
 // in slot order.
+//
+// Group-limited routing ([Scratch] §21: pick a few expert groups first, then the experts inside
+// them) runs in the same kernel before the K rounds: the lanes fold their keys into per-group
+// maxima with LDS atomic max (on the order-preserving keys, so the maximum key is the group's
+// best logit), then topk_groups rounds of the same 16-lane reduction over (group key, ~group id)
+// pick the groups, and the experts of the other groups are dropped from the candidates.
 #include "moe_common.h"
 
 namespace moe {
@@ -64,12 +70,17 @@ __device__ __forceinline__ void row_max(uint32_t &hi, uint32_t &lo)
     max_step<kDppQuadXor1>(hi, lo);
 }
 
+constexpr int kMaxRouteGroups = 256;  // group keys in LDS: 16 tokens x 256 x 4 B per workgroup
+constexpr uint32_t kChosenGroup = 0xffffffffu;  // above every key of a finite logit
+
 template <int J>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
-                                                                   int E, int K, int32_t *__restrict__ topk_idx,
+                                                                   int E, int K, int gs, int M,
+                                                                   int32_t *__restrict__ topk_idx,
                                                                    float *__restrict__ topk_w)
 {
     __shared__ double ex_sh[kTokensPerBlock][MOE_MAX_TOPK];
+    extern __shared__ uint32_t group_sh[];  // [kTokensPerBlock][G] when gs > 0
     const int sub = threadIdx.x & (kLanesPerToken - 1);
     const int tok = threadIdx.x / kLanesPerToken;  // token of this row inside the block
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + tok;
@@ -82,6 +93,58 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
         const int e = sub + kLanesPerToken * j;
         u[j] = (live && e < E) ? orderable(row[e]) : 0u;
     }
+    if (gs > 0) {  // group-limited: keep only the experts of the M best groups (uniform branch)
+        const int G = E / gs;
+        uint32_t *gk = group_sh + tok * G;
+        for (int g = sub; g < G; g += kLanesPerToken)
+            gk[g] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (u[j])
+                atomicMax(&gk[(sub + kLanesPerToken * j) / gs], u[j]);
+        __syncthreads();
+        uint32_t gu[J];  // keys of groups sub + 16 q (G <= E, so J registers suffice)
+        uint32_t gbu = 0;
+        int gbq = 0;
+#pragma unroll
+        for (int q = 0; q < J; ++q) {
+            const int g = sub + kLanesPerToken * q;
+            gu[q] = g < G ? gk[g] : 0u;
+            if (gu[q] > gbu) {
+                gbu = gu[q];
+                gbq = q;
+            }
+        }
+        for (int m = 0; m < M; ++m) {
+            uint32_t hi = gbu;
+            uint32_t lo = gbu ? 0xffffffffu - static_cast<uint32_t>(sub + kLanesPerToken * gbq) : 0u;
+            row_max(hi, lo);
+            const int wg = static_cast<int>(0xffffffffu - lo);  // winning group of this row
+            if (hi != 0 && sub == (wg & (kLanesPerToken - 1))) {
+                const int wq = wg / kLanesPerToken;
+                gbu = 0;
+                gbq = 0;
+#pragma unroll
+                for (int q = 0; q < J; ++q) {
+                    if (q == wq)
+                        gu[q] = 0;
+                    if (gu[q] > gbu) {
+                        gbu = gu[q];
+                        gbq = q;
+                    }
+                }
+            }
+            if (hi != 0 && sub == 0)
+                gk[wg] = kChosenGroup;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (u[j] && gk[(sub + kLanesPerToken * j) / gs] != kChosenGroup)
+                u[j] = 0;
+    }
+
     // this lane's best: strict > over ascending j keeps the lowest id among equal logits
     uint32_t bu = 0;
     int bj = 0;
@@ -203,14 +266,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_backward_kernel(
 }  // namespace
 }  // namespace moe
 
-extern "C" moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
-                                     int32_t *topk_idx, float *topk_w, hipStream_t stream)
+namespace moe {
+namespace {
+
+moe_status launch_route(const float *logits, int64_t T, int32_t E, int32_t K, int32_t gs, int32_t M,
+                        int32_t *topk_idx, float *topk_w, hipStream_t stream)
 {
-    using namespace moe;
-    if (T < 0 || E < 1 || K < 1 || K > E)
-        return MOE_ERR_INVALID;
-    if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
-        return MOE_ERR_UNSUPPORTED;
     if (T == 0)
         return MOE_OK;
     if (!logits || !topk_idx || !topk_w)
@@ -219,22 +280,53 @@ extern "C" moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, 
     if (blocks > 0x7fffffff)
         return MOE_ERR_UNSUPPORTED;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kRouteThreads);
+    const size_t lds = gs > 0 ? sizeof(uint32_t) * kTokensPerBlock * static_cast<size_t>(E / gs) : 0;
     const int nj = static_cast<int>(ceil_div(E, kLanesPerToken));
+#define MOE_ROUTE_LAUNCH(JJ) \
+    hipLaunchKernelGGL(route_topk_kernel<JJ>, grid, block, lds, stream, logits, T, E, K, gs, M, topk_idx, topk_w)
     if (nj <= 1)
-        hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+        MOE_ROUTE_LAUNCH(1);
     else if (nj <= 2)
-        hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+        MOE_ROUTE_LAUNCH(2);
     else if (nj <= 4)
-        hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+        MOE_ROUTE_LAUNCH(4);
     else if (nj <= 8)
-        hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+        MOE_ROUTE_LAUNCH(8);
     else if (nj <= 16)
-        hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+        MOE_ROUTE_LAUNCH(16);
     else if (nj <= 32)
-        hipLaunchKernelGGL(route_topk_kernel<32>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+        MOE_ROUTE_LAUNCH(32);
     else
-        hipLaunchKernelGGL(route_topk_kernel<64>, grid, block, 0, stream, logits, T, E, K, topk_idx, topk_w);
+        MOE_ROUTE_LAUNCH(64);
+#undef MOE_ROUTE_LAUNCH
     return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t K,
+                                     int32_t *topk_idx, float *topk_w, hipStream_t stream)
+{
+    using namespace moe;
+    if (T < 0 || E < 1 || K < 1 || K > E)
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
+        return MOE_ERR_UNSUPPORTED;
+    return launch_route(logits, T, E, K, 0, 0, topk_idx, topk_w, stream);
+}
+
+extern "C" moe_status moe_route_topk_grouped(const float *logits, int64_t T, int32_t E, int32_t K,
+                                             int32_t group_size, int32_t topk_groups, int32_t *topk_idx,
+                                             float *topk_w, hipStream_t stream)
+{
+    using namespace moe;
+    if (T < 0 || E < 1 || K < 1 || K > E || group_size < 1 || E % group_size != 0 || topk_groups < 1 ||
+        topk_groups > E / group_size || static_cast<int64_t>(K) > static_cast<int64_t>(topk_groups) * group_size)
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || E / group_size > kMaxRouteGroups)
+        return MOE_ERR_UNSUPPORTED;
+    return launch_route(logits, T, E, K, group_size, topk_groups, topk_idx, topk_w, stream);
 }
 
 extern "C" moe_status moe_route_topk_backward(const int32_t *topk_idx, const float *topk_w, const float *d_topk_w,

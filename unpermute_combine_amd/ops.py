@@ -55,8 +55,10 @@ def expert_capacity(tokens: int, top_k: int, num_experts: int, cf_num: int = 5, 
     return int(v)
 
 
-def route_topk(logits: torch.Tensor, k: int, out=None):
+def route_topk(logits: torch.Tensor, k: int, out=None, group_size: int = 0, topk_groups: int = 0):
     """Top-k experts per token (ties -> lower id) and softmax over the k selected logits.
+    With group_size > 0 and topk_groups > 0: group-limited routing (the topk_groups groups
+    of group_size experts with the best logit first, then top-k among their experts).
 
     Returns (topk_idx int32 [T, k], topk_w float32 [T, k])."""
     _need(logits, "logits", torch.float32, 2)
@@ -70,7 +72,11 @@ def route_topk(logits: torch.Tensor, k: int, out=None):
         _need(w, "topk_w", torch.float32, 2)
         if tuple(idx.shape) != (T, k) or tuple(w.shape) != (T, k):
             raise ValueError("output shapes must be [T, k]")
-    check("moe_route_topk", lib().moe_route_topk(_p(logits), T, E, k, _p(idx), _p(w), _stream()))
+    if group_size > 0 or topk_groups > 0:
+        check("moe_route_topk_grouped", lib().moe_route_topk_grouped(
+            _p(logits), T, E, k, group_size, topk_groups, _p(idx), _p(w), _stream()))
+    else:
+        check("moe_route_topk", lib().moe_route_topk(_p(logits), T, E, k, _p(idx), _p(w), _stream()))
     return idx, w
 
 
