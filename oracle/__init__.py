@@ -54,7 +54,13 @@ def _declare(lib):
     lib.oracle_build_index.restype = ctypes.c_int
     lib.oracle_permute.argtypes = [P, i64, i64, i32, P, i64, P]
     lib.oracle_permute.restype = ctypes.c_int
-    lib.oracle_unpermute_combine.argtypes = [P, i32, i64, i64, P, P, i64, i32, P, i32]
+    lib.oracle_unpermute_combine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, P, i32]
+    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f32.restype = ctypes.c_float
+    lib.oracle_quantize_fp8.argtypes = [P, i32, i64, i64, i32, P, P]
+    lib.oracle_quantize_fp8.restype = ctypes.c_int
     lib.oracle_unpermute_combine.restype = ctypes.c_int
     lib.oracle_group_precombine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, i32, P, i64, P]
     lib.oracle_route_topk_grouped.argtypes = [P, i64, i32, i32, i32, i32, P, P]
@@ -178,7 +184,8 @@ def permute(src: np.ndarray, src_row: np.ndarray) -> np.ndarray:
     """dst[i] = src[src_row[i]] bitwise; rows outside [0, len(src)) give zeros, except -2
     (unused slack), which leaves the row as it is (here: the NaN poison)."""
     src = np.ascontiguousarray(src)
-    _dt_of(src)
+    if src.dtype != np.uint8:
+        _dt_of(src)
     src_rows, H = src.shape
     src_row = _c(src_row, np.int32).reshape(-1)
     dst = _poisoned((src_row.shape[0], H), src.dtype)
@@ -188,8 +195,8 @@ def permute(src: np.ndarray, src_row: np.ndarray) -> np.ndarray:
     return dst
 
 
-def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype) -> np.ndarray:
-    """out[t] = sum_k w[t,k] * y[row_of[t,k]] (float32 FMA chain in k order)."""
+def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype, bias=None) -> np.ndarray:
+    """out[t] = sum_k w[t,k] * y[row_of[t,k]] (float32 FMA chain in k order) [+ bias[t]]."""
     y = np.ascontiguousarray(y)
     y_dt = _dt_of(y)
     y_rows, H = y.shape
@@ -198,7 +205,10 @@ def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype) -> np.nda
     w = None if w is None else _c(w, np.float32).reshape(T, K)
     out = _poisoned((T, H), out_dtype)
     out_dt = _dt_of(out)
-    rc = _load().oracle_unpermute_combine(_ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
+    if bias is not None:
+        bias = np.ascontiguousarray(bias)
+        assert bias.dtype == out.dtype and bias.shape == (T, H)
+    rc = _load().oracle_unpermute_combine(_ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w), _ptr(bias),
                                           T, K, _ptr(out), out_dt)
     _check(rc, "unpermute_combine")
     return out
@@ -253,3 +263,21 @@ def route_topk_backward(topk_idx: np.ndarray, topk_w: np.ndarray, d_topk_w: np.n
     rc = _load().oracle_route_topk_backward(_ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w), T, E, K, _ptr(d_logits))
     _check(rc, "route_topk_backward")
     return d_logits
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(_load().oracle_f32_to_e4m3(float(x)))
+
+
+def e4m3_to_f32(c: int) -> float:
+    return float(_load().oracle_e4m3_to_f32(int(c)))
+
+
+def quantize_fp8(x: np.ndarray, block: int):
+    """Per-(token, block) E4M3 quantization: returns (q uint8 [T, H], scales float32 [T, H/block])."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    q = np.full((T, H), 0x7F, np.uint8)
+    scales = np.full((T, H // block if block > 0 else 0), np.nan, np.float32)
+    _check(_load().oracle_quantize_fp8(_ptr(x), _dt_of(x), T, H, block, _ptr(q), _ptr(scales)), "quantize_fp8")
+    return q, scales

@@ -74,6 +74,52 @@ static void store_elem(void *base, int dt, int64_t i, float v)
 
 uint16_t oracle_f32_to_bf16(float f) { return f32_to_bf16(f); }
 
+/* FP8 E4M3 (the OCP 8-bit format, "fn": no infinities): 1 sign bit, 4 exponent bits (bias 7),
+ * 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; 0x7f / 0xff are NaN, so the
+ * largest finite magnitude is 0x7e = 1.75 * 2^8 = 448. Rounding to nearest, ties to even; a
+ * magnitude that rounds above 448 saturates to 448 (the conversion used for the dispatch). */
+static uint8_t f32_to_e4m3(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+    if (isnan(f))
+        return (uint8_t)(sign | 0x7f);
+    double a = fabs((double)f);
+    if (a > 448.0)                     /* rounds to 448 or beyond it: saturates (infinity too) */
+        return (uint8_t)(sign | 0x7e);
+    if (a < 0x1p-6) {                 /* subnormal range: a multiple of 2^-9 */
+        double m = nearbyint(a * 512.0); /* exact scaling; default rounding: ties to even */
+        return (uint8_t)(sign | (uint8_t)m); /* m == 8 is the smallest normal, code 0x08 */
+    }
+    int ex;
+    double fr = frexp(a, &ex);          /* a = fr * 2^ex, fr in [0.5, 1) */
+    int E = ex - 1;                     /* a = (1 + t) * 2^E */
+    double mant = nearbyint((a / ldexp(1.0, E) - 1.0) * 8.0);
+    (void)fr;
+    if (mant == 8.0) {
+        mant = 0.0;
+        E += 1;
+    }
+    return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | (int)mant));
+}
+
+static float e4m3_to_f32(uint8_t c)
+{
+    int sign = c & 0x80, E = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (E == 15 && m == 7)
+        v = NAN;
+    else if (E == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, E - 7);
+    return (float)(sign ? -v : v);
+}
+
+uint8_t oracle_f32_to_e4m3(float f) { return f32_to_e4m3(f); }
+float oracle_e4m3_to_f32(uint8_t c) { return e4m3_to_f32(c); }
+
 /* ---------------------------------------------------------------- capacity ---------- */
 
 /* [Scratch] §18: expert_capacity = ceil(tokens * top_k / num_experts * capacity_factor).
@@ -381,11 +427,11 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
  * copy of source row src_row[i]. A src_row outside [0, src_rows) (the padding rows of the
  * drop-and-pad and aligned layouts carry -1) gives a row of zeros ([Scratch] §18 padded expert
  * buffers); src_row = -2 marks unused slack, a row that is left as it is.
- * elem_bytes is the size of one hidden element (4 or 2). */
+ * elem_bytes is the size of one hidden element (4, 2, or 1 for FP8 codes). */
 int oracle_permute(const void *src, int64_t src_rows, int64_t H, int32_t elem_bytes,
                    const int32_t *src_row, int64_t N, void *dst)
 {
-    if (src_rows < 0 || H < 1 || N < 0 || (elem_bytes != 2 && elem_bytes != 4) ||
+    if (src_rows < 0 || H < 1 || N < 0 || (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) ||
         (N > 0 && (!src_row || !dst)) || (src_rows > 0 && !src))
         return ORC_INVALID;
     size_t row_bytes = (size_t)H * (size_t)elem_bytes;
@@ -410,10 +456,12 @@ int oracle_permute(const void *src, int64_t src_rows, int64_t H, int32_t elem_by
  * Arithmetic, as fixed for this path: float32 accumulator starting at +0, one fused
  * multiply-add per slot in slot order k = 0..K-1, skipping slots whose row is outside
  * [0, y_rows); w == NULL means every weight is 1 (the pure-add combine of [Combine] §2.3/§3).
- * The float32 result is stored as is, or rounded to bf16 (nearest even). */
+ * A bias ([Combine] §3: DeepEP's combine adds an optional final bias), an array shaped and typed
+ * like the output, is added in float32 after the sum (one addition), before the output is
+ * stored as float32 or rounded to bf16 (nearest even). */
 int oracle_unpermute_combine(const void *y, int32_t y_dt, int64_t y_rows, int64_t H,
-                             const int32_t *row_of, const float *w, int64_t T, int32_t K,
-                             void *out, int32_t out_dt)
+                             const int32_t *row_of, const float *w, const void *bias, int64_t T,
+                             int32_t K, void *out, int32_t out_dt)
 {
     if (y_rows < 0 || H < 1 || T < 0 || K < 1 || (y_dt != 0 && y_dt != 1) ||
         (out_dt != 0 && out_dt != 1) || (T > 0 && (!row_of || !out)) || (y_rows > 0 && !y))
@@ -428,6 +476,8 @@ int oracle_unpermute_combine(const void *y, int32_t y_dt, int64_t y_rows, int64_
                 float wk = w ? w[t * K + k] : 1.0f;
                 acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);
             }
+            if (bias)
+                acc = acc + load_elem(bias, out_dt, t * H + h);
             store_elem(out, out_dt, t * H + h, acc);
         }
     }
@@ -555,5 +605,41 @@ int oracle_route_topk_backward(const int32_t *topk_idx, const float *topk_w, con
             d_logits[t * E + e] = (float)acc[e];
     }
     free(acc);
+    return ORC_OK;
+}
+
+
+/* ---------------------------------------------------------------- FP8 dispatch -------- */
+
+/* FP8 dispatch ([Combine] §3: the dispatch sends FP8 while the combine stays BF16; [Megatron],
+ * the DeepEP dispatch call: x travels with x_scales, num_scales scale groups per token along
+ * the hidden dimension). Reading: each token's hidden vector is cut into blocks of `block`
+ * consecutive elements (block = H: one scale per token); per block
+ *   amax  = max |x|,  scale = amax / 448 (float32 division; 1 when amax is 0),
+ *   q[i]  = e4m3(x[i] / scale)   (float32 division, then nearest-even E4M3 with saturation),
+ * so that x[i] ~ e4m3_value(q[i]) * scale. q is [T, H] bytes, scales [T, H / block] float32.
+ * The dispatch then moves q rows and scale rows with the same gather map (oracle_permute with
+ * 1-byte and 4-byte elements). Requires block dividing H. */
+int oracle_quantize_fp8(const void *x, int32_t x_dt, int64_t T, int64_t H, int32_t block, uint8_t *q,
+                        float *scales)
+{
+    if (T < 0 || H < 1 || block < 1 || H % block != 0 || (x_dt != 0 && x_dt != 1) ||
+        (T > 0 && (!x || !q || !scales)))
+        return ORC_INVALID;
+    int64_t nb = H / block;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b < nb; ++b) {
+            float amax = 0.0f;
+            for (int64_t i = b * block; i < (b + 1) * block; ++i) {
+                float a = fabsf(load_elem(x, x_dt, t * H + i));
+                if (a > amax)
+                    amax = a;
+            }
+            float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scales[t * nb + b] = scale;
+            for (int64_t i = b * block; i < (b + 1) * block; ++i)
+                q[t * H + i] = f32_to_e4m3(load_elem(x, x_dt, t * H + i) / scale);
+        }
+    }
     return ORC_OK;
 }

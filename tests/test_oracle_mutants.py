@@ -15,6 +15,7 @@ import oracle
 from oracle.build import SRC
 import test_oracle_backward as bw
 import test_oracle_bruteforce as bf
+import test_oracle_fp8 as f8
 import test_oracle_grouped_route as gr
 import test_oracle_pins as pins
 
@@ -49,14 +50,14 @@ MUTANTS = [
      "memcpy(d, (const unsigned char *)src + (size_t)(s + 1 < src_rows ? s + 1 : s) * row_bytes, row_bytes);"),
     ("permute leaves padding rows unwritten", "        else if (s != -2)\n            memset(d, 0, row_bytes);",
      "        else\n            (void)0;"),
-    ("combine drops the accumulator", "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            store_elem(out, out_dt, t * H + h, acc);",
-     "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), 0.0f);\n            }\n            store_elem(out, out_dt, t * H + h, acc);"),
+    ("combine drops the accumulator", "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            if (bias)",
+     "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), 0.0f);\n            }\n            if (bias)"),
     ("combine skips slot 0", "            for (int32_t k = 0; k < K; ++k) {\n                int32_t r = row_of[t * K + k];\n                if (r < 0 || r >= y_rows)\n                    continue;\n                float wk",
      "            for (int32_t k = 1; k < K; ++k) {\n                int32_t r = row_of[t * K + k];\n                if (r < 0 || r >= y_rows)\n                    continue;\n                float wk"),
-    ("combine weights transposed", "                float wk = w ? w[t * K + k] : 1.0f;\n                acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            store_elem",
-     "                float wk = w ? w[k * T + t] : 1.0f;\n                acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            store_elem"),
-    ("combine subtracts", "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            store_elem(out, out_dt, t * H + h, acc);",
-     "acc = fmaf(-wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            store_elem(out, out_dt, t * H + h, acc);"),
+    ("combine weights transposed", "                float wk = w ? w[t * K + k] : 1.0f;\n                acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            if (bias)",
+     "                float wk = w ? w[k * T + t] : 1.0f;\n                acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            if (bias)"),
+    ("combine subtracts", "acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            if (bias)",
+     "acc = fmaf(-wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);\n            }\n            if (bias)"),
     ("bf16 rounding truncates", "    uint32_t lsb = (u >> 16) & 1u;\n    u += 0x7fffu + lsb;", "    uint32_t lsb = 0u;\n    (void)lsb;"),
     ("bf16 ties round up", "    u += 0x7fffu + lsb;", "    u += 0x8000u + 0u * lsb;"),
     ("pre-combine mixes groups", "if (e < 0 || e >= E || e / group_size != g || r < 0 || r >= y_rows)",
@@ -66,6 +67,14 @@ MUTANTS = [
      "                if (0 && s[e] > s[top])\n                    top = e;"),
     ("group ties go to the higher id", "if (bg < 0 || score[g] > score[bg])", "if (bg < 0 || score[g] >= score[bg])"),
     ("experts outside the chosen groups allowed", "taken[e] = chosen[e / group_size] ? 0 : 1;", "taken[e] = 0;"),
+    ("e4m3 ties away from zero", "double mant = nearbyint((a / ldexp(1.0, E) - 1.0) * 8.0);",
+     "double mant = round((a / ldexp(1.0, E) - 1.0) * 8.0);"),
+    ("e4m3 subnormals truncate", "double m = nearbyint(a * 512.0);", "double m = floor(a * 512.0);"),
+    ("e4m3 without saturation", "    if (a > 448.0)", "    if (a > 1e30)"),
+    ("scale for the wrong FP8 maximum", "amax / 448.0f", "amax / 240.0f"),
+    ("combine bias ignored", "acc = acc + load_elem(bias, out_dt, t * H + h);", "acc = acc + 0.0f;"),
+    ("combine bias from the wrong token", "acc = acc + load_elem(bias, out_dt, t * H + h);",
+     "acc = acc + load_elem(bias, out_dt, h);"),
     ("combine backward ignores the weight",
      "store_elem(dy, dy_dt, (int64_t)r * H + h, wk * load_elem(dout, dout_dt, t * H + h));",
      "store_elem(dy, dy_dt, (int64_t)r * H + h, load_elem(dout, dout_dt, t * H + h));"),
@@ -120,6 +129,13 @@ def _pins():
         gr.test_single_expert_groups_is_plain_routing,
         gr.test_k1_is_the_argmax,
         gr.test_selection_is_the_optimal_one_fixed_cases,
+        f8.test_every_code_decodes_like_the_library,
+        f8.test_encoding_matches_the_library_within_range,
+        f8.test_saturation_and_nan,
+        lambda: f8.test_quantize_bounds("f32", 128),
+        lambda: f8.test_quantize_bounds("bf16", 32),
+        f8.test_quantize_blocks_are_independent_and_bf16_is_its_widening,
+        f8.test_combine_bias_is_one_final_addition,
     ]
     return checks
 
