@@ -28,6 +28,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 METRIC = "permute+combine effective HBM GB/s (% of peak) and routed tokens/s"
 _PERMUTE_SRC = ["unpermute_combine_amd/csrc/permute.hip", "unpermute_combine_amd/csrc/moe_common.h"]
 _COMBINE_SRC = ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csrc/moe_common.h"]
+_FP8_SRC = ["unpermute_combine_amd/csrc/fp8.hip", "unpermute_combine_amd/csrc/moe_common.h"]
 # HBM-bound kernel calls of a step: sources (for the PMC summaries' digest) and kernel symbol.
 # Standard and drop-and-pad steps run `permute` and `combine`; group-mode steps run the two
 # dispatch stages (send: one copy per token and group; receive: group slots to expert-major
@@ -39,12 +40,15 @@ _COMBINE_SRC = ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd
 KERNEL_SOURCES = {"permute": _PERMUTE_SRC, "combine": _COMBINE_SRC, "dispatch_send": _PERMUTE_SRC,
                   "dispatch_recv": _PERMUTE_SRC, "precombine": _COMBINE_SRC, "final_sum": _COMBINE_SRC,
                   "combine_bwd": _COMBINE_SRC, "dispatch_bwd": _COMBINE_SRC, "dispatch_bwd_recv": _COMBINE_SRC,
-                  "dispatch_bwd_send": _COMBINE_SRC}
+                  "dispatch_bwd_send": _COMBINE_SRC, "permute_fp8": _FP8_SRC, "dispatch_send_fp8": _FP8_SRC,
+                  "dispatch_recv_scales": _PERMUTE_SRC}
 KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine_kernel",
                   "dispatch_send": "permute_scatter_vec16_kernel", "dispatch_recv": "permute_grouped_vec16_kernel",
                   "precombine": "precombine_kernel", "final_sum": "combine_kernel",
                   "combine_bwd": "combine_backward_kernel", "dispatch_bwd": "combine_kernel",
-                  "dispatch_bwd_recv": "precombine_kernel", "dispatch_bwd_send": "combine_kernel"}
+                  "dispatch_bwd_recv": "precombine_kernel", "dispatch_bwd_send": "combine_kernel",
+                  "permute_fp8": "permute_scatter_fp8_kernel", "dispatch_send_fp8": "permute_scatter_fp8_kernel",
+                  "dispatch_recv_scales": "permute_grouped_vec16_kernel"}
 METRIC_BACKWARD = "backward of permute+combine (and router softmax) effective HBM GB/s (% of peak)"
 
 
@@ -63,6 +67,9 @@ def parse_args():
                    help="round every expert segment up to a multiple of this many rows (padding rows)")
     p.add_argument("--route-groups", type=int, default=0,
                    help="group-limited routing: each token keeps this many of the workload's expert groups")
+    p.add_argument("--fp8", action="store_true",
+                   help="FP8 dispatch: the permute quantizes x to E4M3 codes with one float32 scale per 128 "
+                        "elements and moves codes and scales (the combine stays bf16)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
@@ -163,9 +170,21 @@ def main():
     gw = torch.empty((T, K), dtype=torch.float32, device="cuda")
     ix = m.alloc_index(T, K, E, cap, gs, alignment=align)
     xp = torch.empty((rows, H), dtype=tdt, device="cuda")
+    fp8_block = 128
+    nb = H // fp8_block
+    if args.fp8:
+        if args.backward or c["identity_experts"]:
+            print("--fp8 times the forward dispatch of a workload with expert outputs (not 1, not --backward)",
+                  file=sys.stderr, flush=True)
+            sys.exit(2)
+        xq = torch.empty((rows, H), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((rows, nb), dtype=torch.float32, device="cuda")
     out = torch.empty((T, H), dtype=tdt, device="cuda")
     G = E // gs if gs else 0
-    gbuf = torch.empty((T * min(K, G), H), dtype=tdt, device="cuda") if gs else None
+    gbuf = torch.empty((T * min(K, G), H), dtype=tdt, device="cuda") if gs and not args.fp8 else None
+    if gs and args.fp8:
+        gq = torch.empty((T * min(K, G), H), dtype=torch.uint8, device="cuda")
+        gsc = torch.empty((T * min(K, G), nb), dtype=torch.float32, device="cuda")
     part = torch.empty((T * min(K, G), H), dtype=torch.float32, device="cuda") if gs else None
 
     # the step's calls in order: (kernel name, stage, call)
@@ -200,6 +219,19 @@ def main():
         else:
             calls += [("dispatch_bwd", "dispatch_bwd", lambda: m.unpermute_combine(dxp, ix.row_of, None, out=dx))]
         calls += [("route_bwd", "route_bwd", lambda: m.route_topk_backward(gi, gw, dw, E, out=dlog))]
+    elif args.fp8 and gs:
+        calls += [("dispatch_send_fp8", "permute",
+                   lambda: m.permute_scatter_fp8(x, ix.slot_of, gq.shape[0], fp8_block, out=(gq, gsc))),
+                  ("dispatch_recv", "permute", lambda: m.permute_grouped(gq, ix.esrc, ix.row_of, out=xq)),
+                  ("dispatch_recv_scales", "permute", lambda: m.permute_grouped(gsc, ix.esrc, ix.row_of, out=xs)),
+                  ("precombine", "combine",
+                   lambda: m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)),
+                  ("final_sum", "combine", lambda: m.unpermute_combine(part, ix.slot_of, None, out=out))]
+    elif args.fp8:
+        calls += [("permute_fp8", "permute",
+                   lambda: m.permute_scatter_fp8(x, ix.row_of, rows, fp8_block, src_row=ix.sorted_indices,
+                                                 out=(xq, xs))),
+                  ("combine", "combine", lambda: m.unpermute_combine(src, ix.row_of, gw, out=out))]
     elif gs:
         # the number of group slots is only known on the device; every call is bounded by its
         # upper bound T*min(K,G) instead, so the step never waits for the host
@@ -257,6 +289,16 @@ def main():
                           dispatch_bwd_send=n * H * 4 + T * G * 4 + T * H * b)
         else:
             kbytes.update(dispatch_bwd=valid * H * b + T * K * 4 + T * H * b)
+    elif args.fp8 and gs:
+        n = int(ix.n_slots.item())
+        kbytes.update(dispatch_send_fp8=routed * H * b + n * 4 + n * (H + nb * 4),
+                      dispatch_recv=n * H + rows * 4 + used * H,
+                      dispatch_recv_scales=n * nb * 4 + rows * 4 + used * nb * 4,
+                      precombine=valid * H * b + 2 * T * K * 4 + n * H * 4,
+                      final_sum=n * H * 4 + T * G * 4 + T * H * b)
+    elif args.fp8:
+        kbytes.update(permute_fp8=routed * H * b + rows * 4 + used * (H + nb * 4),
+                      combine=valid * H * b + 2 * T * K * 4 + T * H * b)
     elif gs:
         n = int(ix.n_slots.item())
         kbytes.update(dispatch_send=routed * H * b + n * 4 + n * H * b,
@@ -289,7 +331,8 @@ def main():
         "metric": METRIC_BACKWARD if args.backward else METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
-        "config": {"workload": c["name"] + (f" align{align}" if align else "") + (f" groups{rg}" if rg else ""),
+        "config": {"workload": c["name"] + (f" align{align}" if align else "") + (f" groups{rg}" if rg else "")
+                   + (" fp8-dispatch" if args.fp8 else ""), "fp8_dispatch": bool(args.fp8),
                    "T": T, "H": H, "E": E, "K": K, "capacity": cap, "alignment": align, "route_groups": rg,
                    "group_size": gs, "zipf_s": c["zipf_s"], "seed_key": list(key)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -304,7 +347,9 @@ def main():
     }
     if args.backward:
         result["pass"] = "backward"
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.fp8:
+        result["cpu_baseline"] = None  # the oracle baseline is timed on the bf16 path
+    elif not args.no_cpu_baseline:
         if args.backward:
             result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes)
         else:

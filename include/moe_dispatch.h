@@ -48,7 +48,10 @@ typedef enum {
     MOE_ERR_HIP = 3
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Element types of hidden rows. MOE_FP8_E4M3 (1-byte OCP E4M3 codes, the FP8 dispatch) is
+ * accepted by the permutes only, which copy bytes; the combines work in bf16 / float32 and
+ * return MOE_ERR_UNSUPPORTED for it. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
 /* Upper limits of the kernels. */
 #define MOE_MAX_EXPERTS 1024
@@ -214,6 +217,30 @@ moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe
                                const int32_t *src_row, int64_t N, const int32_t *dst_of, int64_t M,
                                int32_t J, void *dst, hipStream_t stream);
 
+/* FP8 dispatch ([Combine] §3: the dispatch sends FP8, the combine stays BF16; the DeepEP
+ * dispatch call in [Megatron] passes x together with x_scales, num_scales scale groups per token
+ * along the hidden dimension). Each token's row is cut into H / block blocks of `block`
+ * consecutive elements; per block
+ *   amax = max |x|,  scale = amax / 448 (float32 division; 1 when amax is 0),
+ *   q[i] = E4M3 code of x[i] / scale (float32 division, nearest even, saturating at 448),
+ * E4M3 being the OCP 8-bit format (bias 7, no infinities, 448 the largest finite value).
+ *   moe_quantize_fp8: x [T, H] (x_dt float32 or bf16) -> q [T, H] bytes, scales [T, H/block]
+ *     float32. block must divide H.
+ *   moe_permute_scatter_fp8: the same codes and scales, computed once per source row and
+ *     written source-major like moe_permute_scatter: dst[dst_of[t*J+j]] = q[t],
+ *     dst_scales[...] = scales[t]; rows with src_row outside [0, src_rows) get zero codes and
+ *     zero scales (padding), MOE_ROW_UNUSED rows are left untouched. Equal, bit for bit, to
+ *     moe_quantize_fp8 followed by moe_permute_scatter of the codes (MOE_FP8_E4M3) and of the
+ *     scales (float32, H / block columns). block must be a power of two in [8, 1024] dividing H
+ *     (else MOE_ERR_UNSUPPORTED), J <= 64, src and dst 16-byte aligned.
+ * The moved rows then hold half the bytes of bf16 rows; moe_permute / moe_permute_grouped move
+ * FP8 rows (and float32 scale rows) as they move any rows. */
+moe_status moe_quantize_fp8(const void *x, moe_dtype x_dt, int64_t T, int64_t H, int32_t block, uint8_t *q,
+                            float *scales, hipStream_t stream);
+moe_status moe_permute_scatter_fp8(const void *src, moe_dtype src_dt, int64_t src_rows, int64_t H, int32_t block,
+                                   const int32_t *dst_of, int32_t J, const int32_t *src_row, int64_t N, uint8_t *dst,
+                                   float *dst_scales, hipStream_t stream);
+
 /* Unpermute + weighted top-k merge ([Combine] §1: out[t] = sum over the token's top-k experts
  * of probs[t,e] * expert_e(x[t]); [Scratch] §13, §16):
  *   out[t, :] = sum_{k = 0..K-1, row_of[t,k] in [0, y_rows)} w[t,k] * y[row_of[t,k], :]
@@ -223,12 +250,14 @@ moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe
  *   y      [y_rows, H] expert outputs in expert-major order (dtype y_dt).
  *   row_of [T, K] int32 (moe_index.row_of).
  *   w      [T, K] float32, or NULL for unit weights (the pure-add combine, [Combine] §3).
+ *   bias   [T, H] of dtype out_dt, or NULL: the final bias of [Combine] §3, added in float32
+ *          after the sum (one addition) before the output is rounded.
  *   out    [T, H] dtype out_dt.
  * K may be up to 1024 here: the group-mode final sum calls it with y = partials,
  * row_of = slot_of, w = NULL and K = G. */
 moe_status moe_unpermute_combine(const void *y, moe_dtype y_dt, int64_t y_rows, int64_t H,
-                                 const int32_t *row_of, const float *w, int64_t T, int32_t K,
-                                 void *out, moe_dtype out_dt, hipStream_t stream);
+                                 const int32_t *row_of, const float *w, const void *bias, int64_t T,
+                                 int32_t K, void *out, moe_dtype out_dt, hipStream_t stream);
 
 /* Local pre-combine per group ([CANN] §1(2): the outputs of a token's experts on the same rank
  * are merged with their weights before leaving the rank; here a group of group_size experts
@@ -261,7 +290,7 @@ moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, i
  *   (w NULL: unit weights, dy = dout); src_row [y_rows] (moe_index.sorted_indices) or NULL;
  *   dy [y_rows, H] (dy_dt); dw [T, K] float32 or NULL (not computed).
  * The backward of the dispatch needs no call of its own ([Combine] §4.1): it is the unit-weight
- * combine of the expert-row gradient, moe_unpermute_combine(dxp, ..., row_of, NULL, ...); in
+ * combine of the expert-row gradient, moe_unpermute_combine(dxp, ..., row_of, NULL, NULL, ...); in
  * group mode moe_group_precombine with w = NULL followed by the final sum over groups. */
 moe_status moe_unpermute_combine_backward(const void *dout, moe_dtype dout_dt, const void *y, moe_dtype y_dt,
                                           int64_t y_rows, int64_t H, const int32_t *row_of, const float *w,

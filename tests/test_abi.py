@@ -81,9 +81,11 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_permute(fake, 4, 0, 1, fake, 4, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute(fake, 4, 8, 7, fake, 4, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute(None, 0, 8, 1, None, 0, None, None) == capi.MOE_OK
-    assert lib.moe_unpermute_combine(fake, 1, 4, 8, fake, None, 2, 0, fake, 1, None) == capi.MOE_ERR_INVALID
-    assert lib.moe_unpermute_combine(fake, 1, 4, 8, fake, None, 2, 2000, fake, 1, None) == capi.MOE_ERR_UNSUPPORTED
-    assert lib.moe_unpermute_combine(fake, 1, 4, 8, None, None, 2, 2, fake, 1, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_unpermute_combine(fake, 1, 4, 8, fake, None, None, 2, 0, fake, 1, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_unpermute_combine(fake, 1, 4, 8, fake, None, None, 2, 2000, fake, 1, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(fake, 1, 4, 8, None, None, None, 2, 2, fake, 1, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_unpermute_combine(fake, 2, 4, 8, fake, None, None, 2, 2, fake, 1, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # the combine does not take FP8 rows
     assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 3, fake, 4, fake, None) == \
         capi.MOE_ERR_INVALID
     assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, 2, 65, fake, None) == capi.MOE_ERR_UNSUPPORTED
@@ -105,13 +107,23 @@ def test_argument_errors_return_before_any_launch(capi):
                                               None) == capi.MOE_ERR_INVALID
     assert lib.moe_unpermute_combine_backward(None, 1, None, 1, 4, 8, None, None, 0, 2, None, None, 1, None,
                                               None) == capi.MOE_OK  # no tokens, no gather map: nothing to do
+    assert lib.moe_quantize_fp8(fake, 1, 4, 100, 30, fake, fake, None) == capi.MOE_ERR_INVALID  # 30 does not divide 100
+    assert lib.moe_quantize_fp8(fake, 2, 4, 128, 128, fake, fake, None) == capi.MOE_ERR_UNSUPPORTED  # FP8 input
+    assert lib.moe_quantize_fp8(None, 1, 0, 128, 128, None, None, None) == capi.MOE_OK
+    assert lib.moe_permute_scatter_fp8(fake, 1, 4, 384, 96, fake, 2, None, 8, fake, fake, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # block not a power of two
+    assert lib.moe_permute_scatter_fp8(fake, 1, 4, 4096, 2048, fake, 2, None, 8, fake, fake, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # block above 1024
+    assert lib.moe_permute_scatter_fp8(fake, 1, 4, 128, 128, fake, 2, None, 8, None, fake, None) == \
+        capi.MOE_ERR_INVALID
+    assert lib.moe_permute(fake, 4, 8, 2, None, 4, fake, None) == capi.MOE_ERR_INVALID  # FP8 rows: map needed
     # hidden rows longer than 2^31 - 1 bytes are refused (buffer resources address a row in 32 bits)
     big = 1 << 30
     assert lib.moe_permute(fake, 4, big, 1, fake, 4, fake, None) == capi.MOE_ERR_UNSUPPORTED  # bf16: 2 GiB rows
     assert lib.moe_permute(fake, 4, big // 2, 0, fake, 4, fake, None) == capi.MOE_ERR_UNSUPPORTED  # f32
     assert lib.moe_permute_scatter(fake, 4, big, 1, fake, 2, None, 8, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_permute_grouped(fake, 4, big, 1, fake, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
-    assert lib.moe_unpermute_combine(fake, 1, 4, big // 2, fake, None, 2, 2, fake, 0, None) == \
+    assert lib.moe_unpermute_combine(fake, 1, 4, big // 2, fake, None, None, 2, 2, fake, 0, None) == \
         capi.MOE_ERR_UNSUPPORTED  # float32 output rows of 2 GiB
     assert lib.moe_group_precombine(fake, 1, 4, big // 2, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, None) == \
         capi.MOE_ERR_UNSUPPORTED  # float32 partial rows of 2 GiB

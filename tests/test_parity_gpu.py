@@ -359,6 +359,97 @@ def test_permute_aligned(m, dtype, H, T, E, K, align):
                  oracle.unpermute_combine(y, ix["row_of"], w, out_np), "combine over aligned rows")
 
 
+# ------------------------------------------------------------------ FP8 dispatch
+
+
+def fp8_inputs(key, T, H, dtype):
+    x = wl.hidden_states(key, T, H, dtype)
+    x[min(1, T - 1)] = 0  # an all-zero token: scale 1, zero codes
+    if T > 3:
+        f = wl.bf16_bits_to_f32(x[2]) if dtype == "bf16" else x[2]
+        f = (f * 1e-30 if dtype == "f32" else f * 1e-20).astype(np.float32)  # tiny blocks: subnormal quotients
+        x[2] = wl.f32_to_bf16_bits(f) if dtype == "bf16" else f
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,H,block", [(100, 7168, 128), (77, 512, 32), (50, 1024, 512), (30, 7168, 7168),
+                                       (40, 384, 96), (3, 8, 8), (60, 4096, 64), (5, 21, 7)])
+def test_quantize_fp8(m, dtype, T, H, block):
+    say(f"quantize_fp8 {dtype} T={T} H={H} block={block}")
+    x = fp8_inputs(wl.case_key(70, T, H, block), T, H, dtype)
+    want_q, want_s = oracle.quantize_fp8(x, block)
+    q, sc = m.quantize_fp8(dev(x), block)
+    assert_exact(host(q), want_q, "codes")
+    assert_exact(host(sc), want_s, "scales")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H,T,E,K,mode,block", [(7168, 300, 64, 8, "standard", 128), (1024, 200, 16, 4, "drop", 64),
+                                                (4096, 257, 32, 8, "aligned", 128), (512, 100, 8, 2, "holes", 512),
+                                                (64, 90, 12, 6, "standard", 8), (2048, 128, 64, 8, "group", 128),
+                                                (520, 64, 8, 2, "drop", 8), (3072, 50, 16, 4, "standard", 1024),
+                                                (1040, 70, 8, 4, "holes", 16)])
+def test_permute_scatter_fp8(m, dtype, H, T, E, K, mode, block):
+    """Fused FP8 dispatch = the oracle's quantization followed by the oracle's row gather of the
+    codes and of the scales, bit for bit; padding rows zero, unused slack untouched."""
+    say(f"permute_scatter_fp8 {dtype} H={H} T={T} E={E} K={K} {mode} block={block}")
+    key = wl.case_key(71, H, T, E, K)
+    logits = wl.router_logits(key, T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    if mode == "holes":
+        idx[::4, -1] = -1
+    cap = oracle.capacity(T, K, E, 1, 2) if mode == "drop" else 0
+    ix = oracle.build_index(idx, w, E, capacity=cap, alignment=128 if mode == "aligned" else 0,
+                            group_size=8 if mode == "group" else 0)
+    x = fp8_inputs(key, T, H, dtype)
+    qs, ss = oracle.quantize_fp8(x, block)
+    if mode == "group":  # the send stage: one copy per (token, group)
+        n = int(ix["n_slots"][0])
+        q, sc = m.permute_scatter_fp8(dev(x), dev(ix["slot_of"]), n, block)
+        assert_exact(host(q), oracle.permute(qs, ix["gsrc"]), "slot codes")
+        assert_exact(host(sc), oracle.permute(ss, ix["gsrc"]), "slot scales")
+        # the receive stage moves FP8 rows and scale rows like any rows
+        rq = m.permute_grouped(q, dev(ix["esrc"]), dev(ix["row_of"]))
+        live = ix["esrc"] != -2
+        assert_exact(host(rq)[live], oracle.permute(qs, ix["sorted_indices"])[live], "received codes")
+        return
+    si = ix["sorted_indices"]
+    N = len(si)
+    nb = H // block
+    out = (dev(np.full((N, H), 0xA5, np.uint8)), dev(np.full((N, nb), np.float32(-7.0))))
+    q, sc = m.permute_scatter_fp8(dev(x), dev(ix["row_of"]), N, block, src_row=dev(si), out=out)
+    live = si != -2
+    assert_exact(host(q)[live], oracle.permute(qs, si)[live], "codes")
+    assert_exact(host(sc)[live], oracle.permute(ss, si)[live], "scales")
+    assert (host(q)[~live] == 0xA5).all() and (host(sc)[~live] == -7.0).all(), "slack rows must be untouched"
+    # the same bytes as quantizing, then moving codes and scales with the plain permutes
+    q2 = m.permute(dev(qs), dev(si))
+    assert_exact(host(q2)[live], host(q)[live], "byte permute of the codes")
+
+
+@pytest.mark.parametrize("ydt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
+@pytest.mark.parametrize("H,K,T", [(7168, 8, 60), (1000, 2, 50), (5, 3, 20), (512, 8, 40), (64, 1, 30), (24, 40, 16)])
+def test_unpermute_combine_bias(m, ydt, odt, H, K, T):
+    """The combine's final bias: one float32 addition after the slot-order sum, in every path
+    (many and few terms per token, float32 split rows, element-wise rows)."""
+    say(f"combine bias y={ydt} out={odt} H={H} K={K} T={T}")
+    key = wl.case_key(72, H, K, T)
+    y_rows = T * K + 3
+    y = wl.expert_outputs(key, y_rows, H, ydt)
+    g = np.random.default_rng([*key, 1])
+    row_of = g.permutation(y_rows)[: T * K].astype(np.int32).reshape(T, K)
+    row_of[g.random((T, K)) < 0.3] = -1
+    row_of[0] = -1  # no term: the output is the bias
+    w = wl.random_weights(key, T, K)
+    bias = wl.expert_outputs((*key, 2), T, H, odt)
+    out_np = np.uint16 if odt == "bf16" else np.float32
+    want = oracle.unpermute_combine(y, row_of, w, out_np, bias=bias)
+    got = host(m.unpermute_combine(dev(y), dev(row_of), dev(w), bias=dev(bias),
+                                   out_dtype=torch.bfloat16 if odt == "bf16" else torch.float32))
+    assert_exact(got, want, "combined with bias")
+
+
 # ------------------------------------------------------------------ combine
 
 
@@ -439,7 +530,34 @@ def sample_rows(n, count, seed):
     return s.astype(np.int64)
 
 
-def run_workload(m, cfg_id, align=0, route_groups=0):
+def check_fp8_dispatch(m, x, ix, want, gs, T, K, E, block=128):
+    """FP8 dispatch at full size, as bench.py --fp8 launches it: sampled destination rows against
+    the oracle's quantization of their source tokens (codes and scales bit for bit)."""
+    xd = dev(x)
+    H = x.shape[1]
+    si = want["sorted_indices"]
+    if gs > 0:
+        G = E // gs
+        gq, gsc = m.permute_scatter_fp8(xd, ix.slot_of, T * min(K, G), block)
+        q = m.permute_grouped(gq, ix.esrc, ix.row_of)
+        sc = m.permute_grouped(gsc, ix.esrc, ix.row_of)
+    else:
+        q, sc = m.permute_scatter_fp8(xd, ix.row_of, len(si), block, src_row=ix.sorted_indices)
+    torch.cuda.synchronize()
+    rs = sample_rows(len(si), 2000, 5)
+    rs = rs[si[rs] != -2]
+    toks = si[rs]
+    real = toks >= 0
+    qs, ss = oracle.quantize_fp8(x[toks[real]], block)
+    rsd = torch.from_numpy(rs).to(DEV)
+    gq_rows, gs_rows = host(q[rsd]), host(sc[rsd])
+    assert_exact(gq_rows[real], qs, "FP8 codes (sample)")
+    assert_exact(gs_rows[real], ss, "FP8 scales (sample)")
+    assert (gq_rows[~real] == 0).all() and (gs_rows[~real] == 0).all()
+    del xd
+
+
+def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False):
     """Runs route -> index -> permute -> (pre-)combine on the GPU and checks every stage
     (align > 1: the expert-aligned layout; route_groups > 0: group-limited routing over the
     workload's expert groups, that many groups per token)."""
@@ -468,6 +586,9 @@ def run_workload(m, cfg_id, align=0, route_groups=0):
     for name in ("counts", "group_list", "sorted_indices", "row_of", "permuted_probs"):
         assert_exact(host(getattr(ix, name)), want[name], name)
     rows = ix.rows
+    if fp8:
+        check_fp8_dispatch(m, x, ix, want, gs, T, K, E)
+        return None
     xd = dev(x)
     if gs > 0:
         n = int(host(ix.n_slots)[0])
@@ -532,6 +653,12 @@ def run_workload(m, cfg_id, align=0, route_groups=0):
 @pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
 def test_workload_full_size(m, cfg_id):
     run_workload(m, cfg_id)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg_id", [3, 4, 5])
+def test_workload_fp8_dispatch(m, cfg_id):
+    run_workload(m, cfg_id, fp8=True)
     torch.cuda.empty_cache()
 
 

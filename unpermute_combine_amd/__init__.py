@@ -6,10 +6,12 @@ per-group local pre-combine, as hand-written HIP kernels behind a C ABI
 (``include/moe_dispatch.h``, ``libmoe_dispatch.so``). This package is the torch binding.
 """
 from .ops import (MoeIndex, alloc_index, build_index, expert_capacity, group_precombine, index_rows, permute,
-                  permute_grouped, permute_scatter, route_topk, route_topk_backward, unpermute_combine,
+                  permute_grouped, permute_scatter, permute_scatter_fp8, quantize_fp8, route_topk,
+                  route_topk_backward, unpermute_combine,
                   unpermute_combine_backward, workspace_bytes)
 from ._capi import MoeError, lib
 
 __all__ = ["MoeIndex", "MoeError", "alloc_index", "build_index", "expert_capacity", "group_precombine", "index_rows",
-           "lib", "permute", "permute_grouped", "permute_scatter", "route_topk", "route_topk_backward",
+           "lib", "permute", "permute_grouped", "permute_scatter", "permute_scatter_fp8", "quantize_fp8",
+           "route_topk", "route_topk_backward",
            "unpermute_combine", "unpermute_combine_backward", "workspace_bytes"]

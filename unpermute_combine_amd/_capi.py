@@ -7,7 +7,7 @@ import os
 from .build import library_path
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 
 _P = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -32,11 +32,13 @@ SIGNATURES = {
     "moe_index_rows": (ctypes.c_int64, [_i64, _i32, _i32, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _P]),
     "moe_permute_scatter": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i32, _P, _i64, _P, _P]),
+    "moe_quantize_fp8": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _i32, _P, _P, _P]),
+    "moe_permute_scatter_fp8": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _i32, _P, _i32, _P, _i64, _P, _P, _P]),
     "moe_permute_grouped": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _i64, _i32, _P, _P]),
     "moe_unpermute_combine_backward": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, _i64, _i64, _P, _P, _i64,
                                                       _i32, _P, _P, ctypes.c_int, _P, _P]),
     "moe_route_topk_backward": (ctypes.c_int, [_P, _P, _P, _i64, _i32, _i32, _P, _P]),
-    "moe_unpermute_combine": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _P, _P, _i64, _i32, _P,
+    "moe_unpermute_combine": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _P, _P, _P, _i64, _i32, _P,
                                              ctypes.c_int, _P]),
     "moe_group_precombine": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _P, _P, _P, _i64, _i32, _i32,
                                             _i32, _P, _i64, _P, _P]),

@@ -265,11 +265,22 @@ __device__ __forceinline__ void store_parts(__amdgpu_buffer_rsrc_t o, int64_t e0
 template <typename Y, typename O>
 constexpr bool kSplit = sizeof(Y) == 4 || sizeof(O) == 4;
 
+// acc += the 8 bias values of a bf16 chunk (the combine's final bias, one float32 addition each)
+__device__ __forceinline__ void add_bias8(const uint16_t *b, float (&acc)[8])
+{
+    const u32x4 q[1] = {ld16(b)};
+    float v[8];
+    Chunk<uint16_t>::widen(q, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = acc[e] + v[e];
+}
+
 template <typename Y, typename O, bool VEC>
 __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
                                                       const int32_t *__restrict__ row_of,
                                                       const float *__restrict__ w, int K,
-                                                      O *__restrict__ out)
+                                                      O *__restrict__ out, const O *__restrict__ bias)
 {
     __shared__ int32_t rows[kMaxCombineK];
     __shared__ float ws[kMaxCombineK];
@@ -294,6 +305,16 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
                 batch_terms(rows, ws, n, j0, row, w);
                 fma_batch_split<Y>(y, H, row, w, e0, acc);
             }
+            if (bias) {
+                Part<O> b[2];
+                load_parts<O>(bias + t * H, H, 0, e0, b);
+                float v[8];
+                b[0].widen(v);
+                b[1].widen(v + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[e] = acc[e] + v[e];
+            }
             store_parts(orr, e0, acc, o);
         }
     } else if constexpr (VEC) {
@@ -312,6 +333,8 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
                     batch_terms(rows, ws, n, j0, row, w);
                     fma_batch<Y>(y, H, row, w, c, acc);
                 }
+                if (bias)
+                    add_bias8(bias + t * H + c * 8, acc);
                 store8(o + c * 8, acc);
             }
         } else {
@@ -327,6 +350,11 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
                 for (int u = 0; u < kBatch; ++u)
                     row1[u] = c2 < nchunk ? row0[u] : -1;
                 fma_few2<Y>(y, H, row0, row1, w0, c, c2, acc, acc2);
+                if (bias) {
+                    add_bias8(bias + t * H + c * 8, acc);
+                    if (c2 < nchunk)
+                        add_bias8(bias + t * H + c2 * 8, acc2);
+                }
                 store8(o + c * 8, acc);
                 if (c2 < nchunk)
                     store8(o + c2 * 8, acc2);
@@ -337,6 +365,8 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
             float acc = 0.0f;
             for (int j = 0; j < n; ++j)
                 acc = __builtin_fmaf(ws[j], load1(y + static_cast<int64_t>(rows[j]) * H + h), acc);
+            if (bias)
+                acc = acc + load1(bias + t * H + h);
             store1(o + h, acc);
         }
     }
@@ -694,18 +724,18 @@ int split_threads(int64_t H)
 
 template <typename Y, typename O>
 moe_status launch_combine(const void *y, int64_t y_rows, int64_t H, const int32_t *row_of, const float *w,
-                          int64_t T, int K, void *out, hipStream_t stream)
+                          const void *bias, int64_t T, int K, void *out, hipStream_t stream)
 {
-    const bool vec = H % 8 == 0 && aligned16(out) && (y_rows == 0 || aligned16(y));
+    const bool vec = H % 8 == 0 && aligned16(out) && (y_rows == 0 || aligned16(y)) && (!bias || aligned16(bias));
     const int64_t nchunk = vec ? H / 8 : H;
     const dim3 grid(static_cast<unsigned>(T)),
         block(vec && kSplit<Y, O> ? split_threads(H) : block_threads(nchunk, 1));
     if (vec)
         hipLaunchKernelGGL((combine_kernel<Y, O, true>), grid, block, 0, stream, static_cast<const Y *>(y),
-                           y_rows, H, row_of, w, K, static_cast<O *>(out));
+                           y_rows, H, row_of, w, K, static_cast<O *>(out), static_cast<const O *>(bias));
     else
         hipLaunchKernelGGL((combine_kernel<Y, O, false>), grid, block, 0, stream, static_cast<const Y *>(y),
-                           y_rows, H, row_of, w, K, static_cast<O *>(out));
+                           y_rows, H, row_of, w, K, static_cast<O *>(out), static_cast<const O *>(bias));
     return launch_status();
 }
 
@@ -771,10 +801,12 @@ moe_status launch_combine_backward_dy(moe_dtype dy_dt, const void *dout, const v
 }  // namespace moe
 
 extern "C" moe_status moe_unpermute_combine(const void *y, moe_dtype y_dt, int64_t y_rows, int64_t H,
-                                            const int32_t *row_of, const float *w, int64_t T, int32_t K,
-                                            void *out, moe_dtype out_dt, hipStream_t stream)
+                                            const int32_t *row_of, const float *w, const void *bias, int64_t T,
+                                            int32_t K, void *out, moe_dtype out_dt, hipStream_t stream)
 {
     using namespace moe;
+    if (y_dt == MOE_FP8_E4M3 || out_dt == MOE_FP8_E4M3)
+        return MOE_ERR_UNSUPPORTED;  // the combine stays in bf16 / float32
     if (y_rows < 0 || H < 1 || T < 0 || K < 1 || (y_dt != MOE_F32 && y_dt != MOE_BF16) ||
         (out_dt != MOE_F32 && out_dt != MOE_BF16))
         return MOE_ERR_INVALID;
@@ -787,10 +819,10 @@ extern "C" moe_status moe_unpermute_combine(const void *y, moe_dtype y_dt, int64
     if (T > 0x7fffffff || H * ((y_dt == MOE_F32 || out_dt == MOE_F32) ? 4 : 2) > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
     if (y_dt == MOE_BF16)
-        return out_dt == MOE_BF16 ? launch_combine<uint16_t, uint16_t>(y, y_rows, H, row_of, w, T, K, out, stream)
-                                  : launch_combine<uint16_t, float>(y, y_rows, H, row_of, w, T, K, out, stream);
-    return out_dt == MOE_BF16 ? launch_combine<float, uint16_t>(y, y_rows, H, row_of, w, T, K, out, stream)
-                              : launch_combine<float, float>(y, y_rows, H, row_of, w, T, K, out, stream);
+        return out_dt == MOE_BF16 ? launch_combine<uint16_t, uint16_t>(y, y_rows, H, row_of, w, bias, T, K, out, stream)
+                                  : launch_combine<uint16_t, float>(y, y_rows, H, row_of, w, bias, T, K, out, stream);
+    return out_dt == MOE_BF16 ? launch_combine<float, uint16_t>(y, y_rows, H, row_of, w, bias, T, K, out, stream)
+                              : launch_combine<float, float>(y, y_rows, H, row_of, w, bias, T, K, out, stream);
 }
 
 extern "C" moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, int64_t H,
@@ -800,6 +832,8 @@ extern "C" moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_
                                            hipStream_t stream)
 {
     using namespace moe;
+    if (y_dt == MOE_FP8_E4M3)
+        return MOE_ERR_UNSUPPORTED;
     if (y_rows < 0 || H < 1 || T < 0 || K < 1 || E < 1 || group_size < 1 || E % group_size != 0 ||
         slots_cap < 0 || (y_dt != MOE_F32 && y_dt != MOE_BF16))
         return MOE_ERR_INVALID;
@@ -825,6 +859,8 @@ extern "C" moe_status moe_unpermute_combine_backward(const void *dout, moe_dtype
 {
     using namespace moe;
     auto dt_ok = [](moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; };
+    if (dout_dt == MOE_FP8_E4M3 || y_dt == MOE_FP8_E4M3 || dy_dt == MOE_FP8_E4M3)
+        return MOE_ERR_UNSUPPORTED;
     if (y_rows < 0 || H < 1 || T < 0 || K < 1 || !dt_ok(dout_dt) || !dt_ok(y_dt) || !dt_ok(dy_dt))
         return MOE_ERR_INVALID;
     if (K > kMaxCombineK)

@@ -313,7 +313,7 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
                                           void *dst, hipStream_t stream)
 {
     using namespace moe;
-    if (src_rows < 0 || H < 1 || N < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16))
+    if (src_rows < 0 || H < 1 || N < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3))
         return MOE_ERR_INVALID;
     if (J > kMaxScatterDests)
         return MOE_ERR_UNSUPPORTED;
@@ -321,7 +321,7 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
         return MOE_OK;
     if (!dst || (src_rows > 0 && (!src || !dst_of)))
         return MOE_ERR_INVALID;
-    const int64_t esz = dt == MOE_F32 ? 4 : 2;
+    const int64_t esz = dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1);
     const int64_t row_bytes = H * esz;
     if (row_bytes > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
@@ -347,10 +347,14 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
         hipLaunchKernelGGL(permute_scatter_elem_kernel<uint32_t>, grid, block, 0, stream,
                            static_cast<const uint32_t *>(src), src_rows, H, dst_of, J, src_row, N,
                            static_cast<uint32_t *>(dst));
-    } else {
+    } else if (esz == 2) {
         hipLaunchKernelGGL(permute_scatter_elem_kernel<uint16_t>, grid, block, 0, stream,
                            static_cast<const uint16_t *>(src), src_rows, H, dst_of, J, src_row, N,
                            static_cast<uint16_t *>(dst));
+    } else {
+        hipLaunchKernelGGL(permute_scatter_elem_kernel<uint8_t>, grid, block, 0, stream,
+                           static_cast<const uint8_t *>(src), src_rows, H, dst_of, J, src_row, N,
+                           static_cast<uint8_t *>(dst));
     }
     return launch_status();
 }
@@ -359,14 +363,14 @@ extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, 
                                   const int32_t *src_row, int64_t N, void *dst, hipStream_t stream)
 {
     using namespace moe;
-    if (src_rows < 0 || H < 1 || N < 0 || (dt != MOE_F32 && dt != MOE_BF16))
+    if (src_rows < 0 || H < 1 || N < 0 || (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3))
         return MOE_ERR_INVALID;
     if (N == 0)
         return MOE_OK;
     if (!src_row || !dst || (src_rows > 0 && !src))
         return MOE_ERR_INVALID;
     const int64_t blocks = ceil_div(N, kRowsPerBlock);
-    const int64_t esz = dt == MOE_F32 ? 4 : 2;
+    const int64_t esz = dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1);
     const int64_t row_bytes = H * esz;
     if (blocks > 0x7fffffff || row_bytes > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
@@ -378,10 +382,14 @@ extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, 
         hipLaunchKernelGGL(permute_elem_kernel<uint32_t>, grid, block, 0, stream,
                            static_cast<const uint32_t *>(src), src_rows, H, src_row, N,
                            static_cast<uint32_t *>(dst));
-    } else {
+    } else if (esz == 2) {
         hipLaunchKernelGGL(permute_elem_kernel<uint16_t>, grid, block, 0, stream,
                            static_cast<const uint16_t *>(src), src_rows, H, src_row, N,
                            static_cast<uint16_t *>(dst));
+    } else {
+        hipLaunchKernelGGL(permute_elem_kernel<uint8_t>, grid, block, 0, stream,
+                           static_cast<const uint8_t *>(src), src_rows, H, src_row, N,
+                           static_cast<uint8_t *>(dst));
     }
     return launch_status();
 }
@@ -391,7 +399,7 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
                                           int32_t J, void *dst, hipStream_t stream)
 {
     using namespace moe;
-    if (src_rows < 0 || H < 1 || N < 0 || M < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16))
+    if (src_rows < 0 || H < 1 || N < 0 || M < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3))
         return MOE_ERR_INVALID;
     if (J > kMaxScatterDests)
         return MOE_ERR_UNSUPPORTED;
@@ -399,7 +407,7 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
         return MOE_OK;
     if (!src_row || !dst || (M > 0 && !dst_of) || (src_rows > 0 && !src))
         return MOE_ERR_INVALID;
-    const int64_t esz = dt == MOE_F32 ? 4 : 2;
+    const int64_t esz = dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1);
     const int64_t row_bytes = H * esz;
     if (row_bytes > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
@@ -422,10 +430,14 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
         hipLaunchKernelGGL(permute_grouped_elem_kernel<uint32_t>, grid, block, 0, stream,
                            static_cast<const uint32_t *>(src), src_rows, H, src_row, dst_of, M, J, N,
                            static_cast<uint32_t *>(dst));
-    } else {
+    } else if (esz == 2) {
         hipLaunchKernelGGL(permute_grouped_elem_kernel<uint16_t>, grid, block, 0, stream,
                            static_cast<const uint16_t *>(src), src_rows, H, src_row, dst_of, M, J, N,
                            static_cast<uint16_t *>(dst));
+    } else {
+        hipLaunchKernelGGL(permute_grouped_elem_kernel<uint8_t>, grid, block, 0, stream,
+                           static_cast<const uint8_t *>(src), src_rows, H, src_row, dst_of, M, J, N,
+                           static_cast<uint8_t *>(dst));
     }
     return launch_status();
 }

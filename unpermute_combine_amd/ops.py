@@ -14,9 +14,12 @@ from typing import Optional
 import torch
 
 from . import _capi
-from ._capi import MOE_BF16, MOE_F32, check, lib
+from ._capi import MOE_BF16, MOE_F32, MOE_FP8_E4M3, check, lib
 
-_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+# hidden-row element types; uint8 / float8_e4m3fn rows are FP8 (E4M3) codes, which only the
+# permutes accept (they copy bytes)
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_FP8_E4M3,
+       torch.float8_e4m3fn: MOE_FP8_E4M3}
 
 
 def _stream():
@@ -43,7 +46,7 @@ def _need(t: torch.Tensor, name: str, dtype=None, dims=None):
 
 def _hidden_dt(t: torch.Tensor, name: str) -> int:
     if t.dtype not in _DT:
-        raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+        raise TypeError(f"{name} must be float32, bfloat16 or FP8 codes (uint8), got {t.dtype}")
     return _DT[t.dtype]
 
 
@@ -244,9 +247,57 @@ def permute_grouped(src: torch.Tensor, src_row: torch.Tensor, dst_of: torch.Tens
     return out
 
 
+def quantize_fp8(x: torch.Tensor, block: int = 128, out=None):
+    """Per-(token, block) FP8 E4M3 quantization: q [T, H] uint8 codes, scales [T, H/block] float32
+    with x ~ value(q) * scale (scale = amax/448 per block)."""
+    _need(x, "x", None, 2)
+    dt = _hidden_dt(x, "x")
+    T, H = x.shape
+    if block < 1 or H % block:
+        raise ValueError("block must divide H")
+    q, sc = (None, None) if out is None else out
+    q = torch.empty((T, H), dtype=torch.uint8, device=x.device) if q is None else q
+    sc = torch.empty((T, H // block), dtype=torch.float32, device=x.device) if sc is None else sc
+    _need(q, "q", torch.uint8, 2)
+    _need(sc, "scales", torch.float32, 2)
+    check("moe_quantize_fp8", lib().moe_quantize_fp8(_p(x), dt, T, H, block, _p(q), _p(sc), _stream()))
+    return q, sc
+
+
+def permute_scatter_fp8(src: torch.Tensor, dst_of: torch.Tensor, num_rows: int, block: int = 128,
+                        src_row: Optional[torch.Tensor] = None, out=None):
+    """FP8 dispatch: the source rows quantized once (per-block E4M3 + float32 scales) and scattered
+    source-major like permute_scatter. Returns (q [num_rows, H] uint8, scales [num_rows, H/block])."""
+    _need(src, "src", None, 2)
+    dt = _hidden_dt(src, "src")
+    _need(dst_of, "dst_of", torch.int32, 2)
+    if dst_of.shape[0] != src.shape[0]:
+        raise ValueError("dst_of must have one row per source row")
+    H = src.shape[1]
+    if block < 1 or H % block:
+        raise ValueError("block must divide H")
+    if src_row is not None:
+        _need(src_row, "src_row", torch.int32, 1)
+        if src_row.shape[0] != num_rows:
+            raise ValueError("src_row must have num_rows entries")
+    q, sc = (None, None) if out is None else out
+    q = torch.empty((num_rows, H), dtype=torch.uint8, device=src.device) if q is None else q
+    sc = torch.empty((num_rows, H // block), dtype=torch.float32, device=src.device) if sc is None else sc
+    _need(q, "q", torch.uint8, 2)
+    _need(sc, "scales", torch.float32, 2)
+    if tuple(q.shape) != (num_rows, H) or tuple(sc.shape) != (num_rows, H // block):
+        raise ValueError("output shapes must be [num_rows, H] and [num_rows, H/block]")
+    check("moe_permute_scatter_fp8", lib().moe_permute_scatter_fp8(
+        _p(src), dt, src.shape[0], H, block, _p(dst_of), dst_of.shape[1], _p(src_row), num_rows, _p(q), _p(sc),
+        _stream()))
+    return q, sc
+
+
 def unpermute_combine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[torch.Tensor] = None,
-                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out[t] = sum_k weights[t,k] * y[row_of[t,k]] (float32 FMA chain in k order)."""
+                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                      bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = sum_k weights[t,k] * y[row_of[t,k]] (float32 FMA chain in k order) [+ bias[t],
+    one float32 addition; bias has the output's shape and dtype]."""
     _need(y, "y", None, 2)
     y_dt = _hidden_dt(y, "y")
     _need(row_of, "row_of", torch.int32, 2)
@@ -262,8 +313,12 @@ def unpermute_combine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[t
     out_dt = _hidden_dt(out, "out")
     if tuple(out.shape) != (T, H):
         raise ValueError(f"out must be [{T}, {H}]")
+    if bias is not None:
+        _need(bias, "bias", out.dtype, 2)
+        if tuple(bias.shape) != (T, H):
+            raise ValueError(f"bias must be [{T}, {H}]")
     check("moe_unpermute_combine", lib().moe_unpermute_combine(
-        _p(y), y_dt, y.shape[0], H, _p(row_of), _p(weights), T, K, _p(out), out_dt, _stream()))
+        _p(y), y_dt, y.shape[0], H, _p(row_of), _p(weights), _p(bias), T, K, _p(out), out_dt, _stream()))
     return out
 
 
