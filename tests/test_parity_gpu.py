@@ -141,6 +141,27 @@ def test_build_index_skewed_with_empty_experts(m):
     assert (want["counts"] == 0).any()
 
 
+def test_route_and_index_at_a_million_tokens(m):
+    """Large sizes: T = 1 048 576 tokens, E = 256, K = 8 (8.4M slots, 8192 tokens per tile):
+    routing and the full index (standard, and aligned to 128) against the oracle."""
+    T, E, K = 1 << 20, 256, 8
+    say(f"route + index T={T} E={E} K={K}")
+    logits = wl.router_logits(wl.case_key(80), T, E, zipf_s=1.2)
+    want_i, want_w = oracle.route_topk(logits, K)
+    gi, gw = m.route_topk(dev(logits), K)
+    assert_exact(host(gi), want_i, "topk_idx")
+    assert_rel_f32(host(gw), want_w, "topk_w")
+    w_np = host(gw)
+    for align in (0, 128):
+        want = oracle.build_index(want_i, w_np, E, alignment=align)
+        ix = m.build_index(gi, gw, E, alignment=align)
+        torch.cuda.synchronize()
+        for name in ("counts", "group_list", "sorted_indices", "row_of", "permuted_probs"):
+            assert_exact(host(getattr(ix, name)), want[name], f"{name} (align {align})")
+        del ix
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T,E,K,cap", [(300, 8, 2, 3), (4099, 64, 8, 40), (2000, 128, 8, 200),
                                        (1000, 16, 4, 1000), (50, 1024, 8, 1), (1, 4, 2, 5), (40000, 96, 8, 2000)])
 def test_build_index_drop_and_pad(m, T, E, K, cap):
@@ -455,7 +476,7 @@ def test_unpermute_combine_bias(m, ydt, odt, H, K, T):
 
 @pytest.mark.parametrize("ydt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
 @pytest.mark.parametrize("H,K,T", [(1, 1, 10), (5, 2, 33), (512, 2, 1024), (7168, 8, 130), (1000, 8, 77),
-                                   (64, 32, 200), (24, 256, 40)])
+                                   (64, 32, 200), (24, 256, 40), (16, 1024, 6)])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_unpermute_combine(m, ydt, odt, H, K, T, weighted):
     say(f"combine y={ydt} out={odt} H={H} K={K} T={T} weighted={weighted}")
