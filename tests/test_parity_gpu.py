@@ -496,6 +496,34 @@ def test_unpermute_combine(m, ydt, odt, H, K, T, weighted):
     assert exact_fraction(got, want) == 1.0
 
 
+@pytest.mark.parametrize("H,K", [(64, 8), (1000, 5), (7168, 8)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_unpermute_combine_batched_path(m, H, K, with_bias):
+    """Many tokens with 5..8 slots in bf16: the combine that stages 8 tokens' rows in LDS and
+    writes them in one burst; T = 16 389 leaves a ragged last batch. Every token against the oracle."""
+    T = 16389 if H < 7168 else 16392
+    say(f"combine batched H={H} K={K} T={T} bias={with_bias}")
+    key = wl.case_key(73, H, K)
+    y_rows = T * K + 7
+    y = wl.expert_outputs(key, y_rows, H, "bf16")
+    g = np.random.default_rng([*key, 1])
+    row_of = g.permutation(y_rows)[: T * K].astype(np.int32).reshape(T, K)
+    row_of[g.random((T, K)) < 0.1] = -1
+    row_of[5] = -1
+    w = wl.random_weights(key, T, K)
+    bias = wl.expert_outputs((*key, 2), T, H, "bf16") if with_bias else None
+    if H == 7168:  # full-width rows: compare a sample of tokens
+        ts = sample_rows(T, 800, 73)
+        want = oracle.unpermute_combine(y, row_of[ts], w[ts], np.uint16,
+                                        bias=None if bias is None else bias[ts])
+        got = host(m.unpermute_combine(dev(y), dev(row_of), dev(w), bias=None if bias is None else dev(bias))
+                   [torch.from_numpy(ts).to(DEV)])
+    else:
+        want = oracle.unpermute_combine(y, row_of, w, np.uint16, bias=bias)
+        got = host(m.unpermute_combine(dev(y), dev(row_of), dev(w), bias=None if bias is None else dev(bias)))
+    assert_exact(got, want, "combined")
+
+
 def test_combine_no_tokens(m):
     out = m.unpermute_combine(torch.zeros((4, 8), dtype=torch.bfloat16, device=DEV),
                               torch.zeros((0, 2), dtype=torch.int32, device=DEV))
