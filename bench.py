@@ -49,6 +49,15 @@ KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine
                   "dispatch_bwd_recv": "precombine_kernel", "dispatch_bwd_send": "combine_kernel",
                   "permute_fp8": "permute_scatter_fp8_kernel", "dispatch_send_fp8": "permute_scatter_fp8_kernel",
                   "dispatch_recv_scales": "permute_grouped_vec16_kernel"}
+def combine_symbol(y_bf16: bool, out_bf16: bool, K: int, H: int, T: int) -> str:
+    """Kernel the library launches for a combine call: bf16 rows with 5..8 slots per token, at
+    most 128 KB of staged rows (8 * H * 2 bytes) and at least 2048 workgroups of 8 tokens take
+    the batched combine, everything else the per-token one."""
+    if y_bf16 and out_bf16 and H % 8 == 0 and 4 < K <= 8 and 16 * H <= 128 * 1024 and -(-T // 8) >= 2048:
+        return "combine_batched_kernel"
+    return "combine_kernel"
+
+
 METRIC_BACKWARD = "backward of permute+combine (and router softmax) effective HBM GB/s (% of peak)"
 
 
@@ -85,10 +94,10 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: int, backward: bool = False):
+def read_traffic(kernel: str, workload: int, backward: bool = False, symbol: str = None, fp8: bool = False):
     """HBM bytes per launch from a committed PMC summary; None if absent or stale."""
-    tag = f"workload{workload}_bwd" if backward else f"workload{workload}"
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_SYMBOLS[kernel]}__{tag}__pmc.txt")
+    tag = f"workload{workload}" + ("_bwd" if backward else "") + ("_fp8" if fp8 else "")
+    path = os.path.join(ROOT, "profiles", f"{symbol or KERNEL_SYMBOLS[kernel]}__{tag}__pmc.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -322,9 +331,13 @@ def main():
     hbm_kernels = [name for name, stage, _ in calls if stage in hbm_stages]
     dom = max(hbm_kernels, key=lambda k: kernel_us[k])
     achieved = kbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
+    symbol = KERNEL_SYMBOLS[dom]
+    if dom == "combine":
+        symbol = combine_symbol(dt == "bf16", dt == "bf16", K, H, T)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dom, cid, args.backward),
-                "kernel": KERNEL_SYMBOLS[dom], "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(dom, cid, args.backward, symbol, args.fp8),
+                "kernel": symbol, "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kernel_us[dom], 2)}
 
     result = {
