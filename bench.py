@@ -79,6 +79,10 @@ def parse_args():
     p.add_argument("--fp8", action="store_true",
                    help="FP8 dispatch: the permute quantizes x to E4M3 codes with one float32 scale per 128 "
                         "elements and moves codes and scales (the combine stays bf16)")
+    p.add_argument("--eager", action="store_true",
+                   help="time the eagerly launched steps only; by default the step is also captured once in a "
+                        "HIP graph and value / ms_per_step come from K replays of it (per-kernel times always "
+                        "come from the eager pass)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
@@ -274,6 +278,24 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step_eager = ms_per_step
+    if not args.eager:
+        # the same calls captured once; no call allocates, waits on the host or records a memset
+        graph = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            with torch.cuda.graph(graph, stream=cap_stream):
+                step()
+        torch.cuda.current_stream().wait_stream(cap_stream)
+        for _ in range(max(3, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
     kernel_us = {}
     for i, (name, _, _) in enumerate(calls):
         kernel_us[name] = float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.steps)]))
@@ -360,6 +382,8 @@ def main():
     }
     if args.backward:
         result["pass"] = "backward"
+    result["launch"] = ("eager" if args.eager else "hip graph replay")
+    result["ms_per_step_eager"] = round(ms_per_step_eager, 4)
     if not args.no_cpu_baseline and args.fp8:
         result["cpu_baseline"] = None  # the oracle baseline is timed on the bf16 path
     elif not args.no_cpu_baseline:

@@ -726,6 +726,116 @@ def test_workload_aligned(m, cfg_id, align):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("cfg_id,mode", [(2, "standard"), (5, "drop"), (4, "group"), (2, "aligned"),
+                                         (4, "route_groups"), (2, "fp8"), (4, "fp8"), (2, "backward"),
+                                         (4, "backward")])
+def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
+    """A whole step (route, index, permute, combine; or its backward) captured once in a HIP
+    graph and replayed three times, with eager work (the outputs cleared by a fill kernel) and
+    synchronizations between the replays: every replay matches the eager step bit for bit.
+    Nothing in the step allocates, waits on the host or records a memset."""
+    c = wl.WORKLOADS[cfg_id]
+    T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
+    say(f"graph replay workload {cfg_id} ({mode})")
+    key = wl.workload_key(cfg_id)
+    cap = oracle.capacity(T, K, E, *c["cf"]) if c["cf"] else 0
+    gs = c["group_size"]
+    align = 128 if mode == "aligned" else 0
+    rg = 4 if mode == "route_groups" else 0
+    logits = dev(wl.router_logits(key, T, E, zipf_s=c["zipf_s"]))
+    x = dev(wl.hidden_states(key, T, H, dt))
+    rows = m.index_rows(T, K, E, cap, align)
+    y = dev(wl.expert_outputs(key, rows, H, dt))
+    tdt = x.dtype
+    gi = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    gw = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    ix = m.alloc_index(T, K, E, cap, gs, alignment=align)
+    G = E // gs if gs else 0
+    slots = T * min(K, G) if gs else 0
+    outs = {"out": torch.empty((T, H), dtype=tdt, device=DEV)}
+    block = 128
+    if mode == "fp8":
+        outs["xp"] = torch.empty((rows, H), dtype=torch.uint8, device=DEV)
+        outs["xs"] = torch.empty((rows, H // block), dtype=torch.float32, device=DEV)
+        gq = torch.empty((slots, H), dtype=torch.uint8, device=DEV) if gs else None
+        gsc = torch.empty((slots, H // block), dtype=torch.float32, device=DEV) if gs else None
+    else:
+        outs["xp"] = torch.empty((rows, H), dtype=tdt, device=DEV)
+    gbuf = torch.empty((slots, H), dtype=tdt, device=DEV) if gs else None
+    part = torch.empty((slots, H), dtype=torch.float32, device=DEV) if gs else None
+    if mode == "backward":
+        dout = dev(wl.expert_outputs((*key, 7), T, H, dt))
+        dxp = dev(wl.expert_outputs((*key, 8), rows, H, dt))
+        outs["dy"] = torch.empty((rows, H), dtype=tdt, device=DEV)
+        outs["dw"] = torch.empty((T, K), dtype=torch.float32, device=DEV)
+        outs["dx"] = torch.empty((T, H), dtype=tdt, device=DEV)
+        outs["dlog"] = torch.empty((T, E), dtype=torch.float32, device=DEV)
+
+    def step():
+        m.route_topk(logits, K, out=(gi, gw), group_size=gs if rg else 0, topk_groups=rg)
+        m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix, alignment=align)
+        if mode == "fp8" and gs:
+            m.permute_scatter_fp8(x, ix.slot_of, slots, block, out=(gq, gsc))
+            m.permute_grouped(gq, ix.esrc, ix.row_of, out=outs["xp"])
+            m.permute_grouped(gsc, ix.esrc, ix.row_of, out=outs["xs"])
+        elif mode == "fp8":
+            m.permute_scatter_fp8(x, ix.row_of, rows, block, src_row=ix.sorted_indices,
+                                  out=(outs["xp"], outs["xs"]))
+        elif gs:
+            m.permute_scatter(x, ix.slot_of, slots, out=gbuf)
+            m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=outs["xp"])
+        else:
+            m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=outs["xp"])
+        if gs:
+            m.group_precombine(y, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)
+            m.unpermute_combine(part, ix.slot_of, None, out=outs["out"])
+        else:
+            m.unpermute_combine(y, ix.row_of, gw, out=outs["out"])
+        if mode == "backward":
+            m.unpermute_combine_backward(dout, y, ix.row_of, gw, src_row=ix.sorted_indices,
+                                         out=(outs["dy"], outs["dw"]))
+            if gs:
+                m.group_precombine(dxp, ix.row_of, None, gi, E, gs, ix.slot_of, out=part)
+                m.unpermute_combine(part, ix.slot_of, None, out=outs["dx"])
+            else:
+                m.unpermute_combine(dxp, ix.row_of, None, out=outs["dx"])
+            m.route_topk_backward(gi, gw, outs["dw"], E, out=outs["dlog"])
+
+    def results():
+        live = host(ix.sorted_indices) >= 0  # rows that hold a token (pads and slack are not compared)
+        r = {k: host(v).copy() for k, v in outs.items()}
+        for k in ("xp", "xs", "dy"):
+            if k in r:
+                r[k] = r[k][live[: len(r[k])]]
+        r.update(row_of=host(ix.row_of).copy(), gi=host(gi).copy(), gw=host(gw).copy(), live=live)
+        return r
+
+    step()
+    torch.cuda.synchronize()
+    want = results()
+    assert want["live"].sum() > 0
+    step()  # warm the allocator and the launch paths outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (*outs.values(), gi, gw, ix.row_of, ix.sorted_indices):
+            t.zero_()  # eager fill kernels between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = results()
+        for k, v in want.items():
+            assert np.array_equal(got[k], v), f"replay {rep}: {k}"
+    del g
+
+
 def test_pipeline_is_deterministic(m):
     """No atomics decide positions or sums: two runs give identical bits."""
     a = host(run_workload(m, 2))
