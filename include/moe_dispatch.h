@@ -143,8 +143,10 @@ typedef struct moe_index {
  * invalid sizes, capacity together with alignment > 1, or R above 2^31 - 1. */
 int64_t moe_index_rows(int64_t T, int32_t K, int32_t E, int32_t capacity, int32_t alignment);
 
-/* Bytes of device workspace that moe_build_index needs for these sizes (the caller allocates
- * it, any alignment of at least 256 bytes). */
+/* Bytes of device workspace that moe_build_index needs for these sizes: the tile counts of the
+ * experts (and of the groups), at most 128 tiles. The caller allocates it, 16-byte aligned
+ * (NULL when the size is 0); its contents need no initialisation and mean nothing after the
+ * call. */
 moe_status moe_build_index_workspace_size(int64_t T, int32_t K, int32_t E, int32_t group_size,
                                           size_t *bytes);
 

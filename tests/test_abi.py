@@ -57,11 +57,14 @@ def test_workspace_size_and_limits(capi):
     lib = capi.lib()
     n = ctypes.c_size_t(0)
     assert lib.moe_build_index_workspace_size(16384, 8, 256, 0, ctypes.byref(n)) == capi.MOE_OK
-    assert n.value >= 256 * 4
+    assert n.value == 128 * 256 * 4  # one row of expert counts per tile, 128 tiles
+    assert lib.moe_build_index_workspace_size(16384, 8, 256, 8, ctypes.byref(n)) == capi.MOE_OK
+    assert n.value == 128 * 256 * 4 + 128 * 32 * 4  # and one row of group counts per tile
     assert lib.moe_build_index_workspace_size(16, 8, 4, 0, ctypes.byref(n)) == capi.MOE_ERR_INVALID  # K > E
     assert lib.moe_build_index_workspace_size(16, 2, 2048, 0, ctypes.byref(n)) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_build_index_workspace_size(16, 2, 12, 5, ctypes.byref(n)) == capi.MOE_ERR_INVALID
     assert lib.moe_build_index_workspace_size(0, 2, 8, 0, ctypes.byref(n)) == capi.MOE_OK
+    assert n.value == 0  # no tokens, no tiles
 
 
 def test_argument_errors_return_before_any_launch(capi):

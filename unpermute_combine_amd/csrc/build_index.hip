@@ -9,23 +9,26 @@
 // gfx950 design. A dependent global-memory round trip costs microseconds here, so every pass
 // issues its loads together, stores whole cache lines, and orders loads before stores (on gfx9
 // the vector-memory counter retires loads and stores in issue order, so a load issued after a
-// store cannot be waited for without waiting for the store too). Three launches, plus one in
+// store cannot be waited for without waiting for the store too). Two launches, plus one in
 // group mode:
 //   1. hist   one workgroup per tile of whole tokens: the tile's expert histogram (and the
 //             group histogram of each token's first slot in a group) with LDS atomics -- only
 //             counts come from atomics, never positions, so the result is deterministic -- and
 //             one coalesced row hist[tile][0..E) per tile.
-//   2. scan   one workgroup: lanes own 4 consecutive keys, wavefronts own ranges of tiles; the
-//             per-wave partial sums meet in LDS, giving each (tile, key) its first row inside
-//             the key; a block scan over the key totals gives each key's first row. Also
-//             counts, group_list and the capacity bookkeeping.
-//   3. rank   one workgroup per tile, its tokens split over 4 wavefronts (per-wave counts and
-//             a prefix over the waves in LDS); each wavefront walks its slots 64 at a time in
-//             slot order. Lanes with the same key find each other with one ballot per key bit
+//   2. rank   one workgroup per tile. It first adds up the tile counts of all tiles itself
+//             (threads own 4 consecutive keys and a range of tiles, 16 loads in flight each;
+//             the partial sums meet in LDS): every key's total, a block scan of the totals for
+//             every key's first row, and the counts of the tiles before its own; tile 0 also
+//             writes counts, group_list and the capacity bookkeeping. (A separate one-workgroup
+//             scan launch between the two took 5.9 us at T16384 K8 E256, the rank kernel
+//             re-reading its results.) Its tokens are split over 8 wavefronts (per-wave counts
+//             and a prefix over the waves in LDS); each wavefront walks its slots 64 at a time
+//             in slot order. Lanes with the same key find each other with one ballot per key bit
 //             (a match-any built from ballots); their stable rank is popcount(peers &
 //             lanes_below) and the last peer advances the key's running row counter in LDS.
 //             The workgroups then write the padding or unused rows together.
-//   4. esrc   (group mode) expert-major row -> group slot.
+//   3. esrc   (group mode) expert-major row -> group slot.
+// With no tokens one single-workgroup launch writes the zero counts and the marks.
 // The drop-and-pad capacity rule ([Scratch] §18, §26.6), the expert alignment ([Combine] §6:
 // segments rounded up to a multiple of A with padding rows, the segment starts being the scan of
 // the aligned lengths) and the group (send once per rank) slots ([CANN] §1(1)) are applied
@@ -38,10 +41,7 @@ namespace moe {
 namespace {
 
 constexpr int kMaxTiles = 128;      // tiles grow with T so that there are never more
-constexpr int kScanThreads = 1024;  // the scan workgroup: 16 wavefronts
-constexpr int kScanWaves = kScanThreads / kWave;
-constexpr int kKeysPerChunk = 4 * kWave;                                  // 4 keys per lane
-constexpr int kTilesPerWave = (kMaxTiles + kScanWaves - 1) / kScanWaves;  // 8
+constexpr int kEmptyThreads = 1024;
 constexpr int kRankBatch = 8;  // 64-slot groups whose loads a rank wave issues together
 
 struct IndexArgs {
@@ -53,10 +53,8 @@ struct IndexArgs {
     int32_t Ep, Gp;  // row strides of the histograms (E, G rounded up to a multiple of 4)
     int32_t tile_tokens, ntiles;
     int32_t ebits, gbits;
-    int32_t *hist_e;  // [ntiles][Ep] tile counts -> first row of (tile, expert) inside the expert
+    int32_t *hist_e;  // [ntiles][Ep] tile counts of the experts
     int32_t *hist_g;  // [ntiles][Gp] the same for group slots
-    int32_t *seg_e;   // [E] first row of each expert
-    int32_t *seg_g;   // [G] first slot of each group
     moe_index ix;
 };
 
@@ -124,14 +122,7 @@ __global__ __launch_bounds__(256) void hist_kernel(IndexArgs a)
     }
 }
 
-// ---------------------------------------------------------------- 2. scan
-struct ScanShared {
-    int32_t part[kScanWaves][kKeysPerChunk];  // per-wave partial sums -> per-wave prefixes
-    int32_t tot[MOE_MAX_EXPERTS];
-    int32_t seg[MOE_MAX_EXPERTS];
-    int32_t waves[kWave + 1];
-};
-
+// ---------------------------------------------------------------- no tokens
 __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -144,138 +135,35 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v)
     return v;
 }
 
-// Exclusive scan of one value per thread over the workgroup; *total gets the sum.
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *sh_waves, int32_t *total)
+// T == 0: zero counts and group_list (every segment is empty), and every row marked -- padding
+// in drop-and-pad, unused slack otherwise.
+__global__ __launch_bounds__(kEmptyThreads) void empty_index_kernel(IndexArgs a)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int32_t inc = wave_inclusive_scan(v);
-    if (lane == kWave - 1)
-        sh_waves[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        const int32_t w = lane < kScanWaves ? sh_waves[lane] : 0;
-        const int32_t winc = wave_inclusive_scan(w);
-        if (lane < kScanWaves)
-            sh_waves[lane] = winc - w;
-        if (lane == kScanWaves - 1)
-            sh_waves[kWave] = winc;
-    }
-    __syncthreads();
-    const int32_t r = sh_waves[wave] + inc - v;
-    *total = sh_waves[kWave];
-    __syncthreads();
-    return r;
-}
-
-// hist [ntiles][stride] (stride a multiple of 4, 16-byte aligned rows) holds tile counts; on
-// return it holds, for every (tile, key), the first row of that tile inside the key, sh.tot the
-// key totals and sh.seg each key's first row, the keys' segments being their totals rounded up
-// to a multiple of `align`. Returns the grand total of the segments.
-__device__ __forceinline__ int32_t scan_tiles(int32_t *hist, int nkeys, int stride, int ntiles, int align,
-                                              ScanShared &sh)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int tpw = (ntiles + kScanWaves - 1) / kScanWaves;  // <= kTilesPerWave
-    const int j0 = wave * tpw;
-    for (int kc = 0; kc < nkeys; kc += kKeysPerChunk) {
-        const int key = kc + 4 * lane;  // this lane's 4 keys: key .. key+3
-        const bool mine = key < stride;
-        u32x4 c[kTilesPerWave];
-#pragma unroll
-        for (int j = 0; j < kTilesPerWave; ++j) {
-            const int tile = j0 + j;
-            c[j] = (j < tpw && tile < ntiles && mine) ? ld16(hist + static_cast<int64_t>(tile) * stride + key)
-                                                      : u32x4{0u, 0u, 0u, 0u};
-        }
-        u32x4 s{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < kTilesPerWave; ++j) {
-            s.x += c[j].x;
-            s.y += c[j].y;
-            s.z += c[j].z;
-            s.w += c[j].w;
-        }
-        sh.part[wave][4 * lane + 0] = static_cast<int32_t>(s.x);
-        sh.part[wave][4 * lane + 1] = static_cast<int32_t>(s.y);
-        sh.part[wave][4 * lane + 2] = static_cast<int32_t>(s.z);
-        sh.part[wave][4 * lane + 3] = static_cast<int32_t>(s.w);
-        __syncthreads();
-        if (threadIdx.x < kKeysPerChunk) {  // one thread per key: prefix over the waves
-            int32_t run = 0;
-            for (int w = 0; w < kScanWaves; ++w) {
-                const int32_t v = sh.part[w][threadIdx.x];
-                sh.part[w][threadIdx.x] = run;
-                run += v;
-            }
-            if (kc + static_cast<int>(threadIdx.x) < nkeys)
-                sh.tot[kc + threadIdx.x] = run;
-        }
-        __syncthreads();
-        u32x4 run{static_cast<uint32_t>(sh.part[wave][4 * lane + 0]), static_cast<uint32_t>(sh.part[wave][4 * lane + 1]),
-                  static_cast<uint32_t>(sh.part[wave][4 * lane + 2]), static_cast<uint32_t>(sh.part[wave][4 * lane + 3])};
-#pragma unroll
-        for (int j = 0; j < kTilesPerWave; ++j) {
-            const int tile = j0 + j;
-            if (j < tpw && tile < ntiles && mine)
-                st16(hist + static_cast<int64_t>(tile) * stride + key, run);
-            run.x += c[j].x;
-            run.y += c[j].y;
-            run.z += c[j].z;
-            run.w += c[j].w;
-        }
-        __syncthreads();  // sh.part is reused by the next chunk of keys
-    }
-    int32_t total;
-    const int32_t v = static_cast<int>(threadIdx.x) < nkeys ? static_cast<int32_t>(round_up(sh.tot[threadIdx.x], align)) : 0;
-    const int32_t ex = block_exclusive_scan(v, sh.waves, &total);
-    if (static_cast<int>(threadIdx.x) < nkeys)
-        sh.seg[threadIdx.x] = ex;
-    __syncthreads();
-    return total;
-}
-
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(IndexArgs a)
-{
-    __shared__ ScanShared sh;
     const int tid = threadIdx.x;
-    const int64_t R = index_rows(a.T, a.K, a.E, a.cap, a.align);
-    scan_tiles(a.hist_e, a.E, a.Ep, a.ntiles, a.cap > 0 ? 1 : a.align, sh);
-    for (int e = tid; e < a.E; e += kScanThreads) {
-        const int32_t cnt = sh.tot[e];
-        const int32_t start = sh.seg[e];
-        a.seg_e[e] = start;
-        a.ix.counts[e] = cnt;
-        a.ix.group_list[e] = start + (a.cap > 0 ? cnt : static_cast<int32_t>(round_up(cnt, a.align)));
+    for (int e = tid; e < a.E; e += kEmptyThreads) {
+        a.ix.counts[e] = 0;
+        a.ix.group_list[e] = 0;
         if (a.ix.kept_counts)
-            a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
+            a.ix.kept_counts[e] = 0;
     }
-    if (a.ntiles == 0) {
-        // no tokens (otherwise the rank kernel writes these rows): every row of every expert is
-        // padding in drop-and-pad, every row is unused slack otherwise
-        const int32_t mark = a.cap > 0 ? MOE_ROW_PAD : MOE_ROW_UNUSED;
-        for (int64_t r = tid; r < R; r += kScanThreads) {
-            a.ix.sorted_indices[r] = mark;
-            if (a.ix.permuted_probs)
-                a.ix.permuted_probs[r] = 0.0f;
-            if (a.gs > 0)
-                a.ix.esrc[r] = mark;
-        }
+    const int64_t R = index_rows(a.T, a.K, a.E, a.cap, a.align);
+    const int32_t mark = a.cap > 0 ? MOE_ROW_PAD : MOE_ROW_UNUSED;
+    for (int64_t r = tid; r < R; r += kEmptyThreads) {
+        a.ix.sorted_indices[r] = mark;
+        if (a.ix.permuted_probs)
+            a.ix.permuted_probs[r] = 0.0f;
+        if (a.gs > 0)
+            a.ix.esrc[r] = mark;
     }
     if (a.gs > 0) {
-        __syncthreads();  // sh is reused for the group keys
-        const int32_t m = scan_tiles(a.hist_g, a.G, a.Gp, a.ntiles, 1, sh);
-        for (int g = tid; g < a.G; g += kScanThreads) {
-            a.seg_g[g] = sh.seg[g];
-            a.ix.group_counts[g] = sh.tot[g];
-        }
+        for (int g = tid; g < a.G; g += kEmptyThreads)
+            a.ix.group_counts[g] = 0;
         if (tid == 0)
-            a.ix.n_slots[0] = m;
+            a.ix.n_slots[0] = 0;
     }
 }
 
-// ---------------------------------------------------------------- 3. stable ranks
+// ---------------------------------------------------------------- 2. stable ranks
 // Bitwise match-any over the low `bits` bits of key among the lanes in `active`.
 __device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t active)
 {
@@ -290,7 +178,9 @@ __device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t acti
 
 __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(m); }
 
-constexpr int kRankWaves = 4;  // a tile's tokens are split across 4 wavefronts
+// a tile's tokens are split across 8 wavefronts (at T16384 K8 E256: 10.2 us per launch, 13.3 us
+// with 4; more and smaller tiles did not help)
+constexpr int kRankWaves = 8;
 constexpr int kRankThreads = kRankWaves * kWave;
 constexpr int kSpan = kRankBatch * kWave;  // slots whose loads a wavefront issues together
 
@@ -322,7 +212,103 @@ __device__ __forceinline__ void load_batch(const IndexArgs &a, int64_t base0, in
     }
 }
 
-// One workgroup per tile, kRankWaves wavefronts, each owning a contiguous quarter of the tile's
+constexpr int kOffsetLoads = 16;  // tile-count vectors a thread has in flight
+static_assert(kRankWaves * kSpan >= 2 * 4 * kRankThreads, "the id buffers hold the partial sums of tile_sums");
+
+// Per key of the tile counts hist[0..ntiles)[0..nkeys) (rows of `stride` keys, 16-byte aligned):
+// tot[key] = the sum over all tiles, pre[key] = the sum over the tiles before `tile`. A thread
+// owns 4 consecutive keys and a contiguous range of tiles; the ranges' partial sums meet in LDS
+// (`scratch`: 2 * kRankThreads * 4 ints) and are added in range order. Ends with a barrier.
+__device__ void tile_sums(const int32_t *hist, int nkeys, int stride, int ntiles, int tile, int32_t *tot,
+                          int32_t *pre, int32_t *scratch)
+{
+    const int tid = threadIdx.x;
+    const int nq = stride / 4;             // stride is a multiple of 4 and at most 4 * kRankThreads
+    const int splits = kRankThreads / nq;  // tile ranges
+    const int q = tid % nq, r = tid / nq;
+    const int tps = (ntiles + splits - 1) / splits;
+    int32_t *part_tot = scratch;                   // [splits][stride]
+    int32_t *part_pre = scratch + splits * stride;  // [splits][stride]
+    if (r < splits) {
+        const int j0 = r * tps, j1 = min(ntiles, j0 + tps);
+        u32x4 st{0u, 0u, 0u, 0u}, sp{0u, 0u, 0u, 0u};
+        for (int jb = j0; jb < j1; jb += kOffsetLoads) {
+            u32x4 c[kOffsetLoads];
+#pragma unroll
+            for (int u = 0; u < kOffsetLoads; ++u)
+                c[u] = jb + u < j1 ? ld16(hist + static_cast<int64_t>(jb + u) * stride + 4 * q) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < kOffsetLoads; ++u) {
+                const bool before = jb + u < tile;
+                st.x += c[u].x;
+                st.y += c[u].y;
+                st.z += c[u].z;
+                st.w += c[u].w;
+                sp.x += before ? c[u].x : 0u;
+                sp.y += before ? c[u].y : 0u;
+                sp.z += before ? c[u].z : 0u;
+                sp.w += before ? c[u].w : 0u;
+            }
+        }
+        int32_t *pt = part_tot + r * stride + 4 * q;
+        int32_t *pp = part_pre + r * stride + 4 * q;
+        pt[0] = static_cast<int32_t>(st.x);
+        pt[1] = static_cast<int32_t>(st.y);
+        pt[2] = static_cast<int32_t>(st.z);
+        pt[3] = static_cast<int32_t>(st.w);
+        pp[0] = static_cast<int32_t>(sp.x);
+        pp[1] = static_cast<int32_t>(sp.y);
+        pp[2] = static_cast<int32_t>(sp.z);
+        pp[3] = static_cast<int32_t>(sp.w);
+    }
+    __syncthreads();
+    for (int key = tid; key < nkeys; key += kRankThreads) {
+        int32_t t = 0, p = 0;
+        for (int rr = 0; rr < splits; ++rr) {
+            t += part_tot[rr * stride + key];
+            p += part_pre[rr * stride + key];
+        }
+        tot[key] = t;
+        pre[key] = p;
+    }
+    __syncthreads();
+}
+
+// seg[key] = the sum of round_up(tot, align) over the keys before it (nkeys <= 4 * kRankThreads;
+// each thread takes 4 consecutive keys); returns the sum over all keys. Ends with a barrier.
+__device__ int32_t segment_starts(const int32_t *tot, int nkeys, int align, int32_t *seg, int32_t *wsum)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int k0 = 4 * tid;
+    int32_t v[4];
+    int32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = k0 + i < nkeys ? static_cast<int32_t>(round_up(tot[k0 + i], align)) : 0;
+        sum += v[i];
+    }
+    const int32_t inc = wave_inclusive_scan(sum);
+    if (lane == kWave - 1)
+        wsum[wave] = inc;
+    __syncthreads();
+    int32_t run = inc - sum, total = 0;
+    for (int w = 0; w < kRankWaves; ++w) {
+        run += w < wave ? wsum[w] : 0;
+        total += wsum[w];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (k0 + i < nkeys)
+            seg[k0 + i] = run;
+        run += v[i];
+    }
+    __syncthreads();
+    return total;
+}
+
+// One workgroup per tile, kRankWaves wavefronts, each owning a contiguous share of the tile's
 // tokens (whole tokens). Phase A: every wave counts its slots per expert (and its first-in-group
 // slots per group) in LDS. Phase B: per key, a prefix over the waves starting at the tile's
 // first row of the key. Phase C: every wave walks its slots in order, 64 at a time, and ranks
@@ -331,10 +317,16 @@ __device__ __forceinline__ void load_batch(const IndexArgs &a, int64_t base0, in
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
+    __shared__ int32_t wsum[kRankWaves];
     int32_t *cnt_e = sh;                        // [kRankWaves][E] counts -> next row of the wave
     int32_t *cnt_g = cnt_e + kRankWaves * a.E;  // [kRankWaves][G]
     int32_t *seg_e = cnt_g + kRankWaves * a.G;  // [E] first row of each expert
-    int32_t *ids_all = seg_e + a.E;             // [kRankWaves][kSpan] expert ids of each wave's batch
+    int32_t *tot_e = seg_e + a.E;               // [E] slots routed to each expert
+    int32_t *pre_e = tot_e + a.E;               // [E] of those, the ones in tiles before this one
+    int32_t *seg_g = pre_e + a.E;               // [G] the same three for the group slots
+    int32_t *tot_g = seg_g + a.G;
+    int32_t *pre_g = tot_g + a.G;
+    int32_t *ids_all = pre_g + a.G;  // [kRankWaves][kSpan] expert ids of each wave's batch (first: sums)
     const int tile = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -344,8 +336,6 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     int32_t *ids = ids_all + wave * kSpan;
     for (int i = tid; i < kRankWaves * (a.E + a.G); i += kRankThreads)
         sh[i] = 0;
-    for (int e = tid; e < a.E; e += kRankThreads)
-        seg_e[e] = a.seg_e[e];
 
     // this wave's tokens and slots
     const int64_t tile_t0 = static_cast<int64_t>(tile) * a.tile_tokens;
@@ -358,7 +348,31 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     int e_first[kRankBatch];
     float w_first[kRankBatch];
     load_batch(a, s0, s1, want_w, e_first, w_first);
-    __syncthreads();
+
+    // ---- every key's first row, and this tile's first row inside it, from the tile counts
+    // (each workgroup adds up the counts of all tiles itself: no separate scan pass)
+    tile_sums(a.hist_e, a.E, a.Ep, a.ntiles, tile, tot_e, pre_e, ids_all);
+    const int32_t rows_used = segment_starts(tot_e, a.E, a.cap > 0 ? 1 : a.align, seg_e, wsum);
+    int32_t n_slots = 0;
+    if (a.gs > 0) {
+        tile_sums(a.hist_g, a.G, a.Gp, a.ntiles, tile, tot_g, pre_g, ids_all);
+        n_slots = segment_starts(tot_g, a.G, 1, seg_g, wsum);
+    }
+    if (tile == 0) {  // the per-expert (and per-group) results, once
+        for (int e = tid; e < a.E; e += kRankThreads) {
+            const int32_t cnt = tot_e[e];
+            a.ix.counts[e] = cnt;
+            a.ix.group_list[e] = seg_e[e] + (a.cap > 0 ? cnt : static_cast<int32_t>(round_up(cnt, a.align)));
+            if (a.ix.kept_counts)
+                a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
+        }
+        if (a.gs > 0) {
+            for (int g = tid; g < a.G; g += kRankThreads)
+                a.ix.group_counts[g] = tot_g[g];
+            if (tid == 0)
+                a.ix.n_slots[0] = n_slots;
+        }
+    }
 
     // ---- phase A: per-wave counts
     for (int64_t base0 = s0; base0 < s1; base0 += kSpan) {
@@ -398,9 +412,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 
     // ---- phase B: each wave's first row per key
     {
-        const int32_t *hrow = a.hist_e + static_cast<int64_t>(tile) * a.Ep;
         for (int e = tid; e < a.E; e += kRankThreads) {
-            int32_t run = seg_e[e] + hrow[e];
+            int32_t run = seg_e[e] + pre_e[e];
             for (int w = 0; w < kRankWaves; ++w) {
                 const int32_t c = cnt_e[w * a.E + e];
                 cnt_e[w * a.E + e] = run;
@@ -408,9 +421,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
             }
         }
         if (a.gs > 0) {
-            const int32_t *hrowg = a.hist_g + static_cast<int64_t>(tile) * a.Gp;
             for (int g = tid; g < a.G; g += kRankThreads) {
-                int32_t run = a.seg_g[g] + hrowg[g];
+                int32_t run = seg_g[g] + pre_g[g];
                 for (int w = 0; w < kRankWaves; ++w) {
                     const int32_t c = cnt_g[w * a.G + g];
                     cnt_g[w * a.G + g] = run;
@@ -501,11 +513,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     }
 
     // ---- padding rows (drop-and-pad) or rows after the last routed slot
-    __syncthreads();
-    int32_t *cnt = cnt_e;  // reused: per-expert counts
-    for (int e = tid; e < a.E; e += kRankThreads)
-        cnt[e] = a.ix.counts[e];
-    __syncthreads();
+    const int32_t *cnt = tot_e;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kRankThreads;
     if (a.cap > 0) {
         const int64_t R = static_cast<int64_t>(a.E) * a.cap;
@@ -536,7 +544,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
                 }
             }
         }
-        const int64_t total = static_cast<int64_t>(seg_e[a.E - 1]) + round_up(cnt[a.E - 1], A);
+        const int64_t total = rows_used;
         const int64_t R = index_rows(a.T, a.K, a.E, 0, A);
         for (int64_t r = total + static_cast<int64_t>(tile) * kRankThreads + tid; r < R; r += stride) {
             a.ix.sorted_indices[r] = MOE_ROW_UNUSED;
@@ -548,7 +556,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     }
 }
 
-// ---------------------------------------------------------------- 4. group mode: esrc
+// ---------------------------------------------------------------- 3. group mode: esrc
 __global__ __launch_bounds__(256) void esrc_kernel(IndexArgs a)
 {
     const int64_t n = a.T * a.K;
@@ -575,8 +583,7 @@ int round4(int n) { return (n + 3) & ~3; }
 
 struct Plan {
     int32_t tile_tokens, ntiles;
-    size_t ws_hist_e, ws_e;  // bytes of the expert tile counts, and of those plus the expert starts
-    size_t ws_hist_g, ws_g;  // the same for groups
+    size_t ws_e, ws_g;  // workspace bytes of the expert and of the group tile counts
 };
 
 // Tiles hold whole tokens (so a token's group test stays inside one tile), at least ~512 slots
@@ -589,10 +596,8 @@ Plan make_plan(int64_t T, int32_t K, int32_t E, int32_t G)
     p.tile_tokens = static_cast<int32_t>(std::min<int64_t>(tt, 0x7fffffff));
     p.ntiles = static_cast<int32_t>(T == 0 ? 0 : ceil_div(T, p.tile_tokens));
     auto al = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
-    p.ws_hist_e = al(sizeof(int32_t) * static_cast<size_t>(round4(E)) * p.ntiles);
-    p.ws_e = p.ws_hist_e + al(sizeof(int32_t) * static_cast<size_t>(E));
-    p.ws_hist_g = G > 0 ? al(sizeof(int32_t) * static_cast<size_t>(round4(G)) * p.ntiles) : 0;
-    p.ws_g = G > 0 ? p.ws_hist_g + al(sizeof(int32_t) * static_cast<size_t>(G)) : 0;
+    p.ws_e = al(sizeof(int32_t) * static_cast<size_t>(round4(E)) * p.ntiles);
+    p.ws_g = G > 0 ? al(sizeof(int32_t) * static_cast<size_t>(round4(G)) * p.ntiles) : 0;
     return p;
 }
 
@@ -665,7 +670,8 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     const Plan p = make_plan(T, K, E, G);
     if (p.ntiles > kMaxTiles)
         return MOE_ERR_UNSUPPORTED;  // cannot happen: tiles grow with T to stay within the limit
-    if (!workspace || workspace_bytes < p.ws_e + p.ws_g || !aligned16(workspace))
+    const size_t need = p.ws_e + p.ws_g;
+    if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
         return MOE_ERR_INVALID;
 
     IndexArgs a{};
@@ -686,14 +692,12 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     a.gbits = bits_for(G);
     char *ws = static_cast<char *>(workspace);
     a.hist_e = reinterpret_cast<int32_t *>(ws);
-    a.seg_e = reinterpret_cast<int32_t *>(ws + p.ws_hist_e);
     a.hist_g = G > 0 ? reinterpret_cast<int32_t *>(ws + p.ws_e) : nullptr;
-    a.seg_g = G > 0 ? reinterpret_cast<int32_t *>(ws + p.ws_e + p.ws_hist_g) : nullptr;
     a.ix = *out;
 
     if (T == 0) {
-        // nothing routed: the scan alone writes zero counts and the padding rows
-        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
+        // nothing routed: zero counts and the padding or unused marks
+        hipLaunchKernelGGL(empty_index_kernel, dim3(1), dim3(kEmptyThreads), 0, stream, a);
         return launch_status();
     }
 
@@ -701,11 +705,8 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     hipLaunchKernelGGL(hist_kernel, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
-    if ((st = launch_status()) != MOE_OK)
-        return st;
-    const size_t lds_rank =
-        sizeof(int32_t) * (static_cast<size_t>(kRankWaves) * (E + G) + E + static_cast<size_t>(kRankWaves) * kSpan);
+    const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 3) * (E + G) +
+                                               static_cast<size_t>(kRankWaves) * kSpan);
     hipLaunchKernelGGL(rank_kernel, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
