@@ -836,6 +836,41 @@ def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
     del g
 
 
+def test_binding_rejects_wrong_shapes_before_launch(m):
+    """Output or side-input tensors whose shapes do not match the call raise ValueError in the
+    binding (the kernels index them by the call's sizes), and nothing is written."""
+    T, H, E, K, gs = 6, 64, 8, 2, 4
+    G = E // gs
+    i32 = dict(dtype=torch.int32, device=DEV)
+    x = torch.ones((T, H), dtype=torch.bfloat16, device=DEV)
+    row_of = torch.zeros((T, K), **i32)
+    idx = torch.zeros((T, K), **i32)
+    w = torch.ones((T, K), dtype=torch.float32, device=DEV)
+    slot_of = torch.zeros((T, G), **i32)
+    q_bad = torch.full((T, H - 8), 7, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        m.quantize_fp8(x, 32, out=(q_bad, torch.empty((T, H // 32), dtype=torch.float32, device=DEV)))
+    with pytest.raises(ValueError):
+        m.quantize_fp8(x, 32, out=(torch.empty((T, H), dtype=torch.uint8, device=DEV),
+                                   torch.empty((T, 1), dtype=torch.float32, device=DEV)))
+    part = torch.empty((T * G, H), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):  # weights not [T, K]
+        m.group_precombine(x, row_of, w[:, :1].contiguous(), idx, E, gs, slot_of, out=part)
+    with pytest.raises(ValueError):  # topk_idx not [T, K]
+        m.group_precombine(x, row_of, w, idx[:3].contiguous(), E, gs, slot_of, out=part)
+    with pytest.raises(ValueError):  # slot_of not [T, G]
+        m.group_precombine(x, row_of, w, idx, E, gs, torch.zeros((T, G + 1), **i32), out=part)
+    with pytest.raises(ValueError):  # partial rows of another length
+        m.group_precombine(x, row_of, w, idx, E, gs, slot_of, out=torch.empty((T * G, H // 2), dtype=torch.float32,
+                                                                              device=DEV))
+    with pytest.raises(ValueError):  # group size not dividing E
+        m.group_precombine(x, row_of, w, idx, E, 3, slot_of, out=part)
+    with pytest.raises(ValueError):  # preallocated index for other sizes
+        m.build_index(idx, w, E, out=m.alloc_index(T + 1, K, E))
+    torch.cuda.synchronize()
+    assert (q_bad == 7).all()
+
+
 def test_pipeline_is_deterministic(m):
     """No atomics decide positions or sums: two runs give identical bits."""
     a = host(run_workload(m, 2))

@@ -35,6 +35,9 @@ def _need(t: torch.Tensor, name: str, dtype=None, dims=None):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the calls launch on the current device "
+                         f"cuda:{torch.cuda.current_device()} (use torch.cuda.device(...))")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if dims is not None and t.dim() != dims:
@@ -173,6 +176,8 @@ def build_index(topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor], num_expe
     if (ix.T, ix.K, ix.E, ix.capacity, ix.group_size, ix.alignment) != (T, K, num_experts, capacity, group_size,
                                                                         alignment):
         raise ValueError("preallocated index was made for other sizes")
+    if ix.counts.device != topk_idx.device:
+        raise ValueError(f"preallocated index is on {ix.counts.device}, topk_idx on {topk_idx.device}")
     s = ix.struct()
     ws = ix.workspace
     check("moe_build_index", lib().moe_build_index(
@@ -260,6 +265,8 @@ def quantize_fp8(x: torch.Tensor, block: int = 128, out=None):
     sc = torch.empty((T, H // block), dtype=torch.float32, device=x.device) if sc is None else sc
     _need(q, "q", torch.uint8, 2)
     _need(sc, "scales", torch.float32, 2)
+    if tuple(q.shape) != (T, H) or tuple(sc.shape) != (T, H // block):
+        raise ValueError(f"output shapes must be [{T}, {H}] and [{T}, {H // block}]")
     check("moe_quantize_fp8", lib().moe_quantize_fp8(_p(x), dt, T, H, block, _p(q), _p(sc), _stream()))
     return q, sc
 
@@ -333,13 +340,23 @@ def group_precombine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[to
     _need(slot_of, "slot_of", torch.int32, 2)
     T, K = row_of.shape
     H = y.shape[1]
+    if tuple(topk_idx.shape) != (T, K):
+        raise ValueError("topk_idx must have the shape of row_of")
     if weights is not None:
         _need(weights, "weights", torch.float32, 2)
+        if tuple(weights.shape) != (T, K):
+            raise ValueError("weights must have the shape of row_of")
+    if group_size < 1 or num_experts % group_size:
+        raise ValueError("group_size must divide num_experts")
+    if tuple(slot_of.shape) != (T, num_experts // group_size):
+        raise ValueError(f"slot_of must be [{T}, {num_experts // group_size}]")
     if out is None:
         if slots_cap is None:
             raise ValueError("give slots_cap or out")
         out = torch.empty((slots_cap, H), dtype=torch.float32, device=y.device)
     _need(out, "out", torch.float32, 2)
+    if out.shape[1] != H:
+        raise ValueError(f"out rows must have {H} elements")
     check("moe_group_precombine", lib().moe_group_precombine(
         _p(y), y_dt, y.shape[0], H, _p(row_of), _p(weights), _p(topk_idx), T, K, num_experts, group_size,
         _p(slot_of), out.shape[0], _p(out), _stream()))
