@@ -189,7 +189,8 @@ moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, moe_dtype d
  * written to every destination that names it, instead of being read again for each destination
  * (with top-k routing a token row feeds K expert rows, [Scratch] §4).
  *   dst_of  [src_rows, J] int32: dst[dst_of[t*J + j], :] = src[t, :] for every entry in [0, N);
- *           other entries (-1) are skipped. J <= 64.
+ *           other entries (-1) are skipped. J <= MOE_MAX_EXPERTS (one column per expert group
+ *           at most); the entries are read 64 at a time, so a wide map costs a little more.
  *   src_row [N] int32 or NULL: rows i with src_row[i] outside [0, src_rows) are written as zeros
  *           (the padding rows of drop-and-pad); NULL writes no zero rows.
  * When dst_of is the inverse of src_row -- row_of and sorted_indices of one moe_index are -- the
@@ -234,7 +235,7 @@ moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe
  *     zero scales (padding), MOE_ROW_UNUSED rows are left untouched. Equal, bit for bit, to
  *     moe_quantize_fp8 followed by moe_permute_scatter of the codes (MOE_FP8_E4M3) and of the
  *     scales (float32, H / block columns). block must be a power of two in [8, 1024] dividing H
- *     (else MOE_ERR_UNSUPPORTED), J <= 64, src and dst 16-byte aligned.
+ *     (else MOE_ERR_UNSUPPORTED), J <= MOE_MAX_EXPERTS, src and dst 16-byte aligned.
  * The moved rows then hold half the bytes of bf16 rows; moe_permute / moe_permute_grouped move
  * FP8 rows (and float32 scale rows) as they move any rows. */
 moe_status moe_quantize_fp8(const void *x, moe_dtype x_dt, int64_t T, int64_t H, int32_t block, uint8_t *q,

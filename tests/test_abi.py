@@ -125,6 +125,9 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_permute(fake, 4, big, 1, fake, 4, fake, None) == capi.MOE_ERR_UNSUPPORTED  # bf16: 2 GiB rows
     assert lib.moe_permute(fake, 4, big // 2, 0, fake, 4, fake, None) == capi.MOE_ERR_UNSUPPORTED  # f32
     assert lib.moe_permute_scatter(fake, 4, big, 1, fake, 2, None, 8, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_scatter(fake, 4, 8, 1, fake, 1025, None, 8, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_scatter_fp8(fake, 1, 4, 128, 128, fake, 1025, None, 8, fake, fake, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # more destination columns than experts
     assert lib.moe_permute_grouped(fake, 4, big, 1, fake, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(fake, 1, 4, big // 2, fake, None, None, 2, 2, fake, 0, None) == \
         capi.MOE_ERR_UNSUPPORTED  # float32 output rows of 2 GiB

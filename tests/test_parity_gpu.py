@@ -449,6 +449,34 @@ def test_permute_scatter_fp8(m, dtype, H, T, E, K, mode, block):
     assert_exact(host(q2)[live], host(q)[live], "byte permute of the codes")
 
 
+@pytest.mark.parametrize("J", [65, 200, 1024])
+@pytest.mark.parametrize("H,dtype", [(7168, "bf16"), (1000, "f32"), (13, "bf16")])
+def test_permute_scatter_wide_maps(m, J, H, dtype):
+    """Destination maps wider than a wavefront (e.g. slot_of with more than 64 expert groups):
+    each source row names a few destinations spread over J mostly empty columns, some rows name
+    none; the scatter (and, for 16-byte rows, the fused FP8 scatter) equals the oracle's gather
+    through the inverse map, zero rows included."""
+    say(f"permute_scatter wide J={J} H={H} {dtype}")
+    g = np.random.default_rng([72, J, H])
+    src_rows, N = 50, 300
+    dst_of = np.full((src_rows, J), -1, np.int32)
+    cells = g.choice(src_rows * J, size=N - 20, replace=False)  # 20 destination rows stay unnamed
+    rows = g.permutation(N)[: N - 20]
+    dst_of.reshape(-1)[cells] = rows
+    src_row = np.full(N, -1, np.int32)
+    src_row[rows] = (cells // J).astype(np.int32)
+    x = wl.hidden_states(wl.case_key(72, J, H), src_rows, H, dtype)
+    got = host(m.permute_scatter(dev(x), dev(dst_of), N, src_row=dev(src_row)))
+    assert_exact(got, oracle.permute(x, src_row), "rows")
+    if (H * (2 if dtype == "bf16" else 4)) % 16 == 0 and H % 8 == 0:
+        block = 8 if H % 16 else 8 * (H // 8 & -(H // 8))  # a power of two dividing H
+        block = min(block, 1024)
+        qs, ss = oracle.quantize_fp8(x, block)
+        q, sc = m.permute_scatter_fp8(dev(x), dev(dst_of), N, block, src_row=dev(src_row))
+        assert_exact(host(q), oracle.permute(qs, src_row), "codes")
+        assert_exact(host(sc), oracle.permute(ss, src_row), "scales")
+
+
 @pytest.mark.parametrize("ydt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
 @pytest.mark.parametrize("H,K,T", [(7168, 8, 60), (1000, 2, 50), (5, 3, 20), (512, 8, 40), (64, 1, 30), (24, 40, 16)])
 def test_unpermute_combine_bias(m, ydt, odt, H, K, T):
@@ -834,6 +862,79 @@ def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
         for k, v in want.items():
             assert np.array_equal(got[k], v), f"replay {rep}: {k}"
     del g
+
+
+def _random_config(i):
+    g = np.random.default_rng([91, i])
+    mode = ["standard", "drop", "group", "aligned"][i % 4]
+    E = int(g.integers(1, 300))
+    K = int(g.integers(1, min(E, 32) + 1))
+    H = int(8 * g.integers(1, 1100)) if g.random() < 0.7 else int(g.integers(1, 600))
+    T = int(g.integers(1, max(2, min(2500, 3_000_000 // (K * H)))))
+    dtype = "bf16" if g.random() < 0.6 else "f32"
+    cap = gs = align = M = 0
+    if mode == "drop":
+        cap = int(g.integers(1, max(2, 2 * T * K // E)))
+    if mode == "group":
+        divisors = [d for d in range(1, E + 1) if E % d == 0 and E // d <= 1024]
+        gs = int(g.choice(divisors))
+        G = E // gs
+        if g.random() < 0.5 and G > 1:
+            M = int(g.integers(1, G + 1))
+            if K > M * gs:
+                M = 0
+        align = int(g.choice([0, 4])) if g.random() < 0.3 else 0
+    if mode == "aligned":
+        align = int(g.choice([2, 8, 16, 128]))
+    ties = g.random() < 0.3
+    zipf = 1.2 if g.random() < 0.5 else None
+    return dict(mode=mode, T=T, E=E, K=K, H=H, dtype=dtype, cap=cap, gs=gs, align=align, M=M, ties=ties, zipf=zipf)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_configuration(m, i):
+    """Seeded random sizes and modes (standard, drop-and-pad, group with and without limited
+    routing and alignment, aligned; float32 and bf16; hidden sizes with and without a 16-byte
+    multiple; tie-heavy and skewed logits): the whole path against the oracle."""
+    c = _random_config(i)
+    T, E, K, H, dt, cap, gs, align, M = (c[k] for k in ("T", "E", "K", "H", "dtype", "cap", "gs", "align", "M"))
+    say(f"random config {i}: {c}")
+    key = wl.case_key(92, i)
+    logits = tie_logits(key, T, E) if c["ties"] else wl.router_logits(key, T, E, zipf_s=c["zipf"])
+    want_i, want_w = oracle.route_topk_grouped(logits, K, gs, M) if M else oracle.route_topk(logits, K)
+    gi, gw = m.route_topk(dev(logits), K, group_size=gs if M else 0, topk_groups=M)
+    assert_exact(host(gi), want_i, "topk_idx")
+    assert_rel_f32(host(gw), want_w, "topk_w")
+    w = host(gw)  # downstream, both sides use the same weight bits
+    want = oracle.build_index(want_i, w, E, capacity=cap, group_size=gs, alignment=align)
+    ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs, alignment=align)
+    for name in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs"):
+        assert_exact(host(getattr(ix, name)), want[name], name)
+    rows = ix.rows
+    x = wl.hidden_states(key, T, H, dt)
+    y = wl.expert_outputs(key, rows, H, dt)
+    out_dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    live = want["sorted_indices"] != -2
+    if gs:
+        n = int(host(ix.n_slots)[0])
+        assert n == int(want["n_slots"][0])
+        assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
+        for name in ("slot_of", "esrc", "group_counts"):
+            assert_exact(host(getattr(ix, name)), want[name], name)
+        slots = T * min(K, E // gs)
+        gbuf = m.permute_scatter(dev(x), ix.slot_of, slots)
+        xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of)
+        part = m.group_precombine(dev(y), ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=slots)
+        out = m.unpermute_combine(part, ix.slot_of, None, out_dtype=out_dtype)
+        want_p = oracle.group_precombine(y, want["row_of"], w, want_i, E, gs, want["slot_of"], slots)
+        want_o = oracle.unpermute_combine(want_p[:n], want["slot_of"], None, np.uint16 if dt == "bf16" else np.float32)
+        assert_combined(host(part)[:n], want_p[:n], "partials")
+    else:
+        xp = m.permute_scatter(dev(x), ix.row_of, rows, src_row=ix.sorted_indices)
+        out = m.unpermute_combine(dev(y), ix.row_of, gw)
+        want_o = oracle.unpermute_combine(y, want["row_of"], w, np.uint16 if dt == "bf16" else np.float32)
+    assert_exact(host(xp)[live], oracle.permute(x, want["sorted_indices"])[live], "permuted rows")
+    assert_combined(host(out), want_o, "combined")
 
 
 def test_binding_rejects_wrong_shapes_before_launch(m):

@@ -147,8 +147,17 @@ __global__ __launch_bounds__(kFp8Threads) void permute_scatter_fp8_kernel(
         return;
     const int64_t e0 = (cw - t * spr) * kFp8Slice + 16 * lane;  // this lane's 16 elements: two halves
     const bool have0 = e0 < H, have1 = e0 + 8 < H;  // H is a multiple of 8
-    const int32_t my = lane < J ? dst_of[t * J + lane] : -1;
-    uint64_t m = __ballot(my >= 0 && my < N);
+    // the first 64 entries of dst_of that name a destination (a token has fewer than 64 in
+    // practice; later chunks are walked below)
+    int j0 = 0;
+    int32_t my = -1;
+    uint64_t m = 0;
+    for (; j0 < J; j0 += kWave) {
+        my = j0 + lane < J ? dst_of[t * J + j0 + lane] : -1;
+        m = __ballot(my >= 0 && my < N);
+        if (m)
+            break;
+    }
     if (m == 0)
         return;
     float v[16];
@@ -190,7 +199,15 @@ __global__ __launch_bounds__(kFp8Threads) void permute_scatter_fp8_kernel(
     const bool first_lane = block == 8 || (lane % (block / 16)) == 0;
     const int64_t b0 = e0 / block;
     const bool whole16 = H % 16 == 0;
-    while (m) {
+    for (;;) {
+        if (m == 0) {  // next chunk of 64 entries
+            j0 += kWave;
+            if (j0 >= J)
+                break;
+            my = j0 + lane < J ? dst_of[t * J + j0 + lane] : -1;
+            m = __ballot(my >= 0 && my < N);
+            continue;
+        }
         const int j = __builtin_ctzll(m);
         m &= m - 1;
         const int64_t d = __builtin_amdgcn_readlane(my, j);
@@ -252,7 +269,7 @@ extern "C" moe_status moe_permute_scatter_fp8(const void *src, moe_dtype src_dt,
     if (src_rows < 0 || H < 1 || N < 0 || J < 1 || block < 1 || H % block != 0 ||
         (src_dt != MOE_F32 && src_dt != MOE_BF16))
         return MOE_ERR_INVALID;
-    if (J > 64 || !pow2(block) || block < 8 || block > kFp8Slice)
+    if (J > MOE_MAX_EXPERTS || !pow2(block) || block < 8 || block > kFp8Slice)
         return MOE_ERR_UNSUPPORTED;
     if (N == 0 || (src_rows == 0 && !src_row))
         return MOE_OK;
