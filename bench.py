@@ -7,8 +7,10 @@ unpermute_combine (expert outputs back to token order, weighted). In group mode 
 the two-stage dedup dispatch and the combine is the per-group pre-combine plus the final sum.
 
 Prints ONE JSON line. `value` is the whole step's algorithmic bytes (each stage's minimal HBM
-traffic, computed from the actual routing) divided by the measured step time. Every kernel call
-is bracketed by HIP events on the launch stream (`kernel_us`; `stage_us` sums them per stage);
+traffic, computed from the actual routing) divided by the measured step time: by default the
+time of K replays of the step captured once in a HIP graph (`--eager`: the eagerly launched
+steps; `ms_per_step_eager` is reported either way). In the eager pass every kernel call is
+bracketed by HIP events on the launch stream (`kernel_us`; `stage_us` sums them per stage);
 `roofline` describes the dominant HBM-bound kernel with its own event time; `cpu_baseline` is the
 CPU oracle on the same workload on this host.
 """
@@ -49,6 +51,8 @@ KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine
                   "dispatch_bwd_recv": "precombine_kernel", "dispatch_bwd_send": "combine_kernel",
                   "permute_fp8": "permute_scatter_fp8_kernel", "dispatch_send_fp8": "permute_scatter_fp8_kernel",
                   "dispatch_recv_scales": "permute_grouped_vec16_kernel"}
+
+
 def combine_symbol(y_bf16: bool, out_bf16: bool, K: int, H: int, T: int) -> str:
     """Kernel the library launches for a combine call: bf16 rows with 5..8 slots per token, at
     most 128 KB of staged rows (8 * H * 2 bytes) and at least 2048 workgroups of 8 tokens take
@@ -444,7 +448,8 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes):
 
 
 def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes):
-    """The CPU oracle's backward (single thread) on the same saved forward state, 2 passes."""
+    """The CPU oracle's backward (single thread) on the same saved forward state: passes repeated
+    until about 10 s of CPU work, the best pass reported."""
     import numpy as np
 
     import oracle
