@@ -4,7 +4,9 @@
 //
 // gfx950 design: 16 lanes per token, 4 tokens per wavefront. Lane l of a token's 16-lane row
 // holds the logits of experts l, l+16, l+32, ... and keeps the best of its own still-unselected
-// experts. A key orders (logit descending, expert id ascending): high word an order-preserving
+// experts. (Consecutive experts per lane, with 16-byte loads, took 17.7 us instead of 12.7 us at
+// T16384 E256 K8 with Zipf-skewed logits: the popular low ids then sit in one or two lanes,
+// whose candidate caches run dry.) A key orders (logit descending, expert id ascending): high word an order-preserving
 // image of the float, low word ~id. Each lane keeps its best three keys in order; each of the
 // K rounds is a 16-lane all-reduce of the lanes' first keys made of four DPP steps (row_mirror,
 // row_half_mirror, quad xor 2, quad xor 1) -- plain VALU instructions, no LDS round trip --
