@@ -1061,6 +1061,93 @@ def test_route_topk_backward(m, T, E, K, holes):
     assert_exact(got, want, "d_logits")
 
 
+@pytest.mark.parametrize("i", range(24))
+def test_random_configuration_backward(m, i):
+    """The backward over seeded random configurations (the sizes and modes of the forward sweep;
+    dout, dy and y dtypes drawn independently): combine backward (dy bit for bit, dw within the
+    dot-product bound), dispatch backward (the unit-weight combine, or pre-combine + final sum in
+    group mode) and the router backward, all against the oracle."""
+    c = _random_config(100 + i)
+    T, E, K, H, cap, gs, align = (c[k] for k in ("T", "E", "K", "H", "cap", "gs", "align"))
+    g = np.random.default_rng([93, i])
+    ddt, ydt, dydt = (("bf16", "f32")[int(g.random() < 0.4)] for _ in range(3))
+    say(f"random backward {i}: {c} dout={ddt} y={ydt} dy={dydt}")
+    key = wl.case_key(94, i)
+    logits = tie_logits(key, T, E) if c["ties"] else wl.router_logits(key, T, E, zipf_s=c["zipf"])
+    gi, gw = m.route_topk(dev(logits), K)
+    w = host(gw)
+    idx = host(gi)
+    ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs, alignment=align)
+    want = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
+    rows = ix.rows
+    y = wl.expert_outputs(key, rows, H, ydt)
+    dout = wl.expert_outputs((*key, 1), T, H, ddt)
+    dxp = wl.expert_outputs((*key, 2), rows, H, ydt)
+    dy_np = np.uint16 if dydt == "bf16" else np.float32
+    want_dy, want_dw = oracle.combine_backward(dout, y, want["row_of"], w, dy_np)
+    dy, dw = m.unpermute_combine_backward(dev(dout), dev(y), ix.row_of, gw, src_row=ix.sorted_indices,
+                                          dy_dtype=torch.bfloat16 if dydt == "bf16" else torch.float32)
+    live = want["sorted_indices"] != -2
+    assert_exact(host(dy)[live], want_dy[live], "dy")
+    got_dw = host(dw)
+    _check_dw(got_dw, want_dw, _dw_bound(dout, y, want["row_of"], H))
+    # the dispatch's backward: expert-row gradients back to token order with unit weights
+    out_np = np.uint16 if ydt == "bf16" else np.float32
+    if gs:
+        n = int(want["n_slots"][0])
+        slots = T * min(K, E // gs)
+        part = m.group_precombine(dev(dxp), ix.row_of, None, gi, E, gs, ix.slot_of, slots_cap=slots)
+        dx = m.unpermute_combine(part, ix.slot_of, None, out_dtype=torch.bfloat16 if ydt == "bf16" else torch.float32)
+        want_p = oracle.group_precombine(dxp, want["row_of"], None, idx, E, gs, want["slot_of"], slots)
+        want_dx = oracle.unpermute_combine(want_p[:n], want["slot_of"], None, out_np)
+    else:
+        dx = m.unpermute_combine(dev(dxp), ix.row_of, None)
+        want_dx = oracle.unpermute_combine(dxp, want["row_of"], None, out_np)
+    assert_combined(host(dx), want_dx, "dx")
+    # the router's backward, fed the kernel's own dw (the same bits on both sides)
+    assert_exact(host(m.route_topk_backward(gi, gw, dw, E)), oracle.route_topk_backward(idx, w, got_dw, E),
+                 "d_logits")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_configuration_fp8(m, i):
+    """The fused FP8 dispatch over seeded random configurations whose hidden size allows it
+    (a multiple of 8, 16-byte rows): codes and scales equal the oracle's quantization moved by
+    the oracle's gather, in standard, drop-and-pad, aligned and group (send + receive) modes."""
+    j = 200 + i
+    c = _random_config(j)
+    while c["H"] % 8:
+        j += 1000
+        c = _random_config(j)
+    T, E, K, H, dt, cap, gs, align = (c[k] for k in ("T", "E", "K", "H", "dtype", "cap", "gs", "align"))
+    blocks = [b for b in (8, 16, 32, 64, 128, 256, 512, 1024) if H % b == 0]
+    block = blocks[i % len(blocks)]
+    say(f"random fp8 {i}: {c} block={block}")
+    key = wl.case_key(95, i)
+    logits = wl.router_logits(key, T, E, zipf_s=c["zipf"])
+    gi, gw = m.route_topk(dev(logits), K)
+    idx, w = host(gi), host(gw)
+    ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs, alignment=align)
+    want = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
+    x = fp8_inputs(key, T, H, dt)
+    qs, ss = oracle.quantize_fp8(x, block)
+    si = want["sorted_indices"]
+    live = si != -2
+    if gs:
+        n = int(want["n_slots"][0])
+        slots = T * min(K, E // gs)
+        q, sc = m.permute_scatter_fp8(dev(x), ix.slot_of, slots, block)
+        assert_exact(host(q)[:n], oracle.permute(qs, want["gsrc"]), "slot codes")
+        assert_exact(host(sc)[:n], oracle.permute(ss, want["gsrc"]), "slot scales")
+        rq = host(m.permute_grouped(q, ix.esrc, ix.row_of))
+        rs = host(m.permute_grouped(sc, ix.esrc, ix.row_of))
+    else:
+        q, sc = m.permute_scatter_fp8(dev(x), ix.row_of, ix.rows, block, src_row=ix.sorted_indices)
+        rq, rs = host(q), host(sc)
+    assert_exact(rq[live], oracle.permute(qs, si)[live], "codes")
+    assert_exact(rs[live], oracle.permute(ss, si)[live], "scales")
+
+
 def test_backward_no_tokens(m):
     d = m.route_topk_backward(torch.zeros((0, 2), dtype=torch.int32, device=DEV),
                               torch.zeros((0, 2), dtype=torch.float32, device=DEV),
