@@ -283,23 +283,32 @@ def main():
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
     ms_per_step_eager = ms_per_step
+    launch = "eager"
     if not args.eager:
         # the same calls captured once; no call allocates, waits on the host or records a memset
-        graph = torch.cuda.CUDAGraph()
-        cap_stream = torch.cuda.Stream()
-        cap_stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap_stream):
-            with torch.cuda.graph(graph, stream=cap_stream):
-                step()
-        torch.cuda.current_stream().wait_stream(cap_stream)
-        for _ in range(max(3, args.warmup)):
-            graph.replay()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+        try:
+            graph = torch.cuda.CUDAGraph()
+            cap_stream = torch.cuda.Stream()
+            cap_stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap_stream):
+                with torch.cuda.graph(graph, stream=cap_stream):
+                    step()
+            torch.cuda.current_stream().wait_stream(cap_stream)
+            torch.cuda.synchronize()
+        except RuntimeError as e:  # report the eager timing rather than nothing
+            log(f"[bench] HIP graph capture failed, timing eager steps only: {e}")
+            torch.cuda.synchronize()
+            launch = f"eager (graph capture failed: {type(e).__name__})"
+        else:
+            for _ in range(max(3, args.warmup)):
+                graph.replay()
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for _ in range(args.steps):
+                graph.replay()
+            torch.cuda.synchronize()
+            ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+            launch = "hip graph replay"
     kernel_us = {}
     for i, (name, _, _) in enumerate(calls):
         kernel_us[name] = float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.steps)]))
@@ -386,7 +395,7 @@ def main():
     }
     if args.backward:
         result["pass"] = "backward"
-    result["launch"] = ("eager" if args.eager else "hip graph replay")
+    result["launch"] = launch
     result["ms_per_step_eager"] = round(ms_per_step_eager, 4)
     if not args.no_cpu_baseline and args.fp8:
         result["cpu_baseline"] = None  # the oracle baseline is timed on the bf16 path
