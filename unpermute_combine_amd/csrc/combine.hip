@@ -99,22 +99,23 @@ __device__ __forceinline__ void fma_batch(const Y *__restrict__ y, int64_t H, co
     }
 }
 
-// Two chunks (c, c2) of the same (at most kFewTerms) terms with all their loads in flight before
-// the first FMA; row1 marks the terms of chunk c2 (negative: nothing to load).
-template <typename Y>
-__device__ __forceinline__ void fma_few2(const Y *__restrict__ y, int64_t H, const int32_t (&row)[kBatch],
-                                         const int32_t (&row1)[kBatch], const float (&w)[kBatch], int64_t c,
-                                         int64_t c2, float (&acc)[8], float (&acc2)[8])
+// Two chunks (c, c2) of the same (at most N) terms with all their loads in flight before the
+// first FMA; row1 marks the terms of chunk c2 (negative: nothing to load).
+template <typename Y, int N>
+__device__ __forceinline__ void fma_two(const Y *__restrict__ y, int64_t H, const int32_t (&row)[kBatch],
+                                        const int32_t (&row1)[kBatch], const float (&w)[kBatch], int64_t c,
+                                        int64_t c2, float (&acc)[8], float (&acc2)[8])
 {
-    u32x4 q[kFewTerms][Chunk<Y>::kVecs];
-    u32x4 q2[kFewTerms][Chunk<Y>::kVecs];
+    static_assert(N <= kBatch, "at most one batch of terms");
+    u32x4 q[N][Chunk<Y>::kVecs];
+    u32x4 q2[N][Chunk<Y>::kVecs];
 #pragma unroll
-    for (int u = 0; u < kFewTerms; ++u) {
+    for (int u = 0; u < N; ++u) {
         load_chunk<Y>(y, H, row[u], c, q[u]);
         load_chunk<Y>(y, H, row1[u], c2, q2[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kFewTerms; ++u) {
+    for (int u = 0; u < N; ++u) {
         const bool live = row[u] >= 0;
         float v[8], v2[8];
         Chunk<Y>::widen(q[u], v);
@@ -338,8 +339,9 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
                 store8(o + c * 8, acc);
             }
         } else {
-            // few terms (n <= kFewTerms): half the threads take two chunks each, with the loads
-            // of both in flight together; the other half has nothing to do
+            // few terms (n <= kFewTerms): two chunks per thread, the loads of both in flight
+            // together (with a workgroup of one thread per chunk, half the threads have nothing
+            // to do)
             const int64_t half = (nchunk + 1) / 2;
             for (int64_t c = threadIdx.x; c < half; c += blockDim.x) {
                 const int64_t c2 = c + half;
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u)
                     row1[u] = c2 < nchunk ? row0[u] : -1;
-                fma_few2<Y>(y, H, row0, row1, w0, c, c2, acc, acc2);
+                fma_two<Y, kFewTerms>(y, H, row0, row1, w0, c, c2, acc, acc2);
                 if (bias) {
                     add_bias8(bias + t * H + c * 8, acc);
                     if (c2 < nchunk)
@@ -797,9 +799,11 @@ __global__ __launch_bounds__(kMaxThreads) void combine_backward_scalar_kernel(
 }
 
 // Threads per workgroup: one per `cpt` 8-element chunks, whole wavefronts, at most 1024.
-// Measured on MI355X: a token with 8 terms at H = 7168 combines fastest with one chunk per
-// thread (361 us vs 372 us with two per launch of the bf16 combine), tokens with few terms
-// (K = 2, drop-and-pad, the per-group partials) with two chunks per thread.
+// Measured on MI355X (bf16 per-token combine): with at most 8 slots per token a workgroup of one
+// thread per two chunks is faster for every mix of terms -- T8192 H7168 with 8 terms 178 vs 185
+// us, 6 terms (T4096) 70 vs 78 us, drop-and-pad T8192 H4096 E128 48 vs 56 us, K = 2 (T4096
+// H4096) 24 vs 27 us; loading both chunks of a many-term token together instead of one after
+// the other raised the registers to 112 (occupancy 4) and lost on the few-term tokens.
 int block_threads(int64_t nchunk, int cpt)
 {
     const int64_t per = (nchunk + cpt - 1) / cpt;
@@ -819,12 +823,15 @@ moe_status launch_combine(const void *y, int64_t y_rows, int64_t H, const int32_
 {
     const bool vec = H % 8 == 0 && aligned16(out) && (y_rows == 0 || aligned16(y)) && (!bias || aligned16(bias));
     const int64_t nchunk = vec ? H / 8 : H;
+    // per-token kernel, bf16 rows, at most kBatch slots: a workgroup of one thread per two chunks
+    const bool two = vec && !kSplit<Y, O> && K <= kBatch;
     const dim3 grid(static_cast<unsigned>(T)),
-        block(vec && kSplit<Y, O> ? split_threads(H) : block_threads(nchunk, 1));
+        block(vec && kSplit<Y, O> ? split_threads(H) : block_threads(nchunk, two ? 2 : 1));
     if constexpr (!kSplit<Y, O>) {
         const int64_t stage = static_cast<int64_t>(kCombineBatch) * H * 2;
         if (vec && K > kFewTerms && K <= kBatch && stage <= kStageBudget && ceil_div(T, kCombineBatch) >= kBatchMinGroups) {
-            hipLaunchKernelGGL(combine_batched_kernel, dim3(static_cast<unsigned>(ceil_div(T, kCombineBatch))), block,
+            hipLaunchKernelGGL(combine_batched_kernel, dim3(static_cast<unsigned>(ceil_div(T, kCombineBatch))),
+                               dim3(block_threads(nchunk, 1)),
                                static_cast<size_t>(stage), stream, static_cast<const uint16_t *>(y), y_rows, H, row_of,
                                w, K, T, static_cast<uint16_t *>(out), static_cast<const uint16_t *>(bias));
             return launch_status();
