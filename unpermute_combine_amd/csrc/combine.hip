@@ -380,9 +380,11 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const Y *__restric
 // time (the 16-byte loads of both tokens' rows in flight together), the bf16 results wait in LDS,
 // and the workgroup writes its tokens' rows in one burst at the end. Reads and writes then reach
 // HBM in longer runs: at T16384 H7168 K8 the combine took 352 us instead of 365 us (without its
-// stores it reads in 287 us -- the interleaved writes are what costs). It needs enough
-// workgroups to fill the chip: with T8192 (drop-and-pad, H4096, ~2.8 terms per token) it was
-// slower, 65 us against 55 us, so it is used from kBatchMinGroups workgroups (8 per CU) up.
+// stores it reads in 287 us -- the interleaved writes are what costs). A workgroup has one thread
+// per two chunks, each thread taking its two chunks one after the other: 345 us against 355 us
+// with one thread per chunk and 432 us with one per four. It needs enough workgroups to fill the
+// chip: with T8192 (drop-and-pad, H4096, ~2.8 terms per token) it was slower, 65 us against
+// 55 us, so it is used from kBatchMinGroups workgroups (8 per CU) up.
 constexpr int kCombineBatch = 8;
 constexpr int64_t kStageBudget = 128 * 1024;  // LDS bytes of staged output rows per workgroup
 constexpr int64_t kBatchMinGroups = 2048;
@@ -811,10 +813,12 @@ int block_threads(int64_t nchunk, int cpt)
     return static_cast<int>(waves * kWave);
 }
 
-// Threads per workgroup of the split layout: one wavefront per 512-element unit, at most 1024.
+// Threads per workgroup of the split layout: one wavefront per two 512-element units (taken one
+// after the other), at most 1024. Measured at T8192 H7168 (32 groups of 8): pre-combine 288 us
+// against 298 us with one wavefront per unit and 303 us with one per four.
 int split_threads(int64_t H)
 {
-    return static_cast<int>(std::min<int64_t>(kMaxThreads / kWave, ceil_div(H, kUnit)) * kWave);
+    return static_cast<int>(std::min<int64_t>(kMaxThreads / kWave, ceil_div(ceil_div(H, kUnit), 2)) * kWave);
 }
 
 template <typename Y, typename O>
@@ -831,7 +835,7 @@ moe_status launch_combine(const void *y, int64_t y_rows, int64_t H, const int32_
         const int64_t stage = static_cast<int64_t>(kCombineBatch) * H * 2;
         if (vec && K > kFewTerms && K <= kBatch && stage <= kStageBudget && ceil_div(T, kCombineBatch) >= kBatchMinGroups) {
             hipLaunchKernelGGL(combine_batched_kernel, dim3(static_cast<unsigned>(ceil_div(T, kCombineBatch))),
-                               dim3(block_threads(nchunk, 1)),
+                               dim3(block_threads(nchunk, 2)),
                                static_cast<size_t>(stage), stream, static_cast<const uint16_t *>(y), y_rows, H, row_of,
                                w, K, T, static_cast<uint16_t *>(out), static_cast<const uint16_t *>(bias));
             return launch_status();
@@ -871,7 +875,9 @@ moe_status launch_combine_backward(const void *dout, const void *y, int64_t y_ro
     constexpr bool split = sizeof(D) == 4 || sizeof(Y) == 4 || sizeof(DY) == 4;
     const bool vec = H % 8 == 0 && (T == 0 || aligned16(dout)) && (y_rows == 0 || aligned16(dy)) &&
                      (!dw || y_rows == 0 || aligned16(y));
-    const int threads = vec ? (split ? split_threads(H) : block_threads(H / 8, 1)) : block_threads(H, 1);
+    // bf16 rows, at most kBatch slots: one thread per two chunks (taken one after the other);
+    // measured 217 -> 190 us (drop-and-pad T8192 H4096 E128), 713 -> 700 us (T16384 H7168 K8)
+    const int threads = vec ? (split ? split_threads(H) : block_threads(H / 8, K <= kBatch ? 2 : 1)) : block_threads(H, 1);
     const int64_t zero_blocks = src_row ? ceil_div(ceil_div(y_rows, kBwdZeroRowsPerWave), threads / kWave) : 0;
     const int64_t blocks = T + zero_blocks;
     if (blocks > 0x7fffffff)
