@@ -103,6 +103,10 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
 // unpadded case ~1%).
 constexpr int kScatterThreads = 256;
 constexpr int kScatterWaves = kScatterThreads / kWave;
+// 16-byte vectors of a source row per lane of a scatter wavefront: at T16384 H7168 K8 bf16 one
+// (1 KiB per wavefront) took 342 us, two 348 us and four 355 us; 128- or 512-thread workgroups
+// changed nothing at that size and lost at drop-and-pad T8192 H4096 E128 (128: 134 against 125 us)
+constexpr int kScatterVecs = 1;
 constexpr int kZeroRowsPerWave = 16;
 constexpr int kZeroRowsPerWaveFirst = 8;
 constexpr int kMaxScatterDests = MOE_MAX_EXPERTS;  // dst_of columns (e.g. one per expert group)
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
-    const int64_t wpr = (nvec + kWave - 1) / kWave;  // waves per source row
+    const int64_t wpr = (nvec + kWave * kScatterVecs - 1) / (kWave * kScatterVecs);  // waves per source row
     const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterWaves +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = src_rows * wpr;
@@ -151,8 +155,8 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     const int64_t t = cw / wpr;
     if (t >= src_rows)
         return;
-    const int64_t v = (cw - t * wpr) * kWave + lane;  // this lane's vector of the row
-    u32x4 r{0u, 0u, 0u, 0u};
+    const int64_t v0 = (cw - t * wpr) * kWave * kScatterVecs + lane;  // this lane's first vector of the row
+    u32x4 r[kScatterVecs];
     bool loaded = false;                           // wave-uniform
     for (int j0 = 0; j0 < J; j0 += kWave) {        // the destinations, 64 entries at a time
         const int32_t my = j0 + lane < J ? dst_of[t * J + j0 + lane] : -1;
@@ -160,8 +164,13 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
         if (m == 0)
             continue;
         if (!loaded) {
-            if (v < nvec)
-                r = ld16(src + t * row_bytes + v * 16);
+#pragma unroll
+            for (int i = 0; i < kScatterVecs; ++i) {
+                const int64_t v = v0 + i * kWave;
+                r[i] = u32x4{0u, 0u, 0u, 0u};
+                if (v < nvec)
+                    r[i] = ld16(src + t * row_bytes + v * 16);
+            }
             loaded = true;
         }
         while (m) {
@@ -169,8 +178,12 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
             m &= m - 1;
             const __amdgpu_buffer_rsrc_t q = make_rsrc(
                 dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * row_bytes, static_cast<uint32_t>(row_bytes));
-            if (v < nvec)
-                st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r);
+#pragma unroll
+            for (int i = 0; i < kScatterVecs; ++i) {
+                const int64_t v = v0 + i * kWave;
+                if (v < nvec)
+                    st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r[i]);
+            }
         }
     }
 }
@@ -219,15 +232,19 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_elem_kernel(
 // would wait for it), then stored to every destination of the group that names them. Waves past
 // the last group write the zero rows, as in the source-major form.
 constexpr int kGroupLoads = 4;
+// workgroups of the grouped gather: 2 wavefronts (at T8192 H7168 with 32 groups of 8: 241 us
+// against 245 us with 4)
+constexpr int kGroupedThreads = 128;
+constexpr int kGroupedWaves = kGroupedThreads / kWave;
 
-__global__ __launch_bounds__(kScatterThreads) void permute_grouped_vec16_kernel(
+__global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
     const int32_t *__restrict__ dst_of, int64_t M, int J, int64_t N, char *__restrict__ dst)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
     const int64_t wpr = (nvec + kWave - 1) / kWave;
-    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterWaves +
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kGroupedWaves +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = M * wpr;
     if (gw >= copy_waves) {
@@ -340,7 +357,7 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
         const int64_t nvec = row_bytes / 16;
         const bool zero_first = src_row && N > src_rows * J;  // padding rows are certain
         const int64_t zwaves = src_row ? ceil_div(N, zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave) : 0;
-        const int64_t waves = src_rows * ceil_div(nvec, kWave) + zwaves;
+        const int64_t waves = src_rows * ceil_div(nvec, static_cast<int64_t>(kWave) * kScatterVecs) + zwaves;
         const int64_t blocks = ceil_div(waves, kScatterWaves);
         if (blocks > 0x7fffffff)
             return MOE_ERR_UNSUPPORTED;
@@ -424,10 +441,10 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
     const int64_t zero_waves = ceil_div(N, kZeroRowsPerWave);
     if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
         const int64_t nvec = row_bytes / 16;
-        const int64_t blocks = ceil_div(M * ceil_div(nvec, kWave) + zero_waves, kScatterWaves);
+        const int64_t blocks = ceil_div(M * ceil_div(nvec, kWave) + zero_waves, kGroupedWaves);
         if (blocks > 0x7fffffff)
             return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(permute_grouped_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0,
+        hipLaunchKernelGGL(permute_grouped_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kGroupedThreads), 0,
                            stream, static_cast<const char *>(src), src_rows, nvec, src_row, dst_of, M, J, N,
                            static_cast<char *>(dst));
         return launch_status();
