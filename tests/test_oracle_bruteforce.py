@@ -99,6 +99,38 @@ def test_index_matches_tuple_sort(case, weighted):
     assert np.array_equal(ix["permuted_probs"], bf["permuted_probs"])
 
 
+@st.composite
+def repeated_routing(draw, max_t=10, max_e=6, max_k=5):
+    """Rows whose expert ids may repeat (drawn with replacement) or be missing."""
+    E = draw(st.integers(1, max_e))
+    K = draw(st.integers(1, min(max_k, E)))  # K <= E, as the calls require; ids may still repeat
+    T = draw(st.integers(0, max_t))
+    ids = np.asarray([[draw(st.integers(-1, E - 1)) for _ in range(K)] for _ in range(T)], np.int32).reshape(T, K)
+    return ids, E
+
+
+@settings(max_examples=300, deadline=None)
+@given(repeated_routing(), st.sampled_from([0, 1, 2, 3]), st.sampled_from([0, 2, 4]), st.sampled_from([0, 1, 2]))
+def test_repeated_experts_are_ordered_by_slot(case, cap, align, gs):
+    """An expert named twice in one row (outside the pages' routing map, which cannot say it)
+    gets one row per slot, in slot order: the index equals the sort of (expert, token, slot)."""
+    ids, E = case
+    if gs and E % gs:
+        gs = 1
+    if cap:
+        align = gs = 0
+    w = np.random.default_rng(ids.size + 7).random(ids.shape).astype(np.float32)
+    ix = oracle.build_index(ids, w, E, capacity=cap, group_size=gs, alignment=align)
+    bf = brute_index(ids, E, cap=cap, gs=gs, w=w, align=align)
+    assert ix["counts"].tolist() == bf["counts"]
+    assert ix["sorted_indices"].tolist() == bf["sorted_indices"]
+    assert ix["row_of"].tolist() == bf["row_of"]
+    assert np.array_equal(ix["permuted_probs"], bf["permuted_probs"])
+    if gs:
+        assert ix["gsrc"].tolist() == bf["gsrc"] and ix["slot_of"].tolist() == bf["slot_of"]
+        assert ix["esrc"].tolist() == bf["esrc"]
+
+
 @settings(max_examples=200, deadline=None)
 @given(routing(), st.integers(1, 5))
 def test_drop_and_pad_matches_tuple_sort(case, cap):

@@ -133,6 +133,23 @@ def test_build_index_standard(m, T, E, K, weighted):
     check_index(m, ids, w, E)
 
 
+@pytest.mark.parametrize("mode", ["standard", "drop", "group", "aligned"])
+def test_build_index_repeated_experts(m, mode):
+    """Rows that name an expert more than once (drawn with replacement, some slots -1): one row
+    per slot in slot order, as the oracle's (expert, token, slot) order gives -- across tiles
+    and internal batches (T = 5000, K = 8, E = 16)."""
+    T, E, K = 5000, 16, 8
+    g = np.random.default_rng([41, len(mode)])
+    ids = g.integers(-1, E, size=(T, K)).astype(np.int32)  # with replacement: repeats are common
+    ids[:, 1] = ids[:, 0]  # and every row repeats its first slot's expert
+    w = wl.random_weights(wl.case_key(41, len(mode)), T, K)
+    say(f"build_index repeated experts {mode}")
+    cap = 2000 if mode == "drop" else 0
+    gs = 4 if mode == "group" else 0
+    align = 128 if mode == "aligned" else 0
+    check_index(m, ids, w, E, cap=cap, gs=gs, align=align)
+
+
 def test_build_index_skewed_with_empty_experts(m):
     T, E, K = 3000, 256, 8
     logits = wl.router_logits(wl.case_key(22), T, E, zipf_s=1.2)
