@@ -1,5 +1,5 @@
-"""bench.py's contract on the host: more than one GPU is refused with a message (this build
-measures one GPU); the help text lists the workload options."""
+"""bench.py's contract on the host: more than one GPU is refused with a message (the library
+has no multi-GPU path; the bench measures one GPU); the help text lists the workload options."""
 import os
 import subprocess
 import sys
