@@ -16,7 +16,8 @@
  *   - a top-k slot whose expert id is outside [0, E) (the pages' "no expert", written -1)
  *     routes nowhere; a row index outside the valid range selects nothing (a zero row in a
  *     permute, a skipped term in a combine);
- *   - dtype codes: 0 = float32, 1 = bf16 (raw uint16 bits).
+ *   - dtype codes: 0 = float32, 1 = bf16 (raw uint16 bits); FP8 E4M3 codes are raw bytes (the
+ *     permute copies rows of 1, 2 or 4 bytes per element).
  * Return codes: 0 ok, 1 invalid argument, 2 unsupported combination.
  *
  * Parity status: every function here is pinned by the CPU tests (worked examples printed on
