@@ -62,7 +62,7 @@ def _declare(lib):
     lib.oracle_quantize_fp8.argtypes = [P, i32, i64, i64, i32, P, P]
     lib.oracle_quantize_fp8.restype = ctypes.c_int
     lib.oracle_unpermute_combine.restype = ctypes.c_int
-    lib.oracle_group_precombine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, i32, P, i64, P]
+    lib.oracle_group_precombine.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, i32, P, i64, P, i32]
     lib.oracle_route_topk_grouped.argtypes = [P, i64, i32, i32, i32, i32, P, P]
     lib.oracle_route_topk_grouped.restype = ctypes.c_int
     lib.oracle_combine_backward.argtypes = [P, i32, P, i32, i64, i64, P, P, i64, i32, P, i32, P]
@@ -215,8 +215,9 @@ def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype, bias=None
 
 
 def group_precombine(y: np.ndarray, row_of, w, topk_idx, E: int, group_size: int,
-                     slot_of: np.ndarray, slots_cap: int) -> np.ndarray:
-    """Per-(token, group) weighted partial sums in float32, stored at slot_of[t, g]."""
+                     slot_of: np.ndarray, slots_cap: int, out_dtype=np.float32) -> np.ndarray:
+    """Per-(token, group) weighted partial sums (a float32 chain) stored at slot_of[t, g], as
+    float32 or rounded once to bf16 (out_dtype np.uint16)."""
     y = np.ascontiguousarray(y)
     y_dt = _dt_of(y)
     y_rows, H = y.shape
@@ -225,10 +226,10 @@ def group_precombine(y: np.ndarray, row_of, w, topk_idx, E: int, group_size: int
     topk_idx = _c(topk_idx, np.int32)
     w = None if w is None else _c(w, np.float32)
     slot_of = _c(slot_of, np.int32)
-    partials = np.full((slots_cap, H), np.nan, np.float32)
+    partials = _poisoned((slots_cap, H), out_dtype)
     rc = _load().oracle_group_precombine(_ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
                                          _ptr(topk_idx), T, K, E, group_size, _ptr(slot_of),
-                                         slots_cap, _ptr(partials))
+                                         slots_cap, _ptr(partials), _dt_of(partials))
     _check(rc, "group_precombine")
     return partials
 

@@ -493,15 +493,17 @@ int oracle_unpermute_combine(const void *y, int32_t y_dt, int64_t y_rows, int64_
  * For every (t, g) with s = slot_of[t*G + g] in [0, slots_cap):
  *   partials[s] = sum over k with topk_idx[t,k] in group g (and a valid row) of
  *                 w[t,k] * y[row_of[t,k]]   -- float32, fused multiply-add in slot order,
- * an empty sum being +0. The final sum over groups is the combine above called with
- * y = partials, row_of = slot_of, w = NULL and K = G (groups in ascending order). */
+ * an empty sum being +0, stored as float32 (p_dt 0) or rounded once to bf16 (p_dt 1: the
+ * partials are what crosses the exchange, and [Combine] §3 has DeepEP's combine send BF16).
+ * The final sum over groups is the combine above called with y = partials, row_of = slot_of,
+ * w = NULL and K = G (groups in ascending order). */
 int oracle_group_precombine(const void *y, int32_t y_dt, int64_t y_rows, int64_t H,
                             const int32_t *row_of, const float *w, const int32_t *topk_idx,
                             int64_t T, int32_t K, int32_t E, int32_t group_size,
-                            const int32_t *slot_of, int64_t slots_cap, float *partials)
+                            const int32_t *slot_of, int64_t slots_cap, void *partials, int32_t p_dt)
 {
     if (y_rows < 0 || H < 1 || T < 0 || K < 1 || E < 1 || group_size < 1 ||
-        E % group_size != 0 || (y_dt != 0 && y_dt != 1) || slots_cap < 0 ||
+        E % group_size != 0 || (y_dt != 0 && y_dt != 1) || (p_dt != 0 && p_dt != 1) || slots_cap < 0 ||
         (T > 0 && (!row_of || !topk_idx || !slot_of)) || (slots_cap > 0 && !partials) ||
         (y_rows > 0 && !y))
         return ORC_INVALID;
@@ -521,7 +523,7 @@ int oracle_group_precombine(const void *y, int32_t y_dt, int64_t y_rows, int64_t
                     float wk = w ? w[t * K + k] : 1.0f;
                     acc = fmaf(wk, load_elem(y, y_dt, (int64_t)r * H + h), acc);
                 }
-                partials[(int64_t)s * H + h] = acc;
+                store_elem(partials, p_dt, (int64_t)s * H + h, acc);
             }
         }
     }

@@ -351,6 +351,23 @@ def test_precombine_single_group_equals_flat_combine():
     assert np.array_equal(final, oracle.unpermute_combine(y, ix["row_of"], w, np.uint16))
 
 
+def test_bf16_partials_are_the_float32_partials_rounded_once():
+    """The bf16 partials (the pre-combine's output in a BF16 exchange) are the float32 chain's
+    results rounded to nearest even, element by element -- nothing else changes; ties and values
+    near powers of two are covered by scaling the expert rows with odd multiples."""
+    T, H, E, K, gs = 300, 40, 32, 8, 8
+    logits = wl.router_logits(wl.case_key(13), T, E, zipf_s=1.2)
+    idx, w = oracle.route_topk(logits, K)
+    ix = oracle.build_index(idx, w, E, group_size=gs)
+    y = wl.expert_outputs(wl.case_key(13), T * K, H, "f32")
+    y[::3] *= np.float32(3.0)
+    m = int(ix["n_slots"][0])
+    p32 = oracle.group_precombine(y, ix["row_of"], w, idx, E, gs, ix["slot_of"], m)
+    p16 = oracle.group_precombine(y, ix["row_of"], w, idx, E, gs, ix["slot_of"], m, out_dtype=np.uint16)
+    assert p16.dtype == np.uint16
+    assert np.array_equal(p16, wl.f32_to_bf16_bits(p32))
+
+
 @settings(max_examples=80, deadline=None)
 @given(routing(max_t=6, max_e=8, max_k=4), st.sampled_from([1, 2, 4, 8]), st.integers(1, 4),
        st.data())
