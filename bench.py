@@ -80,6 +80,9 @@ def parse_args():
                    help="round every expert segment up to a multiple of this many rows (padding rows)")
     p.add_argument("--route-groups", type=int, default=0,
                    help="group-limited routing: each token keeps this many of the workload's expert groups")
+    p.add_argument("--bf16-partials", action="store_true",
+                   help="group workloads: the per-group partial sums are rounded once to bf16 (the BF16 "
+                        "exchange) instead of stored as float32")
     p.add_argument("--fp8", action="store_true",
                    help="FP8 dispatch: the permute quantizes x to E4M3 codes with one float32 scale per 128 "
                         "elements and moves codes and scales (the combine stays bf16)")
@@ -102,9 +105,11 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: int, backward: bool = False, symbol: str = None, fp8: bool = False):
+def read_traffic(kernel: str, workload: int, backward: bool = False, symbol: str = None, fp8: bool = False,
+                 bf16_partials: bool = False):
     """HBM bytes per launch from a committed PMC summary; None if absent or stale."""
-    tag = f"workload{workload}" + ("_bwd" if backward else "") + ("_fp8" if fp8 else "")
+    tag = (f"workload{workload}" + ("_bwd" if backward else "") + ("_fp8" if fp8 else "")
+           + ("_bf16p" if bf16_partials else ""))
     path = os.path.join(ROOT, "profiles", f"{symbol or KERNEL_SYMBOLS[kernel]}__{tag}__pmc.txt")
     if not os.path.exists(path):
         return None
@@ -202,7 +207,12 @@ def main():
     if gs and args.fp8:
         gq = torch.empty((T * min(K, G), H), dtype=torch.uint8, device="cuda")
         gsc = torch.empty((T * min(K, G), nb), dtype=torch.float32, device="cuda")
-    part = torch.empty((T * min(K, G), H), dtype=torch.float32, device="cuda") if gs else None
+    if args.bf16_partials and not gs:
+        print("--bf16-partials needs a workload with expert groups (workload 4)", file=sys.stderr, flush=True)
+        sys.exit(2)
+    pb = 2 if args.bf16_partials else 4  # bytes per partial element
+    part = torch.empty((T * min(K, G), H), dtype=torch.bfloat16 if args.bf16_partials else torch.float32,
+                       device="cuda") if gs else None
 
     # the step's calls in order: (kernel name, stage, call)
     rg = args.route_groups
@@ -329,8 +339,8 @@ def main():
                   "route_bwd": T * K * 12 + T * E * 4}
         if gs:
             n = int(ix.n_slots.item())
-            kbytes.update(dispatch_bwd_recv=valid * H * b + 2 * T * K * 4 + n * H * 4,
-                          dispatch_bwd_send=n * H * 4 + T * G * 4 + T * H * b)
+            kbytes.update(dispatch_bwd_recv=valid * H * b + 2 * T * K * 4 + n * H * pb,
+                          dispatch_bwd_send=n * H * pb + T * G * 4 + T * H * b)
         else:
             kbytes.update(dispatch_bwd=valid * H * b + T * K * 4 + T * H * b)
     elif args.fp8 and gs:
@@ -338,8 +348,8 @@ def main():
         kbytes.update(dispatch_send_fp8=routed * H * b + n * 4 + n * (H + nb * 4),
                       dispatch_recv=n * H + rows * 4 + used * H,
                       dispatch_recv_scales=n * nb * 4 + rows * 4 + used * nb * 4,
-                      precombine=valid * H * b + 2 * T * K * 4 + n * H * 4,
-                      final_sum=n * H * 4 + T * G * 4 + T * H * b)
+                      precombine=valid * H * b + 2 * T * K * 4 + n * H * pb,
+                      final_sum=n * H * pb + T * G * 4 + T * H * b)
     elif args.fp8:
         kbytes.update(permute_fp8=routed * H * b + rows * 4 + used * (H + nb * 4),
                       combine=valid * H * b + 2 * T * K * 4 + T * H * b)
@@ -347,8 +357,8 @@ def main():
         n = int(ix.n_slots.item())
         kbytes.update(dispatch_send=routed * H * b + n * 4 + n * H * b,
                       dispatch_recv=n * H * b + rows * 4 + used * H * b,
-                      precombine=valid * H * b + 2 * T * K * 4 + n * H * 4,
-                      final_sum=n * H * 4 + T * G * 4 + T * H * b)
+                      precombine=valid * H * b + 2 * T * K * 4 + n * H * pb,
+                      final_sum=n * H * pb + T * G * 4 + T * H * b)
     else:
         kbytes.update(permute=routed * H * b + rows * 4 + used * H * b,
                       combine=valid * H * b + 2 * T * K * 4 + T * H * b)
@@ -371,7 +381,7 @@ def main():
         symbol = combine_symbol(dt == "bf16", dt == "bf16", K, H, T)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic(dom, cid, args.backward, symbol, args.fp8),
+                "traffic": read_traffic(dom, cid, args.backward, symbol, args.fp8, args.bf16_partials),
                 "kernel": symbol, "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kernel_us[dom], 2)}
 
@@ -380,7 +390,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": c["name"] + (f" align{align}" if align else "") + (f" groups{rg}" if rg else "")
-                   + (" fp8-dispatch" if args.fp8 else ""), "fp8_dispatch": bool(args.fp8),
+                   + (" fp8-dispatch" if args.fp8 else "") + (" bf16-partials" if args.bf16_partials else ""),
+                   "fp8_dispatch": bool(args.fp8), "bf16_partials": bool(args.bf16_partials),
                    "T": T, "H": H, "E": E, "K": K, "capacity": cap, "alignment": align, "route_groups": rg,
                    "group_size": gs, "zipf_s": c["zipf_s"], "seed_key": list(key)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -401,9 +412,11 @@ def main():
         result["cpu_baseline"] = None  # the oracle baseline is timed on the bf16 path
     elif not args.no_cpu_baseline:
         if args.backward:
-            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes)
+            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes,
+                                                           args.bf16_partials)
         else:
-            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes)
+            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes,
+                                                  args.bf16_partials)
     print(json.dumps(result), flush=True)
 
 
@@ -422,7 +435,7 @@ def _passes(run_once, min_seconds=10.0, min_passes=2, max_passes=8):
     return min(times), len(times), sum(times)
 
 
-def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes):
+def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16_partials=False):
     """The CPU oracle as it stands (single thread) over the same whole workload: passes repeated
     until about 10 s of CPU work, the best pass reported."""
     import numpy as np
@@ -431,6 +444,7 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes):
 
     T, E, K, gs = c["T"], c["E"], c["K"], c["group_size"]
     out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
+    part_dt = np.uint16 if bf16_partials else np.float32
 
     def run_once():
         idx, w = _oracle_route(oracle, logits_np, K, gs, rg)
@@ -443,7 +457,7 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes):
         y = xp if y_np is None else y_np
         if gs:
             n = int(ix["n_slots"][0])
-            part = oracle.group_precombine(y, ix["row_of"], w, idx, E, gs, ix["slot_of"], n)
+            part = oracle.group_precombine(y, ix["row_of"], w, idx, E, gs, ix["slot_of"], n, out_dtype=part_dt)
             oracle.unpermute_combine(part, ix["slot_of"], None, out_dt)
         else:
             oracle.unpermute_combine(y, ix["row_of"], w, out_dt)
@@ -456,7 +470,7 @@ def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes):
             "routed_tokens_per_s": round(T * K / best, 1)}
 
 
-def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes):
+def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16_partials=False):
     """The CPU oracle's backward (single thread) on the same saved forward state: passes repeated
     until about 10 s of CPU work, the best pass reported."""
     import numpy as np
@@ -466,6 +480,7 @@ def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, st
 
     T, H, E, K, gs = c["T"], c["H"], c["E"], c["K"], c["group_size"]
     out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
+    part_dt = np.uint16 if bf16_partials else np.float32
     idx, w = _oracle_route(oracle, logits_np, K, gs, rg)
     ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
     rows = len(ix["sorted_indices"])
@@ -477,7 +492,7 @@ def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, st
         _, dw = oracle.combine_backward(dout, y, ix["row_of"], w, out_dt)
         if gs:
             n = int(ix["n_slots"][0])
-            part = oracle.group_precombine(dxp, ix["row_of"], None, idx, E, gs, ix["slot_of"], n)
+            part = oracle.group_precombine(dxp, ix["row_of"], None, idx, E, gs, ix["slot_of"], n, out_dtype=part_dt)
             oracle.unpermute_combine(part, ix["slot_of"], None, out_dt)
         else:
             oracle.unpermute_combine(dxp, ix["row_of"], None, out_dt)

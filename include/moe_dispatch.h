@@ -272,12 +272,14 @@ moe_status moe_unpermute_combine(const void *y, moe_dtype y_dt, int64_t y_rows, 
  * group) that exists); a slot_of numbering every (t, g) gives the dense [T, G, H] layout.
  * Rows of partials not named by slot_of are left untouched.
  *   y [y_rows, H] (y_dt), row_of/topk_idx/w [T, K], slot_of [T, G], partials [slots_cap, H]
- *   float32. w may be NULL (unit weights). */
+ *   of dtype partials_dt: MOE_F32 stores the float32 sums, MOE_BF16 rounds each once to bf16
+ *   (nearest, ties to even) -- the BF16 exchange of [Combine] §3 (DeepEP's combine sends BF16),
+ *   half the bytes; the final sum then reads bf16 partials. w may be NULL (unit weights). */
 moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, int64_t H,
                                 const int32_t *row_of, const float *w, const int32_t *topk_idx,
                                 int64_t T, int32_t K, int32_t E, int32_t group_size,
-                                const int32_t *slot_of, int64_t slots_cap, float *partials,
-                                hipStream_t stream);
+                                const int32_t *slot_of, int64_t slots_cap, void *partials,
+                                moe_dtype partials_dt, hipStream_t stream);
 
 /* Backward of moe_unpermute_combine ([Combine] §4: the combine is linear in the expert outputs,
  * so its backward is the transposed map -- a dispatch of the output gradient back to the expert

@@ -89,8 +89,12 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_unpermute_combine(fake, 1, 4, 8, None, None, None, 2, 2, fake, 1, None) == capi.MOE_ERR_INVALID
     assert lib.moe_unpermute_combine(fake, 2, 4, 8, fake, None, None, 2, 2, fake, 1, None) == \
         capi.MOE_ERR_UNSUPPORTED  # the combine does not take FP8 rows
-    assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 3, fake, 4, fake, None) == \
+    assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 3, fake, 4, fake, 0, None) == \
         capi.MOE_ERR_INVALID
+    assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, 7, None) == \
+        capi.MOE_ERR_INVALID  # partials neither float32 nor bf16
+    assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, 2, None) == \
+        capi.MOE_ERR_UNSUPPORTED  # no FP8 partials
     assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, 2, 65, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_permute_grouped(fake, 4, 8, 1, None, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, None, 2, 2, fake, None) == capi.MOE_ERR_INVALID
@@ -131,7 +135,7 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_permute_grouped(fake, 4, big, 1, fake, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(fake, 1, 4, big // 2, fake, None, None, 2, 2, fake, 0, None) == \
         capi.MOE_ERR_UNSUPPORTED  # float32 output rows of 2 GiB
-    assert lib.moe_group_precombine(fake, 1, 4, big // 2, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, None) == \
+    assert lib.moe_group_precombine(fake, 1, 4, big // 2, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, 0, None) == \
         capi.MOE_ERR_UNSUPPORTED  # float32 partial rows of 2 GiB
     ix = capi.MoeIndexStruct()
     assert lib.moe_build_index(fake, None, 4, 2, 8, 4, 2, 0, ctypes.byref(ix), fake, 1 << 20, None) == \

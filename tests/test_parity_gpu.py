@@ -589,8 +589,9 @@ def test_combine_no_tokens(m):
     (400, 64, 8, 8, 1000, "bf16", True),     # some slots route nowhere (id -1)
     (150, 64, 16, 4, 1000, "bf16", True)])
 @pytest.mark.parametrize("layout", ["compact", "dense"])
-def test_group_precombine_and_final_sum(m, T, E, K, gs, H, ydt, holes, layout):
-    say(f"precombine T={T} E={E} K={K} gs={gs} H={H} {ydt} holes={holes} {layout}")
+@pytest.mark.parametrize("pdt", ["f32", "bf16"])
+def test_group_precombine_and_final_sum(m, T, E, K, gs, H, ydt, holes, layout, pdt):
+    say(f"precombine T={T} E={E} K={K} gs={gs} H={H} {ydt} holes={holes} {layout} partials={pdt}")
     key = wl.case_key(27, T, E, K, gs, H)
     logits = wl.router_logits(key, T, E, zipf_s=1.2)
     idx, w = oracle.route_topk(logits, K)
@@ -605,9 +606,10 @@ def test_group_precombine_and_final_sum(m, T, E, K, gs, H, ydt, holes, layout):
         slot_of = np.arange(T * G, dtype=np.int32).reshape(T, G)
         cap = T * G
     y = wl.expert_outputs(key, T * K, H, ydt)
-    want_p = oracle.group_precombine(y, want_ix["row_of"], w, idx, E, gs, slot_of, cap)
+    want_p = oracle.group_precombine(y, want_ix["row_of"], w, idx, E, gs, slot_of, cap,
+                                     out_dtype=np.uint16 if pdt == "bf16" else np.float32)
     got_p = host(m.group_precombine(dev(y), dev(want_ix["row_of"]), dev(w), dev(idx), E, gs, dev(slot_of),
-                                    slots_cap=cap))
+                                    slots_cap=cap, out_dtype=torch.bfloat16 if pdt == "bf16" else torch.float32))
     assert_combined(got_p, want_p, "partials")
     assert exact_fraction(got_p, want_p) == 1.0
     want_o = oracle.unpermute_combine(want_p, slot_of, None, np.uint16)
@@ -651,7 +653,7 @@ def check_fp8_dispatch(m, x, ix, want, gs, T, K, E, block=128):
     del xd
 
 
-def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False):
+def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False, bf16_partials=False):
     """Runs route -> index -> permute -> (pre-)combine on the GPU and checks every stage
     (align > 1: the expert-aligned layout; route_groups > 0: group-limited routing over the
     workload's expert groups, that many groups per token)."""
@@ -719,13 +721,15 @@ def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False):
     tsd = torch.from_numpy(ts).to(DEV)
     if gs > 0:
         n = int(host(ix.n_slots)[0])
-        part = m.group_precombine(yd, ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=n)
+        part = m.group_precombine(yd, ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=n,
+                                  out_dtype=torch.bfloat16 if bf16_partials else torch.float32)
         out = m.unpermute_combine(part, ix.slot_of, None, out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
         slot_rows = want["slot_of"][ts]
         want_p = oracle.group_precombine(y_np, want["row_of"][ts], w_np[ts], want_i[ts], E, gs,
                                          np.where(slot_rows >= 0, np.arange(slot_rows.size).reshape(slot_rows.shape),
-                                                  -1).astype(np.int32), slot_rows.size)
+                                                  -1).astype(np.int32), slot_rows.size,
+                                         out_dtype=np.uint16 if bf16_partials else np.float32)
         got_p = host(part[torch.from_numpy(np.maximum(slot_rows.reshape(-1), 0)).to(DEV)])
         present = slot_rows.reshape(-1) >= 0
         assert_combined(got_p[present], want_p[present], "partials (sample)")
@@ -753,6 +757,13 @@ def test_workload_full_size(m, cfg_id):
 @pytest.mark.parametrize("cfg_id", [3, 4, 5])
 def test_workload_fp8_dispatch(m, cfg_id):
     run_workload(m, cfg_id, fp8=True)
+    torch.cuda.empty_cache()
+
+
+def test_workload_bf16_partials(m):
+    """Workload 4 with the per-group partials rounded to bf16 (the BF16 exchange), as bench.py
+    --bf16-partials launches it: sampled partials and combined rows against the oracle."""
+    run_workload(m, 4, bf16_partials=True)
     torch.cuda.empty_cache()
 
 

@@ -41,7 +41,7 @@ SIGNATURES = {
     "moe_unpermute_combine": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _P, _P, _P, _i64, _i32, _P,
                                              ctypes.c_int, _P]),
     "moe_group_precombine": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _P, _P, _P, _i64, _i32, _i32,
-                                            _i32, _P, _i64, _P, _P]),
+                                            _i32, _P, _i64, _P, ctypes.c_int, _P]),
 }
 
 

@@ -468,14 +468,14 @@ __global__ __launch_bounds__(kMaxThreads) void combine_batched_kernel(const uint
 }
 
 // ---------------------------------------------------------------- group pre-combine
-template <typename Y, bool VEC>
+template <typename Y, typename P, bool VEC>
 __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
                                                          const int32_t *__restrict__ row_of,
                                                          const float *__restrict__ w,
                                                          const int32_t *__restrict__ topk_idx, int K,
                                                          int E, int gs, int G,
                                                          const int32_t *__restrict__ slot_of,
-                                                         int64_t slots_cap, float *__restrict__ partials)
+                                                         int64_t slots_cap, P *__restrict__ partials)
 {
     __shared__ int32_t grp[MOE_MAX_TOPK];   // group of slot k, -1 if it adds nothing
     __shared__ int32_t rows[MOE_MAX_TOPK];
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
                     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                     fma_parts<Y>(q, wv, take, acc);
                     const int32_t s = __builtin_amdgcn_readfirstlane(item_s[it]);
-                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * 4)), e0,
+                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * sizeof(P))), e0,
                                 acc, partials);
                 }
             }
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
                         fma_batch_split<Y>(y, H, row, w, e0, acc);
                     }
                     const int32_t s = __builtin_amdgcn_readfirstlane(item_s[it]);
-                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * 4)), e0,
+                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * sizeof(P))), e0,
                                 acc, partials);
                 }
             }
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
     } else {
         for (int it = 0; it < n_items; ++it) {
             const int g = item_g[it];
-            float *o = partials + static_cast<int64_t>(item_s[it]) * H;
+            P *o = partials + static_cast<int64_t>(item_s[it]) * H;
             for (int64_t h = tid; h < H; h += blockDim.x) {
                 float acc = 0.0f;
                 for (int k = 0; k < K; ++k) {
@@ -850,20 +850,20 @@ moe_status launch_combine(const void *y, int64_t y_rows, int64_t H, const int32_
     return launch_status();
 }
 
-template <typename Y>
+template <typename Y, typename P>
 moe_status launch_precombine(const void *y, int64_t y_rows, int64_t H, const int32_t *row_of, const float *w,
                              const int32_t *topk_idx, int64_t T, int K, int E, int gs,
-                             const int32_t *slot_of, int64_t slots_cap, float *partials, hipStream_t stream)
+                             const int32_t *slot_of, int64_t slots_cap, void *partials, hipStream_t stream)
 {
-    const bool vec = H % 8 == 0 && aligned16(partials) && (y_rows == 0 || aligned16(y));
+    const bool vec = H % 8 == 0 && (slots_cap == 0 || aligned16(partials)) && (y_rows == 0 || aligned16(y));
     const dim3 grid(static_cast<unsigned>(T)), block(vec ? split_threads(H) : block_threads(H, 2));
     const int G = E / gs;
     if (vec)
-        hipLaunchKernelGGL((precombine_kernel<Y, true>), grid, block, 0, stream, static_cast<const Y *>(y),
-                           y_rows, H, row_of, w, topk_idx, K, E, gs, G, slot_of, slots_cap, partials);
+        hipLaunchKernelGGL((precombine_kernel<Y, P, true>), grid, block, 0, stream, static_cast<const Y *>(y),
+                           y_rows, H, row_of, w, topk_idx, K, E, gs, G, slot_of, slots_cap, static_cast<P *>(partials));
     else
-        hipLaunchKernelGGL((precombine_kernel<Y, false>), grid, block, 0, stream, static_cast<const Y *>(y),
-                           y_rows, H, row_of, w, topk_idx, K, E, gs, G, slot_of, slots_cap, partials);
+        hipLaunchKernelGGL((precombine_kernel<Y, P, false>), grid, block, 0, stream, static_cast<const Y *>(y),
+                           y_rows, H, row_of, w, topk_idx, K, E, gs, G, slot_of, slots_cap, static_cast<P *>(partials));
     return launch_status();
 }
 
@@ -941,14 +941,14 @@ extern "C" moe_status moe_unpermute_combine(const void *y, moe_dtype y_dt, int64
 extern "C" moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_t y_rows, int64_t H,
                                            const int32_t *row_of, const float *w, const int32_t *topk_idx,
                                            int64_t T, int32_t K, int32_t E, int32_t group_size,
-                                           const int32_t *slot_of, int64_t slots_cap, float *partials,
-                                           hipStream_t stream)
+                                           const int32_t *slot_of, int64_t slots_cap, void *partials,
+                                           moe_dtype partials_dt, hipStream_t stream)
 {
     using namespace moe;
-    if (y_dt == MOE_FP8_E4M3)
+    if (y_dt == MOE_FP8_E4M3 || partials_dt == MOE_FP8_E4M3)
         return MOE_ERR_UNSUPPORTED;
     if (y_rows < 0 || H < 1 || T < 0 || K < 1 || E < 1 || group_size < 1 || E % group_size != 0 ||
-        slots_cap < 0 || (y_dt != MOE_F32 && y_dt != MOE_BF16))
+        slots_cap < 0 || (y_dt != MOE_F32 && y_dt != MOE_BF16) || (partials_dt != MOE_F32 && partials_dt != MOE_BF16))
         return MOE_ERR_INVALID;
     if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
         return MOE_ERR_UNSUPPORTED;
@@ -959,10 +959,16 @@ extern "C" moe_status moe_group_precombine(const void *y, moe_dtype y_dt, int64_
     if (T > 0x7fffffff || H * 4 > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
     if (y_dt == MOE_BF16)
-        return launch_precombine<uint16_t>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size, slot_of,
-                                           slots_cap, partials, stream);
-    return launch_precombine<float>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size, slot_of, slots_cap,
-                                    partials, stream);
+        return partials_dt == MOE_BF16
+                   ? launch_precombine<uint16_t, uint16_t>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size,
+                                                           slot_of, slots_cap, partials, stream)
+                   : launch_precombine<uint16_t, float>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size,
+                                                        slot_of, slots_cap, partials, stream);
+    return partials_dt == MOE_BF16
+               ? launch_precombine<float, uint16_t>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size, slot_of,
+                                                    slots_cap, partials, stream)
+               : launch_precombine<float, float>(y, y_rows, H, row_of, w, topk_idx, T, K, E, group_size, slot_of,
+                                                 slots_cap, partials, stream);
 }
 
 extern "C" moe_status moe_unpermute_combine_backward(const void *dout, moe_dtype dout_dt, const void *y, moe_dtype y_dt,

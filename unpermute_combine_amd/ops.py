@@ -331,8 +331,10 @@ def unpermute_combine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[t
 
 def group_precombine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[torch.Tensor],
                      topk_idx: torch.Tensor, num_experts: int, group_size: int, slot_of: torch.Tensor,
-                     slots_cap: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-(token, group) weighted partial sums (float32) stored at row slot_of[t, g]."""
+                     slots_cap: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Per-(token, group) weighted partial sums (a float32 chain) stored at row slot_of[t, g], as
+    float32 or, with out_dtype (or out) bfloat16, rounded once to bf16."""
     _need(y, "y", None, 2)
     y_dt = _hidden_dt(y, "y")
     _need(row_of, "row_of", torch.int32, 2)
@@ -353,13 +355,17 @@ def group_precombine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[to
     if out is None:
         if slots_cap is None:
             raise ValueError("give slots_cap or out")
-        out = torch.empty((slots_cap, H), dtype=torch.float32, device=y.device)
-    _need(out, "out", torch.float32, 2)
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("partials are float32 or bfloat16")
+        out = torch.empty((slots_cap, H), dtype=out_dtype, device=y.device)
+    _need(out, "out", None, 2)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("partials are float32 or bfloat16")
     if out.shape[1] != H:
         raise ValueError(f"out rows must have {H} elements")
     check("moe_group_precombine", lib().moe_group_precombine(
         _p(y), y_dt, y.shape[0], H, _p(row_of), _p(weights), _p(topk_idx), T, K, num_experts, group_size,
-        _p(slot_of), out.shape[0], _p(out), _stream()))
+        _p(slot_of), out.shape[0], _p(out), _DT[out.dtype], _stream()))
     return out
 
 
