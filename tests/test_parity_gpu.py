@@ -784,7 +784,7 @@ def test_workload_aligned(m, cfg_id, align):
 
 @pytest.mark.parametrize("cfg_id,mode", [(2, "standard"), (5, "drop"), (4, "group"), (2, "aligned"),
                                          (4, "route_groups"), (2, "fp8"), (4, "fp8"), (2, "backward"),
-                                         (4, "backward")])
+                                         (4, "backward"), (4, "bf16_partials")])
 def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
     """A whole step (route, index, permute, combine; or its backward) captured once in a HIP
     graph and replayed three times, with eager work (the outputs cleared by a fill kernel) and
@@ -818,7 +818,8 @@ def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
     else:
         outs["xp"] = torch.empty((rows, H), dtype=tdt, device=DEV)
     gbuf = torch.empty((slots, H), dtype=tdt, device=DEV) if gs else None
-    part = torch.empty((slots, H), dtype=torch.float32, device=DEV) if gs else None
+    part = torch.empty((slots, H), dtype=torch.bfloat16 if mode == "bf16_partials" else torch.float32,
+                       device=DEV) if gs else None
     if mode == "backward":
         dout = dev(wl.expert_outputs((*key, 7), T, H, dt))
         dxp = dev(wl.expert_outputs((*key, 8), rows, H, dt))
@@ -916,7 +917,9 @@ def _random_config(i):
         align = int(g.choice([2, 8, 16, 128]))
     ties = g.random() < 0.3
     zipf = 1.2 if g.random() < 0.5 else None
-    return dict(mode=mode, T=T, E=E, K=K, H=H, dtype=dtype, cap=cap, gs=gs, align=align, M=M, ties=ties, zipf=zipf)
+    pdt = "bf16" if mode == "group" and i % 8 == 6 else "f32"  # partials of the group pre-combine
+    return dict(mode=mode, T=T, E=E, K=K, H=H, dtype=dtype, cap=cap, gs=gs, align=align, M=M, ties=ties, zipf=zipf,
+                pdt=pdt)
 
 
 @pytest.mark.parametrize("i", range(40))
@@ -952,9 +955,12 @@ def test_random_configuration(m, i):
         slots = T * min(K, E // gs)
         gbuf = m.permute_scatter(dev(x), ix.slot_of, slots)
         xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of)
-        part = m.group_precombine(dev(y), ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=slots)
+        p16 = c["pdt"] == "bf16"
+        part = m.group_precombine(dev(y), ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=slots,
+                                  out_dtype=torch.bfloat16 if p16 else torch.float32)
         out = m.unpermute_combine(part, ix.slot_of, None, out_dtype=out_dtype)
-        want_p = oracle.group_precombine(y, want["row_of"], w, want_i, E, gs, want["slot_of"], slots)
+        want_p = oracle.group_precombine(y, want["row_of"], w, want_i, E, gs, want["slot_of"], slots,
+                                         out_dtype=np.uint16 if p16 else np.float32)
         want_o = oracle.unpermute_combine(want_p[:n], want["slot_of"], None, np.uint16 if dt == "bf16" else np.float32)
         assert_combined(host(part)[:n], want_p[:n], "partials")
     else:
