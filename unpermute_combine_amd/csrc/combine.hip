@@ -802,7 +802,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_backward_scalar_kernel(
 
 // Threads per workgroup: one per `cpt` 8-element chunks, whole wavefronts, at most 1024.
 // Measured on MI355X (bf16 per-token combine): with at most 8 slots per token a workgroup of one
-// thread per two chunks is faster for every mix of terms -- T8192 H7168 with 8 terms 178 vs 185
+// thread per two chunks is faster for every mix of terms (for more slots, see launch_combine) -- T8192 H7168 with 8 terms 178 vs 185
 // us, 6 terms (T4096) 70 vs 78 us, drop-and-pad T8192 H4096 E128 48 vs 56 us, K = 2 (T4096
 // H4096) 24 vs 27 us; loading both chunks of a many-term token together instead of one after
 // the other raised the registers to 112 (occupancy 4) and lost on the few-term tokens.
@@ -827,8 +827,10 @@ moe_status launch_combine(const void *y, int64_t y_rows, int64_t H, const int32_
 {
     const bool vec = H % 8 == 0 && aligned16(out) && (y_rows == 0 || aligned16(y)) && (!bias || aligned16(bias));
     const int64_t nchunk = vec ? H / 8 : H;
-    // per-token kernel, bf16 rows, at most kBatch slots: a workgroup of one thread per two chunks
-    const bool two = vec && !kSplit<Y, O> && K <= kBatch;
+    // per-token kernel, bf16 rows: a workgroup of one thread per two chunks. For K > 8 this
+    // favours sparse rows (the group final sum over bf16 partials, K = 32 with ~3 terms: 86 ->
+    // 76 us) over dense ones (T4096 H4096 K = 32, every slot valid: 182 -> 191 us).
+    const bool two = vec && !kSplit<Y, O>;
     const dim3 grid(static_cast<unsigned>(T)),
         block(vec && kSplit<Y, O> ? split_threads(H) : block_threads(nchunk, two ? 2 : 1));
     if constexpr (!kSplit<Y, O>) {
