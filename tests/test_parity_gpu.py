@@ -228,7 +228,7 @@ def test_build_index_aligned(m, T, E, K, align, gs):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("H", [1, 3, 8, 64, 1000, 7168, 4095])
+@pytest.mark.parametrize("H", [1, 3, 8, 64, 1000, 7168, 4095, 65536])
 def test_permute(m, dtype, H):
     say(f"permute {dtype} H={H}")
     key = wl.case_key(25, H)
@@ -258,7 +258,8 @@ def test_permute_empty_source_gives_zero_rows(m):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("H,T,E,K,mode", [(7168, 600, 64, 8, "standard"), (1000, 300, 16, 4, "drop"),
                                           (3, 257, 8, 2, "standard"), (4096, 513, 32, 8, "drop"),
-                                          (64, 100, 8, 2, "missing"), (24, 90, 12, 6, "group")])
+                                          (64, 100, 8, 2, "missing"), (24, 90, 12, 6, "group"),
+                                          (65536, 40, 8, 4, "standard")])
 def test_permute_scatter_matches_gather(m, dtype, H, T, E, K, mode):
     """Source-major permute with the index's inverse maps equals the pages' gather, bit for bit."""
     say(f"permute_scatter {dtype} H={H} T={T} E={E} K={K} {mode}")
@@ -521,7 +522,8 @@ def test_unpermute_combine_bias(m, ydt, odt, H, K, T):
 
 @pytest.mark.parametrize("ydt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
 @pytest.mark.parametrize("H,K,T", [(1, 1, 10), (5, 2, 33), (512, 2, 1024), (7168, 8, 130), (1000, 8, 77),
-                                   (64, 32, 200), (24, 256, 40), (16, 1024, 6)])
+                                   (64, 32, 200), (24, 256, 40), (16, 1024, 6),
+                                   (65536, 8, 24), (32776, 3, 20)])  # long rows: > 1024 threads' worth
 @pytest.mark.parametrize("weighted", [True, False])
 def test_unpermute_combine(m, ydt, odt, H, K, T, weighted):
     say(f"combine y={ydt} out={odt} H={H} K={K} T={T} weighted={weighted}")
