@@ -45,17 +45,6 @@ __device__ __forceinline__ void st16(void *p, const u32x4 &v)
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-__device__ __forceinline__ u32x4 ld16_stream(const void *p)
-{
-    u32x4 v;
-    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-    v.x = __builtin_nontemporal_load(q + 0);
-    v.y = __builtin_nontemporal_load(q + 1);
-    v.z = __builtin_nontemporal_load(q + 2);
-    v.w = __builtin_nontemporal_load(q + 3);
-    return v;
-}
-
 __device__ __forceinline__ void st16_stream(void *p, const u32x4 &v)
 {
     uint32_t *q = reinterpret_cast<uint32_t *>(p);
