@@ -388,7 +388,7 @@ def main():
     result = {
         "metric": METRIC_BACKWARD if args.backward else METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "accum_dtype": "f32", "data": "synthetic",
         "config": {"workload": c["name"] + (f" align{align}" if align else "") + (f" groups{rg}" if rg else "")
                    + (" fp8-dispatch" if args.fp8 else "") + (" bf16-partials" if args.bf16_partials else ""),
                    "fp8_dispatch": bool(args.fp8), "bf16_partials": bool(args.bf16_partials),
