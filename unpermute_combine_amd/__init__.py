@@ -1,8 +1,10 @@
 """MI355X (gfx950) MoE token dispatch / unpermute-combine.
 
-Top-k routing with a softmax over the selected logits, the expert histogram with its running
-sum (group_list), the stable expert-major permute, the weighted unpermute-combine and the
-per-group local pre-combine, as hand-written HIP kernels behind a C ABI
+Top-k routing with a softmax over the selected logits (optionally group-limited), the expert
+histogram with its running sum (group_list), the stable expert-major permute (standard,
+drop-and-pad, expert-aligned, the two-stage group dispatch, an FP8 E4M3 dispatch), the weighted
+unpermute-combine (optional bias) and the per-group local pre-combine, with the backward of the
+combine and of the routing softmax, as hand-written HIP kernels behind a C ABI
 (``include/moe_dispatch.h``, ``libmoe_dispatch.so``). This package is the torch binding.
 """
 from .ops import (MoeIndex, alloc_index, build_index, expert_capacity, group_precombine, index_rows, permute,
