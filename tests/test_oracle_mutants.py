@@ -87,6 +87,11 @@ MUTANTS = [
     ("router gradient drops the mean term", "((double)d_topk_w[t * K + k] - s)", "((double)d_topk_w[t * K + k])"),
     ("router gradient sign flipped", "((double)d_topk_w[t * K + k] - s)", "(s - (double)d_topk_w[t * K + k])"),
     ("router gradient uses slot 0's weight", "acc[e] += (double)topk_w[t * K + k] *", "acc[e] += (double)topk_w[t * K] *"),
+    ("bf16 partials stored without rounding", "store_elem(partials, p_dt, (int64_t)s * H + h, acc);",
+     "store_elem(partials, p_dt, (int64_t)s * H + h, p_dt ? truncf(acc * 256.0f) / 256.0f : acc);"),
+    ("repeated experts take the later slot first",
+     "        for (int64_t t = 0; t < T; ++t) {\n            for (int32_t k = 0; k < K; ++k) {\n                if (topk_idx[t * K + k] != e)",
+     "        for (int64_t t = 0; t < T; ++t) {\n            for (int32_t k = K - 1; k >= 0; --k) {\n                if (topk_idx[t * K + k] != e)"),
 ]
 
 
@@ -136,6 +141,8 @@ def _pins():
         lambda: f8.test_quantize_bounds("bf16", 32),
         f8.test_quantize_blocks_are_independent_and_bf16_is_its_widening,
         f8.test_combine_bias_is_one_final_addition,
+        bf.test_bf16_partials_are_the_float32_partials_rounded_once,
+        _repeated_experts,
     ]
     return checks
 
@@ -188,6 +195,19 @@ def _index_brute_force():
                 assert ix["gsrc"].tolist() == want["gsrc"]
                 assert ix["slot_of"].tolist() == want["slot_of"]
                 assert ix["esrc"].tolist() == want["esrc"]
+
+
+def _repeated_experts():
+    """Rows naming an expert twice (fixed cases): the index equals the (expert, token, slot) sort."""
+    g = np.random.default_rng(17)
+    for T, E, K in ((9, 4, 3), (12, 3, 3), (7, 5, 4)):
+        ids = g.integers(-1, E, size=(T, K)).astype(np.int32)
+        ids[:, 1] = ids[:, 0]
+        w = g.random((T, K)).astype(np.float32)
+        ix = oracle.build_index(ids, w, E)
+        b = bf.brute_index(ids, E, w=w)
+        assert ix["sorted_indices"].tolist() == b["sorted_indices"] and ix["row_of"].tolist() == b["row_of"]
+        assert np.array_equal(ix["permuted_probs"], b["permuted_probs"])
 
 
 def _combine_exact_bound():
