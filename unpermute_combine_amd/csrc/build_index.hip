@@ -14,7 +14,8 @@
 //   1. hist   one workgroup per tile of whole tokens: the tile's expert histogram (and the
 //             group histogram of each token's first slot in a group) with LDS atomics -- only
 //             counts come from atomics, never positions, so the result is deterministic -- and
-//             one coalesced row hist[tile][0..E) per tile.
+//             one coalesced row per tile: the expert counts, then (group mode) the group
+//             counts, so that the rank kernel gets both with one pass of loads.
 //   2. rank   one workgroup per tile. It first adds up the tile counts of all tiles itself
 //             (threads own 4 consecutive keys and a range of tiles, 16 loads in flight each;
 //             the partial sums meet in LDS): every key's total, a block scan of the totals for
@@ -50,11 +51,11 @@ struct IndexArgs {
     int64_t T;
     int32_t K, E, cap, gs, G;
     int32_t align;   // expert alignment (1: none)
-    int32_t Ep, Gp;  // row strides of the histograms (E, G rounded up to a multiple of 4)
+    int32_t Ep, Gp;  // E, G rounded up to a multiple of 4
+    int32_t Hp;      // Ep + Gp (Gp only in group mode): the stride of a tile's row of counts
     int32_t tile_tokens, ntiles;
     int32_t ebits, gbits;
-    int32_t *hist_e;  // [ntiles][Ep] tile counts of the experts
-    int32_t *hist_g;  // [ntiles][Gp] the same for group slots
+    int32_t *hist;    // [ntiles][Hp] tile counts: experts at [0, Ep), group slots at [Ep, Ep + Gp)
     moe_index ix;
 };
 
@@ -112,14 +113,9 @@ __global__ __launch_bounds__(256) void hist_kernel(IndexArgs a)
             a.ix.slot_of[i] = -1;
     }
     __syncthreads();
-    int32_t *row = a.hist_e + static_cast<int64_t>(tile) * a.Ep;
-    for (int e = threadIdx.x; e < a.Ep; e += blockDim.x)
-        row[e] = he[e];
-    if (a.gs > 0) {
-        int32_t *rowg = a.hist_g + static_cast<int64_t>(tile) * a.Gp;
-        for (int g = threadIdx.x; g < a.Gp; g += blockDim.x)
-            rowg[g] = hg[g];
-    }
+    int32_t *row = a.hist + static_cast<int64_t>(tile) * a.Hp;  // expert and group counts, one row
+    for (int i = threadIdx.x; i < a.Hp; i += blockDim.x)
+        row[i] = sh[i];
 }
 
 // ---------------------------------------------------------------- no tokens
@@ -321,12 +317,12 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     int32_t *cnt_e = sh;                        // [kRankWaves][E] counts -> next row of the wave
     int32_t *cnt_g = cnt_e + kRankWaves * a.E;  // [kRankWaves][G]
     int32_t *seg_e = cnt_g + kRankWaves * a.G;  // [E] first row of each expert
-    int32_t *tot_e = seg_e + a.E;               // [E] slots routed to each expert
-    int32_t *pre_e = tot_e + a.E;               // [E] of those, the ones in tiles before this one
-    int32_t *seg_g = pre_e + a.E;               // [G] the same three for the group slots
-    int32_t *tot_g = seg_g + a.G;
-    int32_t *pre_g = tot_g + a.G;
-    int32_t *ids_all = pre_g + a.G;  // [kRankWaves][kSpan] expert ids of each wave's batch (first: sums)
+    int32_t *seg_g = seg_e + a.E;               // [G] first slot of each group
+    int32_t *tot = seg_g + a.G;                 // [Hp] slots per key: experts, then groups at Ep
+    int32_t *pre = tot + a.Hp;                  // [Hp] of those, the ones in tiles before this one
+    int32_t *tot_e = tot, *pre_e = pre;
+    int32_t *tot_g = tot + a.Ep, *pre_g = pre + a.Ep;
+    int32_t *ids_all = pre + a.Hp;  // [kRankWaves][kSpan] expert ids of each wave's batch (first: sums)
     const int tile = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -351,13 +347,12 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 
     // ---- every key's first row, and this tile's first row inside it, from the tile counts
     // (each workgroup adds up the counts of all tiles itself: no separate scan pass)
-    tile_sums(a.hist_e, a.E, a.Ep, a.ntiles, tile, tot_e, pre_e, ids_all);
+    // (expert and group counts share a row, so one pass of loads covers both)
+    tile_sums(a.hist, a.Hp, a.Hp, a.ntiles, tile, tot, pre, ids_all);
     const int32_t rows_used = segment_starts(tot_e, a.E, a.cap > 0 ? 1 : a.align, seg_e, wsum);
     int32_t n_slots = 0;
-    if (a.gs > 0) {
-        tile_sums(a.hist_g, a.G, a.Gp, a.ntiles, tile, tot_g, pre_g, ids_all);
+    if (a.gs > 0)
         n_slots = segment_starts(tot_g, a.G, 1, seg_g, wsum);
-    }
     if (tile == 0) {  // the per-expert (and per-group) results, once
         for (int e = tid; e < a.E; e += kRankThreads) {
             const int32_t cnt = tot_e[e];
@@ -583,7 +578,7 @@ int round4(int n) { return (n + 3) & ~3; }
 
 struct Plan {
     int32_t tile_tokens, ntiles;
-    size_t ws_e, ws_g;  // workspace bytes of the expert and of the group tile counts
+    size_t ws;  // workspace bytes: the tile counts
 };
 
 // Tiles hold whole tokens (so a token's group test stays inside one tile), at least ~512 slots
@@ -596,8 +591,7 @@ Plan make_plan(int64_t T, int32_t K, int32_t E, int32_t G)
     p.tile_tokens = static_cast<int32_t>(std::min<int64_t>(tt, 0x7fffffff));
     p.ntiles = static_cast<int32_t>(T == 0 ? 0 : ceil_div(T, p.tile_tokens));
     auto al = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
-    p.ws_e = al(sizeof(int32_t) * static_cast<size_t>(round4(E)) * p.ntiles);
-    p.ws_g = G > 0 ? al(sizeof(int32_t) * static_cast<size_t>(round4(G)) * p.ntiles) : 0;
+    p.ws = al(sizeof(int32_t) * static_cast<size_t>(round4(E) + (G > 0 ? round4(G) : 0)) * p.ntiles);
     return p;
 }
 
@@ -627,7 +621,7 @@ extern "C" moe_status moe_build_index_workspace_size(int64_t T, int32_t K, int32
     if (st != MOE_OK)
         return st;
     const Plan p = make_plan(T, K, E, group_size > 0 ? E / group_size : 0);
-    *bytes = p.ws_e + p.ws_g;
+    *bytes = p.ws;
     return MOE_OK;
 }
 
@@ -670,7 +664,7 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     const Plan p = make_plan(T, K, E, G);
     if (p.ntiles > kMaxTiles)
         return MOE_ERR_UNSUPPORTED;  // cannot happen: tiles grow with T to stay within the limit
-    const size_t need = p.ws_e + p.ws_g;
+    const size_t need = p.ws;
     if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
         return MOE_ERR_INVALID;
 
@@ -686,13 +680,13 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     a.align = A;
     a.Ep = round4(E);
     a.Gp = round4(G);
+    a.Hp = a.Ep + (G > 0 ? a.Gp : 0);
     a.tile_tokens = p.tile_tokens;
     a.ntiles = p.ntiles;
     a.ebits = bits_for(E);
     a.gbits = bits_for(G);
     char *ws = static_cast<char *>(workspace);
-    a.hist_e = reinterpret_cast<int32_t *>(ws);
-    a.hist_g = G > 0 ? reinterpret_cast<int32_t *>(ws + p.ws_e) : nullptr;
+    a.hist = reinterpret_cast<int32_t *>(ws);
     a.ix = *out;
 
     if (T == 0) {
@@ -701,11 +695,11 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
         return launch_status();
     }
 
-    const size_t lds_hist = sizeof(int32_t) * (static_cast<size_t>(a.Ep) + (G > 0 ? a.Gp : 0));
+    const size_t lds_hist = sizeof(int32_t) * static_cast<size_t>(a.Hp);
     hipLaunchKernelGGL(hist_kernel, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
-    const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 3) * (E + G) +
+    const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 1) * (E + G) + 2 * static_cast<size_t>(a.Hp) +
                                                static_cast<size_t>(kRankWaves) * kSpan);
     hipLaunchKernelGGL(rank_kernel, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     if ((st = launch_status()) != MOE_OK)
