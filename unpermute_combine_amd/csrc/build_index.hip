@@ -81,34 +81,71 @@ __device__ __forceinline__ bool group_leader(const int32_t *ids, int k, int g, i
     return true;
 }
 
+// Bitwise match-any over the low `bits` bits of key among the lanes in `active`.
+__device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t active)
+{
+    uint64_t m = active;
+    for (int b = 0; b < bits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t ones = __ballot(bit);
+        m &= bit ? ones : ~ones;
+    }
+    return m;
+}
+
+// group_leader by ballots, for a wavefront whose 64 lanes hold consecutive slots starting at a
+// token boundary with K a power of two (so a token's K slots are lanes first .. first+K-1).
+// `peers` are the valid lanes naming this lane's group (match_peers over the group ids); the
+// lowest of them inside this lane's token is the leader. True iff the lane is valid and holds
+// its token's first slot in its group.
+__device__ __forceinline__ bool token_leader(uint64_t peers, bool valid, int K)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int first = lane & ~(K - 1);
+    const uint64_t tok = K >= kWave ? ~0ull : ((1ull << K) - 1) << first;
+    const uint64_t mine = peers & tok;
+    return valid && mine != 0 && __builtin_ctzll(mine) == lane;
+}
+
 // ---------------------------------------------------------------- 1. per-tile histograms
+// kGroups: group mode (a.gs > 0), a template argument so that the expert-only build carries no
+// group code
+template <bool kGroups>
 __global__ __launch_bounds__(256) void hist_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
     int32_t *he = sh;         // [Ep]
     int32_t *hg = sh + a.Ep;  // [Gp]
     const int tile = blockIdx.x;
-    const int nsh = a.Ep + (a.gs > 0 ? a.Gp : 0);
+    const int nsh = a.Ep + (kGroups ? a.Gp : 0);
     for (int i = threadIdx.x; i < nsh; i += blockDim.x)
         sh[i] = 0;
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(tile) * a.tile_tokens;
     const int64_t t1 = min(a.T, t0 + a.tile_tokens);
     const int64_t s0 = t0 * a.K, s1 = t1 * a.K;
+    // with K a power of two each wavefront's 64 slots start at a token boundary (s0, 64 and the
+    // workgroup's stride are multiples of K) and the group test runs on ballots; lanes past s1
+    // hold whole tokens, so the inactive ones never split a token
+    const bool wave_lead = (a.K & (a.K - 1)) == 0;
     for (int64_t i = s0 + threadIdx.x; i < s1; i += blockDim.x) {
         const int e = a.topk_idx[i];
-        if (!valid_expert(e, a.E))
+        const bool ok = valid_expert(e, a.E);
+        bool lead = false;
+        if (kGroups && wave_lead)
+            lead = token_leader(match_peers(ok ? e / a.gs : -1, a.gbits, __ballot(ok)), ok, a.K);
+        if (!ok)
             continue;
         atomicAdd(&he[e], 1);
-        if (a.gs > 0) {
+        if (kGroups) {
             const int64_t t = i / a.K;
             const int k = static_cast<int>(i - t * a.K);
             const int g = e / a.gs;
-            if (group_leader(a.topk_idx + t * a.K, k, g, a.E, a.gs))
+            if (wave_lead ? lead : group_leader(a.topk_idx + t * a.K, k, g, a.E, a.gs))
                 atomicAdd(&hg[g], 1);
         }
     }
-    if (a.gs > 0) {  // slot_of starts as "absent" for this tile's tokens
+    if (kGroups) {  // slot_of starts as "absent" for this tile's tokens
         for (int64_t i = t0 * a.G + threadIdx.x; i < t1 * a.G; i += blockDim.x)
             a.ix.slot_of[i] = -1;
     }
@@ -160,17 +197,6 @@ __global__ __launch_bounds__(kEmptyThreads) void empty_index_kernel(IndexArgs a)
 }
 
 // ---------------------------------------------------------------- 2. stable ranks
-// Bitwise match-any over the low `bits` bits of key among the lanes in `active`.
-__device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t active)
-{
-    uint64_t m = active;
-    for (int b = 0; b < bits; ++b) {
-        const bool bit = (key >> b) & 1;
-        const uint64_t ones = __ballot(bit);
-        m &= bit ? ones : ~ones;
-    }
-    return m;
-}
 
 __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(m); }
 
@@ -310,6 +336,7 @@ __device__ int32_t segment_starts(const int32_t *tot, int nkeys, int align, int3
 // first row of the key. Phase C: every wave walks its slots in order, 64 at a time, and ranks
 // them against its own running counters. Finally the workgroups together write the padding
 // (drop-and-pad) or unused rows.
+template <bool kGroups>
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
@@ -340,6 +367,10 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     const int64_t t0 = min(tile_t1, tile_t0 + wave * per);
     const int64_t t1 = min(tile_t1, t0 + per);
     const int64_t s0 = t0 * a.K, s1 = t1 * a.K;
+    // K a power of two: every batch of 64 slots starts at a token boundary (s0 and kWave are
+    // multiples of K), so the first-slot-in-group test runs on ballots instead of reading the
+    // token's earlier slots back from LDS
+    const bool wave_lead = (a.K & (a.K - 1)) == 0;
     const bool want_w = a.ix.permuted_probs && a.topk_w;
     int e_first[kRankBatch];
     float w_first[kRankBatch];
@@ -351,7 +382,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     tile_sums(a.hist, a.Hp, a.Hp, a.ntiles, tile, tot, pre, ids_all);
     const int32_t rows_used = segment_starts(tot_e, a.E, a.cap > 0 ? 1 : a.align, seg_e, wsum);
     int32_t n_slots = 0;
-    if (a.gs > 0)
+    if (kGroups)
         n_slots = segment_starts(tot_g, a.G, 1, seg_g, wsum);
     if (tile == 0) {  // the per-expert (and per-group) results, once
         for (int e = tid; e < a.E; e += kRankThreads) {
@@ -361,7 +392,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
             if (a.ix.kept_counts)
                 a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
         }
-        if (a.gs > 0) {
+        if (kGroups) {
             for (int g = tid; g < a.G; g += kRankThreads)
                 a.ix.group_counts[g] = tot_g[g];
             if (tid == 0)
@@ -380,7 +411,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
         } else {
             load_batch(a, base0, s1, false, e_b, w_b);
         }
-        if (a.gs > 0) {
+        if (kGroups && !wave_lead) {
 #pragma unroll
             for (int b = 0; b < kRankBatch; ++b)
                 ids[b * kWave + lane] = e_b[b];
@@ -390,14 +421,18 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
         for (int b = 0; b < kRankBatch; ++b) {
             const int64_t i = base0 + b * kWave + lane;
             const int e = e_b[b];
-            if (i >= s1 || !valid_expert(e, a.E))
+            const bool ok = i < s1 && valid_expert(e, a.E);
+            bool lead = false;
+            if (kGroups && wave_lead)
+                lead = token_leader(match_peers(ok ? e / a.gs : -1, a.gbits, __ballot(ok)), ok, a.K);
+            if (!ok)
                 continue;
             atomicAdd(&cw_e[e], 1);
-            if (a.gs > 0) {
+            if (kGroups) {
                 const int64_t t = i / a.K;
                 const int k = static_cast<int>(i - t * a.K);
                 const int g = e / a.gs;
-                if (first_in_group(a, i, k, g, base0, ids))
+                if (wave_lead ? lead : first_in_group(a, i, k, g, base0, ids))
                     atomicAdd(&cw_g[g], 1);
             }
         }
@@ -415,7 +450,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
                 run += c;
             }
         }
-        if (a.gs > 0) {
+        if (kGroups) {
             for (int g = tid; g < a.G; g += kRankThreads) {
                 int32_t run = seg_g[g] + pre_g[g];
                 for (int w = 0; w < kRankWaves; ++w) {
@@ -447,7 +482,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
         }
         if (base0 + kSpan < s1)  // next batch in flight, issued before this batch's stores
             load_batch(a, base0 + kSpan, s1, want_w, e_nx, w_nx);
-        if (a.gs > 0) {
+        if (kGroups && !wave_lead) {
 #pragma unroll
             for (int b = 0; b < kRankBatch; ++b)
                 ids[b * kWave + lane] = e_cur[b];
@@ -487,10 +522,18 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
             }
 
             // group slots: one per (token, group), listed group by group, tokens ascending
-            if (a.gs > 0) {
+            if (kGroups) {
                 const int g = ok ? e / a.gs : -1;
-                const bool lead = ok && first_in_group(a, i, k, g, base0, ids);
-                const uint64_t pg = match_peers(g, a.gbits, __ballot(lead));
+                bool lead;
+                uint64_t pg;
+                if (wave_lead) {
+                    const uint64_t peers = match_peers(g, a.gbits, __ballot(ok));
+                    lead = token_leader(peers, ok, a.K);
+                    pg = peers & __ballot(lead);
+                } else {
+                    lead = ok && first_in_group(a, i, k, g, base0, ids);
+                    pg = match_peers(g, a.gbits, __ballot(lead));
+                }
                 int32_t slot = -1;
                 if (lead)
                     slot = cw_g[g] + __popcll(pg & below);
@@ -534,7 +577,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
                     a.ix.sorted_indices[r] = MOE_ROW_PAD;
                     if (a.ix.permuted_probs)
                         a.ix.permuted_probs[r] = 0.0f;
-                    if (a.gs > 0)
+                    if (kGroups)
                         a.ix.esrc[r] = MOE_ROW_PAD;
                 }
             }
@@ -545,7 +588,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
             a.ix.sorted_indices[r] = MOE_ROW_UNUSED;
             if (a.ix.permuted_probs)
                 a.ix.permuted_probs[r] = 0.0f;
-            if (a.gs > 0)
+            if (kGroups)
                 a.ix.esrc[r] = MOE_ROW_UNUSED;
         }
     }
@@ -696,12 +739,18 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     }
 
     const size_t lds_hist = sizeof(int32_t) * static_cast<size_t>(a.Hp);
-    hipLaunchKernelGGL(hist_kernel, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
+    if (G > 0)
+        hipLaunchKernelGGL(hist_kernel<true>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
+    else
+        hipLaunchKernelGGL(hist_kernel<false>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
     const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 1) * (E + G) + 2 * static_cast<size_t>(a.Hp) +
                                                static_cast<size_t>(kRankWaves) * kSpan);
-    hipLaunchKernelGGL(rank_kernel, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+    if (G > 0)
+        hipLaunchKernelGGL(rank_kernel<true>, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+    else
+        hipLaunchKernelGGL(rank_kernel<false>, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
     if (G > 0) {
