@@ -10,7 +10,7 @@
 // issues its loads together, stores whole cache lines, and orders loads before stores (on gfx9
 // the vector-memory counter retires loads and stores in issue order, so a load issued after a
 // store cannot be waited for without waiting for the store too). Two launches, plus one in
-// group mode:
+// group mode when K is not a power of two:
 //   1. hist   one workgroup per tile of whole tokens: the tile's expert histogram (and the
 //             group histogram of each token's first slot in a group) with LDS atomics -- only
 //             counts come from atomics, never positions, so the result is deterministic -- and
@@ -28,7 +28,10 @@
 //             (a match-any built from ballots); their stable rank is popcount(peers &
 //             lanes_below) and the last peer advances the key's running row counter in LDS.
 //             The workgroups then write the padding or unused rows together.
-//   3. esrc   (group mode) expert-major row -> group slot.
+//   3. esrc   (group mode, K not a power of two) expert-major row -> group slot. With K a power
+//             of two a token's slots sit in consecutive lanes of one wavefront: the first slot
+//             of each (token, group) is found with ballots, and the rank kernel hands its group
+//             slot to the token's other slots of the group and writes esrc itself.
 // With no tokens one single-workgroup launch writes the zero counts and the marks.
 // The drop-and-pad capacity rule ([Scratch] §18, §26.6), the expert alignment ([Combine] §6:
 // segments rounded up to a multiple of A with padding rows, the segment starts being the scan of
@@ -95,16 +98,22 @@ __device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t acti
 
 // group_leader by ballots, for a wavefront whose 64 lanes hold consecutive slots starting at a
 // token boundary with K a power of two (so a token's K slots are lanes first .. first+K-1).
-// `peers` are the valid lanes naming this lane's group (match_peers over the group ids); the
-// lowest of them inside this lane's token is the leader. True iff the lane is valid and holds
-// its token's first slot in its group.
-__device__ __forceinline__ bool token_leader(uint64_t peers, bool valid, int K)
+// `peers` are the valid lanes naming this lane's group (match_peers over the group ids);
+// token_first gives the lowest of them inside this lane's token (64 if there is none), the lane
+// holding the token's first slot in that group.
+__device__ __forceinline__ int token_first(uint64_t peers, int K)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int first = lane & ~(K - 1);
     const uint64_t tok = K >= kWave ? ~0ull : ((1ull << K) - 1) << first;
     const uint64_t mine = peers & tok;
-    return valid && mine != 0 && __builtin_ctzll(mine) == lane;
+    return mine ? __builtin_ctzll(mine) : kWave;
+}
+
+// True iff the lane is valid and holds its token's first slot in its group.
+__device__ __forceinline__ bool token_leader(uint64_t peers, bool valid, int K)
+{
+    return valid && token_first(peers, K) == static_cast<int>(threadIdx.x & (kWave - 1));
 }
 
 // ---------------------------------------------------------------- 1. per-tile histograms
@@ -526,9 +535,12 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
                 const int g = ok ? e / a.gs : -1;
                 bool lead;
                 uint64_t pg;
+                int from = lane;  // the lane that gets this slot's group slot (wave_lead)
                 if (wave_lead) {
                     const uint64_t peers = match_peers(g, a.gbits, __ballot(ok));
-                    lead = token_leader(peers, ok, a.K);
+                    if (ok)
+                        from = token_first(peers, a.K);
+                    lead = ok && from == lane;
                     pg = peers & __ballot(lead);
                 } else {
                     lead = ok && first_in_group(a, i, k, g, base0, ids);
@@ -540,6 +552,11 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
                 __builtin_amdgcn_wave_barrier();
                 if (lead && lane == last_lane(pg))
                     cw_g[g] += __popcll(pg);
+                if (wave_lead) {  // every kept slot of the group takes the leader's group slot
+                    const int32_t gslot = __shfl(slot, from, kWave);
+                    if (row >= 0)
+                        a.ix.esrc[row] = gslot;
+                }
                 if (lead) {
                     a.ix.slot_of[t * a.G + g] = slot;
                     a.ix.gsrc[slot] = static_cast<int32_t>(t);
@@ -753,7 +770,7 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
         hipLaunchKernelGGL(rank_kernel<false>, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
-    if (G > 0) {
+    if (G > 0 && (K & (K - 1)) != 0) {  // with K a power of two the rank kernel writes esrc
         const int64_t n = T * K;
         const int blocks = static_cast<int>(std::min<int64_t>(ceil_div(n, 256), 4096));
         hipLaunchKernelGGL(esrc_kernel, dim3(blocks), dim3(256), 0, stream, a);
