@@ -6,20 +6,24 @@
 // holds the logits of experts l, l+16, l+32, ... and keeps the best of its own still-unselected
 // experts. (Consecutive experts per lane, with 16-byte loads, took 17.7 us instead of 12.7 us at
 // T16384 E256 K8 with Zipf-skewed logits: the popular low ids then sit in one or two lanes,
-// whose candidate caches run dry.) A key orders (logit descending, expert id ascending): high word an order-preserving
-// image of the float, low word ~id. Each lane keeps its best three keys in order; each of the
-// K rounds is a 16-lane all-reduce of the lanes' first keys made of four DPP steps (row_mirror,
-// row_half_mirror, quad xor 2, quad xor 1) -- plain VALU instructions, no LDS round trip --
-// after which the lane that owned the winner moves its next keys up; it rescans its keys only
-// once all three are gone (at T16384 E256 K8: 12.6 us per launch, 15.1 us with a rescan after
-// every round, both before the loads were issued together). The softmax runs in double; the K exponentials meet in LDS and every lane sums
-// them in slot order.
+// whose candidate caches run dry.) A key is the logit's order-preserving 32-bit image (-0 taken
+// as +0); among equal keys the lower expert id comes first. Each lane keeps its best three keys
+// in order (key descending, id ascending). Each of the K rounds takes the maximum of the lanes'
+// first keys over the 16 lanes with four DPP max steps (row_mirror, row_half_mirror, quad xor 2,
+// quad xor 1: VALU instructions, no LDS round trip); the lanes holding that key are the
+// candidates, found with one ballot, and only when a row has two candidates (equal logits) does a
+// second 16-lane DPP reduction pick the lowest expert id among them. The winner lane records the
+// slot in LDS and moves its next keys up; it rescans its keys only once all three are gone.
+// Measured at T16384 E256 K8 (event time per launch): 15.4 us with a (key, ~id) pair reduced
+// each round and one load wait per key, 13.3 us with the loads in flight together, 12.0 us with
+// the keys-only max. The softmax runs in double; the K exponentials meet in LDS and every lane
+// sums them in slot order.
 //
 // Group-limited routing ([Scratch] §21: pick a few expert groups first, then the experts inside
 // them) runs in the same kernel before the K rounds: the lanes fold their keys into per-group
 // maxima with LDS atomic max (on the order-preserving keys, so the maximum key is the group's
-// best logit), then topk_groups rounds of the same 16-lane reduction over (group key, ~group id)
-// pick the groups, and the experts of the other groups are dropped from the candidates.
+// best logit), then topk_groups rounds of a 16-lane DPP reduction of (group key, ~group id)
+// pairs pick the groups, and the experts of the other groups are dropped from the candidates.
 #include "moe_common.h"
 
 namespace moe {
@@ -72,6 +76,29 @@ __device__ __forceinline__ void row_max(uint32_t &hi, uint32_t &lo)
     max_step<kDppRowHalfMirror>(hi, lo);
     max_step<kDppQuadXor2>(hi, lo);
     max_step<kDppQuadXor1>(hi, lo);
+}
+
+// Largest (or smallest) of one 32-bit value over the 16 lanes of this lane's row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v)
+{
+    return max(v, dpp<CTRL>(v));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t min_dpp(uint32_t v)
+{
+    return min(v, dpp<CTRL>(v));
+}
+
+__device__ __forceinline__ uint32_t row_max1(uint32_t v)
+{
+    return max_dpp<kDppQuadXor1>(max_dpp<kDppQuadXor2>(max_dpp<kDppRowHalfMirror>(max_dpp<kDppRowMirror>(v))));
+}
+
+__device__ __forceinline__ uint32_t row_min1(uint32_t v)
+{
+    return min_dpp<kDppQuadXor1>(min_dpp<kDppQuadXor2>(min_dpp<kDppRowHalfMirror>(min_dpp<kDppRowMirror>(v))));
 }
 
 constexpr int kMaxRouteGroups = 256;  // group keys in LDS: 16 tokens x 256 x 4 B per workgroup
@@ -185,30 +212,29 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
     fill();
     bool complete = cu2 == 0;  // fewer than three keys: the cache holds all that are left
 
-    uint32_t slot_u[kSlotRegs];
-    int slot_e[kSlotRegs];
-#pragma unroll
-    for (int q = 0; q < kSlotRegs; ++q) {
-        slot_u[q] = 0;
-        slot_e[q] = 0;
-    }
+    // Each round: the token's largest first key (a 16-lane max of the keys alone); the lanes
+    // holding it are the candidates, and only when two candidates hold equal keys does a
+    // second 16-lane reduction pick the lowest expert id among them. The winner lane records
+    // the slot in LDS and gives up its first key.
+    __shared__ uint32_t slot_key[kTokensPerBlock][MOE_MAX_TOPK];
+    __shared__ int32_t slot_id[kTokensPerBlock][MOE_MAX_TOPK];
+    const int seg_shift = threadIdx.x & (kWave - kLanesPerToken);  // this row's first lane in the wave
     uint32_t s0u = 0;
     for (int k = 0; k < K; ++k) {
-        uint32_t hi = cu0;
-        uint32_t lo = cu0 ? 0xffffffffu - static_cast<uint32_t>(sub + kLanesPerToken * cj0) : 0u;
-        row_max(hi, lo);
-        const int win = static_cast<int>(0xffffffffu - lo);  // winning expert id of this row
+        const uint32_t m = row_max1(cu0);
         if (k == 0)
-            s0u = hi;
-        if (sub == (k & (kLanesPerToken - 1))) {
-#pragma unroll
-            for (int q = 0; q < kSlotRegs; ++q)
-                if (q == k / kLanesPerToken) {
-                    slot_u[q] = hi;
-                    slot_e[q] = win;
-                }
+            s0u = m;
+        const bool cand = cu0 != 0 && cu0 == m;
+        const uint32_t seg = static_cast<uint32_t>(__ballot(cand) >> seg_shift) & ((1u << kLanesPerToken) - 1);
+        bool win = cand;
+        if (__ballot(__popc(seg) > 1)) {  // equal keys in some row: the lowest expert id wins
+            const uint32_t id = cand ? static_cast<uint32_t>(sub + kLanesPerToken * cj0) : 0xffffffffu;
+            const uint32_t lowest = row_min1(id);  // every lane of the wavefront takes part
+            win = cand && id == lowest;
         }
-        if (hi != 0 && sub == (win & (kLanesPerToken - 1))) {  // the owner gives up its first
+        if (win) {
+            slot_key[tok][k] = cu0;
+            slot_id[tok][k] = sub + kLanesPerToken * cj0;
             taken |= 1ull << cj0;
             cu0 = cu1;
             cj0 = cj1;
@@ -221,16 +247,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
             }
         }
     }
+    __builtin_amdgcn_wave_barrier();
 
     // softmax over the K selected logits, in double, summed in slot order
     const double s0 = static_cast<double>(from_orderable(s0u));
     double ex[kSlotRegs];
+    int32_t slot_e[kSlotRegs];
 #pragma unroll
     for (int q = 0; q < kSlotRegs; ++q) {
         const int k = sub + kLanesPerToken * q;
         ex[q] = 0.0;
+        slot_e[q] = 0;
         if (k < K) {
-            ex[q] = exp(static_cast<double>(from_orderable(slot_u[q])) - s0);
+            ex[q] = exp(static_cast<double>(from_orderable(slot_key[tok][k])) - s0);
+            slot_e[q] = slot_id[tok][k];
             ex_sh[tok][k] = ex[q];
         }
     }
