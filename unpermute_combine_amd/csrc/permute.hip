@@ -236,6 +236,7 @@ constexpr int kGroupLoads = 4;
 // against 245 us with 4)
 constexpr int kGroupedThreads = 128;
 constexpr int kGroupedWaves = kGroupedThreads / kWave;
+constexpr int kGroupLoadPolicy = 0;
 
 __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
@@ -271,13 +272,22 @@ __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
                 m &= ~pb[u];
             }
         }
+        // unguarded loads (an absent source has a zero-size resource, a lane past the row reads
+        // beyond the resource's end: both read zeros), then one wait for all of them, so that the
+        // stores below issue back to back: with a guarded load per source the compiler could not
+        // count the loads and waited for all earlier stores before each source's stores
         u32x4 r[kGroupLoads];
 #pragma unroll
         for (int u = 0; u < kGroupLoads; ++u) {
-            r[u] = u32x4{0u, 0u, 0u, 0u};
-            if (sb[u] >= 0 && v < nvec)
-                r[u] = ld16(src + static_cast<int64_t>(sb[u]) * row_bytes + v * 16);
+            const __amdgpu_buffer_rsrc_t s = make_rsrc(src + static_cast<int64_t>(sb[u] < 0 ? 0 : sb[u]) * row_bytes,
+                                                       sb[u] < 0 ? 0u : static_cast<uint32_t>(row_bytes));
+            r[u] = ld16_buf<kGroupLoadPolicy>(s, static_cast<uint32_t>(v * 16));
         }
+        // the loaded values pass through an empty asm statement: it keeps every load ahead of the
+        // first store (the compiler may not sink one into the store loop) and puts the one wait here
+#pragma unroll
+        for (int u = 0; u < kGroupLoads; ++u)
+            asm volatile("" : : "v"(r[u].x), "v"(r[u].y), "v"(r[u].z), "v"(r[u].w));
 #pragma unroll
         for (int u = 0; u < kGroupLoads; ++u) {
             uint64_t p = pb[u];
