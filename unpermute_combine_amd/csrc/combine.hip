@@ -86,6 +86,7 @@ __device__ __forceinline__ void fma_batch(const Y *__restrict__ y, int64_t H, co
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
         load_chunk<Y>(y, H, row[u], col8, q[u]);
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const bool live = row[u] >= 0;
@@ -114,6 +115,7 @@ __device__ __forceinline__ void fma_two(const Y *__restrict__ y, int64_t H, cons
         load_chunk<Y>(y, H, row[u], c, q[u]);
         load_chunk<Y>(y, H, row1[u], c2, q2[u]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
 #pragma unroll
     for (int u = 0; u < N; ++u) {
         const bool live = row[u] >= 0;
@@ -152,12 +154,13 @@ __device__ int compact_rows(const int32_t *rows_in, const float *w_in, int K, in
     for (int k0 = 0; k0 < K; k0 += kWave) {
         const int k = k0 + lane;
         const int32_t r = k < K ? rows_in[k] : -1;
+        const float wk = (k < K && w_in) ? w_in[k] : 1.0f;  // loaded beside r, not after it
         const bool ok = r >= 0 && r < y_rows;
         const uint64_t m = __ballot(ok);
         if (ok) {
             const int pos = n + __popcll(m & lanemask_lt());
             rows[pos] = r;
-            ws[pos] = w_in ? w_in[k] : 1.0f;
+            ws[pos] = wk;
         }
         n += __popcll(m);
     }
@@ -242,6 +245,7 @@ __device__ __forceinline__ void fma_batch_split(const Y *__restrict__ y, int64_t
         load_parts<Y>(y, H, row[u], e0, q[u]);
         take[u] = row[u] >= 0;
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
     fma_parts<Y>(q, w, take, acc);
 }
 
@@ -407,12 +411,13 @@ __global__ __launch_bounds__(kMaxThreads) void combine_batched_kernel(const uint
     for (int tb = wave; tb < kCombineBatch; tb += nwaves) {  // token tb's valid slots, in slot order (K <= 8)
         const int64_t t = t0 + tb;
         const int32_t r = (t < T && lane < K) ? row_of[t * K + lane] : -1;
+        const float wk = (t < T && lane < K && w) ? w[t * K + lane] : 1.0f;  // loaded beside r
         const bool ok = r >= 0 && r < y_rows;
         const uint64_t m = __ballot(ok);
         if (ok) {
             const int pos = __popcll(m & lanemask_lt());
             rows[tb][pos] = r;
-            ws[tb][pos] = w ? w[t * K + lane] : 1.0f;
+            ws[tb][pos] = wk;
         }
         if (lane == 0)
             n_sh[tb] = __popcll(m);
@@ -430,6 +435,8 @@ __global__ __launch_bounds__(kMaxThreads) void combine_batched_kernel(const uint
                 load_chunk<uint16_t>(y, H, ra[u], c, qa[u]);
                 load_chunk<uint16_t>(y, H, rb[u], c, qb[u]);
             }
+            // (the compiler waits for the first row's load before issuing the other 15; a
+            // scheduling barrier that issues all 16 first measured slower: 352 against 345 us)
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             float acc2[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
