@@ -227,6 +227,8 @@ moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe
  *   amax = max |x|,  scale = amax / 448 (float32 division; 1 when amax is 0),
  *   q[i] = E4M3 code of x[i] / scale (float32 division, nearest even, saturating at 448),
  * E4M3 being the OCP 8-bit format (bias 7, no infinities, 448 the largest finite value).
+ * x must be finite (then |x / scale| exceeds 448 by at most the division's rounding and the
+ * code is at most 448 in magnitude).
  *   moe_quantize_fp8: x [T, H] (x_dt float32 or bf16) -> q [T, H] bytes, scales [T, H/block]
  *     float32. block must divide H.
  *   moe_permute_scatter_fp8: the same codes and scales, computed once per source row and

@@ -424,6 +424,42 @@ def test_quantize_fp8(m, dtype, T, H, block):
     assert_exact(host(sc), want_s, "scales")
 
 
+def _e4m3_boundary_rows():
+    """float32 rows of 8 whose first element is 448 (so the block's scale is exactly 1 and every
+    code is the E4M3 rounding of the value itself), the other 7 taken in turn from: every finite
+    E4M3 value, every midpoint between neighbouring values (the round-to-nearest-even ties), the
+    float32 neighbours of each midpoint, and the negatives of all of them."""
+    vals = sorted({oracle.e4m3_to_f32(c) for c in range(0x7F)})
+    mids = [np.float32((a + b) / 2) for a, b in zip(vals[:-1], vals[1:])]
+    pool = [np.float32(v) for v in vals] + mids
+    pool += [np.nextafter(m, np.float32(np.inf)) for m in mids] + [np.nextafter(m, np.float32(-np.inf)) for m in mids]
+    pool += [np.float32(2.0 ** -10), np.float32(2.0 ** -11), np.float32(3 * 2.0 ** -11), np.float32(1e-30)]
+    pool = np.asarray(pool, np.float32)
+    pool = np.concatenate([pool, -pool])
+    n = -(-len(pool) // 7)
+    rows = np.zeros((n, 8), np.float32)
+    rows[:, 0] = 448.0
+    rows[:, 1:].flat[:len(pool)] = pool
+    return rows
+
+
+def test_fp8_codes_at_rounding_boundaries(m):
+    """E4M3 codes of every finite value, every tie and the float32 neighbours of every tie,
+    with a scale of exactly 1: the quantizer and the fused dispatch against the oracle, bit for bit."""
+    say("fp8 codes at rounding boundaries")
+    x = _e4m3_boundary_rows()
+    want_q, want_s = oracle.quantize_fp8(x, 8)
+    assert (want_s == 1.0).all()
+    q, sc = m.quantize_fp8(dev(x), 8)
+    assert_exact(host(q), want_q, "codes")
+    assert_exact(host(sc), want_s, "scales")
+    T = x.shape[0]
+    ident = np.arange(T, dtype=np.int32).reshape(T, 1)
+    q2, sc2 = m.permute_scatter_fp8(dev(x), dev(ident), T, 8)
+    assert_exact(host(q2), want_q, "dispatched codes")
+    assert_exact(host(sc2), want_s, "dispatched scales")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("H,T,E,K,mode,block", [(7168, 300, 64, 8, "standard", 128), (1024, 200, 16, 4, "drop", 64),
                                                 (4096, 257, 32, 8, "aligned", 128), (512, 100, 8, 2, "holes", 512),

@@ -9,16 +9,19 @@
 // E4M3 code of x / scale (both divisions IEEE float32), rounded to nearest even and saturated at
 // 448 -- the largest finite E4M3 value -- so x ~ value(code) * scale.
 //
-// gfx950 design. The encoder works on the float's bits: the exponent field picks the E4M3
-// binade, the top three mantissa bits are rounded to nearest even with the 20 bits below them,
-// and a carry out of the mantissa steps the exponent. The fused dispatch runs like the bf16
-// source-major permute -- one wavefront per (source row, 1024-element slice), each lane holding
-// 16 consecutive elements -- with the block's amax reduced over the block's lanes by xor
-// shuffles, then 16 codes (16 bytes) per lane stored to every destination row: 1 KiB per
-// wavefront instruction, half the bytes of the bf16 rows. Scales are one float32 per block and
-// row. Measured at T16384 H7168 K8: 212 us per launch (5.7 TB/s) against 241 us with 8
-// elements (8-byte stores) per lane; dividing or multiplying by a reciprocal made no difference
-// (the kernel is not ALU bound), so the division of the definition stays.
+// gfx950 design. The codes come from the conversion instruction (v_cvt_pk_fp8_f32, two values
+// per instruction, round to nearest even): it gives the definition's code for every finite
+// E4M3 value, every tie between neighbours and the float32 neighbours of every tie (tested
+// against the oracle), and replaced a bit-level encoder of ~12 instructions per element (the
+// fused dispatch at T8192 H7168 in 32 groups: 73.7 -> 52.9 us; drop-and-pad T8192 H4096:
+// 81.8 -> 69.0 us; unchanged at T16384 H7168 K8, where the stores dominate). The fused dispatch
+// runs like the bf16 source-major permute -- one wavefront per (source row, 1024-element slice),
+// each lane holding 16 consecutive elements -- with the block's amax reduced over the block's
+// lanes by xor shuffles, then 16 codes (16 bytes) per lane stored to every destination row:
+// 1 KiB per wavefront instruction, half the bytes of the bf16 rows. Scales are one float32 per
+// block and row. Measured at T16384 H7168 K8: 212 us per launch (5.7 TB/s) against 241 us with
+// 8 elements (8-byte stores) per lane; the divisions of the definition stay (multiplying by a
+// reciprocal would change codes).
 #include "moe_common.h"
 
 namespace moe {
@@ -30,24 +33,20 @@ constexpr int kFp8Threads = 256;
 constexpr int kFp8Waves = kFp8Threads / kWave;
 constexpr int kFp8ZeroRows = 8;       // padding rows checked per zero wavefront
 
-// E4M3 code of v: nearest even, saturating at +-448, NaN -> 0x7f with the sign.
+// Four E4M3 codes packed in element order (byte i = code of the i-th value) by the gfx950
+// conversion instruction (two values per instruction, round to nearest even into the OCP E4M3
+// format). For finite x, |x / scale| exceeds 448 by at most the division's rounding, which
+// rounds back to 448: the saturation of the definition is never needed beyond that.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return static_cast<uint32_t>(w);
+}
+
 __device__ __forceinline__ uint32_t e4m3_code(float v)
 {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t mag = u & 0x7fffffffu;
-    if (mag > 0x7f800000u)
-        return sign | 0x7fu;
-    if (mag > 0x43e00000u)  // above 448 (and infinity): saturate
-        return sign | 0x7eu;
-    if (mag < 0x3c800000u)  // below 2^-6: subnormal codes, a multiple of 2^-9 (scaling by 512 is exact)
-        return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(mag) * 512.0f));
-    const int e = static_cast<int>(mag >> 23) - 127;  // -6 .. 8
-    const uint32_t m23 = mag & 0x7fffffu;
-    uint32_t q = m23 >> 20;
-    const uint32_t rest = m23 & 0xfffffu;
-    q += (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) ? 1u : 0u;
-    return sign | ((static_cast<uint32_t>(e + 7) << 3) + q);  // q = 8 carries into the exponent
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false)) & 0xffu;
 }
 
 __device__ __forceinline__ float load_x(const uint16_t *p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
@@ -191,9 +190,9 @@ __global__ __launch_bounds__(kFp8Threads) void permute_scatter_fp8_kernel(
     const float s0 = block_scale(a0), s1 = block_scale(a1);
     uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        c[i / 4] |= e4m3_code(v[i] / s0) << (8 * (i % 4));
-        c[2 + i / 4] |= e4m3_code(v[8 + i] / s1) << (8 * (i % 4));
+    for (int h = 0; h < 2; ++h) {
+        c[h] = e4m3_pack4(v[4 * h] / s0, v[4 * h + 1] / s0, v[4 * h + 2] / s0, v[4 * h + 3] / s0);
+        c[2 + h] = e4m3_pack4(v[8 + 4 * h] / s1, v[8 + 4 * h + 1] / s1, v[8 + 4 * h + 2] / s1, v[8 + 4 * h + 3] / s1);
     }
     // scales: with block 8 each half is a block; otherwise the block's first lane writes it
     const bool first_lane = block == 8 || (lane % (block / 16)) == 0;
