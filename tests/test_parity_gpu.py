@@ -424,6 +424,49 @@ def test_quantize_fp8(m, dtype, T, H, block):
     assert_exact(host(sc), want_s, "scales")
 
 
+def _bf16_rounding_rows():
+    """float32 values whose bf16 rounding is a boundary case: exact ties with an even and with an
+    odd kept mantissa, one float32 step either side of a tie, carries into the next binade,
+    float32 subnormals (ties among them too), values rounding up past the largest bf16 to
+    infinity, infinities, zeros, and the negatives of all of them; 256 per row."""
+    rng = np.random.default_rng(20260)
+    hi = rng.integers(0, 0x7f7f, size=600, dtype=np.uint32) << 16      # finite bf16 patterns
+    tie = hi | 0x8000
+    bits = np.concatenate([tie, tie + 1, tie - 1, hi | 0x7fff, hi | 0xffff, hi | 0x0001,
+                           rng.integers(1, 0x800000, size=200, dtype=np.uint32),     # subnormals
+                           (rng.integers(0, 0x80, size=100, dtype=np.uint32) << 16) | 0x8000,
+                           np.asarray([0x7f7f8000, 0x7f7fffff, 0x7f7f7fff, 0x7f800000, 0, 0x00008000,
+                                       0x00018000, 0x3f808000, 0x3f818000], np.uint32)])
+    bits = np.concatenate([bits, bits | 0x80000000]).astype(np.uint32)
+    n = -(-len(bits) // 256) * 256
+    bits = np.concatenate([bits, np.zeros(n - len(bits), np.uint32)])
+    return bits.view(np.float32).reshape(-1, 256)
+
+
+def test_bf16_output_rounding_at_boundaries(m):
+    """float32 rows combined with unit weights into bf16: every output is the round-to-nearest-
+    even of one float32 value, at ties, around ties, in the subnormal range and at overflow --
+    against the oracle, bit for bit; then bf16 rows through the batched combine (an FMA with
+    weight 1 from +0 reproduces each row)."""
+    say("bf16 output rounding at boundaries")
+    y = _bf16_rounding_rows()
+    R = y.shape[0]
+    row_of = np.arange(R, dtype=np.int32).reshape(R, 1)
+    want = oracle.unpermute_combine(y, row_of, None, np.uint16)
+    got = host(m.unpermute_combine(dev(y), dev(row_of), None, out_dtype=torch.bfloat16))
+    assert_exact(got, want, "bf16 outputs")
+    # the same float32 values reach the batched combine as bf16 rows (8 slots per token, one
+    # valid): 16384 tokens, row t % R each
+    yb = want
+    T = 16384
+    rows8 = np.full((T, 8), -1, np.int32)
+    rows8[:, 0] = np.arange(T) % R
+    w8 = np.ones((T, 8), np.float32)
+    want8 = oracle.unpermute_combine(yb, rows8, w8, np.uint16)
+    got8 = host(m.unpermute_combine(dev(yb), dev(rows8), dev(w8), out_dtype=torch.bfloat16))
+    assert_exact(got8, want8, "bf16 batched outputs")
+
+
 def _e4m3_boundary_rows():
     """float32 rows of 8 whose first element is 448 (so the block's scale is exactly 1 and every
     code is the E4M3 rounding of the value itself), the other 7 taken in turn from: every finite
