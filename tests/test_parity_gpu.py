@@ -121,8 +121,8 @@ def check_index(m, ids, w, E, cap=0, gs=0, align=0):
     return ix, want
 
 
-@pytest.mark.parametrize("T,E,K", [(1, 1, 1), (5, 3, 2), (300, 8, 2), (4099, 64, 8), (2000, 256, 8),
-                                   (1500, 1024, 32), (700, 40, 7), (9000, 128, 4), (50000, 64, 8),
+@pytest.mark.parametrize("T,E,K", [(1, 1, 1), (5, 3, 2), (300, 8, 2), (512, 64, 8), (4097, 16, 1), (4099, 64, 8),
+                                   (2000, 256, 8), (1500, 1024, 32), (700, 40, 7), (9000, 128, 4), (50000, 64, 8),
                                    (33333, 130, 6)])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_build_index_standard(m, T, E, K, weighted):
@@ -193,7 +193,8 @@ def test_build_index_drop_and_pad(m, T, E, K, cap):
 @pytest.mark.parametrize("T,E,K,gs", [(300, 8, 2, 2), (4099, 64, 8, 8), (2000, 256, 8, 8), (500, 32, 8, 32),
                                       (700, 96, 6, 1), (1000, 1024, 8, 32), (3, 4, 2, 2), (50000, 64, 6, 8),
                                       (20000, 36, 5, 3), (3000, 1024, 8, 1), (1000, 64, 32, 4),
-                                      (777, 128, 16, 16), (900, 16, 1, 4), (1200, 48, 4, 6)])
+                                      (777, 128, 16, 16), (900, 16, 1, 4), (1200, 48, 4, 6), (512, 64, 8, 8),
+                                      (4097, 16, 1, 2), (1365, 30, 3, 5)])
 def test_build_index_groups(m, T, E, K, gs):
     say(f"build_index group T={T} E={E} K={K} gs={gs}")
     key = wl.case_key(24, T, E, K)

@@ -32,7 +32,9 @@
 //             of two a token's slots sit in consecutive lanes of one wavefront: the first slot
 //             of each (token, group) is found with ballots, and the rank kernel hands its group
 //             slot to the token's other slots of the group and writes esrc itself.
-// With no tokens one single-workgroup launch writes the zero counts and the marks.
+// With no tokens one single-workgroup launch writes the zero counts and the marks; with at most
+// one 512-slot batch per rank wavefront (T*K <= 4096) the rank kernel runs alone as one
+// workgroup and takes the totals from its own per-wave counts (no histogram launch).
 // The drop-and-pad capacity rule ([Scratch] §18, §26.6), the expert alignment ([Combine] §6:
 // segments rounded up to a multiple of A with padding rows, the segment starts being the scan of
 // the aligned lengths) and the group (send once per rank) slots ([CANN] §1(1)) are applied
@@ -214,6 +216,10 @@ __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(m); }
 constexpr int kRankWaves = 8;
 constexpr int kRankThreads = kRankWaves * kWave;
 constexpr int kSpan = kRankBatch * kWave;  // slots whose loads a wavefront issues together
+// up to this many routed slots (one batch per wavefront) the index is built by one workgroup
+// in one launch: T1024 K2 E8 0.030 -> 0.025 ms per step; at T4096 K2 E64 (two batches per
+// wavefront) the single workgroup lost, 0.061 against 0.055 ms
+constexpr int64_t kSingleTileSlots = static_cast<int64_t>(kRankWaves) * kSpan;
 
 // True when slot i = (t, k) is the first of token t's slots in group g. The token's earlier
 // slots are in `ids` (the current batch, starting at slot base0) or, when the token straddles
@@ -345,7 +351,9 @@ __device__ int32_t segment_starts(const int32_t *tot, int nkeys, int align, int3
 // first row of the key. Phase C: every wave walks its slots in order, 64 at a time, and ranks
 // them against its own running counters. Finally the workgroups together write the padding
 // (drop-and-pad) or unused rows.
-template <bool kGroups>
+// kSingle: one workgroup holds all tokens (small inputs): the totals come from its own per-wave
+// counts after phase A, with no histogram launch and no tile sums before it.
+template <bool kGroups, bool kSingle>
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
@@ -385,28 +393,41 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     float w_first[kRankBatch];
     load_batch(a, s0, s1, want_w, e_first, w_first);
 
-    // ---- every key's first row, and this tile's first row inside it, from the tile counts
-    // (each workgroup adds up the counts of all tiles itself: no separate scan pass)
-    // (expert and group counts share a row, so one pass of loads covers both)
-    tile_sums(a.hist, a.Hp, a.Hp, a.ntiles, tile, tot, pre, ids_all);
-    const int32_t rows_used = segment_starts(tot_e, a.E, a.cap > 0 ? 1 : a.align, seg_e, wsum);
-    int32_t n_slots = 0;
-    if (kGroups)
-        n_slots = segment_starts(tot_g, a.G, 1, seg_g, wsum);
-    if (tile == 0) {  // the per-expert (and per-group) results, once
-        for (int e = tid; e < a.E; e += kRankThreads) {
-            const int32_t cnt = tot_e[e];
-            a.ix.counts[e] = cnt;
-            a.ix.group_list[e] = seg_e[e] + (a.cap > 0 ? cnt : static_cast<int32_t>(round_up(cnt, a.align)));
-            if (a.ix.kept_counts)
-                a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
+    // every key's first row from the totals; tile 0 writes the per-expert (and per-group) results
+    int32_t rows_used = 0;
+    auto segments = [&]() {
+        rows_used = segment_starts(tot_e, a.E, a.cap > 0 ? 1 : a.align, seg_e, wsum);
+        int32_t n_slots = 0;
+        if (kGroups)
+            n_slots = segment_starts(tot_g, a.G, 1, seg_g, wsum);
+        if (tile == 0) {
+            for (int e = tid; e < a.E; e += kRankThreads) {
+                const int32_t cnt = tot_e[e];
+                a.ix.counts[e] = cnt;
+                a.ix.group_list[e] = seg_e[e] + (a.cap > 0 ? cnt : static_cast<int32_t>(round_up(cnt, a.align)));
+                if (a.ix.kept_counts)
+                    a.ix.kept_counts[e] = a.cap > 0 ? min(cnt, a.cap) : cnt;
+            }
+            if (kGroups) {
+                for (int g = tid; g < a.G; g += kRankThreads)
+                    a.ix.group_counts[g] = tot_g[g];
+                if (tid == 0)
+                    a.ix.n_slots[0] = n_slots;
+            }
         }
-        if (kGroups) {
-            for (int g = tid; g < a.G; g += kRankThreads)
-                a.ix.group_counts[g] = tot_g[g];
-            if (tid == 0)
-                a.ix.n_slots[0] = n_slots;
+    };
+    if constexpr (kSingle) {
+        if (kGroups) {  // slot_of starts as "absent" (the histogram kernel does this otherwise)
+            for (int64_t i = tid; i < a.T * a.G; i += kRankThreads)
+                a.ix.slot_of[i] = -1;
         }
+        __syncthreads();  // the zeroed counters before phase A's atomics
+    } else {
+        // the totals, and this tile's first row inside each key, from the tile counts (each
+        // workgroup adds up the counts of all tiles itself: no separate scan pass; expert and
+        // group counts share a row, so one pass of loads covers both)
+        tile_sums(a.hist, a.Hp, a.Hp, a.ntiles, tile, tot, pre, ids_all);
+        segments();
     }
 
     // ---- phase A: per-wave counts
@@ -448,6 +469,27 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
+
+    if constexpr (kSingle) {  // the totals are this workgroup's own counts
+        for (int e = tid; e < a.E; e += kRankThreads) {
+            int32_t sum = 0;
+            for (int w = 0; w < kRankWaves; ++w)
+                sum += cnt_e[w * a.E + e];
+            tot_e[e] = sum;
+            pre_e[e] = 0;
+        }
+        if (kGroups) {
+            for (int g = tid; g < a.G; g += kRankThreads) {
+                int32_t sum = 0;
+                for (int w = 0; w < kRankWaves; ++w)
+                    sum += cnt_g[w * a.G + g];
+                tot_g[g] = sum;
+                pre_g[g] = 0;
+            }
+        }
+        __syncthreads();
+        segments();
+    }
 
     // ---- phase B: each wave's first row per key
     {
@@ -755,19 +797,28 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
         return launch_status();
     }
 
-    const size_t lds_hist = sizeof(int32_t) * static_cast<size_t>(a.Hp);
-    if (G > 0)
-        hipLaunchKernelGGL(hist_kernel<true>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
-    else
-        hipLaunchKernelGGL(hist_kernel<false>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
-    if ((st = launch_status()) != MOE_OK)
-        return st;
     const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 1) * (E + G) + 2 * static_cast<size_t>(a.Hp) +
                                                static_cast<size_t>(kRankWaves) * kSpan);
-    if (G > 0)
-        hipLaunchKernelGGL(rank_kernel<true>, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
-    else
-        hipLaunchKernelGGL(rank_kernel<false>, dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+    if (T * K <= kSingleTileSlots) {  // one workgroup, one launch
+        a.tile_tokens = static_cast<int32_t>(T);
+        a.ntiles = 1;
+        if (G > 0)
+            hipLaunchKernelGGL((rank_kernel<true, true>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
+        else
+            hipLaunchKernelGGL((rank_kernel<false, true>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
+    } else {
+        const size_t lds_hist = sizeof(int32_t) * static_cast<size_t>(a.Hp);
+        if (G > 0)
+            hipLaunchKernelGGL(hist_kernel<true>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
+        else
+            hipLaunchKernelGGL(hist_kernel<false>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
+        if ((st = launch_status()) != MOE_OK)
+            return st;
+        if (G > 0)
+            hipLaunchKernelGGL((rank_kernel<true, false>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+        else
+            hipLaunchKernelGGL((rank_kernel<false, false>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+    }
     if ((st = launch_status()) != MOE_OK)
         return st;
     if (G > 0 && (K & (K - 1)) != 0) {  // with K a power of two the rank kernel writes esrc
