@@ -122,8 +122,8 @@ def check_index(m, ids, w, E, cap=0, gs=0, align=0):
 
 
 @pytest.mark.parametrize("T,E,K", [(1, 1, 1), (5, 3, 2), (300, 8, 2), (512, 64, 8), (4097, 16, 1), (4099, 64, 8),
-                                   (2000, 256, 8), (1500, 1024, 32), (700, 40, 7), (9000, 128, 4), (50000, 64, 8),
-                                   (33333, 130, 6)])
+                                   (1024, 64, 8), (8193, 16, 1), (256, 1024, 32), (2000, 256, 8), (1500, 1024, 32),
+                                   (700, 40, 7), (9000, 128, 4), (50000, 64, 8), (33333, 130, 6)])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_build_index_standard(m, T, E, K, weighted):
     say(f"build_index standard T={T} E={E} K={K} weighted={weighted}")
