@@ -19,8 +19,10 @@
  *     H < 1, group size not dividing E, ...) or MOE_ERR_UNSUPPORTED (E > 1024, K > 32, a
  *     hidden row longer than 2^31 - 1 bytes, more than 2^31 - 1 tokens, or a combination the
  *     call does not implement). MOE_ERR_HIP means a launch failed.
- *   - A size of zero tokens / rows is valid and launches nothing (an empty rank or an expert
- *     with no tokens must work, [Scratch] §26.1-26.2).
+ *   - A size of zero tokens / rows is valid (an empty rank or an expert with no tokens must
+ *     work, [Scratch] §26.1-26.2): a call with nothing to write launches nothing, and
+ *     moe_build_index with T = 0 still writes its per-expert results (zero counts) and the
+ *     marks of its rows (padding or unused).
  *   - Memory safety does not depend on the data: an expert id outside [0, E) routes nowhere
  *     (the pages write -1 for "no expert"), a row index outside the source range selects a
  *     zero row (permute) or no term (combine). Expert ids in one row of topk_idx must be
