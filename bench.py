@@ -8,11 +8,17 @@ the two-stage dedup dispatch and the combine is the per-group pre-combine plus t
 
 Prints ONE JSON line. `value` is the whole step's algorithmic bytes (each stage's minimal HBM
 traffic, computed from the actual routing) divided by the measured step time: by default the
-time of K replays of the step captured once in a HIP graph (`--eager`: the eagerly launched
-steps; `ms_per_step_eager` is reported either way). In the eager pass every kernel call is
-bracketed by HIP events on the launch stream (`kernel_us`; `stage_us` sums them per stage);
-`roofline` describes the dominant HBM-bound kernel with its own event time; `cpu_baseline` is the
-CPU oracle on the same workload on this host.
+mean of K replays of the step captured once in a HIP graph, each replay timed by HIP events on
+its stream and preceded (outside the events) by a cache flush -- 512 MiB written, then another
+512 MiB read, which leaves the 256 MB MALL and every XCD's L2 holding only clean lines of
+neither the step's inputs nor its outputs -- so that no workload, however small, is served from
+a cache (`--eager`: the eagerly launched steps, timed the same way). The same K replays
+back to back without flushes give `ms_per_step_warm`; K eager steps back to back give
+`ms_per_step_eager`. Per-kernel times (`kernel_us`: mean, with `kernel_us_median` and
+`kernel_us_min`) come from a separate eager pass in which every kernel call is flushed before
+and bracketed by events; `stage_us` sums them per stage; `roofline` describes the dominant
+HBM-bound kernel with its own mean event time; `cpu_baseline` is the CPU oracle on the same
+workload on this host, all usable cores (up to 16 threads) and one thread.
 """
 from __future__ import annotations
 
@@ -89,12 +95,42 @@ def parse_args():
     p.add_argument("--eager", action="store_true",
                    help="time the eagerly launched steps only; by default the step is also captured once in a "
                         "HIP graph and value / ms_per_step come from K replays of it (per-kernel times always "
-                        "come from the eager pass)")
+                        "come from an eager pass)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    p.add_argument("--no-flush", action="store_true",
+                   help="no cache flush before the timed steps and kernel calls (they still run one by one "
+                        "between events)")
     return p.parse_args()
+
+
+FLUSH_BYTES = 512 << 20  # twice the MI355X MALL (256 MB)
+
+
+class CacheFlush:
+    """Evicts the step's data from the caches: 512 MiB written by a fill kernel, then a different
+    512 MiB read by a reduction. The read also pushes the fill's dirty lines out to HBM, so the
+    caches end up holding only clean lines of the second buffer, which a timed kernel can evict
+    without writing anything back."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.empty(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda")
+        self.b = torch.zeros(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.a.fill_(self.n)
+        self.b.sum()
+
+
+def _stats(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return float(a.mean()), float(np.median(a)), float(a.min())
 
 
 def source_digest(kernel: str) -> str:
@@ -272,28 +308,53 @@ def main():
                    lambda: m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=xp)),
                   ("combine", "combine", lambda: m.unpermute_combine(src, ix.row_of, gw, out=out))]
 
-    def step(ev=None):
-        for i, (_, _, call) in enumerate(calls):
-            if ev is not None:
-                ev[i].record()
+    def step():
+        for _, _, call in calls:
             call()
-        if ev is not None:
-            ev[len(calls)].record()
+
+    flush = None if args.no_flush else CacheFlush(torch)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # eager steps back to back (launch gaps included)
     t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_per_step = elapsed * 1e3 / args.steps
-    ms_per_step_eager = ms_per_step
+    ms_per_step_eager = (time.perf_counter() - t_start) * 1e3 / args.steps
+
+    # per-kernel times: every call flushed before and bracketed by events on its stream
+    kev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        for i, (_, _, call) in enumerate(calls):
+            if flush is not None:
+                flush()
+            kev[s_][i][0].record()
+            call()
+            kev[s_][i][1].record()
+    torch.cuda.synchronize()
+
+    def timed_steps(run_step):
+        """K steps, each flushed before (outside its events) unless --no-flush; per-step ms."""
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in sev:
+            if flush is not None:
+                flush()
+            a.record()
+            run_step()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in sev]
+
     launch = "eager"
+    ms_per_step_warm = ms_per_step_eager
+    replay = step
     if not args.eager:
         # the same calls captured once; no call allocates, waits on the host or records a memset
         try:
@@ -310,18 +371,22 @@ def main():
             torch.cuda.synchronize()
             launch = f"eager (graph capture failed: {type(e).__name__})"
         else:
+            replay = graph.replay
             for _ in range(max(3, args.warmup)):
-                graph.replay()
+                replay()
             torch.cuda.synchronize()
             t_start = time.perf_counter()
             for _ in range(args.steps):
-                graph.replay()
+                replay()
             torch.cuda.synchronize()
-            ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+            ms_per_step_warm = (time.perf_counter() - t_start) * 1e3 / args.steps
             launch = "hip graph replay"
-    kernel_us = {}
+    step_ms = timed_steps(replay)
+    ms_per_step, ms_per_step_median, ms_per_step_min = _stats(step_ms)
+    kernel_us, kernel_us_median, kernel_us_min = {}, {}, {}
     for i, (name, _, _) in enumerate(calls):
-        kernel_us[name] = float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) * 1e3 for s in range(args.steps)]))
+        kernel_us[name], kernel_us_median[name], kernel_us_min[name] = _stats(
+            [kev[s_][i][0].elapsed_time(kev[s_][i][1]) * 1e3 for s_ in range(args.steps)])
     stage_us = {}
     for name, stage, _ in calls:
         stage_us[stage] = stage_us.get(stage, 0.0) + kernel_us[name]
@@ -399,6 +464,8 @@ def main():
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
         "stage_gbs": {k: gbs(stage_bytes[k], stage_us[k]) for k in stage_us if k in hbm_stages},
         "kernel_us": {k: round(v, 2) for k, v in kernel_us.items()},
+        "kernel_us_median": {k: round(v, 2) for k, v in kernel_us_median.items()},
+        "kernel_us_min": {k: round(v, 2) for k, v in kernel_us_min.items()},
         "kernel_gbs": {k: gbs(kbytes[k], kernel_us[k]) for k in hbm_kernels},
         "kernel_bytes": kbytes,
         "max_expert_count": int(counts.max()), "empty_experts": int((counts == 0).sum()),
@@ -407,26 +474,22 @@ def main():
     if args.backward:
         result["pass"] = "backward"
     result["launch"] = launch
+    result["timing"] = (("each step and each kernel call preceded by a 512 MiB write + 512 MiB read cache flush "
+                         "outside its events" if flush is not None else "no cache flush") +
+                        "; ms_per_step = mean of the per-step event times")
+    result["ms_per_step_median"] = round(ms_per_step_median, 4)
+    result["ms_per_step_min"] = round(ms_per_step_min, 4)
+    result["ms_per_step_warm"] = round(ms_per_step_warm, 4)
     result["ms_per_step_eager"] = round(ms_per_step_eager, 4)
-    if not args.no_cpu_baseline and args.fp8:
-        result["cpu_baseline"] = None  # the oracle baseline is timed on the bf16 path
-    elif not args.no_cpu_baseline:
-        if args.backward:
-            result["cpu_baseline"] = cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes,
-                                                           args.bf16_partials)
-        else:
-            result["cpu_baseline"] = cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes,
-                                                  args.bf16_partials)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes,
+                                              args.bf16_partials, args.fp8, fp8_block, args.backward)
     print(json.dumps(result), flush=True)
 
 
-def _oracle_route(oracle, logits_np, K, gs, rg):
-    return oracle.route_topk_grouped(logits_np, K, gs, rg) if rg else oracle.route_topk(logits_np, K)
-
-
-def _passes(run_once, min_seconds=10.0, min_passes=2, max_passes=8):
-    """Runs the oracle pass until at least min_seconds of CPU work (2..8 passes); returns the
-    best pass time, the number of passes and the total seconds."""
+def _passes(run_once, min_seconds, min_passes=2, max_passes=8):
+    """Runs the oracle pass until at least min_seconds of wall-clock time (2..8 passes); returns
+    the best pass time, the number of passes and the total seconds."""
     times = []
     while len(times) < max_passes and (len(times) < min_passes or sum(times) < min_seconds):
         t0 = time.perf_counter()
@@ -435,74 +498,81 @@ def _passes(run_once, min_seconds=10.0, min_passes=2, max_passes=8):
     return min(times), len(times), sum(times)
 
 
-def cpu_baseline(cid, c, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16_partials=False):
-    """The CPU oracle as it stands (single thread) over the same whole workload: passes repeated
-    until about 10 s of CPU work, the best pass reported."""
-    import numpy as np
-
-    import oracle
-
-    T, E, K, gs = c["T"], c["E"], c["K"], c["group_size"]
-    out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
-    part_dt = np.uint16 if bf16_partials else np.float32
-
-    def run_once():
-        idx, w = _oracle_route(oracle, logits_np, K, gs, rg)
-        ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
-        if gs:
-            gbuf = oracle.permute(x_np, ix["gsrc"])
-            xp = oracle.permute(gbuf, ix["esrc"])
-        else:
-            xp = oracle.permute(x_np, ix["sorted_indices"])
-        y = xp if y_np is None else y_np
-        if gs:
-            n = int(ix["n_slots"][0])
-            part = oracle.group_precombine(y, ix["row_of"], w, idx, E, gs, ix["slot_of"], n, out_dtype=part_dt)
-            oracle.unpermute_combine(part, ix["slot_of"], None, out_dt)
-        else:
-            oracle.unpermute_combine(y, ix["row_of"], w, out_dt)
-
-    best, n, total = _passes(run_once)
-    return {"value": round(step_bytes / best / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole workload ({c['name']}) per pass, best of {n} passes "
-                      f"({total:.1f} s of CPU work), single thread",
-            "seconds_per_pass": round(best, 3),
-            "routed_tokens_per_s": round(T * K / best, 1)}
-
-
-def cpu_baseline_backward(cid, c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16_partials=False):
-    """The CPU oracle's backward (single thread) on the same saved forward state: passes repeated
-    until about 10 s of CPU work, the best pass reported."""
+def cpu_baseline(c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16_partials=False, fp8=False,
+                 fp8_block=128, backward=False):
+    """The CPU oracle as it stands, over the same whole workload and mode as the GPU step (the
+    forward: route, index, dispatch -- the FP8 one with --fp8 --, combine; or the backward on one
+    saved forward index), timed twice: on all usable host cores (the oracle's per-token and
+    per-row functions over disjoint slices on up to 16 threads; the index build stays one call)
+    and on one thread. Passes repeat until a few seconds of wall-clock time; the best pass of
+    each leg is reported, `value` from the all-cores leg."""
     import numpy as np
 
     import oracle
     import workloads as wl
+    from oracle.parallel import Pool, Serial, cpu_model, usable_cores
 
     T, H, E, K, gs = c["T"], c["H"], c["E"], c["K"], c["group_size"]
     out_dt = np.uint16 if c["dtype"] == "bf16" else np.float32
     part_dt = np.uint16 if bf16_partials else np.float32
-    idx, w = _oracle_route(oracle, logits_np, K, gs, rg)
-    ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
-    rows = len(ix["sorted_indices"])
-    y = oracle.permute(x_np, ix["sorted_indices"]) if y_np is None else y_np
-    dout = wl.expert_outputs((*key, 7), T, H, c["dtype"])
-    dxp = wl.expert_outputs((*key, 8), rows, H, c["dtype"])
+    if backward:
+        idx0, w0 = Serial.route_topk(logits_np, K, gs, rg)
+        ix0 = oracle.build_index(idx0, w0, E, capacity=cap, group_size=gs, alignment=align)
+        rows = len(ix0["sorted_indices"])
+        y_b = oracle.permute(x_np, ix0["sorted_indices"]) if y_np is None else y_np
+        dout = wl.expert_outputs((*key, 7), T, H, c["dtype"])
+        dxp = wl.expert_outputs((*key, 8), rows, H, c["dtype"])
 
-    def run_once():
-        _, dw = oracle.combine_backward(dout, y, ix["row_of"], w, out_dt)
+    def run_once(o):
+        if backward:
+            _, dw = o.combine_backward(dout, y_b, ix0["row_of"], w0, out_dt)
+            if gs:
+                n = int(ix0["n_slots"][0])
+                part = o.group_precombine(dxp, ix0["row_of"], None, idx0, E, gs, ix0["slot_of"], n, out_dtype=part_dt)
+                o.unpermute_combine(part, ix0["slot_of"], None, out_dt)
+            else:
+                o.unpermute_combine(dxp, ix0["row_of"], None, out_dt)
+            o.route_topk_backward(idx0, w0, dw, E)
+            return
+        idx, w = o.route_topk(logits_np, K, gs, rg)
+        ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
+        maps = [ix["gsrc"], ix["esrc"]] if gs else [ix["sorted_indices"]]  # group mode: send, then receive
+        if fp8:
+            xp = None
+            for a in o.quantize_fp8(x_np, fp8_block):  # the codes, then the scales, each moved like rows
+                for mp in maps:
+                    a = o.permute(a, mp)
+        else:
+            xp = x_np
+            for mp in maps:
+                xp = o.permute(xp, mp)
+        y = xp if y_np is None else y_np
         if gs:
             n = int(ix["n_slots"][0])
-            part = oracle.group_precombine(dxp, ix["row_of"], None, idx, E, gs, ix["slot_of"], n, out_dtype=part_dt)
-            oracle.unpermute_combine(part, ix["slot_of"], None, out_dt)
+            part = o.group_precombine(y, ix["row_of"], w, idx, E, gs, ix["slot_of"], n, out_dtype=part_dt)
+            o.unpermute_combine(part, ix["slot_of"], None, out_dt)
         else:
-            oracle.unpermute_combine(dxp, ix["row_of"], None, out_dt)
-        oracle.route_topk_backward(idx, w, dw, E)
+            o.unpermute_combine(y, ix["row_of"], w, out_dt)
 
-    best, n, total = _passes(run_once)
-    return {"value": round(step_bytes / best / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole backward of the workload ({c['name']}) per pass, best of {n} passes "
-                      f"({total:.1f} s of CPU work), single thread",
-            "seconds_per_pass": round(best, 3)}
+    with Pool() as pool:
+        best, n, total = _passes(lambda: run_once(pool), min_seconds=4.0)
+        threads = pool.threads
+    best1, n1, total1 = _passes(lambda: run_once(Serial()), min_seconds=6.0)
+    what = ("the whole backward of the workload" if backward else "the whole workload") + f" ({c['name']}"
+    what += (", FP8 dispatch" if fp8 else "") + (", bf16 partials" if bf16_partials else "") + ")"
+    res = {"value": round(step_bytes / best / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{what} per pass, best of {n} passes ({total:.1f} s wall, {threads} threads); the "
+                     f"oracle's per-token / per-row functions over disjoint slices, the index build in one call",
+           "seconds_per_pass": round(best, 3),
+           "host": {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "usable_cores": usable_cores(),
+                    "threads_used": threads},
+           "single_thread": {"value": round(step_bytes / best1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                             "seconds_per_pass": round(best1, 3),
+                             "sample": f"{what} per pass, best of {n1} passes ({total1:.1f} s)"}}
+    if not backward:
+        res["routed_tokens_per_s"] = round(T * K / best, 1)
+        res["single_thread"]["routed_tokens_per_s"] = round(T * K / best1, 1)
+    return res
 
 
 if __name__ == "__main__":

@@ -102,6 +102,16 @@ def _poisoned(shape, dtype) -> np.ndarray:
     return a
 
 
+def _out(out, shape, dtype, what) -> np.ndarray:
+    """The caller's output array (written in place: a C-contiguous array of exactly this shape and
+    dtype, e.g. a slice of rows of a larger one), or a fresh poisoned one."""
+    if out is None:
+        return _poisoned(shape, dtype)
+    if out.shape != tuple(shape) or out.dtype != np.dtype(dtype) or not out.flags.c_contiguous:
+        raise ValueError(f"{what}: out must be a C-contiguous {np.dtype(dtype)} array of shape {tuple(shape)}")
+    return out
+
+
 def capacity(tokens: int, top_k: int, num_experts: int, cf_num: int, cf_den: int) -> int:
     """Expert capacity ceil(tokens*top_k/num_experts*cf), cf = cf_num/cf_den, exact."""
     v = _load().oracle_capacity(tokens, top_k, num_experts, cf_num, cf_den)
@@ -180,22 +190,22 @@ def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_s
     return out
 
 
-def permute(src: np.ndarray, src_row: np.ndarray) -> np.ndarray:
+def permute(src: np.ndarray, src_row: np.ndarray, out=None) -> np.ndarray:
     """dst[i] = src[src_row[i]] bitwise; rows outside [0, len(src)) give zeros, except -2
-    (unused slack), which leaves the row as it is (here: the NaN poison)."""
+    (unused slack), which leaves the row as it is (here: the NaN poison, or out's contents)."""
     src = np.ascontiguousarray(src)
     if src.dtype != np.uint8:
         _dt_of(src)
     src_rows, H = src.shape
     src_row = _c(src_row, np.int32).reshape(-1)
-    dst = _poisoned((src_row.shape[0], H), src.dtype)
+    dst = _out(out, (src_row.shape[0], H), src.dtype, "permute")
     rc = _load().oracle_permute(_ptr(src), src_rows, H, src.dtype.itemsize, _ptr(src_row),
                                 src_row.shape[0], _ptr(dst))
     _check(rc, "permute")
     return dst
 
 
-def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype, bias=None) -> np.ndarray:
+def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype, bias=None, out=None) -> np.ndarray:
     """out[t] = sum_k w[t,k] * y[row_of[t,k]] (float32 FMA chain in k order) [+ bias[t]]."""
     y = np.ascontiguousarray(y)
     y_dt = _dt_of(y)
@@ -203,7 +213,7 @@ def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype, bias=None
     row_of = _c(row_of, np.int32)
     T, K = row_of.shape
     w = None if w is None else _c(w, np.float32).reshape(T, K)
-    out = _poisoned((T, H), out_dtype)
+    out = _out(out, (T, H), out_dtype, "unpermute_combine")
     out_dt = _dt_of(out)
     if bias is not None:
         bias = np.ascontiguousarray(bias)
@@ -215,9 +225,10 @@ def unpermute_combine(y: np.ndarray, row_of: np.ndarray, w, out_dtype, bias=None
 
 
 def group_precombine(y: np.ndarray, row_of, w, topk_idx, E: int, group_size: int,
-                     slot_of: np.ndarray, slots_cap: int, out_dtype=np.float32) -> np.ndarray:
+                     slot_of: np.ndarray, slots_cap: int, out_dtype=np.float32, out=None) -> np.ndarray:
     """Per-(token, group) weighted partial sums (a float32 chain) stored at slot_of[t, g], as
-    float32 or rounded once to bf16 (out_dtype np.uint16)."""
+    float32 or rounded once to bf16 (out_dtype np.uint16); rows slot_of does not name are left
+    as they are (the poison, or out's contents)."""
     y = np.ascontiguousarray(y)
     y_dt = _dt_of(y)
     y_rows, H = y.shape
@@ -226,7 +237,7 @@ def group_precombine(y: np.ndarray, row_of, w, topk_idx, E: int, group_size: int
     topk_idx = _c(topk_idx, np.int32)
     w = None if w is None else _c(w, np.float32)
     slot_of = _c(slot_of, np.int32)
-    partials = _poisoned((slots_cap, H), out_dtype)
+    partials = _out(out, (slots_cap, H), out_dtype, "group_precombine")
     rc = _load().oracle_group_precombine(_ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
                                          _ptr(topk_idx), T, K, E, group_size, _ptr(slot_of),
                                          slots_cap, _ptr(partials), _dt_of(partials))
@@ -234,9 +245,11 @@ def group_precombine(y: np.ndarray, row_of, w, topk_idx, E: int, group_size: int
     return partials
 
 
-def combine_backward(dout: np.ndarray, y: np.ndarray, row_of: np.ndarray, w, dy_dtype, want_dw: bool = True):
+def combine_backward(dout: np.ndarray, y: np.ndarray, row_of: np.ndarray, w, dy_dtype, want_dw: bool = True,
+                     out=None):
     """Backward of the weighted combine: dy[row_of[t,k]] = w[t,k] * dout[t] (zero elsewhere),
-    dw[t,k] = <dout[t], y[row_of[t,k]]> (double sum, rounded to float32). Returns (dy, dw|None)."""
+    dw[t,k] = <dout[t], y[row_of[t,k]]> (double sum, rounded to float32). Returns (dy, dw|None);
+    out = (dy, dw|None) writes into the caller's arrays."""
     dout = np.ascontiguousarray(dout)
     dout_dt = _dt_of(dout)
     y = np.ascontiguousarray(y)
@@ -246,8 +259,11 @@ def combine_backward(dout: np.ndarray, y: np.ndarray, row_of: np.ndarray, w, dy_
     T, K = row_of.shape
     assert dout.shape == (T, H)
     w = None if w is None else _c(w, np.float32).reshape(T, K)
-    dy = _poisoned((y_rows, H), dy_dtype)
-    dw = np.full((T, K), np.nan, np.float32) if want_dw else None
+    dy = _out(None if out is None else out[0], (y_rows, H), dy_dtype, "combine_backward dy")
+    dw = None
+    if want_dw:
+        dw = np.full((T, K), np.nan, np.float32) if out is None or out[1] is None else \
+            _out(out[1], (T, K), np.float32, "combine_backward dw")
     rc = _load().oracle_combine_backward(_ptr(dout), dout_dt, _ptr(y), y_dt, y_rows, H, _ptr(row_of), _ptr(w),
                                          T, K, _ptr(dy), _dt_of(dy), _ptr(dw))
     _check(rc, "combine_backward")
@@ -274,11 +290,16 @@ def e4m3_to_f32(c: int) -> float:
     return float(_load().oracle_e4m3_to_f32(int(c)))
 
 
-def quantize_fp8(x: np.ndarray, block: int):
-    """Per-(token, block) E4M3 quantization: returns (q uint8 [T, H], scales float32 [T, H/block])."""
+def quantize_fp8(x: np.ndarray, block: int, out=None):
+    """Per-(token, block) E4M3 quantization: returns (q uint8 [T, H], scales float32 [T, H/block]);
+    out = (q, scales) writes into the caller's arrays."""
     x = np.ascontiguousarray(x)
     T, H = x.shape
-    q = np.full((T, H), 0x7F, np.uint8)
-    scales = np.full((T, H // block if block > 0 else 0), np.nan, np.float32)
+    if out is None:
+        q = np.full((T, H), 0x7F, np.uint8)
+        scales = np.full((T, H // block if block > 0 else 0), np.nan, np.float32)
+    else:
+        q = _out(out[0], (T, H), np.uint8, "quantize_fp8 q")
+        scales = _out(out[1], (T, H // block if block > 0 else 0), np.float32, "quantize_fp8 scales")
     _check(_load().oracle_quantize_fp8(_ptr(x), _dt_of(x), T, H, block, _ptr(q), _ptr(scales)), "quantize_fp8")
     return q, scales

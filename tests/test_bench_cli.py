@@ -24,3 +24,40 @@ def test_help_lists_the_options():
     assert r.returncode == 0
     for opt in ("--steps", "--warmup", "--workload", "--alignment", "--route-groups", "--fp8", "--backward", "--eager", "--bf16-partials"):
         assert opt in r.stdout
+
+
+def test_help_lists_the_flush_option():
+    assert "--no-flush" in _run("--help").stdout
+
+
+def test_cpu_baseline_legs_on_the_host():
+    """The CPU-baseline leg on workload 1 (the small float32 workload), forward, FP8-free and
+    backward: both legs report a rate, the all-cores leg names its threads and the host."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as wl
+
+    c = wl.WORKLOADS[1]
+    key = wl.workload_key(1)
+    logits = wl.router_logits(key, c["T"], c["E"], zipf_s=c["zipf_s"])
+    x = wl.hidden_states(key, c["T"], c["H"], c["dtype"])
+    for backward in (False, True):
+        r = bench.cpu_baseline(c, key, logits, x, None, 0, 0, 0, 10 ** 7, backward=backward)
+        assert r["kind"] == "oracle" and r["value"] > 0 and r["single_thread"]["value"] > 0
+        assert 1 <= r["cores"] <= 16 and r["host"]["threads_used"] == r["cores"]
+        assert r["host"]["nproc"] >= 1 and r["host"]["usable_cores"] >= 1 and r["host"]["cpu_model"]
+
+
+def test_cpu_baseline_fp8_and_group_modes():
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as wl
+
+    c = dict(wl.WORKLOADS[4], T=256, H=256)  # workload 4's layout at a host-friendly size
+    key = (4000,)
+    logits = wl.router_logits(key, c["T"], c["E"], zipf_s=c["zipf_s"])
+    x = wl.hidden_states(key, c["T"], c["H"], c["dtype"])
+    y = wl.expert_outputs(key, c["T"] * c["K"], c["H"], c["dtype"])
+    for fp8, bf16p, rg in ((True, False, 0), (False, True, 4), (True, True, 4)):
+        r = bench.cpu_baseline(c, key, logits, x, y, 0, 0, rg, 10 ** 7, bf16_partials=bf16p, fp8=fp8)
+        assert r["value"] > 0 and ("FP8" in r["sample"]) == fp8

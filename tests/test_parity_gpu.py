@@ -3,8 +3,10 @@
 Small cases span several tiles and ragged tails; edge cases cover empty inputs, experts and
 groups with no tokens, slots that route nowhere, out-of-range ids and rows, capacities below
 and above the largest count; the five named workloads run at full size through the same
-entry points and launch configuration that bench.py times, with index arrays compared in full
-and permuted / combined rows compared on a sample the oracle computes row by row.
+entry points and launch configuration that bench.py times (every mode it offers: expert
+alignment, group-limited routing, the FP8 dispatch, bf16 partials, the backward), with every
+index entry, every dispatched row, every partial and every combined token compared with the
+oracle on the same inputs.
 """
 import numpy as np
 import pytest
@@ -640,15 +642,8 @@ def test_unpermute_combine_batched_path(m, H, K, with_bias):
     row_of[5] = -1
     w = wl.random_weights(key, T, K)
     bias = wl.expert_outputs((*key, 2), T, H, "bf16") if with_bias else None
-    if H == 7168:  # full-width rows: compare a sample of tokens
-        ts = sample_rows(T, 800, 73)
-        want = oracle.unpermute_combine(y, row_of[ts], w[ts], np.uint16,
-                                        bias=None if bias is None else bias[ts])
-        got = host(m.unpermute_combine(dev(y), dev(row_of), dev(w), bias=None if bias is None else dev(bias))
-                   [torch.from_numpy(ts).to(DEV)])
-    else:
-        want = oracle.unpermute_combine(y, row_of, w, np.uint16, bias=bias)
-        got = host(m.unpermute_combine(dev(y), dev(row_of), dev(w), bias=None if bias is None else dev(bias)))
+    want = oracle.unpermute_combine(y, row_of, w, np.uint16, bias=bias)
+    got = host(m.unpermute_combine(dev(y), dev(row_of), dev(w), bias=None if bias is None else dev(bias)))
     assert_exact(got, want, "combined")
 
 
@@ -701,55 +696,40 @@ def test_group_precombine_and_final_sum(m, T, E, K, gs, H, ydt, holes, layout, p
 
 
 # ------------------------------------------------------------------ the five workloads at full size
+# Every row and every token of the bench's launch configuration is compared with the oracle on the
+# same inputs; device tensors are brought to the host in row chunks so that host memory stays bounded.
+
+ROW_CHUNK = 8192
 
 
-def sample_rows(n, count, seed):
-    g = np.random.default_rng(seed)
-    s = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, size=min(count, n))]))
-    return s.astype(np.int64)
+def assert_rows_exact(got, want: np.ndarray, what: str, live=None):
+    """Device tensor `got` [N, H] against the oracle's host array `want`, bit for bit, every row
+    (rows with live[i] False -- the unused slack that no call writes -- are skipped)."""
+    assert tuple(got.shape) == want.shape, f"{what}: shape {tuple(got.shape)} != {want.shape}"
+    for a in range(0, want.shape[0], ROW_CHUNK):
+        b = min(a + ROW_CHUNK, want.shape[0])
+        g, w_ = host(got[a:b]), want[a:b]
+        if live is not None:
+            g, w_ = g[live[a:b]], w_[live[a:b]]
+        if not np.array_equal(g.view(np.uint8), w_.view(np.uint8)):
+            bad = np.flatnonzero((g.view(np.uint8) != w_.view(np.uint8)).reshape(len(g), -1).any(axis=1))
+            rows = (np.flatnonzero(live[a:b]) if live is not None else np.arange(b - a))[bad] + a
+            raise AssertionError(f"{what}: {len(bad)} rows differ in rows {a}..{b - 1}, first {rows[:5].tolist()}")
 
 
-def check_fp8_dispatch(m, x, ix, want, gs, T, K, E, block=128):
-    """FP8 dispatch at full size, as bench.py --fp8 launches it: sampled destination rows against
-    the oracle's quantization of their source tokens (codes and scales bit for bit)."""
-    xd = dev(x)
-    H = x.shape[1]
-    si = want["sorted_indices"]
-    if gs > 0:
-        G = E // gs
-        gq, gsc = m.permute_scatter_fp8(xd, ix.slot_of, T * min(K, G), block)
-        q = m.permute_grouped(gq, ix.esrc, ix.row_of)
-        sc = m.permute_grouped(gsc, ix.esrc, ix.row_of)
-    else:
-        q, sc = m.permute_scatter_fp8(xd, ix.row_of, len(si), block, src_row=ix.sorted_indices)
-    torch.cuda.synchronize()
-    rs = sample_rows(len(si), 2000, 5)
-    rs = rs[si[rs] != -2]
-    toks = si[rs]
-    real = toks >= 0
-    qs, ss = oracle.quantize_fp8(x[toks[real]], block)
-    rsd = torch.from_numpy(rs).to(DEV)
-    gq_rows, gs_rows = host(q[rsd]), host(sc[rsd])
-    assert_exact(gq_rows[real], qs, "FP8 codes (sample)")
-    assert_exact(gs_rows[real], ss, "FP8 scales (sample)")
-    assert (gq_rows[~real] == 0).all() and (gs_rows[~real] == 0).all()
-    del xd
+def assert_combined_all(got, want: np.ndarray, what: str):
+    """Every combined value within the parity tolerance, and (the same weight bits on both sides)
+    every one bit-identical."""
+    g = host(got)
+    assert_combined(g, want, what)
+    share = exact_fraction(g, want)
+    assert share == 1.0, f"{what}: bit-identical share {share}"
 
 
-def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False, bf16_partials=False):
-    """Runs route -> index -> permute -> (pre-)combine on the GPU and checks every stage
-    (align > 1: the expert-aligned layout; route_groups > 0: group-limited routing over the
-    workload's expert groups, that many groups per token)."""
-    c = wl.WORKLOADS[cfg_id]
-    T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
-    key = wl.workload_key(cfg_id)
-    say(f"workload {cfg_id}: {c['name']}")
-    logits = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])
-    x = wl.hidden_states(key, T, H, dt)
-    cap = oracle.capacity(T, K, E, *c["cf"]) if c["cf"] else 0
-    assert cap == (m.expert_capacity(T, K, E, *c["cf"]) if c["cf"] else 0)
-    gs = c["group_size"]
-
+def check_route_and_index(m, c, logits, route_groups, cap, align):
+    """Routing and the index on the GPU against the oracle, every entry; returns the GPU's
+    outputs and the oracle's index built on the GPU's weight bits."""
+    T, E, K, gs = c["T"], c["E"], c["K"], c["group_size"]
     if route_groups:
         want_i, want_w = oracle.route_topk_grouped(logits, K, gs, route_groups)
         gi, gw = m.route_topk(dev(logits), K, group_size=gs, topk_groups=route_groups)
@@ -758,73 +738,106 @@ def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False, bf16_partials=Fa
         gi, gw = m.route_topk(dev(logits), K)
     assert_exact(host(gi), want_i, "topk_idx")
     assert_rel_f32(host(gw), want_w, "topk_w")
-    # the same weight bits on both sides from here on
-    w_np = host(gw)
+    w_np = host(gw)  # the same weight bits on both sides from here on
     ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs, alignment=align)
     want = oracle.build_index(want_i, w_np, E, capacity=cap, group_size=gs, alignment=align)
-    for name in ("counts", "group_list", "sorted_indices", "row_of", "permuted_probs"):
+    for name in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs"):
         assert_exact(host(getattr(ix, name)), want[name], name)
-    rows = ix.rows
-    if fp8:
-        check_fp8_dispatch(m, x, ix, want, gs, T, K, E)
-        return None
-    xd = dev(x)
     if gs > 0:
         n = int(host(ix.n_slots)[0])
         assert n == int(want["n_slots"][0])
         assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
-        assert_exact(host(ix.esrc), want["esrc"], "esrc")
-        assert_exact(host(ix.slot_of), want["slot_of"], "slot_of")
-        # as bench.py launches it: the group buffer sized by the bound T*min(K,G), not by n
-        gbuf = m.permute_scatter(xd, ix.slot_of, T * min(K, E // gs))
-        assert_exact(host(gbuf[:n]), host(m.permute(xd, ix.gsrc[:n])), "group slots: scatter vs gather")
-        xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of)
-        assert_exact(host(xp), host(m.permute(gbuf, ix.esrc)), "receive side: grouped vs gather")
+        for name in ("slot_of", "esrc", "group_counts"):
+            assert_exact(host(getattr(ix, name)), want[name], name)
+    return gi, gw, ix, want_i, w_np, want
+
+
+FP8_BLOCK = 128  # one float32 scale per 128 elements, as bench.py --fp8
+
+
+def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False, bf16_partials=False):
+    """Runs route -> index -> dispatch -> (pre-)combine on the GPU in bench.py's launch
+    configuration and checks every stage against the oracle in full: every index entry, every
+    dispatched row (the group dispatch against the oracle's two-stage gather x -> group slots ->
+    expert rows; FP8 codes and scales against the oracle's quantization moved by its gather),
+    every partial and every combined token. align > 1: the expert-aligned layout; route_groups >
+    0: group-limited routing over the workload's expert groups, that many groups per token.
+    Returns the combined output (device)."""
+    c = wl.WORKLOADS[cfg_id]
+    T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
+    key = wl.workload_key(cfg_id)
+    say(f"workload {cfg_id}: {c['name']} align={align} route_groups={route_groups} fp8={fp8} "
+        f"bf16_partials={bf16_partials}")
+    logits = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])
+    x = wl.hidden_states(key, T, H, dt)
+    cap = oracle.capacity(T, K, E, *c["cf"]) if c["cf"] else 0
+    assert cap == (m.expert_capacity(T, K, E, *c["cf"]) if c["cf"] else 0)
+    gs = c["group_size"]
+    G = E // gs if gs else 0
+    slots = T * min(K, G) if gs else 0  # group buffers sized by the bound, as bench.py does
+    gi, gw, ix, want_i, w_np, want = check_route_and_index(m, c, logits, route_groups, cap, align)
+    rows = ix.rows
+    si = want["sorted_indices"]
+    live = si != -2  # the unused slack after the last segment is never written
+    n = int(want["n_slots"][0]) if gs else 0
+    xd = dev(x)
+
+    # ---- dispatch
+    if fp8:
+        qs, ss = oracle.quantize_fp8(x, FP8_BLOCK)
+        if gs:
+            gq, gsc = m.permute_scatter_fp8(xd, ix.slot_of, slots, FP8_BLOCK)
+            want_gq, want_gs = oracle.permute(qs, want["gsrc"]), oracle.permute(ss, want["gsrc"])
+            assert_rows_exact(gq[:n], want_gq, "FP8 group-slot codes")
+            assert_rows_exact(gsc[:n], want_gs, "FP8 group-slot scales")
+            xq = m.permute_grouped(gq, ix.esrc, ix.row_of)
+            xs = m.permute_grouped(gsc, ix.esrc, ix.row_of)
+            want_xq, want_xs = oracle.permute(want_gq, want["esrc"]), oracle.permute(want_gs, want["esrc"])
+            del gq, gsc, want_gq, want_gs
+        else:
+            xq, xs = m.permute_scatter_fp8(xd, ix.row_of, rows, FP8_BLOCK, src_row=ix.sorted_indices)
+            want_xq, want_xs = oracle.permute(qs, si), oracle.permute(ss, si)
+        assert_rows_exact(xq, want_xq, "FP8 expert-major codes", live)
+        assert_rows_exact(xs, want_xs, "FP8 expert-major scales", live)
+        del xq, xs, want_xq, want_xs, qs, ss
+        xp = want_xp = None
     else:
-        xp = m.permute_scatter(xd, ix.row_of, rows, src_row=ix.sorted_indices)
-    torch.cuda.synchronize()
-    rs = sample_rows(rows, 3000, cfg_id)
-    rs = rs[want["sorted_indices"][rs] != -2]  # unused slack is never written
-    assert_exact(host(xp[torch.from_numpy(rs).to(DEV)]), oracle.permute(x, want["sorted_indices"][rs]),
-                 "permuted rows (sample)")
-    pads = np.flatnonzero(want["sorted_indices"] == -1)
-    if len(pads):
-        pr = pads[sample_rows(len(pads), 1000, cfg_id + 7)]
-        assert (host(xp[torch.from_numpy(pr).to(DEV)]).view(np.uint16 if dt == "bf16" else np.uint32) == 0).all()
+        if gs:
+            gbuf = m.permute_scatter(xd, ix.slot_of, slots)
+            want_g = oracle.permute(x, want["gsrc"])
+            assert_rows_exact(gbuf[:n], want_g, "group slots (send)")
+            xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of)
+            want_xp = oracle.permute(want_g, want["esrc"])
+            del gbuf, want_g
+        else:
+            xp = m.permute_scatter(xd, ix.row_of, rows, src_row=ix.sorted_indices)
+            want_xp = oracle.permute(x, si)
+        assert_rows_exact(xp, want_xp, "expert-major rows", live)
     del xd
 
+    # ---- combine
     if c["identity_experts"]:
-        y_np = oracle.permute(x, want["sorted_indices"])
-        yd = xp
+        y_np, yd = want_xp, xp  # identity experts: y is the permuted x (checked bit for bit above)
     else:
+        del xp, want_xp
         y_np = wl.expert_outputs(key, rows, H, dt)
         yd = dev(y_np)
     out_np = np.uint16 if dt == "bf16" else np.float32
-    ts = sample_rows(T, 1500, 100 + cfg_id)
-    tsd = torch.from_numpy(ts).to(DEV)
-    if gs > 0:
-        n = int(host(ix.n_slots)[0])
-        part = m.group_precombine(yd, ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=n,
+    out_t = torch.bfloat16 if dt == "bf16" else torch.float32
+    if gs:
+        p_np = np.uint16 if bf16_partials else np.float32
+        part = m.group_precombine(yd, ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=slots,
                                   out_dtype=torch.bfloat16 if bf16_partials else torch.float32)
-        out = m.unpermute_combine(part, ix.slot_of, None, out_dtype=torch.bfloat16)
-        torch.cuda.synchronize()
-        slot_rows = want["slot_of"][ts]
-        want_p = oracle.group_precombine(y_np, want["row_of"][ts], w_np[ts], want_i[ts], E, gs,
-                                         np.where(slot_rows >= 0, np.arange(slot_rows.size).reshape(slot_rows.shape),
-                                                  -1).astype(np.int32), slot_rows.size,
-                                         out_dtype=np.uint16 if bf16_partials else np.float32)
-        got_p = host(part[torch.from_numpy(np.maximum(slot_rows.reshape(-1), 0)).to(DEV)])
-        present = slot_rows.reshape(-1) >= 0
-        assert_combined(got_p[present], want_p[present], "partials (sample)")
-        local_slot = np.where(slot_rows >= 0, np.arange(slot_rows.size).reshape(slot_rows.shape), -1)
-        want_o = oracle.unpermute_combine(want_p, local_slot.astype(np.int32), None, np.uint16)
+        want_p = oracle.group_precombine(y_np, want["row_of"], w_np, want_i, E, gs, want["slot_of"], n,
+                                         out_dtype=p_np)
+        assert_combined_all(part[:n], want_p, "partials")
+        out = m.unpermute_combine(part, ix.slot_of, None, out_dtype=out_t)
+        want_o = oracle.unpermute_combine(want_p, want["slot_of"], None, out_np)
+        del part, want_p
     else:
-        out = m.unpermute_combine(yd, ix.row_of, gw, out_dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
-        torch.cuda.synchronize()
-        want_o = oracle.unpermute_combine(y_np, want["row_of"][ts], w_np[ts], out_np)
-    got_o = host(out[tsd])
-    assert_combined(got_o, want_o, "combined (sample)")
-    say(f"workload {cfg_id}: combined exact share {exact_fraction(got_o, want_o):.6f}")
+        out = m.unpermute_combine(yd, ix.row_of, gw, out_dtype=out_t)
+        want_o = oracle.unpermute_combine(y_np, want["row_of"], w_np, out_np)
+    assert_combined_all(out, want_o, "combined")
     if c["identity_experts"]:
         rel = np.abs(host(out).astype(np.float64) - x) / np.maximum(np.abs(x), np.finfo(np.float32).tiny)
         assert rel.max() <= 1e-6
@@ -837,27 +850,36 @@ def test_workload_full_size(m, cfg_id):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cfg_id", [3, 4, 5])
+@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
 def test_workload_fp8_dispatch(m, cfg_id):
+    """The FP8 dispatch as bench.py --fp8 launches it (workloads with expert outputs)."""
     run_workload(m, cfg_id, fp8=True)
     torch.cuda.empty_cache()
 
 
 def test_workload_bf16_partials(m):
     """Workload 4 with the per-group partials rounded to bf16 (the BF16 exchange), as bench.py
-    --bf16-partials launches it: sampled partials and combined rows against the oracle."""
+    --bf16-partials launches it."""
     run_workload(m, 4, bf16_partials=True)
     torch.cuda.empty_cache()
 
 
-def test_workload_group_limited_routing(m):
+@pytest.mark.parametrize("bf16_partials", [False, True])
+def test_workload_group_limited_routing(m, bf16_partials):
     """Workload 4 with every token limited to 4 of its 32 expert groups, as bench.py
     --route-groups 4 launches it."""
-    run_workload(m, 4, route_groups=4)
+    run_workload(m, 4, route_groups=4, bf16_partials=bf16_partials)
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cfg_id,align", [(3, 128), (2, 128), (4, 128)])
+def test_workload_fp8_group_limited_bf16_partials(m):
+    """Workload 4 with every option bench.py combines: group-limited routing, the FP8 dispatch and
+    bf16 partials."""
+    run_workload(m, 4, route_groups=4, fp8=True, bf16_partials=True)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg_id,align", [(3, 128), (2, 128), (4, 128), (1, 128)])
 def test_workload_aligned(m, cfg_id, align):
     """The named workloads with every expert segment aligned to 128 rows, as bench.py --alignment
     128 launches them."""
@@ -1089,24 +1111,24 @@ def test_binding_rejects_wrong_shapes_before_launch(m):
     assert (q_bad == 7).all()
 
 
-def test_pipeline_is_deterministic(m):
-    """No atomics decide positions or sums: two runs give identical bits."""
-    a = host(run_workload(m, 2))
-    b = host(run_workload(m, 2))
-    assert np.array_equal(a, b)
-
-
 # ------------------------------------------------------------------ backward
 
 
-def _dw_bound(dout, y, row_of, H):
+def _dw_bound(dout, y, row_of, H, chunk=512):
     """Error bound of the kernel's fixed-order float32 dot: at most ceil(H/64) + 30 roundings
     along any product's path (per-lane chain, wavefront butterfly, wavefronts), each at most
-    2^-24 of the sum of |products|; plus the oracle's own rounding to float32."""
-    d = np.abs(wl.bf16_bits_to_f32(dout) if dout.dtype == np.uint16 else dout).astype(np.float64)
-    yy = np.abs(wl.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y).astype(np.float64)
-    mag = np.einsum("th,tkh->tk", d, yy[np.clip(row_of, 0, len(yy) - 1)])
-    mag[(row_of < 0) | (row_of >= len(yy))] = 0.0
+    2^-24 of the sum of |products|; plus the oracle's own rounding to float32. Computed in token
+    chunks so that full-size workloads fit in host memory."""
+    T, K = row_of.shape
+    mag = np.zeros((T, K), np.float64)
+    for a in range(0, T, chunk):
+        b = min(a + chunk, T)
+        d = np.abs(wl.bf16_bits_to_f32(dout[a:b]) if dout.dtype == np.uint16 else dout[a:b]).astype(np.float64)
+        r = row_of[a:b]
+        ok = (r >= 0) & (r < len(y))
+        yc = y[np.where(ok, r, 0)]
+        yy = np.abs(wl.bf16_bits_to_f32(yc) if y.dtype == np.uint16 else yc).astype(np.float64)
+        mag[a:b] = np.where(ok, np.einsum("th,tkh->tk", d, yy), 0.0)
     return (-(-H // 64) + 30) * 2.0 ** -24 * mag + 2.0 ** -130
 
 
@@ -1280,46 +1302,145 @@ def test_backward_no_tokens(m):
     assert (host(dy) == 0).all() and dw.shape == (0, 2)
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3, 5])
-def test_backward_workload(m, cfg_id):
+@pytest.mark.parametrize("cfg_id,bf16_partials", [(2, False), (3, False), (4, False), (4, True), (5, False)])
+def test_backward_workload(m, cfg_id, bf16_partials):
     """Backward at the named workloads' full size, in the launch configuration bench.py --backward
-    times: sampled tokens against the oracle (their dy rows bit for bit, their dw within the
-    bound), every padding row zero, and the dispatch backward against the oracle's combine."""
+    times, every output against the oracle: every dy row bit for bit (padding rows zero), every dw
+    within the dot-product bound, the dispatch backward (the unit-weight combine; in group mode the
+    unit-weight pre-combine and the final sum, float32 or bf16 partials) and the router gradient
+    bit for bit."""
     c = wl.WORKLOADS[cfg_id]
-    T, H, E, K, dt = c["T"], c["H"], c["E"], c["K"], c["dtype"]
-    say(f"backward workload {cfg_id}: {c['name']}")
+    T, H, E, K, dt, gs = c["T"], c["H"], c["E"], c["K"], c["dtype"], c["group_size"]
+    say(f"backward workload {cfg_id}: {c['name']} bf16_partials={bf16_partials}")
     key = wl.workload_key(cfg_id)
     cap = oracle.capacity(T, K, E, *c["cf"]) if c["cf"] else 0
     logits = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])
-    idx, w = m.route_topk(dev(logits), K)
-    ix = m.build_index(idx, w, E, capacity=cap)
+    gi, gw, ix, idx_np, w_np, want = check_route_and_index(m, c, logits, 0, cap, 0)
     rows = ix.rows
+    live = want["sorted_indices"] != -2
+    out_np = np.uint16 if dt == "bf16" else np.float32
     y = wl.expert_outputs(key, rows, H, dt)
     dout = wl.expert_outputs((*key, 7), T, H, dt)
-    dxp = wl.expert_outputs((*key, 8), rows, H, dt)
-    dy, dw = m.unpermute_combine_backward(dev(dout), dev(y), ix.row_of, w, src_row=ix.sorted_indices)
-    dx = m.unpermute_combine(dev(dxp), ix.row_of)
-    dlog = m.route_topk_backward(idx, w, dw, E)
-    torch.cuda.synchronize()
-    row_of, w_np, idx_np = host(ix.row_of), host(w), host(idx)
-    src = host(ix.sorted_indices)
-    ts = sample_rows(T, 600, cfg_id)
-    sub = row_of[ts]
-    used = np.unique(sub[sub >= 0])
-    remap = np.full(rows, -1, np.int32)
-    remap[used] = np.arange(len(used), dtype=np.int32)
-    sub_local = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32)
-    want_dy, want_dw = oracle.combine_backward(dout[ts], y[used], sub_local, w_np[ts],
-                                               np.uint16 if dt == "bf16" else np.float32)
-    got_dy = host(dy[torch.from_numpy(used).to(DEV)])
-    assert_exact(got_dy, want_dy, "dy rows of the sampled tokens")
+    dy, dw = m.unpermute_combine_backward(dev(dout), dev(y), ix.row_of, gw, src_row=ix.sorted_indices)
+    want_dy, want_dw = oracle.combine_backward(dout, y, want["row_of"], w_np, out_np)
+    assert_rows_exact(dy, want_dy, "dy", live)
+    del dy, want_dy
     dw_np = host(dw)
-    _check_dw(dw_np[ts], want_dw, _dw_bound(dout[ts], y[used], sub_local, H))
-    pad = np.flatnonzero(src == -1)
-    if len(pad):
-        pr = pad[sample_rows(len(pad), 500, cfg_id + 1)]
-        assert (host(dy[torch.from_numpy(pr).to(DEV)]) == 0).all(), "padding rows of dy must be zero"
-    want_dx = oracle.unpermute_combine(dxp, row_of[ts], None, np.uint16 if dt == "bf16" else np.float32)
-    assert_exact(host(dx[torch.from_numpy(ts).to(DEV)]), want_dx, "dispatch backward (sampled tokens)")
-    want_dl = oracle.route_topk_backward(idx_np, w_np, dw_np, E)
-    assert_exact(host(dlog), want_dl, "router gradient")
+    _check_dw(dw_np, want_dw, _dw_bound(dout, y, want["row_of"], H))
+    assert (dw_np[want["row_of"] < 0] == 0).all()
+    del y
+    dxp = wl.expert_outputs((*key, 8), rows, H, dt)
+    if gs:
+        n = int(want["n_slots"][0])
+        slots = T * min(K, E // gs)
+        p_np = np.uint16 if bf16_partials else np.float32
+        part = m.group_precombine(dev(dxp), ix.row_of, None, gi, E, gs, ix.slot_of, slots_cap=slots,
+                                  out_dtype=torch.bfloat16 if bf16_partials else torch.float32)
+        want_p = oracle.group_precombine(dxp, want["row_of"], None, idx_np, E, gs, want["slot_of"], n, out_dtype=p_np)
+        assert_combined_all(part[:n], want_p, "dispatch backward partials")
+        dx = m.unpermute_combine(part, ix.slot_of, None, out_dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+        want_dx = oracle.unpermute_combine(want_p, want["slot_of"], None, out_np)
+    else:
+        dx = m.unpermute_combine(dev(dxp), ix.row_of, None)
+        want_dx = oracle.unpermute_combine(dxp, want["row_of"], None, out_np)
+    assert_combined_all(dx, want_dx, "dispatch backward")
+    dlog = m.route_topk_backward(gi, gw, dw, E)
+    assert_exact(host(dlog), oracle.route_topk_backward(idx_np, w_np, dw_np, E), "router gradient")
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ determinism
+
+
+def _bits(t):
+    """Bit pattern of a device tensor (so that -0.0 and +0.0, or two NaNs, are told apart)."""
+    if t.dtype in (torch.float32, torch.int32):
+        return t.view(torch.int32)
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    return t
+
+
+def _poison_like(t):
+    """A tensor of t's shape and dtype filled with 0xFF bytes: entries a run fails to write differ."""
+    p = torch.empty_like(t)
+    p.view(torch.uint8).fill_(0xFF)
+    return p
+
+
+def _same_bits(a, b, what, live=None):
+    if live is not None:
+        a, b = a[live], b[live]
+    assert torch.equal(_bits(a), _bits(b)), f"{what}: two runs differ"
+
+
+@pytest.mark.parametrize("case", ["workload3", "workload4_group", "workload3_backward", "workload5_drop"])
+def test_pipeline_is_deterministic(m, case):
+    """No atomics decide positions or sums: the same step run twice -- the second time into
+    output buffers filled with 0xFF bytes -- gives identical bits in every index array, every
+    dispatched row, every partial and every output (workload 3 forward; workload 4 group mode with
+    its partials and final sum; workload 3 backward with dy, dw and the router gradient; workload
+    5 drop-and-pad)."""
+    cfg_id = {"workload3": 3, "workload4_group": 4, "workload3_backward": 3, "workload5_drop": 5}[case]
+    backward = case.endswith("backward")
+    c = wl.WORKLOADS[cfg_id]
+    T, H, E, K, dt, gs = c["T"], c["H"], c["E"], c["K"], c["dtype"], c["group_size"]
+    say(f"determinism {case}")
+    key = wl.workload_key(cfg_id)
+    cap = m.expert_capacity(T, K, E, *c["cf"]) if c["cf"] else 0
+    rows = m.index_rows(T, K, E, cap, 0)
+    logits = dev(wl.router_logits(key, T, E, zipf_s=c["zipf_s"]))
+    x = dev(wl.hidden_states(key, T, H, dt))
+    y = dev(wl.expert_outputs(key, rows, H, dt))
+    G = E // gs if gs else 0
+    slots = T * min(K, G) if gs else 0
+    dout = dev(wl.expert_outputs((*key, 7), T, H, dt)) if backward else None
+
+    def run(prev=None):
+        P = (lambda t: _poison_like(t)) if prev is not None else (lambda t: torch.empty_like(t))
+        r = {}
+        gi, gw = m.route_topk(logits, K, out=(P(torch.empty((T, K), dtype=torch.int32, device=DEV)),
+                                              P(torch.empty((T, K), dtype=torch.float32, device=DEV))))
+        ix = m.alloc_index(T, K, E, cap, gs)
+        for f in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs", "slot_of",
+                  "gsrc", "esrc", "group_counts", "n_slots"):
+            t = getattr(ix, f)
+            if t is not None and prev is not None:
+                t.view(torch.uint8).fill_(0xFF)
+        m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix)
+        r.update(gi=gi, gw=gw, **{f: getattr(ix, f) for f in ("counts", "group_list", "kept_counts", "sorted_indices",
+                                                              "row_of", "permuted_probs")})
+        if gs:
+            n = int(ix.n_slots.item())
+            r.update(slot_of=ix.slot_of, esrc=ix.esrc, group_counts=ix.group_counts, n_slots=ix.n_slots,
+                     gsrc=ix.gsrc[:n])
+            gbuf = m.permute_scatter(x, ix.slot_of, slots, out=P(torch.empty((slots, H), dtype=x.dtype, device=DEV)))
+            r["gbuf"] = gbuf[:n]
+            r["xp"] = m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=P(torch.empty((rows, H), dtype=x.dtype,
+                                                                                  device=DEV)))
+            part = m.group_precombine(y, ix.row_of, gw, gi, E, gs, ix.slot_of,
+                                      out=P(torch.empty((slots, H), dtype=torch.float32, device=DEV)))
+            r["partials"] = part[:n]
+            r["out"] = m.unpermute_combine(part, ix.slot_of, None, out=P(torch.empty((T, H), dtype=x.dtype,
+                                                                                     device=DEV)))
+        else:
+            r["xp"] = m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices,
+                                        out=P(torch.empty((rows, H), dtype=x.dtype, device=DEV)))
+            r["out"] = m.unpermute_combine(y, ix.row_of, gw, out=P(torch.empty((T, H), dtype=x.dtype, device=DEV)))
+        if backward:
+            dy, dw = m.unpermute_combine_backward(dout, y, ix.row_of, gw, src_row=ix.sorted_indices,
+                                                  out=(P(torch.empty((rows, H), dtype=x.dtype, device=DEV)),
+                                                       P(torch.empty((T, K), dtype=torch.float32, device=DEV))))
+            r.update(dy=dy, dw=dw, dlog=m.route_topk_backward(
+                gi, gw, dw, E, out=P(torch.empty((T, E), dtype=torch.float32, device=DEV))))
+        torch.cuda.synchronize()
+        return r
+
+    a = run()
+    b = run(prev=a)
+    live = a["sorted_indices"] != -2
+    assert bool(live.all()), "these layouts have no unused slack"
+    for k in a:
+        _same_bits(a[k], b[k], k)
+    del a, b
+    torch.cuda.empty_cache()
