@@ -28,8 +28,9 @@
  *     zero row (permute) or no term (combine). Expert ids in one row of topk_idx must be
  *     distinct for the pages' routing map to be defined; if they repeat, slots of the same
  *     expert are ordered by slot.
- *   - The library holds no global state; calls on different streams may run concurrently as
- *     long as they do not write the same memory.
+ *   - The library holds no global state (apart from the scratch of moe_build_index_noalloc);
+ *     calls on different streams may run concurrently as long as they do not write the same
+ *     memory.
  */
 #ifndef MOE_DISPATCH_H
 #define MOE_DISPATCH_H
@@ -174,6 +175,24 @@ moe_status moe_build_index(const int32_t *topk_idx, const float *topk_w, int64_t
                            int32_t E, int32_t capacity, int32_t group_size, int32_t alignment,
                            const moe_index *out, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* moe_build_index without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * tile counts go to a scratch array inside the library instead -- 1 MiB of device memory per GPU,
+ * enough for every input moe_build_index accepts (at most 128 tiles of 1024 expert and 1024 group
+ * counts), held by each GPU the library runs on until the process ends. Nothing is allocated;
+ * arguments, results and errors are those of moe_build_index (bit for bit the same arrays), plus:
+ *   - the stream must belong to the current device (else MOE_ERR_INVALID): the scratch used is
+ *     the current device's, whose address is looked up on the first call on that device
+ *     (MOE_ERR_HIP if that fails);
+ *   - a plan larger than the scratch returns MOE_ERR_UNSUPPORTED (no valid input makes one);
+ *   - every call on one GPU shares that GPU's scratch: calls on the same stream are ordered, but
+ *     calls that overlap on one GPU (different streams, or different host threads without
+ *     ordering between their streams) race and may write wrong results. The scratch needs no
+ *     clearing: each call writes the counts it reads. */
+moe_status moe_build_index_noalloc(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K,
+                                   int32_t E, int32_t capacity, int32_t group_size, int32_t alignment,
+                                   const moe_index *out, hipStream_t stream);
 
 /* Row gather ([Megatron] §1.1 step 5, permuted_input = tokens.index_select(0, sorted_indices);
  * [Scratch] §12, permuted_tokens = tokens[permute_indices]):

@@ -147,6 +147,18 @@ def test_argument_errors_return_before_any_launch(capi):
         capi.MOE_ERR_UNSUPPORTED  # drop-and-pad with alignment
     assert lib.moe_build_index(fake, None, 4, 2, 8, 0, 0, -3, ctypes.byref(ix), fake, 1 << 20, None) == \
         capi.MOE_ERR_INVALID
+    # the allocation-free index build checks the same arguments before any HIP call
+    assert lib.moe_build_index_noalloc(fake, None, 4, 2, 8, 4, 2, 0, ctypes.byref(ix), None) == \
+        capi.MOE_ERR_UNSUPPORTED  # drop-and-pad with groups
+    assert lib.moe_build_index_noalloc(fake, None, 4, 2, 8, 0, 0, 0, ctypes.byref(ix), None) == \
+        capi.MOE_ERR_INVALID  # null outputs
+    assert lib.moe_build_index_noalloc(fake, None, 4, 2, 8, 0, 0, 0, None, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_build_index_noalloc(fake, None, 4, 9, 8, 0, 0, 0, ctypes.byref(ix), None) == \
+        capi.MOE_ERR_INVALID  # K > E
+    assert lib.moe_build_index_noalloc(fake, None, 4, 2, 2048, 0, 0, 0, ctypes.byref(ix), None) == \
+        capi.MOE_ERR_UNSUPPORTED  # more experts than the kernels take
+    assert lib.moe_build_index_noalloc(fake, None, 4, 2, 12, 0, 5, 0, ctypes.byref(ix), None) == \
+        capi.MOE_ERR_INVALID  # group size not dividing E
     # rows of the expert-major arrays
     assert lib.moe_index_rows(16384, 8, 256, 0, 0) == 16384 * 8
     assert lib.moe_index_rows(16384, 8, 256, 0, 128) == 16384 * 8 + 256 * 127

@@ -40,6 +40,7 @@
 // the aligned lengths) and the group (send once per rank) slots ([CANN] §1(1)) are applied
 // inside the same passes. Rows after the last segment are unused slack (MOE_ROW_UNUSED).
 #include <algorithm>
+#include <mutex>
 
 #include "moe_common.h"
 
@@ -736,12 +737,15 @@ extern "C" int64_t moe_index_rows(int64_t T, int32_t K, int32_t E, int32_t capac
     return R > 0x7fffffffLL ? -1 : R;
 }
 
-extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T,
-                                      int32_t K, int32_t E, int32_t capacity, int32_t group_size,
-                                      int32_t alignment, const moe_index *out, void *workspace,
-                                      size_t workspace_bytes, hipStream_t stream)
+namespace moe {
+namespace {
+
+// Argument checks, then (launch = true) the launches; `workspace` holds at least the plan's tile
+// counts. With launch = false only the arguments other than the workspace are checked.
+moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K, int32_t E,
+                            int32_t capacity, int32_t group_size, int32_t alignment, const moe_index *out,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream, bool launch = true)
 {
-    using namespace moe;
     moe_status st = check_sizes(T, K, E, group_size);
     if (st != MOE_OK)
         return st;
@@ -767,6 +771,8 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     if (p.ntiles > kMaxTiles)
         return MOE_ERR_UNSUPPORTED;  // cannot happen: tiles grow with T to stay within the limit
     const size_t need = p.ws;
+    if (!launch)
+        return MOE_OK;
     if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
         return MOE_ERR_INVALID;
 
@@ -829,4 +835,78 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
             return st;
     }
     return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T,
+                                      int32_t K, int32_t E, int32_t capacity, int32_t group_size,
+                                      int32_t alignment, const moe_index *out, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream)
+{
+    return moe::build_index_impl(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, workspace,
+                                 workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free entry point
+// The tile counts of moe_build_index_noalloc live in this array instead of a caller's workspace:
+// room for the largest plan any valid input makes (kMaxTiles tiles of MOE_MAX_EXPERTS expert
+// counts and MOE_MAX_EXPERTS group counts, 4 bytes each: 1 MiB). Each GPU the library runs on holds
+// its own copy until the process ends. The counts are written before they are read in every
+// call, so nothing needs clearing between calls.
+constexpr size_t kScratchBytes = sizeof(int32_t) * moe::kMaxTiles * (2 * MOE_MAX_EXPERTS);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxScratchDevices];  // device address of `scratch` per device, resolved once
+
+// Device address of this device's copy of `scratch` (the array's name is only a host-side stand-in
+// for it). Resolved on the first call on each device, with that device current.
+moe_status scratch_address(int device, void **p)
+{
+    if (device < 0 || device >= kMaxScratchDevices)
+        return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[device]) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q)
+            return MOE_ERR_HIP;
+        scratch_ptr[device] = q;
+    }
+    *p = scratch_ptr[device];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_build_index_noalloc(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K,
+                                              int32_t E, int32_t capacity, int32_t group_size, int32_t alignment,
+                                              const moe_index *out, hipStream_t stream)
+{
+    using namespace moe;
+    // every argument error first, before any HIP call
+    moe_status st = build_index_impl(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, nullptr, 0,
+                                     stream, false);
+    if (st != MOE_OK)
+        return st;
+    const Plan p = make_plan(T, K, E, group_size > 0 ? E / group_size : 0);
+    if (p.ws > kScratchBytes)
+        return MOE_ERR_UNSUPPORTED;  // beyond the scratch's size (no valid input gets here)
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess)
+        return MOE_ERR_HIP;
+    hipDevice_t stream_device = -1;
+    if (hipStreamGetDevice(stream, &stream_device) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (stream_device != device)
+        return MOE_ERR_INVALID;  // the scratch address is the current device's
+    void *ws = nullptr;
+    if ((st = scratch_address(device, &ws)) != MOE_OK)
+        return st;
+    return build_index_impl(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, ws, kScratchBytes,
+                            stream);
 }

@@ -140,7 +140,9 @@ def index_rows(T: int, K: int, E: int, capacity: int = 0, alignment: int = 0) ->
 
 
 def alloc_index(T: int, K: int, E: int, capacity: int = 0, group_size: int = 0, device="cuda",
-                alignment: int = 0) -> MoeIndex:
+                alignment: int = 0, workspace: bool = True) -> MoeIndex:
+    """Device arrays of an index for these sizes (and the workspace build_index needs, unless
+    workspace=False: build_index_noalloc uses none)."""
     i32 = dict(dtype=torch.int32, device=device)
     rows = index_rows(T, K, E, capacity, alignment)
     ix = MoeIndex(
@@ -155,8 +157,9 @@ def alloc_index(T: int, K: int, E: int, capacity: int = 0, group_size: int = 0, 
         ix.esrc = torch.empty(rows, **i32)
         ix.group_counts = torch.empty(G, **i32)
         ix.n_slots = torch.empty(1, **i32)
-    ws = workspace_bytes(T, K, E, group_size)
-    ix.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+    if workspace:
+        ws = workspace_bytes(T, K, E, group_size)
+        ix.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
     return ix
 
 
@@ -180,9 +183,36 @@ def build_index(topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor], num_expe
         raise ValueError(f"preallocated index is on {ix.counts.device}, topk_idx on {topk_idx.device}")
     s = ix.struct()
     ws = ix.workspace
+    if ws is None:
+        raise ValueError("this index was allocated without a workspace (use build_index_noalloc)")
     check("moe_build_index", lib().moe_build_index(
         _p(topk_idx), _p(topk_w), T, K, num_experts, capacity, group_size, alignment, ctypes.byref(s),
         _p(ws), ws.numel(), _stream()))
+    return ix
+
+
+def build_index_noalloc(topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor], num_experts: int,
+                        capacity: int = 0, group_size: int = 0, out: Optional[MoeIndex] = None,
+                        alignment: int = 0) -> MoeIndex:
+    """build_index through moe_build_index_noalloc: the same arrays, the tile counts in the
+    library's own per-GPU scratch (no workspace; the library allocates nothing). Calls that
+    overlap on one GPU race on that scratch."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    T, K = topk_idx.shape
+    if topk_w is not None:
+        _need(topk_w, "topk_w", torch.float32, 2)
+        if tuple(topk_w.shape) != (T, K):
+            raise ValueError("topk_w must have the shape of topk_idx")
+    ix = out if out is not None else alloc_index(T, K, num_experts, capacity, group_size, topk_idx.device,
+                                                 alignment, workspace=False)
+    if (ix.T, ix.K, ix.E, ix.capacity, ix.group_size, ix.alignment) != (T, K, num_experts, capacity, group_size,
+                                                                        alignment):
+        raise ValueError("preallocated index was made for other sizes")
+    if ix.counts.device != topk_idx.device:
+        raise ValueError(f"preallocated index is on {ix.counts.device}, topk_idx on {topk_idx.device}")
+    s = ix.struct()
+    check("moe_build_index_noalloc", lib().moe_build_index_noalloc(
+        _p(topk_idx), _p(topk_w), T, K, num_experts, capacity, group_size, alignment, ctypes.byref(s), _stream()))
     return ix
 
 
