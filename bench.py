@@ -285,8 +285,10 @@ def main():
     elif args.fp8 and gs:
         calls += [("dispatch_send_fp8", "permute",
                    lambda: m.permute_scatter_fp8(x, ix.slot_of, gq.shape[0], fp8_block, out=(gq, gsc))),
-                  ("dispatch_recv", "permute", lambda: m.permute_grouped(gq, ix.esrc, ix.row_of, out=xq)),
-                  ("dispatch_recv_scales", "permute", lambda: m.permute_grouped(gsc, ix.esrc, ix.row_of, out=xs)),
+                  ("dispatch_recv", "permute", lambda: m.permute_grouped(gq, ix.esrc, ix.row_of, out=xq,
+                                                                         src_of=ix.slot_src)),
+                  ("dispatch_recv_scales", "permute", lambda: m.permute_grouped(gsc, ix.esrc, ix.row_of, out=xs,
+                                                                                src_of=ix.slot_src)),
                   ("precombine", "combine",
                    lambda: m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)),
                   ("final_sum", "combine", lambda: m.unpermute_combine(part, ix.slot_of, None, out=out))]
@@ -299,7 +301,8 @@ def main():
         # the number of group slots is only known on the device; every call is bounded by its
         # upper bound T*min(K,G) instead, so the step never waits for the host
         calls += [("dispatch_send", "permute", lambda: m.permute_scatter(x, ix.slot_of, gbuf.shape[0], out=gbuf)),
-                  ("dispatch_recv", "permute", lambda: m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=xp)),
+                  ("dispatch_recv", "permute", lambda: m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=xp,
+                                                                         src_of=ix.slot_src)),
                   ("precombine", "combine",
                    lambda: m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)),
                   ("final_sum", "combine", lambda: m.unpermute_combine(part, ix.slot_of, None, out=out))]

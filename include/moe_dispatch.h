@@ -138,6 +138,11 @@ typedef struct moe_index {
     int32_t *group_counts;   /* [G] slots per group. */
     int32_t *n_slots;        /* [1] number of group slots M_g (the caller reads it back if it
                                 needs the exact size; gsrc may be sized by the upper bound). */
+    int32_t *slot_src;       /* [T, K] group mode, may be NULL (not written): the group slot
+                                feeding routing slot (t,k), i.e. slot_of[t, group of its expert]
+                                = esrc[row_of[t,k]]; -1 if the slot routes nowhere. The receive
+                                side passes it to moe_permute_grouped as src_of, so that each
+                                destination's source is known without a lookup. */
 } moe_index;
 
 /* Rows R of the expert-major arrays (sorted_indices, permuted_probs, esrc) and buffers for
@@ -235,11 +240,15 @@ moe_status moe_permute_scatter(const void *src, int64_t src_rows, int64_t H, moe
  *   dst_of  [M, J] int32 destination rows, J <= 64; entries outside [0, N) are ignored. A row
  *           may be listed more than once (each copy writes the same bytes); rows with a valid
  *           src_row that dst_of never lists are left untouched.
+ *   src_of  [M, J] int32 or NULL: the source row of each listed destination, which must equal
+ *           src_row[dst_of[m*J + j]] (moe_index.slot_src is that for the group receive); with it
+ *           the sources load together with the destinations instead of after them. Its entries
+ *           for unlisted columns (dst_of outside [0, N)) are ignored. The result is the same.
  * With dst_of = the inverse of src_row (every row listed), the result equals
  * moe_permute(src, src_rows, H, dt, src_row, N, dst) bit for bit. */
 moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
                                const int32_t *src_row, int64_t N, const int32_t *dst_of, int64_t M,
-                               int32_t J, void *dst, hipStream_t stream);
+                               int32_t J, const int32_t *src_of, void *dst, hipStream_t stream);
 
 /* FP8 dispatch ([Combine] §3: the dispatch sends FP8, the combine stays BF16; the DeepEP
  * dispatch call in [Megatron] passes x together with x_scales, num_scales scale groups per token

@@ -50,7 +50,7 @@ def _declare(lib):
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
     lib.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
     lib.oracle_route_topk.restype = ctypes.c_int
-    lib.oracle_build_index.argtypes = [P, P, i64, i32, i32, i32, i32, i32] + [P] * 11
+    lib.oracle_build_index.argtypes = [P, P, i64, i32, i32, i32, i32, i32] + [P] * 12
     lib.oracle_build_index.restype = ctypes.c_int
     lib.oracle_permute.argtypes = [P, i64, i64, i32, P, i64, P]
     lib.oracle_permute.restype = ctypes.c_int
@@ -167,7 +167,7 @@ def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_s
         row_of=np.full((T, K), -7, np.int32),
         permuted_probs=np.full(rows, np.nan, np.float32),
     )
-    g_arrays = [None] * 5
+    g_arrays = [None] * 6
     if group_size > 0:
         G = E // group_size
         out.update(
@@ -176,8 +176,9 @@ def build_index(topk_idx: np.ndarray, topk_w, E: int, capacity: int = 0, group_s
             esrc=np.full(rows, -7, np.int32),
             group_counts=np.zeros(G, np.int32),
             n_slots=np.zeros(1, np.int32),
+            slot_src=np.full((T, K), -7, np.int32),
         )
-        g_arrays = [out["slot_of"], out["gsrc"], out["esrc"], out["group_counts"], out["n_slots"]]
+        g_arrays = [out["slot_of"], out["gsrc"], out["esrc"], out["group_counts"], out["n_slots"], out["slot_src"]]
     rc = _load().oracle_build_index(
         _ptr(topk_idx), _ptr(w), T, K, E, capacity, group_size, alignment,
         _ptr(out["counts"]), _ptr(out["group_list"]), _ptr(out["kept_counts"]),

@@ -297,7 +297,7 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
                        int32_t *counts, int32_t *group_list, int32_t *kept_counts,
                        int32_t *sorted_indices, int32_t *row_of, float *permuted_probs,
                        int32_t *slot_of, int32_t *gsrc, int32_t *esrc, int32_t *group_counts,
-                       int32_t *n_slots)
+                       int32_t *n_slots, int32_t *slot_src)
 {
     if (T < 0 || K < 1 || E < 1 || !counts || !group_list || !sorted_indices || !row_of ||
         (T > 0 && !topk_idx))
@@ -417,6 +417,15 @@ int oracle_build_index(const int32_t *topk_idx, const float *topk_w, int64_t T, 
                     continue;
                 esrc[row] = slot_of[t * G + e / group_size];
             }
+        /* the same group slot seen from the routing slot: slot (t, k) is fed by the group slot of
+           token t and its expert's group, -1 when the slot routes nowhere (may be NULL) */
+        if (slot_src)
+            for (int64_t t = 0; t < T; ++t)
+                for (int32_t k = 0; k < K; ++k) {
+                    int32_t e = topk_idx[t * K + k];
+                    int32_t row = row_of[t * K + k];
+                    slot_src[t * K + k] = (e < 0 || e >= E || row < 0) ? -1 : slot_of[t * G + e / group_size];
+                }
     }
     return ORC_OK;
 }

@@ -95,11 +95,11 @@ def test_argument_errors_return_before_any_launch(capi):
         capi.MOE_ERR_INVALID  # partials neither float32 nor bf16
     assert lib.moe_group_precombine(fake, 1, 4, 8, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, 2, None) == \
         capi.MOE_ERR_UNSUPPORTED  # no FP8 partials
-    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, 2, 65, fake, None) == capi.MOE_ERR_UNSUPPORTED
-    assert lib.moe_permute_grouped(fake, 4, 8, 1, None, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_INVALID
-    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, None, 2, 2, fake, None) == capi.MOE_ERR_INVALID
-    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, -1, 2, fake, None) == capi.MOE_ERR_INVALID
-    assert lib.moe_permute_grouped(None, 0, 8, 1, None, 0, None, 0, 2, None, None) == capi.MOE_OK
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, 2, 65, None, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, None, 4, fake, 2, 2, None, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, None, 2, 2, None, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, -1, 2, None, fake, None) == capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped(None, 0, 8, 1, None, 0, None, 0, 2, None, None, None) == capi.MOE_OK
     assert lib.moe_route_topk_backward(fake, fake, fake, 4, 8, 9, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_route_topk_backward(fake, fake, fake, 4, 2048, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_route_topk_backward(fake, None, fake, 4, 8, 2, fake, None) == capi.MOE_ERR_INVALID
@@ -132,7 +132,7 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_permute_scatter(fake, 4, 8, 1, fake, 1025, None, 8, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_permute_scatter_fp8(fake, 1, 4, 128, 128, fake, 1025, None, 8, fake, fake, None) == \
         capi.MOE_ERR_UNSUPPORTED  # more destination columns than experts
-    assert lib.moe_permute_grouped(fake, 4, big, 1, fake, 4, fake, 2, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_grouped(fake, 4, big, 1, fake, 4, fake, 2, 2, None, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(fake, 1, 4, big // 2, fake, None, None, 2, 2, fake, 0, None) == \
         capi.MOE_ERR_UNSUPPORTED  # float32 output rows of 2 GiB
     assert lib.moe_group_precombine(fake, 1, 4, big // 2, fake, None, fake, 2, 2, 8, 2, fake, 4, fake, 0, None) == \

@@ -61,10 +61,12 @@ def brute_index(ids, E, cap=0, gs=0, w=None, align=0):
         for m, (g, t) in enumerate(pairs):
             slot_of[t, g] = m
         esrc = np.where(np.arange(len(sorted_idx)) < total, -1, -2)
+        slot_src = -np.ones((T, K), np.int64)
         for e, t, k in slots:
             esrc[row_of[t, k]] = slot_of[t, e // gs]
+            slot_src[t, k] = slot_of[t, e // gs]
         out.update(gsrc=[t for _, t in pairs], slot_of=slot_of.tolist(),
-                   esrc=esrc.tolist(), n_slots=len(pairs),
+                   esrc=esrc.tolist(), slot_src=slot_src.tolist(), n_slots=len(pairs),
                    group_counts=[sum(1 for g, _ in pairs if g == gg) for gg in range(G)])
     return out
 
@@ -129,6 +131,7 @@ def test_repeated_experts_are_ordered_by_slot(case, cap, align, gs):
     if gs:
         assert ix["gsrc"].tolist() == bf["gsrc"] and ix["slot_of"].tolist() == bf["slot_of"]
         assert ix["esrc"].tolist() == bf["esrc"]
+        assert ix["slot_src"].tolist() == bf["slot_src"]
 
 
 @settings(max_examples=200, deadline=None)
@@ -158,6 +161,7 @@ def test_group_mode_matches_pair_sort(case, gs):
     assert ix["gsrc"].tolist() == bf["gsrc"]
     assert ix["slot_of"].tolist() == bf["slot_of"]
     assert ix["esrc"].tolist() == bf["esrc"]
+    assert ix["slot_src"].tolist() == bf["slot_src"]
     assert int(ix["n_slots"][0]) == bf["n_slots"]
     assert ix["group_counts"].tolist() == bf["group_counts"]
 
@@ -179,6 +183,7 @@ def test_aligned_index_matches_tuple_sort(case, align, gs):
     if gs:
         assert ix["esrc"].tolist() == bf["esrc"]
         assert ix["gsrc"].tolist() == bf["gsrc"]
+        assert ix["slot_src"].tolist() == bf["slot_src"]
     gl = np.concatenate([[0], ix["group_list"]])
     assert (gl % align == 0).all()  # every segment starts (and ends) at a multiple of the alignment
     assert (np.diff(gl) - ix["counts"] >= 0).all() and (np.diff(gl) - ix["counts"] < align).all()
@@ -206,6 +211,8 @@ def test_group_mode_hand_example():
     assert ix["slot_of"].tolist() == [[0, -1], [1, 3], [2, 4], [-1, 5]]
     assert ix["sorted_indices"].tolist() == [0, 2, 0, 1, 1, 3, 2, 3]
     assert ix["esrc"].tolist() == [0, 2, 0, 1, 3, 5, 4, 5]
+    # each routing slot's group slot: token 2's experts 3 and 0 sit in groups 1 and 0
+    assert ix["slot_src"].tolist() == [[0, 0], [1, 3], [4, 2], [5, 5]]
 
 
 def test_index_invariants_at_workload_scale():

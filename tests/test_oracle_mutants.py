@@ -46,6 +46,8 @@ MUTANTS = [
      "if (e >= 0 && e < E && e % (E / group_size) == g)\n                        uses = 1;"),
     ("esrc uses the expert instead of its group", "esrc[row] = slot_of[t * G + e / group_size];",
      "esrc[row] = slot_of[t * G + e % G];"),
+    ("slot_src uses the expert instead of its group", "-1 : slot_of[t * G + e / group_size];",
+     "-1 : slot_of[t * G + e % G];"),
     ("permute copies the next row", "memcpy(d, (const unsigned char *)src + (size_t)s * row_bytes, row_bytes);",
      "memcpy(d, (const unsigned char *)src + (size_t)(s + 1 < src_rows ? s + 1 : s) * row_bytes, row_bytes);"),
     ("permute leaves padding rows unwritten", "        else if (s != -2)\n            memset(d, 0, row_bytes);",
@@ -195,6 +197,7 @@ def _index_brute_force():
                 assert ix["gsrc"].tolist() == want["gsrc"]
                 assert ix["slot_of"].tolist() == want["slot_of"]
                 assert ix["esrc"].tolist() == want["esrc"]
+                assert ix["slot_src"].tolist() == want["slot_src"]
 
 
 def _repeated_experts():

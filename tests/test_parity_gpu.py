@@ -118,7 +118,7 @@ def check_index(m, ids, w, E, cap=0, gs=0, align=0):
         n = int(host(ix.n_slots)[0])
         assert n == int(want["n_slots"][0])
         assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
-        for name in ("slot_of", "esrc", "group_counts"):
+        for name in ("slot_of", "esrc", "group_counts", "slot_src"):
             assert_exact(host(getattr(ix, name)), want[name], name)
     return ix, want
 
@@ -322,6 +322,9 @@ def test_permute_grouped_group_receive(m, dtype, H, T, E, K, gs):
     assert np.array_equal(want[live], oracle.permute(x, ix["sorted_indices"])[live])
     got = host(m.permute_grouped(dev(gbuf), dev(ix["esrc"]), dev(ix["row_of"])))
     assert_exact(got[live], want[live], "expert-major rows")
+    # the same with each destination's source given beside it (the per-slot group slots)
+    got2 = host(m.permute_grouped(dev(gbuf), dev(ix["esrc"]), dev(ix["row_of"]), src_of=dev(ix["slot_src"])))
+    assert_exact(got2[live], want[live], "expert-major rows (src_of)")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -354,14 +357,19 @@ def test_permute_grouped_random_maps(m, dtype, H, J):
     zero = (src_row < 0) | (src_row >= src_rows)
     want = oracle.permute(x, src_row)
     poison = np.full((N, H), 0x3F01 if dtype == "bf16" else 0x7FC00001, np.uint16 if dtype == "bf16" else np.uint32)
-    out = dev(poison.view(np.float32) if dtype == "f32" else poison)
-    m.permute_grouped(dev(x), dev(src_row), dev(dst_of), out=out)
-    got = host(out)
-    if dtype == "f32":
-        got, want, poison = got.view(np.uint32), want.view(np.uint32), poison
-    sel = listed | zero
-    assert_exact(got[sel], want[sel], "listed and zero rows")
-    assert np.array_equal(got[~sel], poison[~sel]), "rows never listed must be left untouched"
+    # src_of: each listed entry's source; entries outside [0, N) carry junk, which must be ignored
+    src_of = np.where((dst_of >= 0) & (dst_of < N), src_row[np.clip(dst_of, 0, N - 1)], 12345).astype(np.int32)
+    for so in (None, src_of):
+        out = dev(poison.view(np.float32) if dtype == "f32" else poison)
+        m.permute_grouped(dev(x), dev(src_row), dev(dst_of), out=out, src_of=None if so is None else dev(so))
+        got = host(out)
+        if dtype == "f32":
+            got, want_b = got.view(np.uint32), want.view(np.uint32)
+        else:
+            want_b = want
+        sel = listed | zero
+        assert_exact(got[sel], want_b[sel], "listed and zero rows")
+        assert np.array_equal(got[~sel], poison[~sel]), "rows never listed must be left untouched"
 
 
 def test_permute_grouped_without_groups_writes_zero_rows(m):
@@ -578,6 +586,37 @@ def test_permute_scatter_wide_maps(m, J, H, dtype):
         assert_exact(host(sc), oracle.permute(ss, src_row), "scales")
 
 
+@pytest.mark.parametrize("J,holes", [(5, 0.0), (8, 0.0), (8, 0.3), (8, 0.9), (9, 0.2), (64, 0.5), (65, 0.0),
+                                     (200, 0.4), (1024, 0.97)])
+@pytest.mark.parametrize("H,dtype", [(7168, "bf16"), (1000, "f32"), (8, "bf16")])
+def test_permute_scatter_dense_maps(m, J, holes, H, dtype):
+    """Maps with one output row per entry (N = rows * J, the standard dispatch's shape), whose
+    destinations the scatter shares among two waves per slice by their rank among a row's valid
+    entries: holes (-1 entries) shift the ranks, maps wider than a wavefront count them across
+    64-entry chunks; every listed row equals the oracle's gather, the unnamed rows are untouched."""
+    say(f"permute_scatter dense J={J} holes={holes} H={H} {dtype}")
+    g = np.random.default_rng([74, J, int(holes * 100), H])
+    src_rows = max(3, 3000 // J)
+    N = src_rows * J
+    dst = g.permutation(N).astype(np.int32)
+    dst_of = dst.reshape(src_rows, J).copy()
+    dst_of[g.random((src_rows, J)) < holes] = -1
+    dst_of[0] = -1  # a row with no destination
+    if J > 5:
+        dst_of[1, :5] = -1  # valid entries only past the first wave's share
+    src_row = np.full(N, -3, np.int32)
+    live = dst_of >= 0
+    src_row[dst_of[live]] = np.nonzero(live)[0].astype(np.int32)
+    x = wl.hidden_states(wl.case_key(74, J, H), src_rows, H, dtype)
+    u = np.uint16 if dtype == "bf16" else np.uint32
+    out = dev(np.full((N, H), 0x7F81 if dtype == "bf16" else 0x7F800001, u).view(
+        np.uint16 if dtype == "bf16" else np.float32))
+    got = host(m.permute_scatter(dev(x), dev(dst_of), N, out=out))
+    named = src_row >= 0
+    assert_exact(got[named], oracle.permute(x, src_row)[named], "named rows")
+    assert (got[~named].view(u) == (0x7F81 if dtype == "bf16" else 0x7F800001)).all(), "unnamed rows untouched"
+
+
 @pytest.mark.parametrize("ydt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
 @pytest.mark.parametrize("H,K,T", [(7168, 8, 60), (1000, 2, 50), (5, 3, 20), (512, 8, 40), (64, 1, 30), (24, 40, 16)])
 def test_unpermute_combine_bias(m, ydt, odt, H, K, T):
@@ -747,7 +786,7 @@ def check_route_and_index(m, c, logits, route_groups, cap, align):
         n = int(host(ix.n_slots)[0])
         assert n == int(want["n_slots"][0])
         assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
-        for name in ("slot_of", "esrc", "group_counts"):
+        for name in ("slot_of", "esrc", "group_counts", "slot_src"):
             assert_exact(host(getattr(ix, name)), want[name], name)
     return gi, gw, ix, want_i, w_np, want
 
@@ -790,8 +829,8 @@ def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False, bf16_partials=Fa
             want_gq, want_gs = oracle.permute(qs, want["gsrc"]), oracle.permute(ss, want["gsrc"])
             assert_rows_exact(gq[:n], want_gq, "FP8 group-slot codes")
             assert_rows_exact(gsc[:n], want_gs, "FP8 group-slot scales")
-            xq = m.permute_grouped(gq, ix.esrc, ix.row_of)
-            xs = m.permute_grouped(gsc, ix.esrc, ix.row_of)
+            xq = m.permute_grouped(gq, ix.esrc, ix.row_of, src_of=ix.slot_src)
+            xs = m.permute_grouped(gsc, ix.esrc, ix.row_of, src_of=ix.slot_src)
             want_xq, want_xs = oracle.permute(want_gq, want["esrc"]), oracle.permute(want_gs, want["esrc"])
             del gq, gsc, want_gq, want_gs
         else:
@@ -806,7 +845,7 @@ def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False, bf16_partials=Fa
             gbuf = m.permute_scatter(xd, ix.slot_of, slots)
             want_g = oracle.permute(x, want["gsrc"])
             assert_rows_exact(gbuf[:n], want_g, "group slots (send)")
-            xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of)
+            xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of, src_of=ix.slot_src)
             want_xp = oracle.permute(want_g, want["esrc"])
             del gbuf, want_g
         else:
@@ -938,14 +977,14 @@ def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
         m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix, alignment=align)
         if mode == "fp8" and gs:
             m.permute_scatter_fp8(x, ix.slot_of, slots, block, out=(gq, gsc))
-            m.permute_grouped(gq, ix.esrc, ix.row_of, out=outs["xp"])
-            m.permute_grouped(gsc, ix.esrc, ix.row_of, out=outs["xs"])
+            m.permute_grouped(gq, ix.esrc, ix.row_of, out=outs["xp"], src_of=ix.slot_src)
+            m.permute_grouped(gsc, ix.esrc, ix.row_of, out=outs["xs"], src_of=ix.slot_src)
         elif mode == "fp8":
             m.permute_scatter_fp8(x, ix.row_of, rows, block, src_row=ix.sorted_indices,
                                   out=(outs["xp"], outs["xs"]))
         elif gs:
             m.permute_scatter(x, ix.slot_of, slots, out=gbuf)
-            m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=outs["xp"])
+            m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=outs["xp"], src_of=ix.slot_src)
         else:
             m.permute_scatter(x, ix.row_of, rows, src_row=ix.sorted_indices, out=outs["xp"])
         if gs:
@@ -1055,11 +1094,11 @@ def test_random_configuration(m, i):
         n = int(host(ix.n_slots)[0])
         assert n == int(want["n_slots"][0])
         assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
-        for name in ("slot_of", "esrc", "group_counts"):
+        for name in ("slot_of", "esrc", "group_counts", "slot_src"):
             assert_exact(host(getattr(ix, name)), want[name], name)
         slots = T * min(K, E // gs)
         gbuf = m.permute_scatter(dev(x), ix.slot_of, slots)
-        xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of)
+        xp = m.permute_grouped(gbuf, ix.esrc, ix.row_of, src_of=ix.slot_src if i % 2 else None)
         p16 = c["pdt"] == "bf16"
         part = m.group_precombine(dev(y), ix.row_of, gw, gi, E, gs, ix.slot_of, slots_cap=slots,
                                   out_dtype=torch.bfloat16 if p16 else torch.float32)
@@ -1403,7 +1442,7 @@ def test_pipeline_is_deterministic(m, case):
                                               P(torch.empty((T, K), dtype=torch.float32, device=DEV))))
         ix = m.alloc_index(T, K, E, cap, gs)
         for f in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs", "slot_of",
-                  "gsrc", "esrc", "group_counts", "n_slots"):
+                  "gsrc", "esrc", "group_counts", "n_slots", "slot_src"):
             t = getattr(ix, f)
             if t is not None and prev is not None:
                 t.view(torch.uint8).fill_(0xFF)
@@ -1413,10 +1452,10 @@ def test_pipeline_is_deterministic(m, case):
         if gs:
             n = int(ix.n_slots.item())
             r.update(slot_of=ix.slot_of, esrc=ix.esrc, group_counts=ix.group_counts, n_slots=ix.n_slots,
-                     gsrc=ix.gsrc[:n])
+                     gsrc=ix.gsrc[:n], slot_src=ix.slot_src)
             gbuf = m.permute_scatter(x, ix.slot_of, slots, out=P(torch.empty((slots, H), dtype=x.dtype, device=DEV)))
             r["gbuf"] = gbuf[:n]
-            r["xp"] = m.permute_grouped(gbuf, ix.esrc, ix.row_of, out=P(torch.empty((rows, H), dtype=x.dtype,
+            r["xp"] = m.permute_grouped(gbuf, ix.esrc, ix.row_of, src_of=ix.slot_src, out=P(torch.empty((rows, H), dtype=x.dtype,
                                                                                   device=DEV)))
             part = m.group_precombine(y, ix.row_of, gw, gi, E, gs, ix.slot_of,
                                       out=P(torch.empty((slots, H), dtype=torch.float32, device=DEV)))

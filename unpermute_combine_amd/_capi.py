@@ -17,7 +17,7 @@ _i32 = ctypes.c_int32
 class MoeIndexStruct(ctypes.Structure):
     _fields_ = [(name, _P) for name in (
         "counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs",
-        "slot_of", "gsrc", "esrc", "group_counts", "n_slots")]
+        "slot_of", "gsrc", "esrc", "group_counts", "n_slots", "slot_src")]
 
 
 # name -> (restype, argtypes); every symbol the header declares
@@ -36,7 +36,7 @@ SIGNATURES = {
     "moe_permute_scatter": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i32, _P, _i64, _P, _P]),
     "moe_quantize_fp8": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _i32, _P, _P, _P]),
     "moe_permute_scatter_fp8": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _i32, _P, _i32, _P, _i64, _P, _P, _P]),
-    "moe_permute_grouped": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _i64, _i32, _P, _P]),
+    "moe_permute_grouped": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _i64, _i32, _P, _P, _P]),
     "moe_unpermute_combine_backward": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, _i64, _i64, _P, _P, _i64,
                                                       _i32, _P, _P, ctypes.c_int, _P, _P]),
     "moe_route_topk_backward": (ctypes.c_int, [_P, _P, _P, _i64, _i32, _i32, _P, _P]),

@@ -28,7 +28,8 @@
 //             (a match-any built from ballots); their stable rank is popcount(peers &
 //             lanes_below) and the last peer advances the key's running row counter in LDS.
 //             The workgroups then write the padding or unused rows together.
-//   3. esrc   (group mode, K not a power of two) expert-major row -> group slot. With K a power
+//   3. esrc   (group mode, K not a power of two) expert-major row -> group slot (and routing
+//             slot -> group slot, slot_src). With K a power
 //             of two a token's slots sit in consecutive lanes of one wavefront: the first slot
 //             of each (token, group) is found with ballots, and the rank kernel hands its group
 //             slot to the token's other slots of the group and writes esrc itself.
@@ -599,6 +600,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
                     const int32_t gslot = __shfl(slot, from, kWave);
                     if (row >= 0)
                         a.ix.esrc[row] = gslot;
+                    if (in && a.ix.slot_src)
+                        a.ix.slot_src[i] = row >= 0 ? gslot : -1;
                 }
                 if (lead) {
                     a.ix.slot_of[t * a.G + g] = slot;
@@ -662,10 +665,13 @@ __global__ __launch_bounds__(256) void esrc_kernel(IndexArgs a)
          i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int e = a.topk_idx[i];
         const int32_t row = a.ix.row_of[i];
-        if (!valid_expert(e, a.E) || row < 0)
-            continue;
+        const bool ok = valid_expert(e, a.E) && row >= 0;
         const int64_t t = i / a.K;
-        a.ix.esrc[row] = a.ix.slot_of[t * a.G + e / a.gs];
+        const int32_t slot = ok ? a.ix.slot_of[t * a.G + e / a.gs] : -1;
+        if (ok)
+            a.ix.esrc[row] = slot;
+        if (a.ix.slot_src)
+            a.ix.slot_src[i] = slot;
     }
 }
 

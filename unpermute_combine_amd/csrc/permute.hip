@@ -90,10 +90,11 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
 }
 
 // ---------------------------------------------------------------- source-major form
-// One wavefront per (source row, 1 KiB slice of it): each lane loads one 16-byte vector of the
-// row once and stores it to every destination; the destinations sit in lanes 0..63 (64 entries
-// of dst_of at a time; the row is loaded when the first valid one turns up) and are walked in
-// lane order with readlane, so the loop is uniform. Other waves write the zero rows:
+// One wavefront per (source row, 1 KiB slice of it) -- two with a dense map, each taking half of
+// the destinations (see kScatterParts) --: each lane loads one 16-byte vector of the row and
+// stores it to the wave's destinations; the destinations sit in lanes 0..63 (64 entries of dst_of
+// at a time; the row is loaded when the wave's first valid one turns up) and are walked in lane
+// order with readlane, so the loop is uniform. Other waves write the zero rows:
 // each checks `zr` entries of src_row and zero-fills those outside [0, src_rows). Measured at
 // T16384 H7168 K8 bf16: 339 us per launch (6.2 TB/s) with slices, 350 us with one 256-thread
 // workgroup per row. When the output has more rows than the map can name (N > src_rows * J:
@@ -109,6 +110,22 @@ constexpr int kScatterWaves = kScatterThreads / kWave;
 constexpr int kScatterVecs = 1;
 constexpr int kZeroRowsPerWave = 16;
 constexpr int kZeroRowsPerWaveFirst = 8;
+// Waves per (source row, slice). With a dense map -- one output row per map entry, as the standard
+// dispatch's row_of is -- every row has J destinations, and two waves per slice each store to half
+// of them: wave p takes the valid destinations ranked [4p, 4p + 4) in column order, the last wave
+// the rest. On MI355X a wave's first stores are the cheap ones (8 GiB of 1 KiB stores ran at 7.1
+// TB/s with one store per wave, 5.7-6.1 TB/s with 2-16; fanned out 1 KiB -> 8 destinations at 5.8
+// TB/s with 2-4 stores per wave, 5.45 TB/s with 8, 4.7 TB/s with 1): at T16384 H7168 K8 bf16 the
+// permute took 379 us instead of 395 us with caches flushed. Sparse maps (the group send's 32
+// columns with ~3 destinations, drop-and-pad rows with ~3 of 8 kept) keep one wave per slice: there
+// the second wave mostly finds nothing to store (drop-and-pad 140 -> 147 us, group send 78 -> 98 us);
+// so did three or four waves per slice on the dense map (473 and 485 us: each loads the slice).
+constexpr int kScatterDestsPerWave = 4;
+constexpr int kScatterParts = 2;
+inline int scatter_parts(int J, int64_t src_rows, int64_t N)
+{
+    return J > kScatterDestsPerWave && N == src_rows * J ? kScatterParts : 1;
+}
 constexpr int kMaxScatterDests = MOE_MAX_EXPERTS;  // dst_of columns (e.g. one per expert group)
 constexpr int kMaxGroupDests = kWave;               // destinations of one group of the grouped gather
 
@@ -135,11 +152,13 @@ __device__ __forceinline__ void zero_rows_wave(int64_t src_rows, int64_t nvec, c
 
 __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ dst_of, int J,
-    const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst, int64_t zero_waves, bool zero_first)
+    const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst, int64_t zero_waves, bool zero_first,
+    int parts)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
-    const int64_t wpr = (nvec + kWave * kScatterVecs - 1) / (kWave * kScatterVecs);  // waves per source row
+    const int64_t spr = (nvec + kWave * kScatterVecs - 1) / (kWave * kScatterVecs);  // slices per source row
+    const int64_t wpr = spr * parts;                                                  // waves per source row
     const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterWaves +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = src_rows * wpr;
@@ -155,27 +174,38 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     const int64_t t = cw / wpr;
     if (t >= src_rows)
         return;
-    const int64_t v0 = (cw - t * wpr) * kWave * kScatterVecs + lane;  // this lane's first vector of the row
+    const int64_t rem = cw - t * wpr;
+    const int part = static_cast<int>(rem % parts);
+    const int64_t v0 = (rem / parts) * kWave * kScatterVecs + lane;  // this lane's first vector of the row
+    // this wave's share: the row's valid destinations ranked [lo, hi) in column order
+    const int lo = part * kScatterDestsPerWave;
+    const int hi = part == parts - 1 ? 0x7fffffff : lo + kScatterDestsPerWave;
     u32x4 r[kScatterVecs];
-    bool loaded = false;                           // wave-uniform
-    for (int j0 = 0; j0 < J; j0 += kWave) {        // the destinations, 64 entries at a time
+    bool loaded = false;                                 // wave-uniform
+    int seen = 0;                                        // valid destinations before this chunk
+    for (int j0 = 0; j0 < J && seen < hi; j0 += kWave) {  // the destinations, 64 entries at a time
         const int32_t my = j0 + lane < J ? dst_of[t * J + j0 + lane] : -1;
         uint64_t m = __ballot(my >= 0 && my < N);
-        if (m == 0)
+        const int nm = __popcll(m);
+        if (seen + nm <= lo) {
+            seen += nm;
             continue;
-        if (!loaded) {
-#pragma unroll
-            for (int i = 0; i < kScatterVecs; ++i) {
-                const int64_t v = v0 + i * kWave;
-                r[i] = u32x4{0u, 0u, 0u, 0u};
-                if (v < nvec)
-                    r[i] = ld16(src + t * row_bytes + v * 16);
-            }
-            loaded = true;
         }
-        while (m) {
+        for (; seen < lo; ++seen)  // the valid destinations of the previous waves' shares
+            m &= m - 1;
+        for (; m && seen < hi; ++seen) {
             const int j = __builtin_ctzll(m);
             m &= m - 1;
+            if (!loaded) {
+#pragma unroll
+                for (int i = 0; i < kScatterVecs; ++i) {
+                    const int64_t v = v0 + i * kWave;
+                    r[i] = u32x4{0u, 0u, 0u, 0u};
+                    if (v < nvec)
+                        r[i] = ld16(src + t * row_bytes + v * 16);
+                }
+                loaded = true;
+            }
             const __amdgpu_buffer_rsrc_t q = make_rsrc(
                 dst + static_cast<int64_t>(__builtin_amdgcn_readlane(my, j)) * row_bytes, static_cast<uint32_t>(row_bytes));
 #pragma unroll
@@ -225,12 +255,15 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_elem_kernel(
 }
 
 // ---------------------------------------------------------------- grouped gather
-// One wavefront per (group of destination rows, 1 KiB slice): lanes 0..J-1 hold the group's
-// destination rows and, one dependent load later, their source rows src_row[d]. The distinct
-// source rows are taken kGroupLoads at a time: their slices are loaded first (all in flight
-// together; gfx9 completes vector-memory operations in order, so a load issued after a store
-// would wait for it), then stored to every destination of the group that names them. Waves past
-// the last group write the zero rows, as in the source-major form.
+// One wavefront per (group of destination rows, 1 KiB slice) -- two for groups of more than four
+// rows, each taking half of them (see kScatterParts) --: lanes 0..J-1 hold the group's
+// destination rows and their source rows (src_of beside them when the caller has it, else
+// src_row[d] one dependent load later). The distinct source rows are taken kGroupLoads at a
+// time: their slices are loaded first (all in flight together; gfx9 completes vector-memory
+// operations in order, so a load issued after a store would wait for it), then stored to every
+// destination of the wave's share that names them. Waves past the last group write the zero
+// rows, as in the source-major form. The element-wise form looks sources up through src_row
+// (src_of, when given, names the same rows).
 constexpr int kGroupLoads = 4;
 // workgroups of the grouped gather: 2 wavefronts (at T8192 H7168 with 32 groups of 8: 241 us
 // against 245 us with 4)
@@ -240,11 +273,12 @@ constexpr int kGroupLoadPolicy = 0;
 
 __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
-    const int32_t *__restrict__ dst_of, int64_t M, int J, int64_t N, char *__restrict__ dst)
+    const int32_t *__restrict__ dst_of, int64_t M, int J, int64_t N, const int32_t *__restrict__ src_of,
+    char *__restrict__ dst, int parts)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
-    const int64_t wpr = (nvec + kWave - 1) / kWave;
+    const int64_t wpr = (nvec + kWave - 1) / kWave * parts;  // waves per group of destination rows
     const int64_t gw = static_cast<int64_t>(blockIdx.x) * kGroupedWaves +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = M * wpr;
@@ -253,12 +287,29 @@ __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
         return;
     }
     const int64_t g = gw / wpr;
-    const int64_t v = (gw - g * wpr) * kWave + lane;
+    const int64_t rem = gw - g * wpr;
+    const int part = static_cast<int>(rem % parts);
+    const int64_t v = (rem / parts) * kWave + lane;
     const int32_t d = lane < J ? dst_of[g * J + lane] : -1;
+    // the source of each destination: given beside it (both loads in flight together), or looked
+    // up through the gather map once the destination is known
+    const int32_t so = src_of && lane < J ? src_of[g * J + lane] : -1;
     const bool dv = d >= 0 && d < N;
-    const int32_t sr = dv ? src_row[d] : -1;
+    const int32_t sr = src_of ? (dv ? so : -1) : (dv ? src_row[d] : -1);
     const bool ok = dv && sr >= 0 && sr < src_rows;
     uint64_t m = __ballot(ok);
+    // this wave's share of the group's rows: ranks [4 part, 4 part + 4) in lane order, the last
+    // wave the rest (see kScatterParts)
+    for (int i = 0; i < part * kScatterDestsPerWave && m; ++i)
+        m &= m - 1;
+    if (part != parts - 1) {
+        uint64_t keep = 0;
+        for (int i = 0; i < kScatterDestsPerWave && m; ++i) {
+            keep |= m & (~m + 1);
+            m &= m - 1;
+        }
+        m = keep;
+    }
     while (m) {
         int32_t sb[kGroupLoads];
         uint64_t pb[kGroupLoads];
@@ -367,13 +418,14 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
         const int64_t nvec = row_bytes / 16;
         const bool zero_first = src_row && N > src_rows * J;  // padding rows are certain
         const int64_t zwaves = src_row ? ceil_div(N, zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave) : 0;
-        const int64_t waves = src_rows * ceil_div(nvec, static_cast<int64_t>(kWave) * kScatterVecs) + zwaves;
+        const int parts = scatter_parts(J, src_rows, N);
+        const int64_t waves = src_rows * ceil_div(nvec, static_cast<int64_t>(kWave) * kScatterVecs) * parts + zwaves;
         const int64_t blocks = ceil_div(waves, kScatterWaves);
         if (blocks > 0x7fffffff)
             return MOE_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(permute_scatter_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0,
                            stream, static_cast<const char *>(src), src_rows, nvec, dst_of, J, src_row, N,
-                           static_cast<char *>(dst), zwaves, zero_first);
+                           static_cast<char *>(dst), zwaves, zero_first, parts);
         return launch_status();
     }
     const int64_t blocks = src_rows + ceil_div(zero_waves, kScatterWaves);
@@ -433,7 +485,7 @@ extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, 
 
 extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
                                           const int32_t *src_row, int64_t N, const int32_t *dst_of, int64_t M,
-                                          int32_t J, void *dst, hipStream_t stream)
+                                          int32_t J, const int32_t *src_of, void *dst, hipStream_t stream)
 {
     using namespace moe;
     if (src_rows < 0 || H < 1 || N < 0 || M < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3))
@@ -451,12 +503,16 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
     const int64_t zero_waves = ceil_div(N, kZeroRowsPerWave);
     if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
         const int64_t nvec = row_bytes / 16;
-        const int64_t blocks = ceil_div(M * ceil_div(nvec, kWave) + zero_waves, kGroupedWaves);
+        // two waves per slice, each storing to half of a group's rows, for groups of more than
+        // four rows of at least one full slice: at T8192 H7168 (32 groups of 8) 233 -> 225 us,
+        // FP8 codes 120 -> 118 us; the 224-byte rows of FP8 scales lost (11.8 -> 15.6 us)
+        const int parts = J > kScatterDestsPerWave && nvec >= kWave ? kScatterParts : 1;
+        const int64_t blocks = ceil_div(M * ceil_div(nvec, kWave) * parts + zero_waves, kGroupedWaves);
         if (blocks > 0x7fffffff)
             return MOE_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(permute_grouped_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kGroupedThreads), 0,
                            stream, static_cast<const char *>(src), src_rows, nvec, src_row, dst_of, M, J, N,
-                           static_cast<char *>(dst));
+                           src_of, static_cast<char *>(dst), parts);
         return launch_status();
     }
     const int64_t blocks = M + ceil_div(zero_waves, kScatterWaves);

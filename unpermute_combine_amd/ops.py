@@ -106,6 +106,7 @@ class MoeIndex:
     esrc: Optional[torch.Tensor] = None
     group_counts: Optional[torch.Tensor] = None
     n_slots: Optional[torch.Tensor] = None
+    slot_src: Optional[torch.Tensor] = None
     workspace: Optional[torch.Tensor] = None
 
     @property
@@ -121,7 +122,8 @@ class MoeIndex:
     def struct(self) -> _capi.MoeIndexStruct:
         return _capi.MoeIndexStruct(*[None if t is None else t.data_ptr() for t in (
             self.counts, self.group_list, self.kept_counts, self.sorted_indices, self.row_of,
-            self.permuted_probs, self.slot_of, self.gsrc, self.esrc, self.group_counts, self.n_slots)])
+            self.permuted_probs, self.slot_of, self.gsrc, self.esrc, self.group_counts, self.n_slots,
+            self.slot_src)])
 
 
 def workspace_bytes(T: int, K: int, E: int, group_size: int = 0) -> int:
@@ -157,6 +159,7 @@ def alloc_index(T: int, K: int, E: int, capacity: int = 0, group_size: int = 0, 
         ix.esrc = torch.empty(rows, **i32)
         ix.group_counts = torch.empty(G, **i32)
         ix.n_slots = torch.empty(1, **i32)
+        ix.slot_src = torch.empty((T, K), **i32)
     if workspace:
         ws = workspace_bytes(T, K, E, group_size)
         ix.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
@@ -259,16 +262,23 @@ def permute_scatter(src: torch.Tensor, dst_of: torch.Tensor, num_rows: int,
 
 
 def permute_grouped(src: torch.Tensor, src_row: torch.Tensor, dst_of: torch.Tensor,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, src_of: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The gather out[r] = src[src_row[r]] (zero rows where src_row is out of range), done in the
     groups of destination rows that dst_of [M, J] lists; a source row named by several rows of
     one group is read once. Rows with a valid src_row that dst_of never lists are not written.
+    src_of [M, J], if given, names each listed row's source (= src_row[dst_of]) so that it need
+    not be looked up.
 
-    The group dispatch's receive side: permute_grouped(group_buffer, index.esrc, index.row_of)."""
+    The group dispatch's receive side: permute_grouped(group_buffer, index.esrc, index.row_of,
+    src_of=index.slot_src)."""
     _need(src, "src", None, 2)
     dt = _hidden_dt(src, "src")
     _need(src_row, "src_row", torch.int32, 1)
     _need(dst_of, "dst_of", torch.int32, 2)
+    if src_of is not None:
+        _need(src_of, "src_of", torch.int32, 2)
+        if tuple(src_of.shape) != tuple(dst_of.shape):
+            raise ValueError("src_of must have the shape of dst_of")
     N = src_row.shape[0]
     H = src.shape[1]
     if out is None:
@@ -277,8 +287,8 @@ def permute_grouped(src: torch.Tensor, src_row: torch.Tensor, dst_of: torch.Tens
     if tuple(out.shape) != (N, H):
         raise ValueError(f"out must be [{N}, {H}]")
     check("moe_permute_grouped", lib().moe_permute_grouped(
-        _p(src), src.shape[0], H, dt, _p(src_row), N, _p(dst_of), dst_of.shape[0], dst_of.shape[1], _p(out),
-        _stream()))
+        _p(src), src.shape[0], H, dt, _p(src_row), N, _p(dst_of), dst_of.shape[0], dst_of.shape[1], _p(src_of),
+        _p(out), _stream()))
     return out
 
 
