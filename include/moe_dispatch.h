@@ -110,11 +110,15 @@ typedef struct moe_index {
     int32_t *counts;         /* [E] rows routed to each expert, before capacity ([Megatron] §1.2
                                 num_tokens_per_expert). Required. */
     int32_t *group_list;     /* [E] inclusive running sum of counts ([Scratch] §7:
-                                [3,2,4] -> [3,5,9]; expert e owns rows
-                                [group_list[e]-counts[e], group_list[e])); with expert
+                                [3,2,4] -> [3,5,9]); in the standard and group modes expert e
+                                owns rows [group_list[e]-counts[e], group_list[e]). With expert
                                 alignment A the running sum of the aligned lengths
                                 ceil(counts/A)*A (expert e's segment ends at group_list[e], its
-                                tokens come first, then padding rows). Required. */
+                                tokens come first, then padding rows). In drop-and-pad mode it
+                                stays the running sum of the counts before capacity and
+                                describes no row layout: there expert e owns rows
+                                [e*capacity, e*capacity + kept_counts[e]), then padding up to
+                                (e+1)*capacity. Required. */
     int32_t *kept_counts;    /* [E] min(counts, capacity) in drop-and-pad mode, counts
                                 otherwise. May be NULL. */
     int32_t *sorted_indices; /* [R] source token of each expert-major row ([Megatron] §1.1,
