@@ -94,6 +94,17 @@ __device__ __forceinline__ uint64_t lanemask_lt()
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b % 8). This renumbers the
+// blocks so that each XCD takes one contiguous range of logical blocks (XCD x the x-th eighth,
+// the first nb % 8 XCDs one block more), a bijection on [0, nb).
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t b, uint32_t nb)
+{
+    const uint32_t per = nb / kXcds, extra = nb % kXcds;
+    const uint32_t x = b % kXcds, i = b / kXcds;
+    return x < extra ? x * (per + 1) + i : extra * (per + 1) + (x - extra) * per + i;
+}
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline moe_status launch_status()
@@ -102,5 +113,14 @@ inline moe_status launch_status()
 }
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The source-major row scatter of moe_permute_scatter for rows of nvec 16-byte vectors (permute.hip):
+// dst[dst_of[t*J + j]] = src[t]; rows i with src_row[i] outside [0, src_rows) other than
+// MOE_ROW_UNUSED become zero rows (src_row may be NULL). With `scaled`, the rows are bf16 and
+// destination j receives scale[t*J + j] * src[t] (float32 products rounded to bf16; scale NULL:
+// unit weights). Launches on `stream`; sizes are the caller's to check.
+moe_status launch_scatter_vec16(const char *src, int64_t src_rows, int64_t nvec, const int32_t *dst_of, int J,
+                                const int32_t *src_row, int64_t N, char *dst, bool scaled, const float *scale,
+                                hipStream_t stream);
 
 }  // namespace moe

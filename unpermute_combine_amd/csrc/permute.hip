@@ -102,8 +102,17 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
 // so that they overlap the copies instead of trailing them (drop-and-pad at T8192 H4096 E128:
 // 134 -> 125 us); otherwise they come last, 16 rows each (putting them first cost the
 // unpadded case ~1%).
-constexpr int kScatterThreads = 256;
+constexpr int kScatterThreads = 256;  // element-wise kernels
 constexpr int kScatterWaves = kScatterThreads / kWave;
+// workgroups of the 16-byte scatter: 8 wavefronts. The waves of a source row are ordered (half of
+// the destinations, slice), so that a workgroup writes up to 8 KiB contiguous to each destination
+// of its half. Measured with caches flushed at T16384 H7168 K8 bf16: 364 us against 379 us with
+// 4-wave workgroups ordered (slice, half) and 367 / 404 us with 16 / 12 waves; 395 us with 4-wave
+// workgroups of 128 threads. Blocks stay in the default round-robin over the XCDs: giving each
+// XCD one contiguous range of blocks made this permute 417 us (and drop-and-pad, whose padding
+// waves then fell on one XCD, 366 against 140 us).
+constexpr int kScatterVecThreads = 512;
+constexpr int kScatterVecWaves = kScatterVecThreads / kWave;
 // 16-byte vectors of a source row per lane of a scatter wavefront: at T16384 H7168 K8 bf16 one
 // (1 KiB per wavefront) took 342 us, two 348 us and four 355 us; 128- or 512-thread workgroups
 // changed nothing at that size and lost at drop-and-pad T8192 H4096 E128 (128: 134 against 125 us)
@@ -150,19 +159,22 @@ __device__ __forceinline__ void zero_rows_wave(int64_t src_rows, int64_t nvec, c
     }
 }
 
-__global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
+// SCALE: bf16 rows, destination j of source row t receives scale[t*J + j] * row (float32
+// products, rounded to bf16 to nearest even): the backward of the weighted combine, dy = w * dout.
+template <bool SCALE>
+__global__ __launch_bounds__(kScatterVecThreads) void permute_scatter_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ dst_of, int J,
     const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst, int64_t zero_waves, bool zero_first,
-    int parts)
+    int parts, const float *__restrict__ scale)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
     const int64_t spr = (nvec + kWave * kScatterVecs - 1) / (kWave * kScatterVecs);  // slices per source row
     const int64_t wpr = spr * parts;                                                  // waves per source row
-    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterWaves +
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterVecWaves +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = src_rows * wpr;
-    // wave index -> zero window or copy wave; the grid's last workgroup may hold up to 3 waves
+    // wave index -> zero window or copy wave; the grid's last workgroup may hold up to 7 waves
     // past both (zero windows past N check nothing, copy rows past src_rows return below)
     const int64_t zw = zero_first ? gw : gw - copy_waves;
     if (zero_first ? gw < zero_waves : gw >= copy_waves) {
@@ -175,8 +187,8 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     if (t >= src_rows)
         return;
     const int64_t rem = cw - t * wpr;
-    const int part = static_cast<int>(rem % parts);
-    const int64_t v0 = (rem / parts) * kWave * kScatterVecs + lane;  // this lane's first vector of the row
+    const int part = static_cast<int>(rem / spr);  // waves of a row: (part, slice)
+    const int64_t v0 = (rem % spr) * kWave * kScatterVecs + lane;  // this lane's first vector of the row
     // this wave's share: the row's valid destinations ranked [lo, hi) in column order
     const int lo = part * kScatterDestsPerWave;
     const int hi = part == parts - 1 ? 0x7fffffff : lo + kScatterDestsPerWave;
@@ -185,6 +197,9 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
     int seen = 0;                                        // valid destinations before this chunk
     for (int j0 = 0; j0 < J && seen < hi; j0 += kWave) {  // the destinations, 64 entries at a time
         const int32_t my = j0 + lane < J ? dst_of[t * J + j0 + lane] : -1;
+        float ws = 1.0f;
+        if constexpr (SCALE)
+            ws = j0 + lane < J && scale ? scale[t * J + j0 + lane] : 1.0f;  // loaded beside the destination
         uint64_t m = __ballot(my >= 0 && my < N);
         const int nm = __popcll(m);
         if (seen + nm <= lo) {
@@ -211,8 +226,16 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_vec16_kernel(
 #pragma unroll
             for (int i = 0; i < kScatterVecs; ++i) {
                 const int64_t v = v0 + i * kWave;
+                u32x4 o = r[i];
+                if constexpr (SCALE) {
+                    const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ws), j));
+                    o = u32x4{pack_bf16x2(wj * bf16_lo(r[i].x), wj * bf16_hi(r[i].x)),
+                              pack_bf16x2(wj * bf16_lo(r[i].y), wj * bf16_hi(r[i].y)),
+                              pack_bf16x2(wj * bf16_lo(r[i].z), wj * bf16_hi(r[i].z)),
+                              pack_bf16x2(wj * bf16_lo(r[i].w), wj * bf16_hi(r[i].w))};
+                }
                 if (v < nvec)
-                    st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r[i]);
+                    st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), o);
             }
         }
     }
@@ -394,6 +417,30 @@ __global__ __launch_bounds__(kScatterThreads) void permute_grouped_elem_kernel(
 }
 
 }  // namespace
+
+moe_status launch_scatter_vec16(const char *src, int64_t src_rows, int64_t nvec, const int32_t *dst_of, int J,
+                                const int32_t *src_row, int64_t N, char *dst, bool scaled, const float *scale,
+                                hipStream_t stream)
+{
+    const bool zero_first = src_row && N > src_rows * J;  // padding rows are certain
+    const int64_t zwaves = src_row ? ceil_div(N, zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave) : 0;
+    const int parts = scatter_parts(J, src_rows, N);
+    const int64_t waves = src_rows * ceil_div(nvec, static_cast<int64_t>(kWave) * kScatterVecs) * parts + zwaves;
+    const int64_t blocks = ceil_div(waves, kScatterVecWaves);
+    if (blocks > 0x7fffffff)
+        return MOE_ERR_UNSUPPORTED;
+    if (blocks == 0)
+        return MOE_OK;
+    if (scaled)
+        hipLaunchKernelGGL(permute_scatter_vec16_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kScatterVecThreads),
+                           0, stream, src, src_rows, nvec, dst_of, J, src_row, N, dst, zwaves, zero_first, parts, scale);
+    else
+        hipLaunchKernelGGL(permute_scatter_vec16_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                           dim3(kScatterVecThreads), 0, stream, src, src_rows, nvec, dst_of, J, src_row, N, dst, zwaves,
+                           zero_first, parts, nullptr);
+    return launch_status();
+}
+
 }  // namespace moe
 
 extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
@@ -414,20 +461,9 @@ extern "C" moe_status moe_permute_scatter(const void *src, int64_t src_rows, int
     if (row_bytes > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
     const int64_t zero_waves = src_row ? ceil_div(N, kZeroRowsPerWave) : 0;
-    if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
-        const int64_t nvec = row_bytes / 16;
-        const bool zero_first = src_row && N > src_rows * J;  // padding rows are certain
-        const int64_t zwaves = src_row ? ceil_div(N, zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave) : 0;
-        const int parts = scatter_parts(J, src_rows, N);
-        const int64_t waves = src_rows * ceil_div(nvec, static_cast<int64_t>(kWave) * kScatterVecs) * parts + zwaves;
-        const int64_t blocks = ceil_div(waves, kScatterWaves);
-        if (blocks > 0x7fffffff)
-            return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(permute_scatter_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScatterThreads), 0,
-                           stream, static_cast<const char *>(src), src_rows, nvec, dst_of, J, src_row, N,
-                           static_cast<char *>(dst), zwaves, zero_first, parts);
-        return launch_status();
-    }
+    if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src)))
+        return launch_scatter_vec16(static_cast<const char *>(src), src_rows, row_bytes / 16, dst_of, J, src_row, N,
+                                    static_cast<char *>(dst), false, nullptr, stream);
     const int64_t blocks = src_rows + ceil_div(zero_waves, kScatterWaves);
     if (blocks > 0x7fffffff)
         return MOE_ERR_UNSUPPORTED;
