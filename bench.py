@@ -37,6 +37,8 @@ METRIC = "permute+combine effective HBM GB/s (% of peak) and routed tokens/s"
 _PERMUTE_SRC = ["unpermute_combine_amd/csrc/permute.hip", "unpermute_combine_amd/csrc/moe_common.h"]
 _COMBINE_SRC = ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csrc/moe_common.h"]
 _FP8_SRC = ["unpermute_combine_amd/csrc/fp8.hip", "unpermute_combine_amd/csrc/moe_common.h"]
+_BWD_SRC = ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csrc/permute.hip",
+            "unpermute_combine_amd/csrc/moe_common.h"]
 # HBM-bound kernel calls of a step: sources (for the PMC summaries' digest) and kernel symbol.
 # Standard and drop-and-pad steps run `permute` and `combine`; group-mode steps run the two
 # dispatch stages (send: one copy per token and group; receive: group slots to expert-major
@@ -44,10 +46,12 @@ _FP8_SRC = ["unpermute_combine_amd/csrc/fp8.hip", "unpermute_combine_amd/csrc/mo
 # With --backward the step is the backward of the path on one saved forward index: the combine's
 # backward (expert-row gradient and weight gradient), the dispatch's backward (the unit-weight
 # combine of the expert-row gradient; in group mode the unit-weight pre-combine, then the final
-# sum) and the router softmax's backward.
+# sum) and the router softmax's backward. With bf16 rows the combine's backward is two kernels, the
+# weighted scatter of dout (dy) and a read-only pass of dots (dw): its PMC summary and roofline are
+# those of the call (both kernels together).
 KERNEL_SOURCES = {"permute": _PERMUTE_SRC, "combine": _COMBINE_SRC, "dispatch_send": _PERMUTE_SRC,
                   "dispatch_recv": _PERMUTE_SRC, "precombine": _COMBINE_SRC, "final_sum": _COMBINE_SRC,
-                  "combine_bwd": _COMBINE_SRC, "dispatch_bwd": _COMBINE_SRC, "dispatch_bwd_recv": _COMBINE_SRC,
+                  "combine_bwd": _BWD_SRC, "dispatch_bwd": _COMBINE_SRC, "dispatch_bwd_recv": _COMBINE_SRC,
                   "dispatch_bwd_send": _COMBINE_SRC, "permute_fp8": _FP8_SRC, "dispatch_send_fp8": _FP8_SRC,
                   "dispatch_recv_scales": _PERMUTE_SRC}
 KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine_kernel",
@@ -100,6 +104,10 @@ def parse_args():
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    p.add_argument("--no-warm", action="store_true",
+                   help="skip the back-to-back (unflushed) passes, so that every kernel launch after the "
+                        "warmup is preceded by a flush (for profiling runs whose per-kernel averages should "
+                        "match kernel_us)")
     p.add_argument("--no-flush", action="store_true",
                    help="no cache flush before the timed steps and kernel calls (they still run one by one "
                         "between events)")
@@ -318,15 +326,19 @@ def main():
     flush = None if args.no_flush else CacheFlush(torch)
 
     for _ in range(args.warmup):
+        if flush is not None:
+            flush()
         step()
     torch.cuda.synchronize()
 
     # eager steps back to back (launch gaps included)
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms_per_step_eager = (time.perf_counter() - t_start) * 1e3 / args.steps
+    ms_per_step_eager = None
+    if not args.no_warm:
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms_per_step_eager = (time.perf_counter() - t_start) * 1e3 / args.steps
 
     # per-kernel times: every call flushed before and bracketed by events on its stream
     kev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
@@ -376,13 +388,16 @@ def main():
         else:
             replay = graph.replay
             for _ in range(max(3, args.warmup)):
+                if flush is not None:
+                    flush()
                 replay()
             torch.cuda.synchronize()
-            t_start = time.perf_counter()
-            for _ in range(args.steps):
-                replay()
-            torch.cuda.synchronize()
-            ms_per_step_warm = (time.perf_counter() - t_start) * 1e3 / args.steps
+            if not args.no_warm:
+                t_start = time.perf_counter()
+                for _ in range(args.steps):
+                    replay()
+                torch.cuda.synchronize()
+                ms_per_step_warm = (time.perf_counter() - t_start) * 1e3 / args.steps
             launch = "hip graph replay"
     step_ms = timed_steps(replay)
     ms_per_step, ms_per_step_median, ms_per_step_min = _stats(step_ms)
@@ -445,12 +460,16 @@ def main():
     dom = max(hbm_kernels, key=lambda k: kernel_us[k])
     achieved = kbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
     symbol = KERNEL_SYMBOLS[dom]
+    kernel_name = symbol
     if dom == "combine":
-        symbol = combine_symbol(dt == "bf16", dt == "bf16", K, H, T)
+        symbol = kernel_name = combine_symbol(dt == "bf16", dt == "bf16", K, H, T)
+    if dom == "combine_bwd" and dt == "bf16":
+        symbol = "combine_backward_call"
+        kernel_name = "permute_scatter_vec16_kernel<true> (dy) + combine_backward_kernel (dw dots)"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic(dom, cid, args.backward, symbol, args.fp8, args.bf16_partials),
-                "kernel": symbol, "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
+                "kernel": kernel_name, "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kernel_us[dom], 2)}
 
     result = {
@@ -482,8 +501,8 @@ def main():
                         "; ms_per_step = mean of the per-step event times")
     result["ms_per_step_median"] = round(ms_per_step_median, 4)
     result["ms_per_step_min"] = round(ms_per_step_min, 4)
-    result["ms_per_step_warm"] = round(ms_per_step_warm, 4)
-    result["ms_per_step_eager"] = round(ms_per_step_eager, 4)
+    result["ms_per_step_warm"] = None if ms_per_step_warm is None else round(ms_per_step_warm, 4)
+    result["ms_per_step_eager"] = None if ms_per_step_eager is None else round(ms_per_step_eager, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes,
                                               args.bf16_partials, args.fp8, fp8_block, args.backward)
