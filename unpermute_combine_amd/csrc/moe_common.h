@@ -12,7 +12,7 @@ constexpr int kWave = 64;  // CDNA wavefront width
 
 // ---------------------------------------------------------------- bf16 <-> float32
 // bf16 is the upper half of an IEEE float32; widening is a shift, narrowing rounds to nearest
-// with ties to even (NaN kept quiet with its sign).
+// with ties to even (NaN kept quiet with its sign; element-wise paths).
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 
@@ -25,9 +25,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return u >> 16;
 }
 
+// Two values rounded to bf16 by gfx950's conversion instruction (v_cvt_pk_bf16_f32: nearest, ties
+// to even; bit for bit f32_to_bf16_bits on finite values, ties, subnormals and overflow), lo in the
+// low half. One instruction per pair instead of ~6 integer operations per value: measured with
+// caches flushed, the weighted scatter of the combine's backward at T16384 H7168 K8 went 408 ->
+// ~365 us (it was ALU-bound) and the batched combine 344 -> 341 us.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // 16-byte vector used for every row access (global_load/store_dwordx4).
