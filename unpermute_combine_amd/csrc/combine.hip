@@ -700,6 +700,43 @@ __device__ __forceinline__ void reduce_dots(float (&p)[kBatch], float (*red)[kBa
     __syncthreads();
 }
 
+// reduce_dots for a compacted list of n slots: p[u] belongs to slot ks[u]; thread u < n writes
+// dw[ks[u]] (the slots left out were written by the caller).
+__device__ __forceinline__ void reduce_dots_compact(float (&p)[kBatch], float (*red)[kBatch], int n, const int *ks,
+                                                    float *dw)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+    float a4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float send = b5 ? p[i] : p[4 + i];
+        const float keep = b5 ? p[4 + i] : p[i];
+        a4[i] = keep + __shfl_xor(send, 32);
+    }
+    float a2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = b4 ? a4[i] : a4[2 + i];
+        const float keep = b4 ? a4[2 + i] : a4[i];
+        a2[i] = keep + __shfl_xor(send, 16);
+    }
+    float a1 = (b3 ? a2[1] : a2[0]) + __shfl_xor(b3 ? a2[0] : a2[1], 8);
+    a1 += __shfl_xor(a1, 4);
+    a1 += __shfl_xor(a1, 2);
+    a1 += __shfl_xor(a1, 1);
+    if ((lane & 7) == 0)
+        red[wave][lane >> 3] = a1;
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) < n) {
+        float sum = 0.0f;
+        for (int q = 0; q < static_cast<int>(blockDim.x / kWave); ++q)
+            sum += red[q][threadIdx.x];
+        dw[ks[threadIdx.x]] = sum;
+    }
+}
+
 template <typename D, typename Y, typename DY, bool SPLIT, bool DW, bool STORE = true>
 __global__ __launch_bounds__(kMaxThreads) void combine_backward_kernel(
     const D *__restrict__ dout, const Y *__restrict__ y, int64_t y_rows, int64_t H, const int32_t *__restrict__ row_of,
@@ -729,6 +766,68 @@ __global__ __launch_bounds__(kMaxThreads) void combine_backward_kernel(
     const int64_t nchunk = SPLIT ? ceil_div(H, kUnit) * kWave : H / 8;
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(dout + t * H, static_cast<uint32_t>(H * sizeof(D)));
     const uint32_t y_bytes = static_cast<uint32_t>(H * sizeof(Y));
+    if constexpr (DW && !STORE && !SPLIT) {
+        // the dots pass of bf16 rows: a token's live slots compacted; with at most kFewTerms of
+        // them (drop-and-pad keeps ~3 of 8) every thread takes two chunks with all their loads in
+        // flight together, as the combine does for few terms
+        __shared__ int32_t live_row[kBatch];
+        __shared__ int live_k[kBatch];
+        __shared__ int n_live_sh;
+        if (K <= kBatch) {
+            if (threadIdx.x < kWave) {
+                const int k = threadIdx.x;
+                const int32_t r = k < K ? row_of[t * K + k] : -1;
+                const bool ok = r >= 0 && r < y_rows;
+                const uint64_t m = __ballot(ok);
+                if (ok) {
+                    const int pos = __popcll(m & lanemask_lt());
+                    live_row[pos] = r;
+                    live_k[pos] = k;
+                }
+                if (k < K && !ok)
+                    dw[t * K + k] = 0.0f;  // a slot that adds nothing
+                if (k == 0)
+                    n_live_sh = __popcll(m);
+            }
+            __syncthreads();
+            const int n = n_live_sh;
+            if (n <= kFewTerms) {
+                int32_t rb[kFewTerms];
+#pragma unroll
+                for (int u = 0; u < kFewTerms; ++u)
+                    rb[u] = u < n ? __builtin_amdgcn_readfirstlane(live_row[u]) : -1;
+                float p[kBatch] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                const int64_t half = (nchunk + 1) / 2;
+                for (int64_t c = threadIdx.x; c < half; c += blockDim.x) {
+                    const int64_t c2 = c + half;
+                    const bool has2 = c2 < nchunk;
+                    float d[8], d2[8], yv[kFewTerms][8], y2[kFewTerms][8];
+                    load8<D, false, 0>(dr, 8 * c, d);
+                    load8<D, false, 0>(dr, 8 * c2, d2);  // past the row: reads zeros, unused
+#pragma unroll
+                    for (int u = 0; u < kFewTerms; ++u) {
+                        const __amdgpu_buffer_rsrc_t yr =
+                            make_rsrc(y + static_cast<int64_t>(rb[u] < 0 ? 0 : rb[u]) * H, rb[u] < 0 ? 0u : y_bytes);
+                        load8<Y, false>(yr, 8 * c, yv[u]);
+                        load8<Y, false>(yr, 8 * c2, y2[u]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < kFewTerms; ++u) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            p[u] = __builtin_fmaf(d[e], yv[u][e], p[u]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float r2 = __builtin_fmaf(d2[e], y2[u][e], p[u]);
+                            p[u] = has2 ? r2 : p[u];
+                        }
+                    }
+                }
+                reduce_dots_compact(p, red, n, live_k, dw + t * K);
+                return;
+            }
+        }
+    }
     for (int k0 = 0; k0 < K; k0 += kBatch) {
         int32_t rb[kBatch];
         float wb[kBatch];
