@@ -125,7 +125,8 @@ def check_index(m, ids, w, E, cap=0, gs=0, align=0):
 
 @pytest.mark.parametrize("T,E,K", [(1, 1, 1), (5, 3, 2), (300, 8, 2), (512, 64, 8), (4097, 16, 1), (4099, 64, 8),
                                    (1024, 64, 8), (8193, 16, 1), (256, 1024, 32), (2000, 256, 8), (1500, 1024, 32),
-                                   (700, 40, 7), (9000, 128, 4), (50000, 64, 8), (33333, 130, 6)])
+                                   (700, 40, 7), (9000, 128, 4), (50000, 64, 8), (33333, 130, 6),
+                                   (2048, 64, 8), (16385, 16, 1)])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_build_index_standard(m, T, E, K, weighted):
     say(f"build_index standard T={T} E={E} K={K} weighted={weighted}")
@@ -196,7 +197,7 @@ def test_build_index_drop_and_pad(m, T, E, K, cap):
                                       (700, 96, 6, 1), (1000, 1024, 8, 32), (3, 4, 2, 2), (50000, 64, 6, 8),
                                       (20000, 36, 5, 3), (3000, 1024, 8, 1), (1000, 64, 32, 4),
                                       (777, 128, 16, 16), (900, 16, 1, 4), (1200, 48, 4, 6), (512, 64, 8, 8),
-                                      (4097, 16, 1, 2), (1365, 30, 3, 5)])
+                                      (4097, 16, 1, 2), (1365, 30, 3, 5), (2730, 60, 6, 6), (2048, 64, 8, 8)])
 def test_build_index_groups(m, T, E, K, gs):
     say(f"build_index group T={T} E={E} K={K} gs={gs}")
     key = wl.case_key(24, T, E, K)

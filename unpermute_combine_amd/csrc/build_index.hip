@@ -347,15 +347,86 @@ __device__ int32_t segment_starts(const int32_t *tot, int nkeys, int align, int3
     return total;
 }
 
+// Up to this many routed slots every rank workgroup counts all of them itself (kCountAll) instead
+// of reading the tile counts of a histogram launch: each small launch costs ~4 us with cold caches
+// (T4096 K2 E64: histogram 4.4 us + ranks 8.2 us), far more than 16 loads and LDS atomics per
+// thread.
+constexpr int64_t kCountAllSlots = 16384;
+constexpr int kCountLoads = 16;  // ids a thread has in flight while counting all slots
+
+// kCountAll: per key, tot = the slots of all tokens (experts) or their first slots in each group
+// (groups, at Ep), pre = those of the tokens before this tile (slots below tile_s0). tot and pre
+// are adjacent in LDS (pre = tot + Hp). Counts come from LDS atomics, positions never do. Ends with
+// a barrier.
+template <bool kGroups>
+__device__ void count_all(const IndexArgs &a, int64_t tile_s0, int32_t *tot)
+{
+    int32_t *pre = tot + a.Hp;
+    const int tid = threadIdx.x;
+    const int64_t n = a.T * a.K;
+    constexpr int64_t kStep = static_cast<int64_t>(kCountLoads) * kRankThreads;
+    int nx[kCountLoads];  // the next batch, in flight while the current one is counted
+    auto load = [&](int64_t base) {
+#pragma unroll
+        for (int u = 0; u < kCountLoads; ++u) {
+            const int64_t i = base + u * kRankThreads + tid;
+            nx[u] = i < n ? a.topk_idx[i] : -1;
+        }
+    };
+    load(0);
+    for (int i = tid; i < 2 * a.Hp; i += kRankThreads)
+        tot[i] = 0;
+    __syncthreads();
+    // with K a power of two each wavefront's 64 slots start at a token boundary, so the group
+    // test runs on ballots; every lane takes part, the ones past n as invalid slots
+    const bool wave_lead = (a.K & (a.K - 1)) == 0;
+    for (int64_t base = 0; base < n; base += kStep) {
+        int ids[kCountLoads];
+#pragma unroll
+        for (int u = 0; u < kCountLoads; ++u)
+            ids[u] = nx[u];
+        if (base + kStep < n)
+            load(base + kStep);
+#pragma unroll
+        for (int u = 0; u < kCountLoads; ++u) {
+            const int64_t i = base + u * kRankThreads + tid;
+            const int e = ids[u];
+            const bool ok = i < n && valid_expert(e, a.E);
+            bool lead = false;
+            if (kGroups && wave_lead)
+                lead = token_leader(match_peers(ok ? e / a.gs : -1, a.gbits, __ballot(ok)), ok, a.K);
+            if (!ok)
+                continue;
+            const bool before = i < tile_s0;
+            atomicAdd(&tot[e], 1);
+            if (before)
+                atomicAdd(&pre[e], 1);
+            if (kGroups) {
+                const int64_t t = i / a.K;
+                const int k = static_cast<int>(i - t * a.K);
+                const int g = e / a.gs;
+                if (wave_lead ? lead : group_leader(a.topk_idx + t * a.K, k, g, a.E, a.gs)) {
+                    atomicAdd(&tot[a.Ep + g], 1);
+                    if (before)
+                        atomicAdd(&pre[a.Ep + g], 1);
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // One workgroup per tile, kRankWaves wavefronts, each owning a contiguous share of the tile's
 // tokens (whole tokens). Phase A: every wave counts its slots per expert (and its first-in-group
 // slots per group) in LDS. Phase B: per key, a prefix over the waves starting at the tile's
 // first row of the key. Phase C: every wave walks its slots in order, 64 at a time, and ranks
 // them against its own running counters. Finally the workgroups together write the padding
 // (drop-and-pad) or unused rows.
-// kSingle: one workgroup holds all tokens (small inputs): the totals come from its own per-wave
-// counts after phase A, with no histogram launch and no tile sums before it.
-template <bool kGroups, bool kSingle>
+// kTotals says where the per-key totals come from: kFromTiles, the tile counts of the histogram
+// launch; kSingle, one workgroup holding all tokens (small inputs), its own per-wave counts after
+// phase A; kCountAll, every workgroup counting all slots itself (small inputs, no histogram launch).
+constexpr int kFromTiles = 0, kSingle = 1, kCountAll = 2;
+template <bool kGroups, int kTotals>
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
@@ -418,12 +489,19 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
             }
         }
     };
-    if constexpr (kSingle) {
+    if constexpr (kTotals == kSingle) {
         if (kGroups) {  // slot_of starts as "absent" (the histogram kernel does this otherwise)
             for (int64_t i = tid; i < a.T * a.G; i += kRankThreads)
                 a.ix.slot_of[i] = -1;
         }
         __syncthreads();  // the zeroed counters before phase A's atomics
+    } else if constexpr (kTotals == kCountAll) {
+        if (kGroups) {  // slot_of starts as "absent" for this tile's tokens
+            for (int64_t i = tile_t0 * a.G + tid; i < tile_t1 * a.G; i += kRankThreads)
+                a.ix.slot_of[i] = -1;
+        }
+        count_all<kGroups>(a, tile_t0 * a.K, tot);  // its barriers also cover the zeroed counters
+        segments();
     } else {
         // the totals, and this tile's first row inside each key, from the tile counts (each
         // workgroup adds up the counts of all tiles itself: no separate scan pass; expert and
@@ -472,7 +550,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     }
     __syncthreads();
 
-    if constexpr (kSingle) {  // the totals are this workgroup's own counts
+    if constexpr (kTotals == kSingle) {  // the totals are this workgroup's own counts
         for (int e = tid; e < a.E; e += kRankThreads) {
             int32_t sum = 0;
             for (int w = 0; w < kRankWaves; ++w)
@@ -815,9 +893,14 @@ moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_
         a.tile_tokens = static_cast<int32_t>(T);
         a.ntiles = 1;
         if (G > 0)
-            hipLaunchKernelGGL((rank_kernel<true, true>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
+            hipLaunchKernelGGL((rank_kernel<true, kSingle>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
         else
-            hipLaunchKernelGGL((rank_kernel<false, true>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
+            hipLaunchKernelGGL((rank_kernel<false, kSingle>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
+    } else if (T * K <= kCountAllSlots) {  // every workgroup counts all slots: no histogram launch
+        if (G > 0)
+            hipLaunchKernelGGL((rank_kernel<true, kCountAll>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+        else
+            hipLaunchKernelGGL((rank_kernel<false, kCountAll>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     } else {
         const size_t lds_hist = sizeof(int32_t) * static_cast<size_t>(a.Hp);
         if (G > 0)
@@ -827,9 +910,9 @@ moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_
         if ((st = launch_status()) != MOE_OK)
             return st;
         if (G > 0)
-            hipLaunchKernelGGL((rank_kernel<true, false>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+            hipLaunchKernelGGL((rank_kernel<true, kFromTiles>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
         else
-            hipLaunchKernelGGL((rank_kernel<false, false>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
+            hipLaunchKernelGGL((rank_kernel<false, kFromTiles>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     }
     if ((st = launch_status()) != MOE_OK)
         return st;
