@@ -135,6 +135,21 @@ inline int scatter_parts(int J, int64_t src_rows, int64_t N)
 {
     return J > kScatterDestsPerWave && N == src_rows * J ? kScatterParts : 1;
 }
+// Paired order (two parts): the workgroups come in blocks of 2 x 8; workgroup j < 8 of a block takes
+// part 0 and workgroup j + 8 part 1 of the same 8 x 8 (source row, slice) pairs. Blocks are dealt
+// to the 8 XCDs round-robin, so the two waves that read one slice run at about the same time on
+// the same XCD and the second read hits its L2: the PMC fetches of the permute at T16384 H7168 K8
+// bf16 fall from 1.11x to 1.00x its algorithmic bytes. It pays only in the weighted scatter (the
+// combine backward's dy = w * dout: 358 -> 352 us); the plain copy's time did not follow its
+// fetches (358 -> 360 us), so it keeps the (row, part, slice) order. The waves are short (1 KiB
+// to at most four rows), so their index arithmetic shows: with 32-bit instead of 64-bit divisions
+// the permute took 355 instead of 358 us (T16384 H7168 K8), 133.0 against 133.3 us with padding
+// (T8192 H4096 E128) and 74.6 against 75.6 us as the group send.
+__host__ __device__ inline int64_t scatter_copy_waves(int64_t units, int parts, bool paired)
+{
+    return paired ? ceil_div(units, static_cast<int64_t>(kXcds) * kScatterVecWaves) * 2 * kXcds * kScatterVecWaves
+                  : units * parts;
+}
 constexpr int kMaxScatterDests = MOE_MAX_EXPERTS;  // dst_of columns (e.g. one per expert group)
 constexpr int kMaxGroupDests = kWave;               // destinations of one group of the grouped gather
 
@@ -165,30 +180,51 @@ template <bool SCALE>
 __global__ __launch_bounds__(kScatterVecThreads) void permute_scatter_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ dst_of, int J,
     const int32_t *__restrict__ src_row, int64_t N, char *__restrict__ dst, int64_t zero_waves, bool zero_first,
-    int parts, const float *__restrict__ scale)
+    int parts, bool paired, const float *__restrict__ scale)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
-    const int64_t spr = (nvec + kWave * kScatterVecs - 1) / (kWave * kScatterVecs);  // slices per source row
-    const int64_t wpr = spr * parts;                                                  // waves per source row
-    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kScatterVecWaves +
-                       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
-    const int64_t copy_waves = src_rows * wpr;
+    // every wave index fits in 32 bits (the launcher refuses grids of 2^31 waves or more), and
+    // 32-bit division is far cheaper than 64-bit for these short-lived waves
+    const uint32_t spr = static_cast<uint32_t>((nvec + kWave * kScatterVecs - 1) / (kWave * kScatterVecs));
+    const uint32_t wpr = spr * static_cast<uint32_t>(parts);
+    const uint32_t gw = blockIdx.x * kScatterVecWaves +
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave)));
+    const uint32_t units = static_cast<uint32_t>(src_rows) * spr;  // (source row, slice) pairs
+    const uint32_t copy_waves = static_cast<uint32_t>(scatter_copy_waves(units, parts, paired));
+    const uint32_t zwaves = static_cast<uint32_t>(zero_waves);
     // wave index -> zero window or copy wave; the grid's last workgroup may hold up to 7 waves
     // past both (zero windows past N check nothing, copy rows past src_rows return below)
-    const int64_t zw = zero_first ? gw : gw - copy_waves;
-    if (zero_first ? gw < zero_waves : gw >= copy_waves) {
+    const uint32_t zw = zero_first ? gw : gw - copy_waves;
+    if (zero_first ? gw < zwaves : gw >= copy_waves) {
         const int zr = zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave;
-        zero_rows_wave(src_rows, nvec, src_row, N, zw * zr, dst, zr);
+        zero_rows_wave(src_rows, nvec, src_row, N, static_cast<int64_t>(zw) * zr, dst, zr);
         return;
     }
-    const int64_t cw = zero_first ? gw - zero_waves : gw;
-    const int64_t t = cw / wpr;
-    if (t >= src_rows)
-        return;
-    const int64_t rem = cw - t * wpr;
-    const int part = static_cast<int>(rem / spr);  // waves of a row: (part, slice)
-    const int64_t v0 = (rem % spr) * kWave * kScatterVecs + lane;  // this lane's first vector of the row
+    const uint32_t cw = zero_first ? gw - zwaves : gw;
+    int part;
+    int64_t t, slice;
+    if (paired) {  // (two parts, so no leading zero waves: cw starts at a workgroup)
+        const uint32_t cb = cw / kScatterVecWaves;
+        const uint32_t sb = cb / (2 * kXcds);
+        const uint32_t j = cb % (2 * kXcds);
+        part = static_cast<int>(j / kXcds);
+        const uint32_t u = (sb * kXcds + j % kXcds) * kScatterVecWaves + cw % kScatterVecWaves;
+        if (u >= units)
+            return;
+        const uint32_t t32 = u / spr;
+        t = t32;
+        slice = u - t32 * spr;
+    } else {  // waves of a row: (part, slice); at most two parts
+        const uint32_t t32 = cw / wpr;
+        if (t32 >= static_cast<uint32_t>(src_rows))
+            return;
+        const uint32_t rem = cw - t32 * wpr;
+        part = rem >= spr ? 1 : 0;
+        t = t32;
+        slice = rem - static_cast<uint32_t>(part) * spr;
+    }
+    const int64_t v0 = slice * kWave * kScatterVecs + lane;  // this lane's first vector of the row
     // this wave's share: the row's valid destinations ranked [lo, hi) in column order
     const int lo = part * kScatterDestsPerWave;
     const int hi = part == parts - 1 ? 0x7fffffff : lo + kScatterDestsPerWave;
@@ -425,19 +461,21 @@ moe_status launch_scatter_vec16(const char *src, int64_t src_rows, int64_t nvec,
     const bool zero_first = src_row && N > src_rows * J;  // padding rows are certain
     const int64_t zwaves = src_row ? ceil_div(N, zero_first ? kZeroRowsPerWaveFirst : kZeroRowsPerWave) : 0;
     const int parts = scatter_parts(J, src_rows, N);
-    const int64_t waves = src_rows * ceil_div(nvec, static_cast<int64_t>(kWave) * kScatterVecs) * parts + zwaves;
+    const int64_t units = src_rows * ceil_div(nvec, static_cast<int64_t>(kWave) * kScatterVecs);
+    const bool paired = scaled && parts == kScatterParts;
+    const int64_t waves = scatter_copy_waves(units, parts, paired) + zwaves;
     const int64_t blocks = ceil_div(waves, kScatterVecWaves);
-    if (blocks > 0x7fffffff)
+    if (blocks * kScatterVecWaves > 0x7fffffff)  // the kernel's wave indices are 32-bit
         return MOE_ERR_UNSUPPORTED;
     if (blocks == 0)
         return MOE_OK;
     if (scaled)
         hipLaunchKernelGGL(permute_scatter_vec16_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kScatterVecThreads),
-                           0, stream, src, src_rows, nvec, dst_of, J, src_row, N, dst, zwaves, zero_first, parts, scale);
+                           0, stream, src, src_rows, nvec, dst_of, J, src_row, N, dst, zwaves, zero_first, parts, paired, scale);
     else
         hipLaunchKernelGGL(permute_scatter_vec16_kernel<false>, dim3(static_cast<unsigned>(blocks)),
                            dim3(kScatterVecThreads), 0, stream, src, src_rows, nvec, dst_of, J, src_row, N, dst, zwaves,
-                           zero_first, parts, nullptr);
+                           zero_first, parts, paired, nullptr);
     return launch_status();
 }
 
