@@ -98,10 +98,12 @@ __global__ __launch_bounds__(kRowsPerBlock *kWave) void permute_elem_kernel(
 // each checks `zr` entries of src_row and zero-fills those outside [0, src_rows). Measured at
 // T16384 H7168 K8 bf16: 339 us per launch (6.2 TB/s) with slices, 350 us with one 256-thread
 // workgroup per row. When the output has more rows than the map can name (N > src_rows * J:
-// drop-and-pad, aligned experts) padding is certain and its waves come first, 8 rows each,
-// so that they overlap the copies instead of trailing them (drop-and-pad at T8192 H4096 E128:
-// 134 -> 125 us); otherwise they come last, 16 rows each (putting them first cost the
-// unpadded case ~1%).
+// drop-and-pad, aligned experts) padding is certain and its waves come first, so that they
+// overlap the copies instead of trailing them (drop-and-pad at T8192 H4096 E128: 134 -> 125 us),
+// 4 rows each (with caches flushed there, 72% of the rows being padding: 129.5 us against 132.5
+// with 8 rows per wave, 134.6 with 2, 140.2 with 1 and 143.5 with 16; nontemporal instead of
+// sc1|nt zero stores 138.3 us); otherwise they come last, 16 rows each (putting them first cost
+// the unpadded case ~1%).
 constexpr int kScatterThreads = 256;  // element-wise kernels
 constexpr int kScatterWaves = kScatterThreads / kWave;
 // workgroups of the 16-byte scatter: 8 wavefronts. The waves of a source row are ordered (half of
@@ -118,7 +120,7 @@ constexpr int kScatterVecWaves = kScatterVecThreads / kWave;
 // changed nothing at that size and lost at drop-and-pad T8192 H4096 E128 (128: 134 against 125 us)
 constexpr int kScatterVecs = 1;
 constexpr int kZeroRowsPerWave = 16;
-constexpr int kZeroRowsPerWaveFirst = 8;
+constexpr int kZeroRowsPerWaveFirst = 4;
 // Waves per (source row, slice). With a dense map -- one output row per map entry, as the standard
 // dispatch's row_of is -- every row has J destinations, and two waves per slice each store to half
 // of them: wave p takes the valid destinations ranked [4p, 4p + 4) in column order, the last wave
