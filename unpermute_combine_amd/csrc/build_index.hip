@@ -50,7 +50,14 @@ namespace {
 
 constexpr int kMaxTiles = 128;      // tiles grow with T so that there are never more
 constexpr int kEmptyThreads = 1024;
-constexpr int kRankBatch = 8;  // 64-slot groups whose loads a rank wave issues together
+// 64-slot groups whose loads a rank wave issues together (a template argument of the rank
+// kernel, 2 or 8): the rank kernel's batch loops are unrolled, and with caches flushed its code
+// comes from HBM as it runs -- the group-mode kernel was 67 KB with 8 groups per batch and 27 KB
+// with 2 (T8192 K8 E256 in 32 groups: 15.2 -> 12.0 us per launch; T16384 K8 E256: 8.6 -> 7.9 us).
+// Waves with more slots take the larger batch (fewer dependent round trips: at T1048576 K8 the
+// launch took 131 us with 8 groups per batch and 147 us with 2).
+constexpr int kRankBatchSmall = 2;
+constexpr int kRankBatchLarge = 8;
 
 struct IndexArgs {
     const int32_t *topk_idx;
@@ -121,50 +128,80 @@ __device__ __forceinline__ bool token_leader(uint64_t peers, bool valid, int K)
 }
 
 // ---------------------------------------------------------------- 1. per-tile histograms
+constexpr int kHistThreads = 256;
+constexpr int kHistLoads = 8;  // expert ids a thread has in flight (2 in group mode, see below)
+
 // kGroups: group mode (a.gs > 0), a template argument so that the expert-only build carries no
-// group code
+// group code. A thread's ids are loaded several at a time, the next batch in flight while the
+// current one is counted: one load and its wait per id took 113 us per launch at T1048576 K8
+// (tiles of 256 ids per thread), 8 in flight 27 us; in group mode 2 in flight (T524288 K8, 32
+// groups: 122 -> 81 us), because the unrolled group test of 8 made the kernel 14 KB instead of
+// 2 KB and, with caches flushed, its code fetch cost 2.4 us per launch at T8192. No difference
+// at T16384 K8 either way.
 template <bool kGroups>
-__global__ __launch_bounds__(256) void hist_kernel(IndexArgs a)
+__global__ __launch_bounds__(kHistThreads) void hist_kernel(IndexArgs a)
 {
     extern __shared__ int32_t sh[];
     int32_t *he = sh;         // [Ep]
     int32_t *hg = sh + a.Ep;  // [Gp]
     const int tile = blockIdx.x;
-    const int nsh = a.Ep + (kGroups ? a.Gp : 0);
-    for (int i = threadIdx.x; i < nsh; i += blockDim.x)
-        sh[i] = 0;
-    __syncthreads();
+    const int tid = threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(tile) * a.tile_tokens;
     const int64_t t1 = min(a.T, t0 + a.tile_tokens);
     const int64_t s0 = t0 * a.K, s1 = t1 * a.K;
+    constexpr int kLoads = kGroups ? 2 : kHistLoads;
+    constexpr int64_t kStep = static_cast<int64_t>(kLoads) * kHistThreads;
+    int nx[kLoads];
+    auto load = [&](int64_t base) {
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int64_t i = base + u * kHistThreads + tid;
+            nx[u] = i < s1 ? a.topk_idx[i] : -1;
+        }
+    };
+    load(s0);
+    const int nsh = a.Ep + (kGroups ? a.Gp : 0);
+    for (int i = tid; i < nsh; i += kHistThreads)
+        sh[i] = 0;
+    __syncthreads();
     // with K a power of two each wavefront's 64 slots start at a token boundary (s0, 64 and the
-    // workgroup's stride are multiples of K) and the group test runs on ballots; lanes past s1
-    // hold whole tokens, so the inactive ones never split a token
+    // workgroup's stride are multiples of K) and the group test runs on ballots; every lane takes
+    // part in the ballots, the ones past s1 as invalid slots of whole tokens
     const bool wave_lead = (a.K & (a.K - 1)) == 0;
-    for (int64_t i = s0 + threadIdx.x; i < s1; i += blockDim.x) {
-        const int e = a.topk_idx[i];
-        const bool ok = valid_expert(e, a.E);
-        bool lead = false;
-        if (kGroups && wave_lead)
-            lead = token_leader(match_peers(ok ? e / a.gs : -1, a.gbits, __ballot(ok)), ok, a.K);
-        if (!ok)
-            continue;
-        atomicAdd(&he[e], 1);
-        if (kGroups) {
-            const int64_t t = i / a.K;
-            const int k = static_cast<int>(i - t * a.K);
-            const int g = e / a.gs;
-            if (wave_lead ? lead : group_leader(a.topk_idx + t * a.K, k, g, a.E, a.gs))
-                atomicAdd(&hg[g], 1);
+    for (int64_t base = s0; base < s1; base += kStep) {
+        int ids[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u)
+            ids[u] = nx[u];
+        if (base + kStep < s1)
+            load(base + kStep);
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int64_t i = base + u * kHistThreads + tid;
+            const int e = ids[u];
+            const bool ok = i < s1 && valid_expert(e, a.E);
+            bool lead = false;
+            if (kGroups && wave_lead)
+                lead = token_leader(match_peers(ok ? e / a.gs : -1, a.gbits, __ballot(ok)), ok, a.K);
+            if (!ok)
+                continue;
+            atomicAdd(&he[e], 1);
+            if (kGroups) {
+                const int64_t t = i / a.K;
+                const int k = static_cast<int>(i - t * a.K);
+                const int g = e / a.gs;
+                if (wave_lead ? lead : group_leader(a.topk_idx + t * a.K, k, g, a.E, a.gs))
+                    atomicAdd(&hg[g], 1);
+            }
         }
     }
     if (kGroups) {  // slot_of starts as "absent" for this tile's tokens
-        for (int64_t i = t0 * a.G + threadIdx.x; i < t1 * a.G; i += blockDim.x)
+        for (int64_t i = t0 * a.G + tid; i < t1 * a.G; i += kHistThreads)
             a.ix.slot_of[i] = -1;
     }
     __syncthreads();
     int32_t *row = a.hist + static_cast<int64_t>(tile) * a.Hp;  // expert and group counts, one row
-    for (int i = threadIdx.x; i < a.Hp; i += blockDim.x)
+    for (int i = tid; i < a.Hp; i += kHistThreads)
         row[i] = sh[i];
 }
 
@@ -217,11 +254,11 @@ __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll(m); }
 // with 4; more and smaller tiles did not help)
 constexpr int kRankWaves = 8;
 constexpr int kRankThreads = kRankWaves * kWave;
-constexpr int kSpan = kRankBatch * kWave;  // slots whose loads a wavefront issues together
+constexpr int kSpanLarge = kRankBatchLarge * kWave;  // slots whose loads a wavefront issues together
 // up to this many routed slots (one batch per wavefront) the index is built by one workgroup
 // in one launch: T1024 K2 E8 0.030 -> 0.025 ms per step; at T4096 K2 E64 (two batches per
 // wavefront) the single workgroup lost, 0.061 against 0.055 ms
-constexpr int64_t kSingleTileSlots = static_cast<int64_t>(kRankWaves) * kSpan;
+constexpr int64_t kSingleTileSlots = static_cast<int64_t>(kRankWaves) * kSpanLarge;
 
 // True when slot i = (t, k) is the first of token t's slots in group g. The token's earlier
 // slots are in `ids` (the current batch, starting at slot base0) or, when the token straddles
@@ -239,12 +276,13 @@ __device__ __forceinline__ bool first_in_group(const IndexArgs &a, int64_t i, in
     return lead;
 }
 
-__device__ __forceinline__ void load_batch(const IndexArgs &a, int64_t base0, int64_t s1, bool want_w,
-                                           int (&e)[kRankBatch], float (&w)[kRankBatch])
+template <int RB>
+__device__ __forceinline__ void load_batch(const IndexArgs &a, int64_t base0, int64_t s1, bool want_w, int (&e)[RB],
+                                           float (&w)[RB])
 {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int b = 0; b < kRankBatch; ++b) {
+    for (int b = 0; b < RB; ++b) {
         const int64_t i = base0 + b * kWave + lane;
         e[b] = i < s1 ? a.topk_idx[i] : -1;
         w[b] = want_w && i < s1 ? a.topk_w[i] : 1.0f;
@@ -252,7 +290,11 @@ __device__ __forceinline__ void load_batch(const IndexArgs &a, int64_t base0, in
 }
 
 constexpr int kOffsetLoads = 16;  // tile-count vectors a thread has in flight
-static_assert(kRankWaves * kSpan >= 2 * 4 * kRankThreads, "the id buffers hold the partial sums of tile_sums");
+// ints of the per-wave id buffers, which tile_sums also uses for its partial sums
+constexpr int ids_ints(int rb)
+{
+    return kRankWaves * rb * kWave > 2 * 4 * kRankThreads ? kRankWaves * rb * kWave : 2 * 4 * kRankThreads;
+}
 
 // Per key of the tile counts hist[0..ntiles)[0..nkeys) (rows of `stride` keys, 16-byte aligned):
 // tot[key] = the sum over all tiles, pre[key] = the sum over the tiles before `tile`. A thread
@@ -426,9 +468,10 @@ __device__ void count_all(const IndexArgs &a, int64_t tile_s0, int32_t *tot)
 // launch; kSingle, one workgroup holding all tokens (small inputs), its own per-wave counts after
 // phase A; kCountAll, every workgroup counting all slots itself (small inputs, no histogram launch).
 constexpr int kFromTiles = 0, kSingle = 1, kCountAll = 2;
-template <bool kGroups, int kTotals>
+template <bool kGroups, int kTotals, int RB>
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 {
+    constexpr int kSpan = RB * kWave;  // slots of one batch of a wave
     extern __shared__ int32_t sh[];
     __shared__ int32_t wsum[kRankWaves];
     int32_t *cnt_e = sh;                        // [kRankWaves][E] counts -> next row of the wave
@@ -462,8 +505,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
     // token's earlier slots back from LDS
     const bool wave_lead = (a.K & (a.K - 1)) == 0;
     const bool want_w = a.ix.permuted_probs && a.topk_w;
-    int e_first[kRankBatch];
-    float w_first[kRankBatch];
+    int e_first[RB];
+    float w_first[RB];
     load_batch(a, s0, s1, want_w, e_first, w_first);
 
     // every key's first row from the totals; tile 0 writes the per-expert (and per-group) results
@@ -512,23 +555,23 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 
     // ---- phase A: per-wave counts
     for (int64_t base0 = s0; base0 < s1; base0 += kSpan) {
-        int e_b[kRankBatch];
-        float w_b[kRankBatch];
+        int e_b[RB];
+        float w_b[RB];
         if (base0 == s0) {
 #pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
+            for (int b = 0; b < RB; ++b)
                 e_b[b] = e_first[b];
         } else {
             load_batch(a, base0, s1, false, e_b, w_b);
         }
         if (kGroups && !wave_lead) {
 #pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
+            for (int b = 0; b < RB; ++b)
                 ids[b * kWave + lane] = e_b[b];
             __builtin_amdgcn_wave_barrier();
         }
 #pragma unroll
-        for (int b = 0; b < kRankBatch; ++b) {
+        for (int b = 0; b < RB; ++b) {
             const int64_t i = base0 + b * kWave + lane;
             const int e = e_b[b];
             const bool ok = i < s1 && valid_expert(e, a.E);
@@ -596,18 +639,18 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
 
     // ---- phase C: stable ranks
     const uint64_t below = lanemask_lt();
-    int e_nx[kRankBatch];
-    float w_nx[kRankBatch];
+    int e_nx[RB];
+    float w_nx[RB];
 #pragma unroll
-    for (int b = 0; b < kRankBatch; ++b) {
+    for (int b = 0; b < RB; ++b) {
         e_nx[b] = e_first[b];
         w_nx[b] = w_first[b];
     }
     for (int64_t base0 = s0; base0 < s1; base0 += kSpan) {
-        int e_cur[kRankBatch];
-        float w_cur[kRankBatch];
+        int e_cur[RB];
+        float w_cur[RB];
 #pragma unroll
-        for (int b = 0; b < kRankBatch; ++b) {
+        for (int b = 0; b < RB; ++b) {
             e_cur[b] = e_nx[b];
             w_cur[b] = w_nx[b];
         }
@@ -615,12 +658,12 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(IndexArgs a)
             load_batch(a, base0 + kSpan, s1, want_w, e_nx, w_nx);
         if (kGroups && !wave_lead) {
 #pragma unroll
-            for (int b = 0; b < kRankBatch; ++b)
+            for (int b = 0; b < RB; ++b)
                 ids[b * kWave + lane] = e_cur[b];
             __builtin_amdgcn_wave_barrier();
         }
 #pragma unroll
-        for (int b = 0; b < kRankBatch; ++b) {
+        for (int b = 0; b < RB; ++b) {
             if (base0 + b * kWave >= s1)
                 break;
             const int64_t i = base0 + b * kWave + lane;
@@ -763,6 +806,35 @@ int bits_for(int n)  // bits needed to tell apart the keys 0..n-1
 
 int round4(int n) { return (n + 3) & ~3; }
 
+// rank_kernel<groups, totals, batch> for runtime choices of the three
+template <bool kGroups, int kTotals>
+void launch_rank_rb(int rb, dim3 grid, size_t lds, hipStream_t stream, const IndexArgs &a)
+{
+    if (rb == kRankBatchSmall)
+        hipLaunchKernelGGL((rank_kernel<kGroups, kTotals, kRankBatchSmall>), grid, dim3(kRankThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL((rank_kernel<kGroups, kTotals, kRankBatchLarge>), grid, dim3(kRankThreads), lds, stream, a);
+}
+
+template <bool kGroups>
+void launch_rank_totals(int totals, int rb, dim3 grid, size_t lds, hipStream_t stream, const IndexArgs &a)
+{
+    if (totals == kSingle)
+        launch_rank_rb<kGroups, kSingle>(rb, grid, lds, stream, a);
+    else if (totals == kCountAll)
+        launch_rank_rb<kGroups, kCountAll>(rb, grid, lds, stream, a);
+    else
+        launch_rank_rb<kGroups, kFromTiles>(rb, grid, lds, stream, a);
+}
+
+void launch_rank(bool groups, int totals, int rb, dim3 grid, size_t lds, hipStream_t stream, const IndexArgs &a)
+{
+    if (groups)
+        launch_rank_totals<true>(totals, rb, grid, lds, stream, a);
+    else
+        launch_rank_totals<false>(totals, rb, grid, lds, stream, a);
+}
+
 struct Plan {
     int32_t tile_tokens, ntiles;
     size_t ws;  // workspace bytes: the tile counts
@@ -887,33 +959,27 @@ moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_
         return launch_status();
     }
 
-    const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 1) * (E + G) + 2 * static_cast<size_t>(a.Hp) +
-                                               static_cast<size_t>(kRankWaves) * kSpan);
-    if (T * K <= kSingleTileSlots) {  // one workgroup, one launch
+    const bool single = T * K <= kSingleTileSlots;  // one workgroup, one launch
+    if (single) {
         a.tile_tokens = static_cast<int32_t>(T);
         a.ntiles = 1;
-        if (G > 0)
-            hipLaunchKernelGGL((rank_kernel<true, kSingle>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
-        else
-            hipLaunchKernelGGL((rank_kernel<false, kSingle>), dim3(1), dim3(kRankThreads), lds_rank, stream, a);
-    } else if (T * K <= kCountAllSlots) {  // every workgroup counts all slots: no histogram launch
-        if (G > 0)
-            hipLaunchKernelGGL((rank_kernel<true, kCountAll>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
-        else
-            hipLaunchKernelGGL((rank_kernel<false, kCountAll>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
-    } else {
+    }
+    // the smaller batch when one batch of it holds each rank wave's slots
+    const int64_t wave_slots = ceil_div(a.tile_tokens, kRankWaves) * K;
+    const int rb = wave_slots <= static_cast<int64_t>(kRankBatchSmall) * kWave ? kRankBatchSmall : kRankBatchLarge;
+    const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 1) * (E + G) + 2 * static_cast<size_t>(a.Hp) +
+                                               static_cast<size_t>(ids_ints(rb)));
+    const int totals = single ? kSingle : (T * K <= kCountAllSlots ? kCountAll : kFromTiles);
+    if (totals == kFromTiles) {
         const size_t lds_hist = sizeof(int32_t) * static_cast<size_t>(a.Hp);
         if (G > 0)
-            hipLaunchKernelGGL(hist_kernel<true>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
+            hipLaunchKernelGGL(hist_kernel<true>, dim3(p.ntiles), dim3(kHistThreads), lds_hist, stream, a);
         else
-            hipLaunchKernelGGL(hist_kernel<false>, dim3(p.ntiles), dim3(256), lds_hist, stream, a);
+            hipLaunchKernelGGL(hist_kernel<false>, dim3(p.ntiles), dim3(kHistThreads), lds_hist, stream, a);
         if ((st = launch_status()) != MOE_OK)
             return st;
-        if (G > 0)
-            hipLaunchKernelGGL((rank_kernel<true, kFromTiles>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
-        else
-            hipLaunchKernelGGL((rank_kernel<false, kFromTiles>), dim3(p.ntiles), dim3(kRankThreads), lds_rank, stream, a);
     }
+    launch_rank(G > 0, totals, rb, dim3(static_cast<unsigned>(a.ntiles)), lds_rank, stream, a);
     if ((st = launch_status()) != MOE_OK)
         return st;
     if (G > 0 && (K & (K - 1)) != 0) {  // with K a power of two the rank kernel writes esrc
