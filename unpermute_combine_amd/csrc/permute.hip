@@ -143,7 +143,8 @@ inline int scatter_parts(int J, int64_t src_rows, int64_t N)
 // the same XCD and the second read hits its L2: the PMC fetches of the permute at T16384 H7168 K8
 // bf16 fall from 1.11x to 1.00x its algorithmic bytes. It pays only in the weighted scatter (the
 // combine backward's dy = w * dout: 358 -> 352 us); the plain copy's time did not follow its
-// fetches (358 -> 360 us), so it keeps the (row, part, slice) order. The waves are short (1 KiB
+// fetches (358 -> 360 us; 355 -> 365 us once both orders had 32-bit indices), so it keeps the
+// (row, part, slice) order. The waves are short (1 KiB
 // to at most four rows), so their index arithmetic shows: with 32-bit instead of 64-bit divisions
 // the permute took 355 instead of 358 us (T16384 H7168 K8), 133.0 against 133.3 us with padding
 // (T8192 H4096 E128) and 74.6 against 75.6 us as the group send.
