@@ -24,10 +24,12 @@
 //             scan launch between the two took 5.9 us at T16384 K8 E256, the rank kernel
 //             re-reading its results.) Its tokens are split over 8 wavefronts (per-wave counts
 //             and a prefix over the waves in LDS); each wavefront walks its slots 64 at a time
-//             in slot order. Lanes with the same key find each other with one ballot per key bit
-//             (a match-any built from ballots); their stable rank is popcount(peers &
-//             lanes_below) and the last peer advances the key's running row counter in LDS.
-//             The workgroups then write the padding or unused rows together.
+//             in slot order, in batches of 2 or 8 such groups (the smaller batch whenever it
+//             holds a wave's slots: smaller code, see kRankBatchSmall). Lanes with the same key
+//             find each other with one ballot per key bit (a match-any built from ballots); their
+//             stable rank is popcount(peers & lanes_below) and the last peer advances the key's
+//             running row counter in LDS. The workgroups then write the padding or unused rows
+//             together.
 //   3. esrc   (group mode, K not a power of two) expert-major row -> group slot (and routing
 //             slot -> group slot, slot_src). With K a power
 //             of two a token's slots sit in consecutive lanes of one wavefront: the first slot
@@ -35,7 +37,8 @@
 //             slot to the token's other slots of the group and writes esrc itself.
 // With no tokens one single-workgroup launch writes the zero counts and the marks; with at most
 // one 512-slot batch per rank wavefront (T*K <= 4096) the rank kernel runs alone as one
-// workgroup and takes the totals from its own per-wave counts (no histogram launch).
+// workgroup and takes the totals from its own per-wave counts; up to T*K = 16384 every rank
+// workgroup counts all slots itself. Neither needs the histogram launch.
 // The drop-and-pad capacity rule ([Scratch] §18, §26.6), the expert alignment ([Combine] §6:
 // segments rounded up to a multiple of A with padding rows, the segment starts being the scan of
 // the aligned lengths) and the group (send once per rank) slots ([CANN] §1(1)) are applied
