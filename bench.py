@@ -2,7 +2,7 @@
 """Throughput of the MoE token dispatch / unpermute-combine hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input, inputs already
-resident in HBM: route_topk -> build_index -> permute (x into expert-major rows) ->
+resident in HBM: route_topk + build_index (one call, route_topk_index) -> permute (x into expert-major rows) ->
 unpermute_combine (expert outputs back to token order, weighted). In group mode the permute is
 the two-stage dedup dispatch and the combine is the per-group pre-combine plus the final sum.
 
@@ -263,10 +263,12 @@ def main():
     if rg and not gs:
         print("--route-groups needs a workload with expert groups (workload 4)", file=sys.stderr, flush=True)
         sys.exit(2)
-    calls = [("route", "route", lambda: m.route_topk(logits, K, out=(gi, gw), group_size=gs if rg else 0,
-                                                     topk_groups=rg)),
-             ("index", "index", lambda: m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix,
-                                                      alignment=align))]
+    # routing and index build in one call: for large inputs the workgroups that route a tile also
+    # count its slots, one launch fewer than route_topk followed by build_index (same arrays)
+    calls = [("route_index", "route_index",
+              lambda: m.route_topk_index(logits, K, capacity=cap, group_size=gs, alignment=align,
+                                         route_group_size=gs if rg else 0, topk_groups=rg, out=(gi, gw),
+                                         index=ix))]
     src = xp if y is None else y
     if args.backward:
         # one forward pass (not timed) leaves the saved state the backward consumes
@@ -415,8 +417,7 @@ def main():
     valid = int((row_of >= 0).sum())  # rows the combine reads
     used = int((ix.sorted_indices != -2).sum().item())  # rows written (the slack after the last segment is not)
     routed = int((row_of >= 0).any(axis=1).sum()) if K else 0  # distinct source rows the permute reads
-    kbytes = {"route": T * E * 4 + T * K * 8,
-              "index": T * K * 8 + rows * 8 + T * K * 4 + E * 4 * 3}
+    kbytes = {"route_index": T * E * 4 + T * K * 8 + T * K * 8 + rows * 8 + T * K * 4 + E * 4 * 3}
     if args.backward:
         kbytes = {"combine_bwd": T * H * b + valid * H * b + used * H * b + T * K * 8 + rows * 4 + T * K * 4,
                   "route_bwd": T * K * 12 + T * E * 4}

@@ -203,6 +203,23 @@ moe_status moe_build_index_noalloc(const int32_t *topk_idx, const float *topk_w,
                                    int32_t E, int32_t capacity, int32_t group_size, int32_t alignment,
                                    const moe_index *out, hipStream_t stream);
 
+/* Routing and index build in one call ([Scratch] §3, §27: top-k and the softmax over the K
+ * selected logits; §7: the per-expert counts behind group_list; [Megatron] §1.1: the index):
+ * the same topk_idx, topk_w and moe_index arrays, bit for bit, as moe_route_topk (route_group_size
+ * <= 0) or moe_route_topk_grouped(route_group_size, topk_groups) followed by moe_build_index(
+ * topk_idx, topk_w, T, K, E, capacity, group_size, alignment, ...). Where moe_build_index would
+ * count its tiles in a launch of its own, the workgroups that route a tile count its slots
+ * instead, one launch fewer. Arguments are those of the two calls (route_group_size and
+ * topk_groups as moe_route_topk_grouped's group_size and topk_groups; group_size is the index's);
+ * the workspace (16-byte aligned; contents need no initialisation and mean nothing after the
+ * call) must hold moe_route_topk_index_workspace_size bytes. Every argument error of either call
+ * is returned before anything is launched. */
+moe_status moe_route_topk_index_workspace_size(int64_t T, int32_t K, int32_t E, int32_t group_size, size_t *bytes);
+moe_status moe_route_topk_index(const float *logits, int64_t T, int32_t E, int32_t K, int32_t route_group_size,
+                                int32_t topk_groups, int32_t *topk_idx, float *topk_w, int32_t capacity,
+                                int32_t group_size, int32_t alignment, const moe_index *out, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* Row gather ([Megatron] §1.1 step 5, permuted_input = tokens.index_select(0, sorted_indices);
  * [Scratch] §12, permuted_tokens = tokens[permute_indices]):
  *   dst[i, :] = src[src_row[i], :] copied bit for bit, for i in [0, N); a src_row outside

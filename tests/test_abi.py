@@ -165,3 +165,43 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_index_rows(8192, 8, 128, 640, 0) == 128 * 640
     assert lib.moe_index_rows(8192, 8, 128, 640, 128) == -1
     assert lib.moe_index_rows(1 << 30, 8, 8, 0, 0) == -1
+
+
+def test_route_topk_index_sizes_and_argument_errors(capi):
+    """moe_route_topk_index: its workspace (the fused route's tile counts, a multiple of 64 tokens
+    per tile and at most 256 tiles, where the index build counts tiles; otherwise the index build's
+    own), and every argument error of either of its two calls returned before any launch."""
+    lib = capi.lib()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_route_topk_index_workspace_size(16384, 8, 256, 0, ctypes.byref(n)) == capi.MOE_OK
+    assert n.value == 256 * 256 * 4  # 64-token tiles
+    assert lib.moe_route_topk_index_workspace_size(8192, 8, 256, 8, ctypes.byref(n)) == capi.MOE_OK
+    assert n.value == 128 * (256 + 32) * 4
+    assert lib.moe_route_topk_index_workspace_size(1 << 20, 8, 256, 0, ctypes.byref(n)) == capi.MOE_OK
+    assert n.value == 256 * 256 * 4  # 4096-token tiles
+    small = ctypes.c_size_t(0)
+    assert lib.moe_build_index_workspace_size(2048, 8, 256, 0, ctypes.byref(small)) == capi.MOE_OK
+    assert lib.moe_route_topk_index_workspace_size(2048, 8, 256, 0, ctypes.byref(n)) == capi.MOE_OK
+    assert n.value == small.value  # 16384 slots: the index build counts no tiles
+    assert lib.moe_route_topk_index_workspace_size(16, 8, 4, 0, ctypes.byref(n)) == capi.MOE_ERR_INVALID
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    ix = capi.MoeIndexStruct()
+    for name, _ in capi.MoeIndexStruct._fields_:
+        setattr(ix, name, fake.value)
+    ok_ws = 1 << 20
+
+    def call(logits, T, E, K, rgs, m, cap, gs, align, ws=fake, ws_bytes=ok_ws, out=ix):
+        return lib.moe_route_topk_index(logits, T, E, K, rgs, m, fake, fake, cap, gs, align,
+                                        ctypes.byref(out) if out is not None else None, ws, ws_bytes, None)
+
+    assert call(fake, 4, 8, 9, 0, 0, 0, 0, 0) == capi.MOE_ERR_INVALID  # K > E
+    assert call(fake, 4, 16, 2, 3, 2, 0, 0, 0) == capi.MOE_ERR_INVALID  # route groups of 3 in 16 experts
+    assert call(fake, 4, 16, 2, 4, 5, 0, 0, 0) == capi.MOE_ERR_INVALID  # 5 of 4 route groups
+    assert call(fake, 4, 2048, 2, 0, 0, 0, 0, 0) == capi.MOE_ERR_UNSUPPORTED
+    assert call(fake, 4, 16, 2, 0, 0, 0, 3, 0) == capi.MOE_ERR_INVALID  # index groups of 3
+    assert call(fake, 4, 16, 2, 0, 0, 4, 4, 0) == capi.MOE_ERR_UNSUPPORTED  # capacity with groups
+    assert call(fake, 4, 16, 2, 0, 0, 0, 0, -1) == capi.MOE_ERR_INVALID
+    assert call(fake, 4, 16, 2, 0, 0, 0, 0, 0, out=None) == capi.MOE_ERR_INVALID
+    assert call(None, 4, 16, 2, 0, 0, 0, 0, 0) == capi.MOE_ERR_INVALID  # no logits
+    assert call(fake, 100000, 256, 8, 0, 0, 0, 0, 0, ws_bytes=16) == capi.MOE_ERR_INVALID  # workspace too small
+    assert call(fake, 100000, 256, 8, 0, 0, 0, 0, 0, ws=ctypes.c_void_p(0x1004)) == capi.MOE_ERR_INVALID  # unaligned

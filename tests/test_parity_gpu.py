@@ -229,6 +229,54 @@ def test_build_index_aligned(m, T, E, K, align, gs):
     assert (gl % align == 0).all()
 
 
+INDEX_FIELDS = ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs")
+GROUP_FIELDS = ("slot_of", "esrc", "group_counts", "slot_src")
+
+
+@pytest.mark.parametrize("T,E,K,cap,gs,align,rgs,M,ties", [
+    (16384, 256, 8, 0, 0, 0, 0, 0, False),     # 64-token tiles, 256 of them
+    (8192, 256, 8, 0, 8, 0, 0, 0, False),      # index groups
+    (8192, 128, 8, 640, 0, 0, 0, 0, False),    # drop-and-pad
+    (16384, 256, 8, 0, 0, 128, 0, 0, False),   # expert alignment
+    (8192, 256, 8, 0, 8, 0, 8, 4, False),      # group-limited routing and index groups
+    (5000, 64, 8, 0, 0, 0, 0, 0, True),        # a partial last tile, tie-heavy logits
+    (3001, 96, 6, 0, 8, 0, 0, 0, False),       # K not a power of two: the separate esrc launch
+    (2049, 1024, 32, 0, 32, 4, 32, 8, False),  # the largest E and K
+    (300000, 64, 8, 0, 0, 0, 0, 0, False),     # 1216-token tiles: 19 passes per workgroup
+    (1000, 64, 8, 0, 8, 0, 0, 0, False),       # 8000 slots: route, then the index build alone
+    (0, 64, 8, 0, 0, 0, 0, 0, False),
+])
+def test_route_topk_index(m, T, E, K, cap, gs, align, rgs, M, ties):
+    """moe_route_topk_index against the oracle (routing, then the index of the oracle's routing
+    with the GPU's weights) and bit for bit against moe_route_topk(_grouped) + moe_build_index."""
+    say(f"route_topk_index T={T} E={E} K={K} cap={cap} gs={gs} align={align} route groups {rgs}/{M}")
+    key = wl.case_key(42, T, E, K, gs, rgs)
+    logits = tie_logits(key, T, E) if ties else wl.router_logits(key, T, E, zipf_s=1.2)
+    dl = dev(logits)
+    gi, gw, ix = m.route_topk_index(dl, K, capacity=cap, group_size=gs, alignment=align, route_group_size=rgs,
+                                    topk_groups=M)
+    si, sw = m.route_topk(dl, K, group_size=rgs, topk_groups=M)
+    six = m.build_index(si, sw, E, capacity=cap, group_size=gs, alignment=align)
+    torch.cuda.synchronize()
+    assert_exact(host(gi), host(si), "topk_idx against the separate route")
+    assert_exact(host(gw).view(np.int32), host(sw).view(np.int32), "topk_w against the separate route")
+    for name in INDEX_FIELDS + (GROUP_FIELDS if gs else ()):
+        assert_exact(host(getattr(ix, name)), host(getattr(six, name)), f"{name} against the separate calls")
+    want_i, want_w = oracle.route_topk_grouped(logits, K, rgs, M) if rgs else oracle.route_topk(logits, K)
+    assert_exact(host(gi), want_i, "topk_idx")
+    assert_rel_f32(host(gw), want_w, "topk_w")
+    want = oracle.build_index(want_i, host(gw), E, capacity=cap, group_size=gs, alignment=align)
+    for name in INDEX_FIELDS:
+        assert_exact(host(getattr(ix, name)), want[name], name)
+    if gs:
+        n = int(host(ix.n_slots)[0])
+        assert n == int(want["n_slots"][0])
+        assert_exact(host(ix.gsrc)[:n], want["gsrc"], "gsrc")
+        assert_exact(host(six.gsrc)[:n], want["gsrc"], "gsrc (separate calls)")
+        for name in GROUP_FIELDS:
+            assert_exact(host(getattr(ix, name)), want[name], name)
+
+
 # ------------------------------------------------------------------ permute
 
 
@@ -772,14 +820,14 @@ def check_route_and_index(m, c, logits, route_groups, cap, align):
     T, E, K, gs = c["T"], c["E"], c["K"], c["group_size"]
     if route_groups:
         want_i, want_w = oracle.route_topk_grouped(logits, K, gs, route_groups)
-        gi, gw = m.route_topk(dev(logits), K, group_size=gs, topk_groups=route_groups)
     else:
         want_i, want_w = oracle.route_topk(logits, K)
-        gi, gw = m.route_topk(dev(logits), K)
+    # routing and index in one call, as bench.py launches them
+    gi, gw, ix = m.route_topk_index(dev(logits), K, capacity=cap, group_size=gs, alignment=align,
+                                    route_group_size=gs if route_groups else 0, topk_groups=route_groups)
     assert_exact(host(gi), want_i, "topk_idx")
     assert_rel_f32(host(gw), want_w, "topk_w")
     w_np = host(gw)  # the same weight bits on both sides from here on
-    ix = m.build_index(gi, gw, E, capacity=cap, group_size=gs, alignment=align)
     want = oracle.build_index(want_i, w_np, E, capacity=cap, group_size=gs, alignment=align)
     for name in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs"):
         assert_exact(host(getattr(ix, name)), want[name], name)
@@ -974,8 +1022,8 @@ def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
         outs["dlog"] = torch.empty((T, E), dtype=torch.float32, device=DEV)
 
     def step():
-        m.route_topk(logits, K, out=(gi, gw), group_size=gs if rg else 0, topk_groups=rg)
-        m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix, alignment=align)
+        m.route_topk_index(logits, K, capacity=cap, group_size=gs, alignment=align, route_group_size=gs if rg else 0,
+                           topk_groups=rg, out=(gi, gw), index=ix)
         if mode == "fp8" and gs:
             m.permute_scatter_fp8(x, ix.slot_of, slots, block, out=(gq, gsc))
             m.permute_grouped(gq, ix.esrc, ix.row_of, out=outs["xp"], src_of=ix.slot_src)
@@ -1440,15 +1488,15 @@ def test_pipeline_is_deterministic(m, case):
     def run(prev=None):
         P = (lambda t: _poison_like(t)) if prev is not None else (lambda t: torch.empty_like(t))
         r = {}
-        gi, gw = m.route_topk(logits, K, out=(P(torch.empty((T, K), dtype=torch.int32, device=DEV)),
-                                              P(torch.empty((T, K), dtype=torch.float32, device=DEV))))
         ix = m.alloc_index(T, K, E, cap, gs)
         for f in ("counts", "group_list", "kept_counts", "sorted_indices", "row_of", "permuted_probs", "slot_of",
                   "gsrc", "esrc", "group_counts", "n_slots", "slot_src"):
             t = getattr(ix, f)
             if t is not None and prev is not None:
                 t.view(torch.uint8).fill_(0xFF)
-        m.build_index(gi, gw, E, capacity=cap, group_size=gs, out=ix)
+        gi, gw, _ = m.route_topk_index(logits, K, capacity=cap, group_size=gs,
+                                       out=(P(torch.empty((T, K), dtype=torch.int32, device=DEV)),
+                                            P(torch.empty((T, K), dtype=torch.float32, device=DEV))), index=ix)
         r.update(gi=gi, gw=gw, **{f: getattr(ix, f) for f in ("counts", "group_list", "kept_counts", "sorted_indices",
                                                               "row_of", "permuted_probs")})
         if gs:

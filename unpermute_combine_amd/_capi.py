@@ -32,6 +32,9 @@ SIGNATURES = {
     "moe_build_index_noalloc": (ctypes.c_int, [_P, _P, _i64, _i32, _i32, _i32, _i32, _i32,
                                                ctypes.POINTER(MoeIndexStruct), _P]),
     "moe_index_rows": (ctypes.c_int64, [_i64, _i32, _i32, _i32, _i32]),
+    "moe_route_topk_index_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_route_topk_index": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _i32, _P, _P, _i32, _i32, _i32,
+                                            ctypes.POINTER(MoeIndexStruct), _P, ctypes.c_size_t, _P]),
     "moe_permute": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _P]),
     "moe_permute_scatter": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i32, _P, _i64, _P, _P]),
     "moe_quantize_fp8": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _i32, _P, _P, _P]),

@@ -857,6 +857,18 @@ Plan make_plan(int64_t T, int32_t K, int32_t E, int32_t G)
     return p;
 }
 
+// The plan of tile counts written by the fused route kernel: tiles of tile_tokens tokens.
+constexpr int kMaxCountedTiles = 256;
+Plan counted_plan(int64_t T, int32_t E, int32_t G, int32_t tile_tokens)
+{
+    Plan p{};
+    p.tile_tokens = tile_tokens;
+    p.ntiles = static_cast<int32_t>(T == 0 ? 0 : ceil_div(T, tile_tokens));
+    auto al = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+    p.ws = al(sizeof(int32_t) * static_cast<size_t>(round4(E) + (G > 0 ? round4(G) : 0)) * p.ntiles);
+    return p;
+}
+
 moe_status check_sizes(int64_t T, int32_t K, int32_t E, int32_t group_size)
 {
     if (T < 0 || K < 1 || E < 1 || K > E)
@@ -903,7 +915,8 @@ namespace {
 // counts. With launch = false only the arguments other than the workspace are checked.
 moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K, int32_t E,
                             int32_t capacity, int32_t group_size, int32_t alignment, const moe_index *out,
-                            void *workspace, size_t workspace_bytes, hipStream_t stream, bool launch = true)
+                            void *workspace, size_t workspace_bytes, hipStream_t stream, bool launch = true,
+                            int32_t counted_tile_tokens = 0)
 {
     moe_status st = check_sizes(T, K, E, group_size);
     if (st != MOE_OK)
@@ -926,8 +939,10 @@ moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_
         return MOE_ERR_INVALID;
     if (T > 0 && !topk_idx)
         return MOE_ERR_INVALID;
-    const Plan p = make_plan(T, K, E, G);
-    if (p.ntiles > kMaxTiles)
+    // counted_tile_tokens > 0: the tile counts are already in the workspace (tiles of that many
+    // tokens, counted by the fused route kernel), and only the rank pass is launched
+    const Plan p = counted_tile_tokens > 0 ? counted_plan(T, E, G, counted_tile_tokens) : make_plan(T, K, E, G);
+    if (p.ntiles > (counted_tile_tokens > 0 ? kMaxCountedTiles : kMaxTiles))
         return MOE_ERR_UNSUPPORTED;  // cannot happen: tiles grow with T to stay within the limit
     const size_t need = p.ws;
     if (!launch)
@@ -962,7 +977,7 @@ moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_
         return launch_status();
     }
 
-    const bool single = T * K <= kSingleTileSlots;  // one workgroup, one launch
+    const bool single = counted_tile_tokens == 0 && T * K <= kSingleTileSlots;  // one workgroup, one launch
     if (single) {
         a.tile_tokens = static_cast<int32_t>(T);
         a.ntiles = 1;
@@ -972,8 +987,9 @@ moe_status build_index_impl(const int32_t *topk_idx, const float *topk_w, int64_
     const int rb = wave_slots <= static_cast<int64_t>(kRankBatchSmall) * kWave ? kRankBatchSmall : kRankBatchLarge;
     const size_t lds_rank = sizeof(int32_t) * (static_cast<size_t>(kRankWaves + 1) * (E + G) + 2 * static_cast<size_t>(a.Hp) +
                                                static_cast<size_t>(ids_ints(rb)));
-    const int totals = single ? kSingle : (T * K <= kCountAllSlots ? kCountAll : kFromTiles);
-    if (totals == kFromTiles) {
+    const int totals = counted_tile_tokens > 0 ? kFromTiles
+                       : (single ? kSingle : (T * K <= kCountAllSlots ? kCountAll : kFromTiles));
+    if (totals == kFromTiles && counted_tile_tokens == 0) {
         const size_t lds_hist = sizeof(int32_t) * static_cast<size_t>(a.Hp);
         if (G > 0)
             hipLaunchKernelGGL(hist_kernel<true>, dim3(p.ntiles), dim3(kHistThreads), lds_hist, stream, a);
@@ -1006,6 +1022,23 @@ extern "C" moe_status moe_build_index(const int32_t *topk_idx, const float *topk
     return moe::build_index_impl(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, workspace,
                                  workspace_bytes, stream);
 }
+
+namespace moe {
+
+moe_status build_index_from_tile_counts(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K, int32_t E,
+                                        int32_t capacity, int32_t group_size, int32_t alignment, const moe_index *out,
+                                        void *workspace, size_t workspace_bytes, int32_t tile_tokens, bool launch,
+                                        hipStream_t stream)
+{
+    if (tile_tokens < 1)
+        return MOE_ERR_INVALID;
+    return build_index_impl(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, workspace,
+                            workspace_bytes, stream, launch, tile_tokens);
+}
+
+bool build_index_counts_tiles(int64_t T, int32_t K) { return T * K > kCountAllSlots; }
+
+}  // namespace moe
 
 // ---------------------------------------------------------------- allocation-free entry point
 // The tile counts of moe_build_index_noalloc live in this array instead of a caller's workspace:

@@ -131,4 +131,15 @@ moe_status launch_scatter_vec16(const char *src, int64_t src_rows, int64_t nvec,
                                 const int32_t *src_row, int64_t N, char *dst, bool scaled, const float *scale,
                                 hipStream_t stream);
 
+// moe_build_index's rank pass over tile counts already in `workspace` (tiles of tile_tokens whole
+// tokens, the last one partial; per tile a row of round4(E) expert counts followed, with groups,
+// by round4(E / group_size) counts of each token's first slot per group; at most 256 tiles, rows
+// 16-byte aligned). launch = false checks the arguments only. Same outputs as moe_build_index.
+moe_status build_index_from_tile_counts(const int32_t *topk_idx, const float *topk_w, int64_t T, int32_t K, int32_t E,
+                                        int32_t capacity, int32_t group_size, int32_t alignment, const moe_index *out,
+                                        void *workspace, size_t workspace_bytes, int32_t tile_tokens, bool launch,
+                                        hipStream_t stream);
+// True when moe_build_index counts the tiles in a launch of its own for these sizes.
+bool build_index_counts_tiles(int64_t T, int32_t K);
+
 }  // namespace moe

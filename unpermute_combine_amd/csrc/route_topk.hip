@@ -27,6 +27,8 @@
 // That code lives only in the group-limited instance (GROUPS), and the candidate refill is inlined
 // once: with caches flushed the kernel's code is fetched from HBM as it runs, and the plain
 // E = 256 kernel shrank from 15.9 to 6.5 KB (9.2 -> 8.9 us at T16384 K8, 6.8 -> 6.6 us at T8192).
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -107,18 +109,28 @@ __device__ __forceinline__ uint32_t row_min1(uint32_t v)
 constexpr int kMaxRouteGroups = 256;  // group keys in LDS: 16 tokens x 256 x 4 B per workgroup
 constexpr uint32_t kChosenGroup = 0xffffffffu;  // above every key of a finite logit
 
-template <int J, bool GROUPS>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
-                                                                   int E, int K, int gs, int M,
-                                                                   int32_t *__restrict__ topk_idx,
-                                                                   float *__restrict__ topk_w)
+// Per-tile expert (and group) counts of the routed slots, kept in LDS by the fused route + tile
+// count kernel: he[e] += 1 for every selected expert, hg[g] += 1 for the first of a token's slots
+// in each group of gs experts (gs = 0: no groups). Counts only, never positions.
+struct TileCounts {
+    int32_t *he, *hg;
+    int gs;
+};
+
+// One pass of the routing over the TPB tokens t_first .. t_first + TPB - 1 of this workgroup
+// (16 lanes per token; tokens at or past t_end take part with empty keys and store nothing).
+// HIST: the selected experts are also counted into `tc`.
+template <int J, bool GROUPS, int TPB, bool HIST>
+__device__ __forceinline__ void route_pass(const float *__restrict__ logits, int64_t T, int64_t t_first, int64_t t_end,
+                                           int E, int K, int gs, int M, int32_t *__restrict__ topk_idx,
+                                           float *__restrict__ topk_w, TileCounts tc)
 {
-    __shared__ double ex_sh[kTokensPerBlock][MOE_MAX_TOPK];
-    extern __shared__ uint32_t group_sh[];  // [kTokensPerBlock][G] when gs > 0
+    __shared__ double ex_sh[TPB][MOE_MAX_TOPK];
+    extern __shared__ uint32_t group_sh[];  // [TPB][G] when gs > 0
     const int sub = threadIdx.x & (kLanesPerToken - 1);
     const int tok = threadIdx.x / kLanesPerToken;  // token of this row inside the block
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + tok;
-    const bool live = t < T;  // rows past T take part in the DPP steps with empty keys
+    const int64_t t = t_first + tok;
+    const bool live = t < t_end;  // rows past the end take part in the DPP steps with empty keys
     // every load in bounds (rows past T read row T-1, experts past E read expert E-1) and the
     // absent ones masked afterwards: the J loads issue back to back with one wait (a guarded
     // load per key made the compiler wait for each one before issuing the next: 15.4 against
@@ -218,8 +230,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
     // holding it are the candidates, and only when two candidates hold equal keys does a
     // second 16-lane reduction pick the lowest expert id among them. The winner lane records
     // the slot in LDS and gives up its first key.
-    __shared__ uint32_t slot_key[kTokensPerBlock][MOE_MAX_TOPK];
-    __shared__ int32_t slot_id[kTokensPerBlock][MOE_MAX_TOPK];
+    __shared__ uint32_t slot_key[TPB][MOE_MAX_TOPK];
+    __shared__ int32_t slot_id[TPB][MOE_MAX_TOPK];
     const int seg_shift = threadIdx.x & (kWave - kLanesPerToken);  // this row's first lane in the wave
     uint32_t s0u = 0;
     for (int k = 0; k < K; ++k) {
@@ -277,9 +289,76 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *
             if (k < K) {
                 topk_idx[t * K + k] = slot_e[q];
                 topk_w[t * K + k] = static_cast<float>(ex[q] / z);
+                if constexpr (HIST) {
+                    const int e = slot_e[q];
+                    atomicAdd(&tc.he[e], 1);
+                    if (tc.gs > 0) {  // the token's first slot in its group
+                        const int g = e / tc.gs;
+                        bool lead = true;
+                        for (int j = 0; j < k; ++j)
+                            lead = lead && slot_id[tok][j] / tc.gs != g;
+                        if (lead)
+                            atomicAdd(&tc.hg[g], 1);
+                    }
+                }
             }
         }
     }
+}
+
+template <int J, bool GROUPS>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float *__restrict__ logits, int64_t T,
+                                                                   int E, int K, int gs, int M,
+                                                                   int32_t *__restrict__ topk_idx,
+                                                                   float *__restrict__ topk_w)
+{
+    route_pass<J, GROUPS, kTokensPerBlock, false>(logits, T, static_cast<int64_t>(blockIdx.x) * kTokensPerBlock, T, E,
+                                                  K, gs, M, topk_idx, topk_w, TileCounts{});
+}
+
+// ---------------------------------------------------------------- fused route + tile counts
+// The routing of moe_route_topk_index for inputs whose index build counts tiles ([Scratch] §3:
+// top-k and softmax; §7: the per-expert counts behind group_list): one workgroup per index tile
+// of whole tokens, 64 tokens per pass, so that the workgroup that routes a tile also counts its
+// slots -- per expert, and with index groups per (token, group) first slot -- into one row of
+// tile counts, the rows the rank pass of the index build reads. This replaces the separate
+// histogram launch, which re-read topk_idx.
+constexpr int kFusedTokens = 64;
+constexpr int kFusedThreads = kFusedTokens * kLanesPerToken;  // 1024
+constexpr int kFusedMaxTiles = 256;
+
+struct CountArgs {
+    int32_t tile_tokens;
+    int32_t idx_gs, G;  // index groups (idx_gs = 0: none)
+    int32_t Ep, Hp;     // E and G rounded up to multiples of 4; Hp = Ep (+ Gp): a tile's row
+    int32_t *hist;      // [tiles][Hp]
+    int32_t *slot_of;   // [T][G]: -1 for the tile's tokens (index group mode)
+};
+
+template <int J, bool GROUPS>
+__global__ __launch_bounds__(kFusedThreads) void route_count_kernel(const float *__restrict__ logits, int64_t T, int E,
+                                                                    int K, int gs, int M,
+                                                                    int32_t *__restrict__ topk_idx,
+                                                                    float *__restrict__ topk_w, CountArgs c)
+{
+    extern __shared__ uint32_t group_sh[];  // route group keys [kFusedTokens][E / gs], then the counts
+    int32_t *cnt = reinterpret_cast<int32_t *>(group_sh + (GROUPS ? kFusedTokens * (E / gs) : 0));
+    for (int i = threadIdx.x; i < c.Hp; i += kFusedThreads)
+        cnt[i] = 0;
+    __syncthreads();
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * c.tile_tokens;
+    const int64_t t1 = min(T, t0 + c.tile_tokens);
+    const TileCounts tc{cnt, cnt + c.Ep, c.idx_gs};
+    for (int64_t tf = t0; tf < t1; tf += kFusedTokens)
+        route_pass<J, GROUPS, kFusedTokens, true>(logits, T, tf, t1, E, K, gs, M, topk_idx, topk_w, tc);
+    if (c.idx_gs > 0) {  // slot_of starts as "absent" for this tile's tokens
+        for (int64_t i = t0 * c.G + threadIdx.x; i < t1 * c.G; i += kFusedThreads)
+            c.slot_of[i] = -1;
+    }
+    __syncthreads();
+    int32_t *row = c.hist + static_cast<int64_t>(blockIdx.x) * c.Hp;
+    for (int i = threadIdx.x; i < c.Hp; i += kFusedThreads)
+        row[i] = cnt[i];
 }
 
 // ---------------------------------------------------------------- backward
@@ -369,6 +448,78 @@ moe_status launch_route(const float *logits, int64_t T, int32_t E, int32_t K, in
     return launch_status();
 }
 
+// The fused route when the index build counts tiles, E <= 256 and the routing is not
+// group-limited: with 1024-thread workgroups a thread has 128 registers, and the routing of more
+// experts per lane, or the group-limited routing, spills (J = 32: 75 to 112 registers to scratch;
+// group-limited at E = 256: 28 us against 13 + 5 us for the separate route and histogram).
+// Otherwise moe_route_topk_index makes the two separate calls.
+bool use_fused(int64_t T, int32_t K, int32_t E, int32_t route_group_size)
+{
+    return build_index_counts_tiles(T, K) && ceil_div(E, kLanesPerToken) <= 16 && route_group_size <= 0;
+}
+
+// Tiles of the fused route: a multiple of its 64-token passes, at most kFusedMaxTiles of them.
+int32_t fused_tile_tokens(int64_t T)
+{
+    const int64_t tt = ceil_div(ceil_div(T, kFusedMaxTiles), kFusedTokens) * kFusedTokens;
+    return static_cast<int32_t>(tt < kFusedTokens ? kFusedTokens : tt);
+}
+
+// Bytes of the tile counts the fused route writes (the rank pass's rows; 256-byte rounded).
+size_t fused_counts_bytes(int64_t T, int32_t E, int32_t group_size)
+{
+    const int64_t ntiles = ceil_div(T, fused_tile_tokens(T));
+    const int64_t hp = ((E + 3) & ~3) + (group_size > 0 ? ((E / group_size + 3) & ~3) : 0);
+    const size_t b = sizeof(int32_t) * static_cast<size_t>(hp * ntiles);
+    return (b + 255) & ~static_cast<size_t>(255);
+}
+
+moe_status check_route(int64_t T, int32_t E, int32_t K, int32_t gs, int32_t M)
+{
+    if (T < 0 || E < 1 || K < 1 || K > E)
+        return MOE_ERR_INVALID;
+    if (gs > 0 && (E % gs != 0 || M < 1 || M > E / gs || static_cast<int64_t>(K) > static_cast<int64_t>(M) * gs))
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || (gs > 0 && E / gs > kMaxRouteGroups))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status launch_route_count(const float *logits, int64_t T, int32_t E, int32_t K, int32_t gs, int32_t M,
+                              int32_t *topk_idx, float *topk_w, const CountArgs &c, hipStream_t stream)
+{
+    const int64_t blocks = ceil_div(T, c.tile_tokens);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kFusedThreads);
+    const size_t lds = (gs > 0 ? sizeof(uint32_t) * kFusedTokens * static_cast<size_t>(E / gs) : 0) +
+                       sizeof(int32_t) * static_cast<size_t>(c.Hp);
+    const int nj = static_cast<int>(ceil_div(E, kLanesPerToken));
+#define MOE_ROUTE_COUNT_LAUNCH(JJ)                                                                               \
+    do {                                                                                                         \
+        if (gs > 0)                                                                                              \
+            hipLaunchKernelGGL((route_count_kernel<JJ, true>), grid, block, lds, stream, logits, T, E, K, gs, M,     \
+                               topk_idx, topk_w, c);                                                             \
+        else                                                                                                     \
+            hipLaunchKernelGGL((route_count_kernel<JJ, false>), grid, block, lds, stream, logits, T, E, K, gs, M,    \
+                               topk_idx, topk_w, c);                                                             \
+    } while (0)
+    if (nj <= 1)
+        MOE_ROUTE_COUNT_LAUNCH(1);
+    else if (nj <= 2)
+        MOE_ROUTE_COUNT_LAUNCH(2);
+    else if (nj <= 4)
+        MOE_ROUTE_COUNT_LAUNCH(4);
+    else if (nj <= 8)
+        MOE_ROUTE_COUNT_LAUNCH(8);
+    else if (nj <= 16)
+        MOE_ROUTE_COUNT_LAUNCH(16);
+    else if (nj <= 32)
+        MOE_ROUTE_COUNT_LAUNCH(32);
+    else
+        MOE_ROUTE_COUNT_LAUNCH(64);
+#undef MOE_ROUTE_COUNT_LAUNCH
+    return launch_status();
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -414,4 +565,62 @@ extern "C" moe_status moe_route_topk_backward(const int32_t *topk_idx, const flo
     hipLaunchKernelGGL(route_topk_backward_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRouteThreads), 0, stream,
                        topk_idx, topk_w, d_topk_w, T, E, K, d_logits);
     return launch_status();
+}
+
+extern "C" moe_status moe_route_topk_index_workspace_size(int64_t T, int32_t K, int32_t E, int32_t group_size,
+                                                          size_t *bytes)
+{
+    using namespace moe;
+    if (!bytes)
+        return MOE_ERR_INVALID;
+    size_t separate = 0;
+    const moe_status st = moe_build_index_workspace_size(T, K, E, group_size, &separate);
+    if (st != MOE_OK)
+        return st;
+    // enough for either path (the fused one has at least as many tiles)
+    *bytes = use_fused(T, K, E, 0) ? std::max(fused_counts_bytes(T, E, group_size), separate) : separate;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_route_topk_index(const float *logits, int64_t T, int32_t E, int32_t K,
+                                           int32_t route_group_size, int32_t topk_groups, int32_t *topk_idx,
+                                           float *topk_w, int32_t capacity, int32_t group_size, int32_t alignment,
+                                           const moe_index *out, void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream)
+{
+    using namespace moe;
+    const int32_t rgs = route_group_size > 0 ? route_group_size : 0;
+    moe_status st = check_route(T, E, K, rgs, rgs > 0 ? topk_groups : 0);
+    if (st != MOE_OK)
+        return st;
+    // every index argument error before any launch
+    st = build_index_from_tile_counts(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, nullptr, 0,
+                                      fused_tile_tokens(T), false, stream);
+    if (st != MOE_OK)
+        return st;
+    if (T > 0 && (!logits || !topk_idx || !topk_w))
+        return MOE_ERR_INVALID;
+    size_t need = 0;
+    if ((st = moe_route_topk_index_workspace_size(T, K, E, group_size, &need)) != MOE_OK)
+        return st;
+    if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
+        return MOE_ERR_INVALID;
+    if (!use_fused(T, K, E, rgs)) {  // the two calls
+        if ((st = launch_route(logits, T, E, K, rgs, topk_groups, topk_idx, topk_w, stream)) != MOE_OK)
+            return st;
+        return moe_build_index(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, workspace,
+                               workspace_bytes, stream);
+    }
+    CountArgs c{};
+    c.tile_tokens = fused_tile_tokens(T);
+    c.idx_gs = group_size > 0 ? group_size : 0;
+    c.G = group_size > 0 ? E / group_size : 0;
+    c.Ep = (E + 3) & ~3;
+    c.Hp = c.Ep + (c.G > 0 ? ((c.G + 3) & ~3) : 0);
+    c.hist = static_cast<int32_t *>(workspace);
+    c.slot_of = out->slot_of;
+    if ((st = launch_route_count(logits, T, E, K, rgs, topk_groups, topk_idx, topk_w, c, stream)) != MOE_OK)
+        return st;
+    return build_index_from_tile_counts(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, workspace,
+                                        workspace_bytes, c.tile_tokens, true, stream);
 }

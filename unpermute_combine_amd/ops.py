@@ -127,10 +127,14 @@ class MoeIndex:
 
 
 def workspace_bytes(T: int, K: int, E: int, group_size: int = 0) -> int:
+    """Workspace bytes for these sizes: enough for build_index and for route_topk_index."""
     n = ctypes.c_size_t(0)
     check("moe_build_index_workspace_size",
           lib().moe_build_index_workspace_size(T, K, E, group_size, ctypes.byref(n)))
-    return int(n.value)
+    f = ctypes.c_size_t(0)
+    check("moe_route_topk_index_workspace_size",
+          lib().moe_route_topk_index_workspace_size(T, K, E, group_size, ctypes.byref(f)))
+    return max(int(n.value), int(f.value))
 
 
 def index_rows(T: int, K: int, E: int, capacity: int = 0, alignment: int = 0) -> int:
@@ -192,6 +196,37 @@ def build_index(topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor], num_expe
         _p(topk_idx), _p(topk_w), T, K, num_experts, capacity, group_size, alignment, ctypes.byref(s),
         _p(ws), ws.numel(), _stream()))
     return ix
+
+
+def route_topk_index(logits: torch.Tensor, k: int, capacity: int = 0, group_size: int = 0, alignment: int = 0,
+                     route_group_size: int = 0, topk_groups: int = 0, out=None, index: Optional[MoeIndex] = None):
+    """route_topk (group-limited when route_group_size > 0) followed by build_index, in one call
+    (moe_route_topk_index: the same arrays, bit for bit, with one launch fewer for large inputs).
+    Returns (topk_idx, topk_w, index)."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if out is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    else:
+        idx, w = out
+        _need(idx, "topk_idx", torch.int32, 2)
+        _need(w, "topk_w", torch.float32, 2)
+        if tuple(idx.shape) != (T, k) or tuple(w.shape) != (T, k):
+            raise ValueError("output shapes must be [T, k]")
+    ix = index if index is not None else alloc_index(T, k, E, capacity, group_size, logits.device, alignment)
+    if (ix.T, ix.K, ix.E, ix.capacity, ix.group_size, ix.alignment) != (T, k, E, capacity, group_size, alignment):
+        raise ValueError("preallocated index was made for other sizes")
+    if ix.counts.device != logits.device:
+        raise ValueError(f"preallocated index is on {ix.counts.device}, logits on {logits.device}")
+    ws = ix.workspace
+    if ws is None:
+        raise ValueError("this index was allocated without a workspace")
+    s = ix.struct()
+    check("moe_route_topk_index", lib().moe_route_topk_index(
+        _p(logits), T, E, k, route_group_size, topk_groups, _p(idx), _p(w), capacity, group_size, alignment,
+        ctypes.byref(s), _p(ws), ws.numel(), _stream()))
+    return idx, w, ix
 
 
 def build_index_noalloc(topk_idx: torch.Tensor, topk_w: Optional[torch.Tensor], num_experts: int,
