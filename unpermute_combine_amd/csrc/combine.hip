@@ -250,21 +250,23 @@ __device__ __forceinline__ void fma_batch_split(const Y *__restrict__ y, int64_t
 }
 
 // Stores the 8 results of one lane at elements e0.. and e0+256.. of row `o` (stores past the
-// resource's size, i.e. past H, are dropped by the hardware).
+// resource's size, i.e. past H, are dropped by the hardware), with cache policy POL.
+template <int POL = kPolicyNontemporal>
 __device__ __forceinline__ void store_parts(__amdgpu_buffer_rsrc_t o, int64_t e0, const float (&a)[8], uint16_t *)
 {
     __attribute__((ext_vector_type(2))) unsigned int lo = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
     __attribute__((ext_vector_type(2))) unsigned int hi = {pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
-    __builtin_amdgcn_raw_buffer_store_b64(lo, o, static_cast<int>(e0 * 2), 0, kPolicyNontemporal);
-    __builtin_amdgcn_raw_buffer_store_b64(hi, o, static_cast<int>((e0 + kUnit / 2) * 2), 0, kPolicyNontemporal);
+    __builtin_amdgcn_raw_buffer_store_b64(lo, o, static_cast<int>(e0 * 2), 0, POL);
+    __builtin_amdgcn_raw_buffer_store_b64(hi, o, static_cast<int>((e0 + kUnit / 2) * 2), 0, POL);
 }
 
+template <int POL = kPolicyNontemporal>
 __device__ __forceinline__ void store_parts(__amdgpu_buffer_rsrc_t o, int64_t e0, const float (&a)[8], float *)
 {
-    st16_buf<kPolicyNontemporal>(o, static_cast<uint32_t>(e0 * 4),
-                u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])});
-    st16_buf<kPolicyNontemporal>(o, static_cast<uint32_t>((e0 + kUnit / 2) * 4),
-                u32x4{__float_as_uint(a[4]), __float_as_uint(a[5]), __float_as_uint(a[6]), __float_as_uint(a[7])});
+    st16_buf<POL>(o, static_cast<uint32_t>(e0 * 4),
+                  u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])});
+    st16_buf<POL>(o, static_cast<uint32_t>((e0 + kUnit / 2) * 4),
+                  u32x4{__float_as_uint(a[4]), __float_as_uint(a[5]), __float_as_uint(a[6]), __float_as_uint(a[7])});
 }
 
 template <typename Y, typename O>
@@ -478,6 +480,14 @@ __global__ __launch_bounds__(kMaxThreads) void combine_batched_kernel(const uint
 }
 
 // ---------------------------------------------------------------- group pre-combine
+// Store policy of the partials: device-scope stores that keep the normal (temporal) cache policy.
+// Every store instruction covers whole lines (1 KiB of float32, 512 B of bf16), and measured with
+// caches flushed at T8192 H7168 (32 groups of 8) the pre-combine took 255 us against 284 us with
+// nontemporal or sc1|nt stores (264 us with plain or sc0 stores), the final sum that reads the
+// partials 138 instead of 131 us: the step 0.746 -> 0.732 ms. With bf16 partials the pre-combine
+// took 213 instead of 222 us and the final sum 70 instead of 73 us (step 0.627 -> 0.612 ms).
+constexpr int kPartialsStore = kPolicyDeviceStore;
+
 template <typename Y, typename P, bool VEC>
 __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__restrict__ y, int64_t y_rows, int64_t H,
                                                          const int32_t *__restrict__ row_of,
@@ -554,8 +564,9 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
                     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                     fma_parts<Y>(q, wv, take, acc);
                     const int32_t s = __builtin_amdgcn_readfirstlane(item_s[it]);
-                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * sizeof(P))), e0,
-                                acc, partials);
+                    store_parts<kPartialsStore>(
+                        make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * sizeof(P))), e0, acc,
+                        partials);
                 }
             }
         } else {
@@ -576,8 +587,9 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
                         fma_batch_split<Y>(y, H, row, w, e0, acc);
                     }
                     const int32_t s = __builtin_amdgcn_readfirstlane(item_s[it]);
-                    store_parts(make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * sizeof(P))), e0,
-                                acc, partials);
+                    store_parts<kPartialsStore>(
+                        make_rsrc(partials + static_cast<int64_t>(s) * H, static_cast<uint32_t>(H * sizeof(P))), e0, acc,
+                        partials);
                 }
             }
         }
@@ -627,6 +639,12 @@ __global__ __launch_bounds__(kMaxThreads) void precombine_kernel(const Y *__rest
 // dominant. Measured with caches flushed: T16384 H7168 K8 743 -> 697 us, T8192 H7168 (32 groups
 // of 8) 374 -> 356 us, T4096 H4096 K2 51.5 -> 47.5 us, drop-and-pad T8192 H4096 E128 195 -> 194 us;
 // two workgroups per token (four slots each, dout read by both) lost instead (804 and 259 us).
+// The dots pass runs first. It loads dout with the default policy and y with streaming loads, so
+// most of dout is still in the 256 MB MALL when the scatter reads it again: the scatter, whose
+// short waves wait on that read, then took 119 instead of 131 us at drop-and-pad T8192 H4096
+// E128 and 321 instead of 351 us at T16384 H7168 K8, the dots 2 and 12 us more than when they
+// came second (the call 174 -> 165 us and 644 -> 626 us; in group mode T8192 H7168 328 -> 319 us).
+// Running the dots concurrently on a second stream lost (197 against 180 us by the events).
 constexpr int kBwdZeroRowsPerWave = 16;
 
 template <bool SPLIT>
@@ -1000,18 +1018,20 @@ moe_status launch_combine_backward(const void *dout, const void *y, int64_t y_ro
     if constexpr (sizeof(D) == 2 && sizeof(Y) == 2 && sizeof(DY) == 2) {
         if (vec && K <= MOE_MAX_EXPERTS && H * 2 <= 0x7fffffffLL) {
             // bf16 rows: dy = w * dout is the weighted source-major scatter of dout through row_of
-            // (which also zero-fills the padding rows named by src_row), and dw is a second,
-            // read-only pass of dots; the two take their own best access patterns (see the section
-            // comment) instead of one kernel that loads, stores and reduces together
-            moe_status st = launch_scatter_vec16(static_cast<const char *>(dout), T, H * 2 / 16, row_of, K, src_row,
-                                                 y_rows, static_cast<char *>(dy), true, w, stream);
-            if (st != MOE_OK || !dw || T == 0)
-                return st;
-            const int threads = block_threads(H / 8, K <= kBatch ? 2 : 1);
-            hipLaunchKernelGGL((combine_backward_kernel<D, Y, DY, false, true, false>), dim3(static_cast<unsigned>(T)),
-                               dim3(threads), 0, stream, static_cast<const D *>(dout), static_cast<const Y *>(y), y_rows,
-                               H, row_of, w, K, T, nullptr, static_cast<DY *>(dy), dw);
-            return launch_status();
+            // (which also zero-fills the padding rows named by src_row), and dw is a read-only pass
+            // of dots launched before it; the two take their own best access patterns (see the
+            // section comment) instead of one kernel that loads, stores and reduces together
+            if (dw && T > 0) {  // the dots first: see the section comment
+                const int threads = block_threads(H / 8, K <= kBatch ? 2 : 1);
+                hipLaunchKernelGGL((combine_backward_kernel<D, Y, DY, false, true, false>), dim3(static_cast<unsigned>(T)),
+                                   dim3(threads), 0, stream, static_cast<const D *>(dout), static_cast<const Y *>(y),
+                                   y_rows, H, row_of, w, K, T, nullptr, static_cast<DY *>(dy), dw);
+                const moe_status st = launch_status();
+                if (st != MOE_OK)
+                    return st;
+            }
+            return launch_scatter_vec16(static_cast<const char *>(dout), T, H * 2 / 16, row_of, K, src_row, y_rows,
+                                        static_cast<char *>(dy), true, w, stream);
         }
     }
     // bf16 rows, at most kBatch slots: one thread per two chunks (taken one after the other);

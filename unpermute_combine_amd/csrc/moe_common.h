@@ -69,11 +69,13 @@ __device__ __forceinline__ void st16_stream(void *p, const u32x4 &v)
 //   kPolicyStreamStore = sc1|nt: agent-scope streaming store, written through the per-XCD L2
 //                        (measured: the expert-major permute writes at ~6.0 TB/s instead of ~5.4);
 //   kPolicyStreamLoad  = sc0|nt: streaming load of data read exactly once;
-//   kPolicyNontemporal = nt: streaming store at the default scope (the combine's and the
-//                        pre-combine's outputs, where sc1 measured no faster).
+//   kPolicyNontemporal = nt: streaming store at the default scope (the combine's outputs);
+//   kPolicyDeviceStore = sc1: agent-scope store with the normal cache policy (the pre-combine's
+//                        partials, which it writes 4-10% faster than with nt or sc1|nt).
 constexpr int kPolicyStreamLoad = 1 | 2;
 constexpr int kPolicyStreamStore = 16 | 2;
 constexpr int kPolicyNontemporal = 2;
+constexpr int kPolicyDeviceStore = 16;
 constexpr int kRsrcWord3 = 0x00020000;  // dword 3 of the resource: 32-bit data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
