@@ -335,14 +335,12 @@ struct CountArgs {
     int32_t *slot_of;   // [T][G]: -1 for the tile's tokens (index group mode)
 };
 
-template <int J, bool GROUPS>
+template <int J>
 __global__ __launch_bounds__(kFusedThreads) void route_count_kernel(const float *__restrict__ logits, int64_t T, int E,
-                                                                    int K, int gs, int M,
-                                                                    int32_t *__restrict__ topk_idx,
+                                                                    int K, int32_t *__restrict__ topk_idx,
                                                                     float *__restrict__ topk_w, CountArgs c)
 {
-    extern __shared__ uint32_t group_sh[];  // route group keys [kFusedTokens][E / gs], then the counts
-    int32_t *cnt = reinterpret_cast<int32_t *>(group_sh + (GROUPS ? kFusedTokens * (E / gs) : 0));
+    extern __shared__ int32_t cnt[];  // the tile's row of counts
     for (int i = threadIdx.x; i < c.Hp; i += kFusedThreads)
         cnt[i] = 0;
     __syncthreads();
@@ -350,7 +348,7 @@ __global__ __launch_bounds__(kFusedThreads) void route_count_kernel(const float 
     const int64_t t1 = min(T, t0 + c.tile_tokens);
     const TileCounts tc{cnt, cnt + c.Ep, c.idx_gs};
     for (int64_t tf = t0; tf < t1; tf += kFusedTokens)
-        route_pass<J, GROUPS, kFusedTokens, true>(logits, T, tf, t1, E, K, gs, M, topk_idx, topk_w, tc);
+        route_pass<J, false, kFusedTokens, true>(logits, T, tf, t1, E, K, 0, 0, topk_idx, topk_w, tc);
     if (c.idx_gs > 0) {  // slot_of starts as "absent" for this tile's tokens
         for (int64_t i = t0 * c.G + threadIdx.x; i < t1 * c.G; i += kFusedThreads)
             c.slot_of[i] = -1;
@@ -485,23 +483,14 @@ moe_status check_route(int64_t T, int32_t E, int32_t K, int32_t gs, int32_t M)
     return MOE_OK;
 }
 
-moe_status launch_route_count(const float *logits, int64_t T, int32_t E, int32_t K, int32_t gs, int32_t M,
-                              int32_t *topk_idx, float *topk_w, const CountArgs &c, hipStream_t stream)
+moe_status launch_route_count(const float *logits, int64_t T, int32_t E, int32_t K, int32_t *topk_idx, float *topk_w,
+                              const CountArgs &c, hipStream_t stream)
 {
-    const int64_t blocks = ceil_div(T, c.tile_tokens);
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kFusedThreads);
-    const size_t lds = (gs > 0 ? sizeof(uint32_t) * kFusedTokens * static_cast<size_t>(E / gs) : 0) +
-                       sizeof(int32_t) * static_cast<size_t>(c.Hp);
+    const dim3 grid(static_cast<unsigned>(ceil_div(T, c.tile_tokens))), block(kFusedThreads);
+    const size_t lds = sizeof(int32_t) * static_cast<size_t>(c.Hp);
     const int nj = static_cast<int>(ceil_div(E, kLanesPerToken));
-#define MOE_ROUTE_COUNT_LAUNCH(JJ)                                                                               \
-    do {                                                                                                         \
-        if (gs > 0)                                                                                              \
-            hipLaunchKernelGGL((route_count_kernel<JJ, true>), grid, block, lds, stream, logits, T, E, K, gs, M,     \
-                               topk_idx, topk_w, c);                                                             \
-        else                                                                                                     \
-            hipLaunchKernelGGL((route_count_kernel<JJ, false>), grid, block, lds, stream, logits, T, E, K, gs, M,    \
-                               topk_idx, topk_w, c);                                                             \
-    } while (0)
+#define MOE_ROUTE_COUNT_LAUNCH(JJ)                                                                                   \
+    hipLaunchKernelGGL((route_count_kernel<JJ>), grid, block, lds, stream, logits, T, E, K, topk_idx, topk_w, c)
     if (nj <= 1)
         MOE_ROUTE_COUNT_LAUNCH(1);
     else if (nj <= 2)
@@ -512,10 +501,8 @@ moe_status launch_route_count(const float *logits, int64_t T, int32_t E, int32_t
         MOE_ROUTE_COUNT_LAUNCH(8);
     else if (nj <= 16)
         MOE_ROUTE_COUNT_LAUNCH(16);
-    else if (nj <= 32)
-        MOE_ROUTE_COUNT_LAUNCH(32);
     else
-        MOE_ROUTE_COUNT_LAUNCH(64);
+        return MOE_ERR_UNSUPPORTED;  // more than 256 experts take the separate calls (use_fused)
 #undef MOE_ROUTE_COUNT_LAUNCH
     return launch_status();
 }
@@ -619,7 +606,7 @@ extern "C" moe_status moe_route_topk_index(const float *logits, int64_t T, int32
     c.Hp = c.Ep + (c.G > 0 ? ((c.G + 3) & ~3) : 0);
     c.hist = static_cast<int32_t *>(workspace);
     c.slot_of = out->slot_of;
-    if ((st = launch_route_count(logits, T, E, K, rgs, topk_groups, topk_idx, topk_w, c, stream)) != MOE_OK)
+    if ((st = launch_route_count(logits, T, E, K, topk_idx, topk_w, c, stream)) != MOE_OK)
         return st;
     return build_index_from_tile_counts(topk_idx, topk_w, T, K, E, capacity, group_size, alignment, out, workspace,
                                         workspace_bytes, c.tile_tokens, true, stream);
