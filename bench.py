@@ -149,11 +149,17 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: int, backward: bool = False, symbol: str = None, fp8: bool = False,
-                 bf16_partials: bool = False):
-    """HBM bytes per launch from a committed PMC summary; None if absent or stale."""
-    tag = (f"workload{workload}" + ("_bwd" if backward else "") + ("_fp8" if fp8 else "")
-           + ("_bf16p" if bf16_partials else ""))
+def profile_tag(workload: int, backward: bool = False, fp8: bool = False, bf16_partials: bool = False,
+                alignment: int = 0, route_groups: int = 0) -> str:
+    """The workload-and-mode part of a profiles/ file name, e.g. workload3_align128, workload4_bwd."""
+    return (f"workload{workload}" + (f"_align{alignment}" if alignment else "")
+            + (f"_groups{route_groups}" if route_groups else "") + ("_bwd" if backward else "")
+            + ("_fp8" if fp8 else "") + ("_bf16p" if bf16_partials else ""))
+
+
+def read_traffic(kernel: str, tag: str, symbol: str = None):
+    """HBM bytes per launch from the committed PMC summary of this workload and mode; None if
+    absent or stale."""
     path = os.path.join(ROOT, "profiles", f"{symbol or KERNEL_SYMBOLS[kernel]}__{tag}__pmc.txt")
     if not os.path.exists(path):
         return None
@@ -469,7 +475,8 @@ def main():
         kernel_name = "permute_scatter_vec16_kernel<true> (dy) + combine_backward_kernel (dw dots)"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic(dom, cid, args.backward, symbol, args.fp8, args.bf16_partials),
+                "traffic": read_traffic(dom, profile_tag(cid, args.backward, args.fp8, args.bf16_partials, align, rg),
+                                        symbol),
                 "kernel": kernel_name, "call": dom, "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kernel_us[dom], 2)}
 

@@ -61,3 +61,22 @@ def test_cpu_baseline_fp8_and_group_modes():
     for fp8, bf16p, rg in ((True, False, 0), (False, True, 4), (True, True, 4)):
         r = bench.cpu_baseline(c, key, logits, x, y, 0, 0, rg, 10 ** 7, bf16_partials=bf16p, fp8=fp8)
         assert r["value"] > 0 and ("FP8" in r["sample"]) == fp8
+
+
+def test_pmc_summary_names_follow_workload_and_mode():
+    """The roofline's traffic is read from the PMC summary of the same workload and mode: an
+    aligned or group-limited run does not pick up the plain workload's counters."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    assert bench.profile_tag(3) == "workload3"
+    assert bench.profile_tag(3, alignment=128) == "workload3_align128"
+    assert bench.profile_tag(4, route_groups=4) == "workload4_groups4"
+    assert bench.profile_tag(4, backward=True) == "workload4_bwd"
+    assert bench.profile_tag(4, fp8=True) == "workload4_fp8"
+    assert bench.profile_tag(4, bf16_partials=True) == "workload4_bf16p"
+    names = set(os.listdir(os.path.join(ROOT, "profiles")))
+    for f in names:
+        if f.endswith("__pmc.txt"):
+            tag = f.split("__")[1]
+            assert tag.startswith("workload"), f
