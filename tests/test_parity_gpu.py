@@ -1230,7 +1230,7 @@ def _check_dw(got, want, bound):
 @pytest.mark.parametrize("H,T,E,K,mode", [(7168, 130, 64, 8, "standard"), (1000, 200, 16, 4, "drop"),
                                           (5, 90, 8, 2, "holes"), (520, 150, 32, 8, "holes"), (8, 300, 8, 2, "drop"),
                                           (4096, 64, 128, 16, "standard"), (8, 1000, 16, 8, "standard"),
-                                          (1000, 300, 16, 5, "standard")])
+                                          (1000, 300, 16, 5, "standard"), (264, 70, 64, 32, "standard")])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_combine_backward(m, dts, H, T, E, K, mode, weighted):
     ddt, ydt, dydt = dts
