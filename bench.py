@@ -553,19 +553,33 @@ def cpu_baseline(c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16
         dout = wl.expert_outputs((*key, 7), T, H, c["dtype"])
         dxp = wl.expert_outputs((*key, 8), rows, H, c["dtype"])
 
-    def run_once(o):
+    def run_once(o, st):
+        """One pass; st[stage] collects the stage's seconds (route, index, dispatch, combine; or
+        combine_bwd, dispatch_bwd, route_bwd)."""
+        t = [time.perf_counter()]
+
+        def lap(stage):
+            now = time.perf_counter()
+            st.setdefault(stage, []).append(now - t[0])
+            t[0] = now
+
         if backward:
             _, dw = o.combine_backward(dout, y_b, ix0["row_of"], w0, out_dt)
+            lap("combine_bwd")
             if gs:
                 n = int(ix0["n_slots"][0])
                 part = o.group_precombine(dxp, ix0["row_of"], None, idx0, E, gs, ix0["slot_of"], n, out_dtype=part_dt)
                 o.unpermute_combine(part, ix0["slot_of"], None, out_dt)
             else:
                 o.unpermute_combine(dxp, ix0["row_of"], None, out_dt)
+            lap("dispatch_bwd")
             o.route_topk_backward(idx0, w0, dw, E)
+            lap("route_bwd")
             return
         idx, w = o.route_topk(logits_np, K, gs, rg)
+        lap("route")
         ix = oracle.build_index(idx, w, E, capacity=cap, group_size=gs, alignment=align)
+        lap("index")
         maps = [ix["gsrc"], ix["esrc"]] if gs else [ix["sorted_indices"]]  # group mode: send, then receive
         if fp8:
             xp = None
@@ -576,6 +590,7 @@ def cpu_baseline(c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16
             xp = x_np
             for mp in maps:
                 xp = o.permute(xp, mp)
+        lap("dispatch")
         y = xp if y_np is None else y_np
         if gs:
             n = int(ix["n_slots"][0])
@@ -583,21 +598,26 @@ def cpu_baseline(c, key, logits_np, x_np, y_np, cap, align, rg, step_bytes, bf16
             o.unpermute_combine(part, ix["slot_of"], None, out_dt)
         else:
             o.unpermute_combine(y, ix["row_of"], w, out_dt)
+        lap("combine")
 
+    def medians(st):
+        return {k: round(float(np.median(v)), 4) for k, v in st.items()}
+
+    st_all, st_one = {}, {}
     with Pool() as pool:
-        best, n, total = _passes(lambda: run_once(pool), min_seconds=4.0)
+        best, n, total = _passes(lambda: run_once(pool, st_all), min_seconds=4.0)
         threads = pool.threads
-    best1, n1, total1 = _passes(lambda: run_once(Serial()), min_seconds=6.0)
+    best1, n1, total1 = _passes(lambda: run_once(Serial(), st_one), min_seconds=6.0)
     what = ("the whole backward of the workload" if backward else "the whole workload") + f" ({c['name']}"
     what += (", FP8 dispatch" if fp8 else "") + (", bf16 partials" if bf16_partials else "") + ")"
     res = {"value": round(step_bytes / best / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
            "sample": f"{what} per pass, best of {n} passes ({total:.1f} s wall, {threads} threads); the "
                      f"oracle's per-token / per-row functions over disjoint slices, the index build in one call",
-           "seconds_per_pass": round(best, 3),
+           "seconds_per_pass": round(best, 3), "stage_seconds_median": medians(st_all),
            "host": {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "usable_cores": usable_cores(),
                     "threads_used": threads},
            "single_thread": {"value": round(step_bytes / best1 / 1e9, 3), "unit": "GB/s", "cores": 1,
-                             "seconds_per_pass": round(best1, 3),
+                             "seconds_per_pass": round(best1, 3), "stage_seconds_median": medians(st_one),
                              "sample": f"{what} per pass, best of {n1} passes ({total1:.1f} s)"}}
     if not backward:
         res["routed_tokens_per_s"] = round(T * K / best, 1)

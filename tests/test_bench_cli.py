@@ -46,6 +46,11 @@ def test_cpu_baseline_legs_on_the_host():
         assert r["kind"] == "oracle" and r["value"] > 0 and r["single_thread"]["value"] > 0
         assert 1 <= r["cores"] <= 16 and r["host"]["threads_used"] == r["cores"]
         assert r["host"]["nproc"] >= 1 and r["host"]["usable_cores"] >= 1 and r["host"]["cpu_model"]
+        stages = ("combine_bwd", "dispatch_bwd", "route_bwd") if backward else ("route", "index", "dispatch", "combine")
+        for leg in (r, r["single_thread"]):
+            st = leg["stage_seconds_median"]
+            assert tuple(st) == stages and all(v >= 0 for v in st.values())
+            assert sum(st.values()) <= 2 * leg["seconds_per_pass"] + 0.05
 
 
 def test_cpu_baseline_fp8_and_group_modes():
