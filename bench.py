@@ -497,6 +497,7 @@ def main():
         "kernel_us_median": {k: round(v, 2) for k, v in kernel_us_median.items()},
         "kernel_us_min": {k: round(v, 2) for k, v in kernel_us_min.items()},
         "kernel_gbs": {k: gbs(kbytes[k], kernel_us[k]) for k in hbm_kernels},
+        "kernel_gbs_median": {k: gbs(kbytes[k], kernel_us_median[k]) for k in hbm_kernels},
         "kernel_bytes": kbytes,
         "max_expert_count": int(counts.max()), "empty_experts": int((counts == 0).sum()),
         "roofline": roofline,
