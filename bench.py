@@ -15,10 +15,11 @@ neither the step's inputs nor its outputs -- so that no workload, however small,
 a cache (`--eager`: the eagerly launched steps, timed the same way). The same K replays
 back to back without flushes give `ms_per_step_warm`; K eager steps back to back give
 `ms_per_step_eager`. Per-kernel times (`kernel_us`: mean, with `kernel_us_median` and
-`kernel_us_min`) come from a separate eager pass in which every kernel call is flushed before
-and bracketed by events; `stage_us` sums them per stage; `roofline` describes the dominant
-HBM-bound kernel with its own mean event time; `cpu_baseline` is the CPU oracle on the same
-workload on this host, all usable cores (up to 16 threads) and one thread.
+`kernel_us_min`) come from K eager steps, each flushed before like the timed ones, with an event
+between consecutive calls, so that each call is timed where the step runs it; `stage_us` sums
+them per stage; `roofline` describes the dominant HBM-bound kernel with its own mean event time;
+`cpu_baseline` is the CPU oracle on the same workload on this host, all usable cores (up to 16
+threads) and one thread.
 """
 from __future__ import annotations
 
@@ -105,9 +106,9 @@ def parse_args():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (for scaling PMC byte counters)")
     p.add_argument("--no-warm", action="store_true",
-                   help="skip the back-to-back (unflushed) passes, so that every kernel launch after the "
-                        "warmup is preceded by a flush (for profiling runs whose per-kernel averages should "
-                        "match kernel_us)")
+                   help="skip the back-to-back (unflushed) passes, so that every step after the warmup "
+                        "is preceded by a flush (for profiling runs whose per-kernel averages should match "
+                        "kernel_us)")
     p.add_argument("--no-flush", action="store_true",
                    help="no cache flush before the timed steps and kernel calls (they still run one by one "
                         "between events)")
@@ -348,17 +349,20 @@ def main():
         torch.cuda.synchronize()
         ms_per_step_eager = (time.perf_counter() - t_start) * 1e3 / args.steps
 
-    # per-kernel times: every call flushed before and bracketed by events on its stream
-    kev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-           for _ in range(args.steps)]
+    # per-call times: K eager steps, each after one flush (as in the timed steps), the calls back to
+    # back with an event between consecutive calls, so that every call runs where the step runs it:
+    # after the previous call, not after a flush of its own (a flush between calls would absorb the
+    # write-back that one call leaves to the next, e.g. the pre-combine's partials before the final
+    # sum: 134 us flushed against 149 us in the step)
+    sev_in = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s_ in range(args.steps):
+        if flush is not None:
+            flush()
+        sev_in[s_][0].record()
         for i, (_, _, call) in enumerate(calls):
-            if flush is not None:
-                flush()
-            kev[s_][i][0].record()
             call()
-            kev[s_][i][1].record()
+            sev_in[s_][i + 1].record()
     torch.cuda.synchronize()
 
     def timed_steps(run_step):
@@ -412,7 +416,7 @@ def main():
     kernel_us, kernel_us_median, kernel_us_min = {}, {}, {}
     for i, (name, _, _) in enumerate(calls):
         kernel_us[name], kernel_us_median[name], kernel_us_min[name] = _stats(
-            [kev[s_][i][0].elapsed_time(kev[s_][i][1]) * 1e3 for s_ in range(args.steps)])
+            [sev_in[s_][i].elapsed_time(sev_in[s_][i + 1]) * 1e3 for s_ in range(args.steps)])
     stage_us = {}
     for name, stage, _ in calls:
         stage_us[stage] = stage_us.get(stage, 0.0) + kernel_us[name]
@@ -505,9 +509,10 @@ def main():
     if args.backward:
         result["pass"] = "backward"
     result["launch"] = launch
-    result["timing"] = (("each step and each kernel call preceded by a 512 MiB write + 512 MiB read cache flush "
-                         "outside its events" if flush is not None else "no cache flush") +
-                        "; ms_per_step = mean of the per-step event times")
+    result["timing"] = (("each step preceded by a 512 MiB write + 512 MiB read cache flush outside its events"
+                         if flush is not None else "no cache flush") +
+                        "; ms_per_step = mean of the per-step event times; kernel_us = per-call event times "
+                        "inside such steps (eager launches, an event between consecutive calls)")
     result["ms_per_step_median"] = round(ms_per_step_median, 4)
     result["ms_per_step_min"] = round(ms_per_step_min, 4)
     result["ms_per_step_warm"] = None if ms_per_step_warm is None else round(ms_per_step_warm, 4)
