@@ -105,6 +105,9 @@ def parse_args():
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    p.add_argument("--stream-ceiling", action="store_true",
+                   help="only time plain device streams (torch's 1 GiB device copy, a 2 GiB fill, a 2 GiB "
+                        "reduction read) under the same flush protocol, as the chip's practical ceilings")
     p.add_argument("--no-warm", action="store_true",
                    help="skip the back-to-back (unflushed) passes, so that every step after the warmup "
                         "is preceded by a flush (for profiling runs whose per-kernel averages should match "
@@ -190,6 +193,39 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
+def stream_ceiling(torch, steps: int):
+    """Plain streams timed like the path's kernels (each after a cache flush, HIP events around
+    it): the rates a kernel that only copies, only writes or only reads reaches on this chip."""
+    flush = CacheFlush(torch)
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    c = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    d = torch.ones((2 << 30) // 4, dtype=torch.float32, device="cuda")
+    streams = [("copy_1GiB", 2 << 30, lambda: b.copy_(a)), ("fill_2GiB", 2 << 30, lambda: c.fill_(3)),
+               ("sum_read_2GiB", 2 << 30, lambda: d.sum())]
+    out = {}
+    for name, nbytes, fn in streams:
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        mean, med, mn = _stats(ts)
+        out[name] = {"bytes": nbytes, "us_median": round(med, 1), "us_min": round(mn, 1),
+                     "gbs_median": round(nbytes / (med * 1e-6) / 1e9, 1),
+                     "pct_of_peak": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    print(json.dumps({"stream_ceiling": out, "steps": steps,
+                      "timing": "each stream after a 512 MiB write + 512 MiB read flush, HIP events around it"}),
+          flush=True)
+
+
 def to_dev(torch, a):
     import numpy as np
     if a.dtype == np.uint16:
@@ -212,6 +248,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.stream_ceiling:
+        stream_ceiling(torch, args.steps)
         return
 
     import unpermute_combine_amd as m

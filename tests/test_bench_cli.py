@@ -27,7 +27,8 @@ def test_help_lists_the_options():
 
 
 def test_help_lists_the_flush_option():
-    assert "--no-flush" in _run("--help").stdout
+    out = _run("--help").stdout
+    assert "--no-flush" in out and "--stream-ceiling" in out
 
 
 def test_cpu_baseline_legs_on_the_host():
