@@ -7,13 +7,15 @@ unpermute_combine (expert outputs back to token order, weighted). In group mode 
 the two-stage dedup dispatch and the combine is the per-group pre-combine plus the final sum.
 
 Prints ONE JSON line. `value` is the whole step's algorithmic bytes (each stage's minimal HBM
-traffic, computed from the actual routing) divided by the measured step time: by default the
-mean of K replays of the step captured once in a HIP graph, each replay timed by HIP events on
-its stream and preceded (outside the events) by a cache flush -- 512 MiB written, then another
-512 MiB read, which leaves the 256 MB MALL and every XCD's L2 holding only clean lines of
-neither the step's inputs nor its outputs -- so that no workload, however small, is served from
-a cache (`--eager`: the eagerly launched steps, timed the same way). The same K replays
-back to back without flushes give `ms_per_step_warm`; K eager steps back to back give
+traffic, computed from the actual routing) divided by the measured step time: the mean of K
+steps, each timed by HIP events on its stream and preceded (outside the events) by a cache
+flush -- 512 MiB written, then another 512 MiB read, which leaves the 256 MB MALL and every
+XCD's L2 holding only clean lines of neither the step's inputs nor its outputs -- so that no
+workload, however small, is served from a cache. The step is launched eagerly (its calls
+enqueued behind the flush); the same step captured once in a HIP graph and replayed is timed
+the same way (`ms_per_step_by_launch`; `--graph` reports the replays as `value`): on this
+runtime a replay starts later after the flush than eager launches queued behind it. The graph
+replays back to back without flushes give `ms_per_step_warm`; K eager steps back to back give
 `ms_per_step_eager`. Per-kernel times (`kernel_us`: mean, with `kernel_us_median` and
 `kernel_us_min`) come from K eager steps, each flushed before like the timed ones, with an event
 between consecutive calls, so that each call is timed where the step runs it; `stage_us` sums
@@ -97,10 +99,11 @@ def parse_args():
     p.add_argument("--fp8", action="store_true",
                    help="FP8 dispatch: the permute quantizes x to E4M3 codes with one float32 scale per 128 "
                         "elements and moves codes and scales (the combine stays bf16)")
-    p.add_argument("--eager", action="store_true",
-                   help="time the eagerly launched steps only; by default the step is also captured once in a "
-                        "HIP graph and value / ms_per_step come from K replays of it (per-kernel times always "
-                        "come from an eager pass)")
+    p.add_argument("--graph", action="store_true",
+                   help="report the step replayed from a HIP graph (captured once) as value / ms_per_step; by "
+                        "default both launch modes are timed and value comes from the eager launches, which are "
+                        "faster on this runtime (ms_per_step_by_launch gives both)")
+    p.add_argument("--no-graph", action="store_true", help="skip the HIP graph capture and its timing")
     p.add_argument("--backward", action="store_true",
                    help="time the backward of the path (on one saved forward index) instead of the forward")
     p.add_argument("--copy-calibration", action="store_true",
@@ -418,10 +421,12 @@ def main():
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in sev]
 
-    launch = "eager"
+    # the step launched eagerly: every call enqueued on the current stream behind the flush
+    eager_ms = timed_steps(step)
+    graph_ms = None
+    graph_note = "not timed (--no-graph)"
     ms_per_step_warm = ms_per_step_eager
-    replay = step
-    if not args.eager:
+    if not args.no_graph:
         # the same calls captured once; no call allocates, waits on the host or records a memset
         try:
             graph = torch.cuda.CUDAGraph()
@@ -435,22 +440,26 @@ def main():
         except RuntimeError as e:  # report the eager timing rather than nothing
             log(f"[bench] HIP graph capture failed, timing eager steps only: {e}")
             torch.cuda.synchronize()
-            launch = f"eager (graph capture failed: {type(e).__name__})"
+            graph_note = f"graph capture failed: {type(e).__name__}"
         else:
-            replay = graph.replay
             for _ in range(max(3, args.warmup)):
                 if flush is not None:
                     flush()
-                replay()
+                graph.replay()
             torch.cuda.synchronize()
             if not args.no_warm:
                 t_start = time.perf_counter()
                 for _ in range(args.steps):
-                    replay()
+                    graph.replay()
                 torch.cuda.synchronize()
                 ms_per_step_warm = (time.perf_counter() - t_start) * 1e3 / args.steps
-            launch = "hip graph replay"
-    step_ms = timed_steps(replay)
+            graph_ms = timed_steps(graph.replay)
+            graph_note = None
+    if args.graph and graph_ms is not None:
+        step_ms, launch = graph_ms, "hip graph replay"
+    else:
+        step_ms = eager_ms
+        launch = "eager" if graph_note is None or not args.graph else f"eager ({graph_note})"
     ms_per_step, ms_per_step_median, ms_per_step_min = _stats(step_ms)
     kernel_us, kernel_us_median, kernel_us_min = {}, {}, {}
     for i, (name, _, _) in enumerate(calls):
@@ -548,6 +557,9 @@ def main():
     if args.backward:
         result["pass"] = "backward"
     result["launch"] = launch
+    result["ms_per_step_by_launch"] = {
+        "eager": round(_stats(eager_ms)[0], 4),
+        "hip graph replay": None if graph_ms is None else round(_stats(graph_ms)[0], 4)}
     result["timing"] = (("each step preceded by a 512 MiB write + 512 MiB read cache flush outside its events"
                          if flush is not None else "no cache flush") +
                         "; ms_per_step = mean of the per-step event times; kernel_us = per-call event times "

@@ -22,7 +22,8 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_the_options():
     r = _run("--help")
     assert r.returncode == 0
-    for opt in ("--steps", "--warmup", "--workload", "--alignment", "--route-groups", "--fp8", "--backward", "--eager", "--bf16-partials"):
+    for opt in ("--steps", "--warmup", "--workload", "--alignment", "--route-groups", "--fp8", "--backward", "--graph",
+                "--no-graph", "--bf16-partials"):
         assert opt in r.stdout
 
 
