@@ -1,8 +1,11 @@
-"""bench.py's contract on the host: more than one GPU is refused with a message (the library
-has no multi-GPU path; the bench measures one GPU); the help text lists the workload options."""
+"""bench.py's contract: on the host, more than one GPU is refused with a message (the library
+has no multi-GPU path; the bench measures one GPU), the help text lists the workload options and
+the CPU baseline legs report per stage; on the GPU, a short run prints the JSON line."""
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -87,3 +90,25 @@ def test_pmc_summary_names_follow_workload_and_mode():
         if f.endswith("__pmc.txt"):
             tag = f.split("__")[1]
             assert tag.startswith("workload"), f
+
+
+@pytest.mark.gpu
+def test_bench_line_on_the_gpu():
+    """A short bench run (workload 1, forward and backward) prints one JSON line with the fields
+    the bench contract names, both launch modes timed and a roofline on a named call."""
+    import json
+    for extra in ((), ("--backward",)):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "1", "--steps", "3",
+                            "--warmup", "1", "--no-cpu-baseline", *extra], capture_output=True, text=True, timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        assert len(lines) == 1
+        d = json.loads(lines[0])
+        for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+                  "vs_baseline", "dtype", "data", "config", "roofline"):
+            assert k in d, k
+        assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
+        assert d["config"]["workload"] and d["launch"] == "eager"
+        assert set(d["ms_per_step_by_launch"]) == {"eager", "hip graph replay"}
+        rf = d["roofline"]
+        assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and 0 < rf["frac"] < 1 and rf["call"] in d["kernel_us"]
