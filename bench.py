@@ -89,6 +89,9 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=3, help="named workload id (see workloads.py)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=None,
+                   help="draw the workload's inputs from another seed (same shapes and distributions); by "
+                        "default each named workload has its one fixed draw")
     p.add_argument("--alignment", type=int, default=0,
                    help="round every expert segment up to a multiple of this many rows (padding rows)")
     p.add_argument("--route-groups", type=int, default=0,
@@ -267,7 +270,7 @@ def main():
     cap = m.expert_capacity(T, K, E, *c["cf"]) if c["cf"] else 0
     b = 2 if dt == "bf16" else 4
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
-    key = wl.workload_key(cid)
+    key = wl.workload_key(cid, args.seed)
 
     t0 = time.time()
     logits_np = wl.router_logits(key, T, E, zipf_s=c["zipf_s"])

@@ -26,7 +26,7 @@ def test_help_lists_the_options():
     r = _run("--help")
     assert r.returncode == 0
     for opt in ("--steps", "--warmup", "--workload", "--alignment", "--route-groups", "--fp8", "--backward", "--graph",
-                "--no-graph", "--bf16-partials"):
+                "--no-graph", "--bf16-partials", "--seed"):
         assert opt in r.stdout
 
 

@@ -33,3 +33,16 @@ def test_zipf_bias_skews_low_ids():
     b = wl.zipf_bias(256, 1.2)
     assert b.dtype == np.float32 and (np.diff(b) < 0).all()
     assert np.isclose(np.exp(b.astype(np.float64)).sum(), 1.0, rtol=1e-6)
+
+
+def test_seeded_workload_keys_are_distinct():
+    """--seed draws other inputs of the same shapes: keys differ from the fixed draw, from each
+    other and from the test-case keys."""
+    import workloads as wl
+    assert wl.workload_key(3) == (3,)
+    ks = {wl.workload_key(3, s) for s in range(5)}
+    assert len(ks) == 5 and (3,) not in ks and all(k[0] == 3 for k in ks)
+    assert all(k[0] != 1000 for k in ks)  # test cases use (1000, ...)
+    a = wl.router_logits(wl.workload_key(1, 0), 64, 8)
+    b = wl.router_logits(wl.workload_key(1), 64, 8)
+    assert a.shape == b.shape and not (a == b).all()

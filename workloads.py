@@ -131,8 +131,10 @@ def expert_outputs(key: tuple, rows: int, H: int, dtype: str) -> np.ndarray:
     return _normal_blocks(key, STREAM_EXPERT_OUT, rows, H, _as_dtype(dtype))
 
 
-def workload_key(cfg_id: int) -> tuple:
-    return (int(cfg_id),)
+def workload_key(cfg_id: int, seed=None) -> tuple:
+    """Key of a named workload: (cfg_id,) for its fixed draw, (cfg_id, 2000 + seed) for another
+    draw of the same shapes and distributions (disjoint from the fixed keys and the test cases)."""
+    return (int(cfg_id),) if seed is None else (int(cfg_id), 2000 + int(seed))
 
 
 def case_key(*case: int) -> tuple:
