@@ -55,15 +55,13 @@ _BWD_SRC = ["unpermute_combine_amd/csrc/combine.hip", "unpermute_combine_amd/csr
 KERNEL_SOURCES = {"permute": _PERMUTE_SRC, "combine": _COMBINE_SRC, "dispatch_send": _PERMUTE_SRC,
                   "dispatch_recv": _PERMUTE_SRC, "precombine": _COMBINE_SRC, "final_sum": _COMBINE_SRC,
                   "combine_bwd": _BWD_SRC, "dispatch_bwd": _COMBINE_SRC, "dispatch_bwd_recv": _COMBINE_SRC,
-                  "dispatch_bwd_send": _COMBINE_SRC, "permute_fp8": _FP8_SRC, "dispatch_send_fp8": _FP8_SRC,
-                  "dispatch_recv_scales": _PERMUTE_SRC}
+                  "dispatch_bwd_send": _COMBINE_SRC, "permute_fp8": _FP8_SRC, "dispatch_send_fp8": _FP8_SRC}
 KERNEL_SYMBOLS = {"permute": "permute_scatter_vec16_kernel", "combine": "combine_kernel",
                   "dispatch_send": "permute_scatter_vec16_kernel", "dispatch_recv": "permute_grouped_vec16_kernel",
                   "precombine": "precombine_kernel", "final_sum": "combine_kernel",
                   "combine_bwd": "combine_backward_kernel", "dispatch_bwd": "combine_kernel",
                   "dispatch_bwd_recv": "precombine_kernel", "dispatch_bwd_send": "combine_kernel",
-                  "permute_fp8": "permute_scatter_fp8_kernel", "dispatch_send_fp8": "permute_scatter_fp8_kernel",
-                  "dispatch_recv_scales": "permute_grouped_vec16_kernel"}
+                  "permute_fp8": "permute_scatter_fp8_kernel", "dispatch_send_fp8": "permute_scatter_fp8_kernel"}
 
 
 def combine_symbol(y_bf16: bool, out_bf16: bool, K: int, H: int, T: int) -> str:
@@ -347,10 +345,8 @@ def main():
     elif args.fp8 and gs:
         calls += [("dispatch_send_fp8", "permute",
                    lambda: m.permute_scatter_fp8(x, ix.slot_of, gq.shape[0], fp8_block, out=(gq, gsc))),
-                  ("dispatch_recv", "permute", lambda: m.permute_grouped(gq, ix.esrc, ix.row_of, out=xq,
-                                                                         src_of=ix.slot_src)),
-                  ("dispatch_recv_scales", "permute", lambda: m.permute_grouped(gsc, ix.esrc, ix.row_of, out=xs,
-                                                                                src_of=ix.slot_src)),
+                  ("dispatch_recv", "permute", lambda: m.permute_grouped_fp8(gq, gsc, ix.esrc, ix.row_of,
+                                                                             out=(xq, xs), src_of=ix.slot_src)),
                   ("precombine", "combine",
                    lambda: m.group_precombine(src, ix.row_of, gw, gi, E, gs, ix.slot_of, out=part)),
                   ("final_sum", "combine", lambda: m.unpermute_combine(part, ix.slot_of, None, out=out))]
@@ -491,8 +487,7 @@ def main():
     elif args.fp8 and gs:
         n = int(ix.n_slots.item())
         kbytes.update(dispatch_send_fp8=routed * H * b + n * 4 + n * (H + nb * 4),
-                      dispatch_recv=n * H + rows * 4 + used * H,
-                      dispatch_recv_scales=n * nb * 4 + rows * 4 + used * nb * 4,
+                      dispatch_recv=n * (H + nb * 4) + rows * 4 + used * (H + nb * 4),
                       precombine=valid * H * b + 2 * T * K * 4 + n * H * pb,
                       final_sum=n * H * pb + T * G * 4 + T * H * b)
     elif args.fp8:

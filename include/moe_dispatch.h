@@ -297,6 +297,23 @@ moe_status moe_permute_scatter_fp8(const void *src, moe_dtype src_dt, int64_t sr
                                    const int32_t *dst_of, int32_t J, const int32_t *src_row, int64_t N, uint8_t *dst,
                                    float *dst_scales, hipStream_t stream);
 
+/* The receive side of the FP8 group dispatch: FP8 rows and their scale rows moved together, in one
+ * launch ([Combine] §3 and the DeepEP dispatch call in [Megatron]: the codes travel with their
+ * scales; [CANN] §1(1), [Scratch] §11-12: group slots back to expert-major rows). Bit for bit
+ * moe_permute_grouped of the codes (MOE_FP8_E4M3 rows of H bytes) followed by moe_permute_grouped
+ * of the scales (float32 rows of H / block values) with the same src_row, dst_of and src_of:
+ * every listed row gets its source's codes and scales, every row whose src_row lies outside
+ * [0, src_rows) (MOE_ROW_UNUSED excepted) gets zero codes and zero scales.
+ *   src [src_rows, H] codes, src_scales [src_rows, H/block] float32, dst [N, H], dst_scales
+ *   [N, H/block]; block >= 1 must divide H (else MOE_ERR_INVALID); the other arguments, limits
+ *   and errors as in moe_permute_grouped. The group dispatch's receive:
+ *   moe_permute_grouped_fp8(codes, scales, ..., moe_index.esrc, R, moe_index.row_of, T, K,
+ *   moe_index.slot_src, ...) after moe_permute_scatter_fp8 over moe_index.slot_of. */
+moe_status moe_permute_grouped_fp8(const uint8_t *src, const float *src_scales, int64_t src_rows, int64_t H,
+                                   int32_t block, const int32_t *src_row, int64_t N, const int32_t *dst_of,
+                                   int64_t M, int32_t J, const int32_t *src_of, uint8_t *dst, float *dst_scales,
+                                   hipStream_t stream);
+
 /* Unpermute + weighted top-k merge ([Combine] §1: out[t] = sum over the token's top-k experts
  * of probs[t,e] * expert_e(x[t]); [Scratch] §13, §16):
  *   out[t, :] = sum_{k = 0..K-1, row_of[t,k] in [0, y_rows)} w[t,k] * y[row_of[t,k], :]

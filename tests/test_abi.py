@@ -100,6 +100,21 @@ def test_argument_errors_return_before_any_launch(capi):
     assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, None, 2, 2, None, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute_grouped(fake, 4, 8, 1, fake, 4, fake, -1, 2, None, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_permute_grouped(None, 0, 8, 1, None, 0, None, 0, 2, None, None, None) == capi.MOE_OK
+    # the FP8 group receive: block must divide H, the scale buffers are needed, the rest as moe_permute_grouped
+    assert lib.moe_permute_grouped_fp8(fake, fake, 4, 100, 30, fake, 4, fake, 2, 2, None, fake, fake, None) == \
+        capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped_fp8(fake, fake, 4, 128, 0, fake, 4, fake, 2, 2, None, fake, fake, None) == \
+        capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped_fp8(fake, None, 4, 128, 128, fake, 4, fake, 2, 2, None, fake, fake, None) == \
+        capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped_fp8(fake, fake, 4, 128, 128, fake, 4, fake, 2, 2, None, fake, None, None) == \
+        capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped_fp8(fake, fake, 4, 128, 128, fake, 4, fake, 2, 65, None, fake, fake, None) == \
+        capi.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_grouped_fp8(fake, fake, 4, 128, 128, None, 4, fake, 2, 2, None, fake, fake, None) == \
+        capi.MOE_ERR_INVALID
+    assert lib.moe_permute_grouped_fp8(None, None, 0, 128, 128, None, 0, None, 0, 2, None, None, None, None) == \
+        capi.MOE_OK
     assert lib.moe_route_topk_backward(fake, fake, fake, 4, 8, 9, fake, None) == capi.MOE_ERR_INVALID
     assert lib.moe_route_topk_backward(fake, fake, fake, 4, 2048, 2, fake, None) == capi.MOE_ERR_UNSUPPORTED
     assert lib.moe_route_topk_backward(fake, None, fake, 4, 8, 2, fake, None) == capi.MOE_ERR_INVALID

@@ -421,6 +421,56 @@ def test_permute_grouped_random_maps(m, dtype, H, J):
         assert np.array_equal(got[~sel], poison[~sel]), "rows never listed must be left untouched"
 
 
+@pytest.mark.parametrize("H,block,J", [(16, 8, 8), (7168, 128, 8), (1024, 8, 3), (24, 8, 64), (8192, 8, 16),
+                                       (4096, 4096, 1), (448, 64, 5)])
+def test_permute_grouped_fp8_random_maps(m, H, block, J):
+    """The FP8 group receive moves codes and scale rows together: listed rows get their source's
+    codes and scales, zero rows zero codes and zero scales, unlisted rows stay untouched -- the
+    oracle's gather of both, as two moe_permute_grouped calls give it (scale rows of 1 to 1024
+    floats; H = 24 takes the element-wise path)."""
+    say(f"permute_grouped_fp8 random H={H} block={block} J={J}")
+    key = wl.case_key(36, H, block, J)
+    g = np.random.default_rng([*key, 3])
+    src_rows, N, nb = 83, 500, H // block
+    q = g.integers(0, 256, size=(src_rows, H), dtype=np.uint8)
+    sc = g.standard_normal((src_rows, nb), dtype=np.float32)
+    src_row = g.integers(0, src_rows, size=N).astype(np.int32)
+    src_row[g.random(N) < 0.1] = -1
+    src_row[:4] = [src_rows, -5, src_rows - 1, -2]  # out of range, padding, last row, unused
+    rows = g.permutation(N + 30)  # entries >= N are ignored
+    M = (len(rows) * 3 // 4 + J - 1) // J
+    dst_of = np.full(M * J, -1, np.int64)
+    dst_of[: len(rows) * 3 // 4] = rows[: len(rows) * 3 // 4]
+    dst_of = dst_of.reshape(M, J)
+    if J > 1:
+        dst_of[0, 1] = dst_of[0, 0]  # a row listed twice
+    for i in range(0, M, 5):  # rows of one group naming one source
+        live = dst_of[i][(dst_of[i] >= 0) & (dst_of[i] < N)]
+        src_row[live] = src_row[live[0]] if len(live) else 0
+    dst_of = dst_of.astype(np.int32)
+    listed = np.zeros(N, bool)
+    listed[dst_of[(dst_of >= 0) & (dst_of < N)]] = True
+    zero = ((src_row < 0) | (src_row >= src_rows)) & (src_row != -2)
+    want_q, want_s = oracle.permute(q, src_row), oracle.permute(sc, src_row)
+    src_of = np.where((dst_of >= 0) & (dst_of < N), src_row[np.clip(dst_of, 0, N - 1)], 777).astype(np.int32)
+    sel = (listed | zero) & (src_row != -2)  # unused rows are never written, listed or not
+    for so in (None, src_of):
+        oq = dev(np.full((N, H), 0xA5, np.uint8))
+        os_ = dev(np.full((N, nb), np.float32(-7.25)))
+        rq, rs = m.permute_grouped_fp8(dev(q), dev(sc), dev(src_row), dev(dst_of), out=(oq, os_),
+                                       src_of=None if so is None else dev(so))
+        gq, gs_ = host(rq), host(rs)
+        assert_exact(gq[sel], want_q[sel], "codes of listed and zero rows")
+        assert_exact(gs_[sel].view(np.uint32), want_s[sel].view(np.uint32), "scales of listed and zero rows")
+        assert (gq[~sel] == 0xA5).all() and (gs_[~sel] == np.float32(-7.25)).all(), "unlisted rows untouched"
+        # the same as the two separate grouped gathers
+        tq = host(m.permute_grouped(dev(q), dev(src_row), dev(dst_of), out=dev(np.full((N, H), 0xA5, np.uint8)),
+                                    src_of=None if so is None else dev(so)))
+        ts = host(m.permute_grouped(dev(sc), dev(src_row), dev(dst_of),
+                                    out=dev(np.full((N, nb), np.float32(-7.25))), src_of=None if so is None else dev(so)))
+        assert np.array_equal(gq, tq) and np.array_equal(gs_.view(np.uint32), ts.view(np.uint32))
+
+
 def test_permute_grouped_without_groups_writes_zero_rows(m):
     x = wl.hidden_states(wl.case_key(32), 4, 16, "bf16")
     src_row = np.asarray([-1, 2, 9, -1], np.int32)
@@ -878,8 +928,7 @@ def run_workload(m, cfg_id, align=0, route_groups=0, fp8=False, bf16_partials=Fa
             want_gq, want_gs = oracle.permute(qs, want["gsrc"]), oracle.permute(ss, want["gsrc"])
             assert_rows_exact(gq[:n], want_gq, "FP8 group-slot codes")
             assert_rows_exact(gsc[:n], want_gs, "FP8 group-slot scales")
-            xq = m.permute_grouped(gq, ix.esrc, ix.row_of, src_of=ix.slot_src)
-            xs = m.permute_grouped(gsc, ix.esrc, ix.row_of, src_of=ix.slot_src)
+            xq, xs = m.permute_grouped_fp8(gq, gsc, ix.esrc, ix.row_of, src_of=ix.slot_src)
             want_xq, want_xs = oracle.permute(want_gq, want["esrc"]), oracle.permute(want_gs, want["esrc"])
             del gq, gsc, want_gq, want_gs
         else:
@@ -1026,8 +1075,7 @@ def test_step_replays_from_a_hip_graph(m, cfg_id, mode):
                            topk_groups=rg, out=(gi, gw), index=ix)
         if mode == "fp8" and gs:
             m.permute_scatter_fp8(x, ix.slot_of, slots, block, out=(gq, gsc))
-            m.permute_grouped(gq, ix.esrc, ix.row_of, out=outs["xp"], src_of=ix.slot_src)
-            m.permute_grouped(gsc, ix.esrc, ix.row_of, out=outs["xs"], src_of=ix.slot_src)
+            m.permute_grouped_fp8(gq, gsc, ix.esrc, ix.row_of, out=(outs["xp"], outs["xs"]), src_of=ix.slot_src)
         elif mode == "fp8":
             m.permute_scatter_fp8(x, ix.row_of, rows, block, src_row=ix.sorted_indices,
                                   out=(outs["xp"], outs["xs"]))
@@ -1367,8 +1415,11 @@ def test_random_configuration_fp8(m, i):
         q, sc = m.permute_scatter_fp8(dev(x), ix.slot_of, slots, block)
         assert_exact(host(q)[:n], oracle.permute(qs, want["gsrc"]), "slot codes")
         assert_exact(host(sc)[:n], oracle.permute(ss, want["gsrc"]), "slot scales")
-        rq = host(m.permute_grouped(q, ix.esrc, ix.row_of))
-        rs = host(m.permute_grouped(sc, ix.esrc, ix.row_of))
+        if i % 2:  # the fused receive, or the codes and scales moved one after the other
+            rq, rs = (host(a) for a in m.permute_grouped_fp8(q, sc, ix.esrc, ix.row_of))
+        else:
+            rq = host(m.permute_grouped(q, ix.esrc, ix.row_of))
+            rs = host(m.permute_grouped(sc, ix.esrc, ix.row_of))
     else:
         q, sc = m.permute_scatter_fp8(dev(x), ix.row_of, ix.rows, block, src_row=ix.sorted_indices)
         rq, rs = host(q), host(sc)

@@ -40,6 +40,7 @@ SIGNATURES = {
     "moe_quantize_fp8": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _i32, _P, _P, _P]),
     "moe_permute_scatter_fp8": (ctypes.c_int, [_P, ctypes.c_int, _i64, _i64, _i32, _P, _i32, _P, _i64, _P, _P, _P]),
     "moe_permute_grouped": (ctypes.c_int, [_P, _i64, _i64, ctypes.c_int, _P, _i64, _P, _i64, _i32, _P, _P, _P]),
+    "moe_permute_grouped_fp8": (ctypes.c_int, [_P, _P, _i64, _i64, _i32, _P, _i64, _P, _i64, _i32, _P, _P, _P, _P]),
     "moe_unpermute_combine_backward": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, _i64, _i64, _P, _P, _i64,
                                                       _i32, _P, _P, ctypes.c_int, _P, _P]),
     "moe_route_topk_backward": (ctypes.c_int, [_P, _P, _P, _i64, _i32, _i32, _P, _P]),

@@ -157,10 +157,12 @@ constexpr int kMaxScatterDests = MOE_MAX_EXPERTS;  // dst_of columns (e.g. one p
 constexpr int kMaxGroupDests = kWave;               // destinations of one group of the grouped gather
 
 // Zero-fills rows first .. first+zr-1 whose src_row entry asks for a zero row (one wavefront;
-// no-op without a gather map). zr <= 64.
+// no-op without a gather map), and the same rows of the companion rows dst2 (nw2 4-byte words
+// each; none when nw2 is 0). zr <= 64.
 __device__ __forceinline__ void zero_rows_wave(int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
                                                int64_t N, int64_t first, char *__restrict__ dst,
-                                               int zr = kZeroRowsPerWave)
+                                               int zr = kZeroRowsPerWave, char *__restrict__ dst2 = nullptr,
+                                               int nw2 = 0)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
@@ -174,6 +176,12 @@ __device__ __forceinline__ void zero_rows_wave(int64_t src_rows, int64_t nvec, c
         const __amdgpu_buffer_rsrc_t d = make_rsrc(dst + (first + j) * row_bytes, static_cast<uint32_t>(row_bytes));
         for (int64_t v = lane; v < nvec; v += kWave)
             st16_buf<kPolicyStreamStore>(d, static_cast<uint32_t>(v * 16), z);
+        if (nw2 > 0) {
+            const uint32_t rb2 = static_cast<uint32_t>(nw2) * 4u;
+            const __amdgpu_buffer_rsrc_t d2 = make_rsrc(dst2 + (first + j) * static_cast<int64_t>(rb2), rb2);
+            for (int w = lane; w < nw2; w += kWave)
+                __builtin_amdgcn_raw_buffer_store_b32(0u, d2, w * 4, 0, kPolicyStreamStore);
+        }
     }
 }
 
@@ -364,10 +372,40 @@ constexpr int kGroupedThreads = 128;
 constexpr int kGroupedWaves = kGroupedThreads / kWave;
 constexpr int kGroupLoadPolicy = 0;
 
+// Companion rows (the FP8 scales of moe_permute_grouped_fp8): words [0, nw2) of row s of src2
+// go to row d of dst2 for every destination of the wave's share (mask m over the lanes holding
+// d and their source sr), one source at a time. Taken by the waves of a group's first slice.
+__device__ __forceinline__ void grouped_companion(const char *__restrict__ src2, char *__restrict__ dst2, int nw2,
+                                                  int32_t sr, int32_t d, uint64_t m)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t rb2 = static_cast<uint32_t>(nw2) * 4u;
+    while (m) {
+        const int32_t s = __builtin_amdgcn_readlane(sr, __builtin_ctzll(m));
+        const uint64_t p0 = __ballot(sr == s) & m;
+        m &= ~p0;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src2 + static_cast<int64_t>(s) * rb2, rb2);
+        for (int w = lane; w < nw2; w += kWave) {
+            const uint32_t v = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, w * 4, 0, 0));
+            uint64_t p = p0;
+            while (p) {
+                const int j = __builtin_ctzll(p);
+                p &= p - 1;
+                const __amdgpu_buffer_rsrc_t q =
+                    make_rsrc(dst2 + static_cast<int64_t>(__builtin_amdgcn_readlane(d, j)) * rb2, rb2);
+                __builtin_amdgcn_raw_buffer_store_b32(v, q, w * 4, 0, kPolicyStreamStore);
+            }
+        }
+    }
+}
+
+// COMP: the companion rows are moved too (moe_permute_grouped_fp8); the plain gather's instance
+// carries none of their code.
+template <bool COMP>
 __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
     const char *__restrict__ src, int64_t src_rows, int64_t nvec, const int32_t *__restrict__ src_row,
     const int32_t *__restrict__ dst_of, int64_t M, int J, int64_t N, const int32_t *__restrict__ src_of,
-    char *__restrict__ dst, int parts)
+    char *__restrict__ dst, int parts, const char *__restrict__ src2, char *__restrict__ dst2, int nw2)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row_bytes = nvec * 16;
@@ -376,7 +414,8 @@ __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
     const int64_t copy_waves = M * wpr;
     if (gw >= copy_waves) {
-        zero_rows_wave(src_rows, nvec, src_row, N, (gw - copy_waves) * kZeroRowsPerWave, dst);
+        zero_rows_wave(src_rows, nvec, src_row, N, (gw - copy_waves) * kZeroRowsPerWave, dst, kZeroRowsPerWave,
+                       dst2, COMP ? nw2 : 0);
         return;
     }
     const int64_t g = gw / wpr;
@@ -403,6 +442,13 @@ __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
         }
         m = keep;
     }
+    // the first slice's waves also move the companion rows: up to 64 words with the slice's own
+    // loads and stores (one word per lane), longer rows in a pass of their own first
+    const bool comp = COMP && nw2 > 0 && rem < parts;
+    const bool comp_inline = comp && nw2 <= kWave;
+    if (comp && !comp_inline)
+        grouped_companion(src2, dst2, nw2, sr, d, m);
+    const uint32_t rb2 = static_cast<uint32_t>(nw2) * 4u;
     while (m) {
         int32_t sb[kGroupLoads];
         uint64_t pb[kGroupLoads];
@@ -421,27 +467,38 @@ __global__ __launch_bounds__(kGroupedThreads) void permute_grouped_vec16_kernel(
         // stores below issue back to back: with a guarded load per source the compiler could not
         // count the loads and waited for all earlier stores before each source's stores
         u32x4 r[kGroupLoads];
+        uint32_t c2[kGroupLoads];
 #pragma unroll
         for (int u = 0; u < kGroupLoads; ++u) {
             const __amdgpu_buffer_rsrc_t s = make_rsrc(src + static_cast<int64_t>(sb[u] < 0 ? 0 : sb[u]) * row_bytes,
                                                        sb[u] < 0 ? 0u : static_cast<uint32_t>(row_bytes));
             r[u] = ld16_buf<kGroupLoadPolicy>(s, static_cast<uint32_t>(v * 16));
+            c2[u] = 0u;
+            if (comp_inline) {  // lanes past the row read zeros (the resource's bound)
+                const __amdgpu_buffer_rsrc_t s2 =
+                    make_rsrc(src2 + static_cast<int64_t>(sb[u] < 0 ? 0 : sb[u]) * rb2, sb[u] < 0 ? 0u : rb2);
+                c2[u] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(s2, lane * 4, 0, 0));
+            }
         }
         // the loaded values pass through an empty asm statement: it keeps every load ahead of the
         // first store (the compiler may not sink one into the store loop) and puts the one wait here
 #pragma unroll
         for (int u = 0; u < kGroupLoads; ++u)
-            asm volatile("" : : "v"(r[u].x), "v"(r[u].y), "v"(r[u].z), "v"(r[u].w));
+            asm volatile("" : : "v"(r[u].x), "v"(r[u].y), "v"(r[u].z), "v"(r[u].w), "v"(c2[u]));
 #pragma unroll
         for (int u = 0; u < kGroupLoads; ++u) {
             uint64_t p = pb[u];
             while (p) {
                 const int j = __builtin_ctzll(p);
                 p &= p - 1;
-                const __amdgpu_buffer_rsrc_t q = make_rsrc(
-                    dst + static_cast<int64_t>(__builtin_amdgcn_readlane(d, j)) * row_bytes, static_cast<uint32_t>(row_bytes));
+                const int32_t dj = __builtin_amdgcn_readlane(d, j);
+                const __amdgpu_buffer_rsrc_t q =
+                    make_rsrc(dst + static_cast<int64_t>(dj) * row_bytes, static_cast<uint32_t>(row_bytes));
                 if (v < nvec)
                     st16_buf<kPolicyStreamStore>(q, static_cast<uint32_t>(v * 16), r[u]);
+                if (comp_inline && lane < nw2)
+                    __builtin_amdgcn_raw_buffer_store_b32(c2[u], make_rsrc(dst2 + static_cast<int64_t>(dj) * rb2, rb2),
+                                                          lane * 4, 0, kPolicyStreamStore);
             }
         }
     }
@@ -591,11 +648,14 @@ extern "C" moe_status moe_permute(const void *src, int64_t src_rows, int64_t H, 
     return launch_status();
 }
 
-extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
-                                          const int32_t *src_row, int64_t N, const int32_t *dst_of, int64_t M,
-                                          int32_t J, const int32_t *src_of, void *dst, hipStream_t stream)
+namespace moe {
+namespace {
+// moe_permute_grouped, with companion rows (nw2 > 0: float32 rows of nw2 values, moved to the same
+// destinations from the same sources, zeroed with the same zero rows) for moe_permute_grouped_fp8.
+moe_status launch_grouped(const void *src, int64_t src_rows, int64_t H, moe_dtype dt, const int32_t *src_row,
+                          int64_t N, const int32_t *dst_of, int64_t M, int32_t J, const int32_t *src_of, void *dst,
+                          const float *src2, float *dst2, int64_t nw2, hipStream_t stream)
 {
-    using namespace moe;
     if (src_rows < 0 || H < 1 || N < 0 || M < 0 || J < 1 || (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3))
         return MOE_ERR_INVALID;
     if (J > kMaxGroupDests)
@@ -604,9 +664,11 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
         return MOE_OK;
     if (!src_row || !dst || (M > 0 && !dst_of) || (src_rows > 0 && !src))
         return MOE_ERR_INVALID;
+    if (nw2 > 0 && (!dst2 || (src_rows > 0 && !src2)))
+        return MOE_ERR_INVALID;
     const int64_t esz = dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1);
     const int64_t row_bytes = H * esz;
-    if (row_bytes > 0x7fffffffLL)
+    if (row_bytes > 0x7fffffffLL || nw2 * 4 > 0x7fffffffLL)
         return MOE_ERR_UNSUPPORTED;
     const int64_t zero_waves = ceil_div(N, kZeroRowsPerWave);
     if (row_bytes % 16 == 0 && aligned16(dst) && (src_rows == 0 || aligned16(src))) {
@@ -618,9 +680,16 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
         const int64_t blocks = ceil_div(M * ceil_div(nvec, kWave) * parts + zero_waves, kGroupedWaves);
         if (blocks > 0x7fffffff)
             return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(permute_grouped_vec16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kGroupedThreads), 0,
-                           stream, static_cast<const char *>(src), src_rows, nvec, src_row, dst_of, M, J, N,
-                           src_of, static_cast<char *>(dst), parts);
+        if (nw2 > 0)
+            hipLaunchKernelGGL(permute_grouped_vec16_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                               dim3(kGroupedThreads), 0, stream, static_cast<const char *>(src), src_rows, nvec,
+                               src_row, dst_of, M, J, N, src_of, static_cast<char *>(dst), parts,
+                               reinterpret_cast<const char *>(src2), reinterpret_cast<char *>(dst2),
+                               static_cast<int>(nw2));
+        else
+            hipLaunchKernelGGL(permute_grouped_vec16_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                               dim3(kGroupedThreads), 0, stream, static_cast<const char *>(src), src_rows, nvec,
+                               src_row, dst_of, M, J, N, src_of, static_cast<char *>(dst), parts, nullptr, nullptr, 0);
         return launch_status();
     }
     const int64_t blocks = M + ceil_div(zero_waves, kScatterWaves);
@@ -640,5 +709,31 @@ extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int
                            static_cast<const uint8_t *>(src), src_rows, H, src_row, dst_of, M, J, N,
                            static_cast<uint8_t *>(dst));
     }
-    return launch_status();
+    const moe_status st = launch_status();
+    if (st != MOE_OK || nw2 == 0)
+        return st;
+    // rows without 16-byte vectors: the companion rows by a second element-wise pass
+    return launch_grouped(src2, src_rows, nw2, MOE_F32, src_row, N, dst_of, M, J, src_of, dst2, nullptr, nullptr, 0,
+                          stream);
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_permute_grouped(const void *src, int64_t src_rows, int64_t H, moe_dtype dt,
+                                          const int32_t *src_row, int64_t N, const int32_t *dst_of, int64_t M,
+                                          int32_t J, const int32_t *src_of, void *dst, hipStream_t stream)
+{
+    return moe::launch_grouped(src, src_rows, H, dt, src_row, N, dst_of, M, J, src_of, dst, nullptr, nullptr, 0,
+                               stream);
+}
+
+extern "C" moe_status moe_permute_grouped_fp8(const uint8_t *src, const float *src_scales, int64_t src_rows,
+                                              int64_t H, int32_t block, const int32_t *src_row, int64_t N,
+                                              const int32_t *dst_of, int64_t M, int32_t J, const int32_t *src_of,
+                                              uint8_t *dst, float *dst_scales, hipStream_t stream)
+{
+    if (block < 1 || H < 1 || H % block != 0)
+        return MOE_ERR_INVALID;
+    return moe::launch_grouped(src, src_rows, H, MOE_FP8_E4M3, src_row, N, dst_of, M, J, src_of, dst, src_scales,
+                               dst_scales, H / block, stream);
 }

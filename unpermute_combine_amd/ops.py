@@ -375,6 +375,39 @@ def permute_scatter_fp8(src: torch.Tensor, dst_of: torch.Tensor, num_rows: int, 
     return q, sc
 
 
+def permute_grouped_fp8(codes: torch.Tensor, scales: torch.Tensor, src_row: torch.Tensor, dst_of: torch.Tensor,
+                        out=None, src_of: Optional[torch.Tensor] = None):
+    """The FP8 group receive: permute_grouped of the codes and of their scale rows in one launch,
+    bit for bit the two permute_grouped calls. Returns (codes [N, H] uint8, scales [N, H/block])."""
+    _need(codes, "codes", None, 2)
+    if codes.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"codes must be FP8 codes (uint8), got {codes.dtype}")
+    _need(scales, "scales", torch.float32, 2)
+    _need(src_row, "src_row", torch.int32, 1)
+    _need(dst_of, "dst_of", torch.int32, 2)
+    if scales.shape[0] != codes.shape[0]:
+        raise ValueError("scales must have one row per code row")
+    H, nb = codes.shape[1], scales.shape[1]
+    if nb < 1 or H % nb:
+        raise ValueError("the scale rows must split H into equal blocks")
+    if src_of is not None:
+        _need(src_of, "src_of", torch.int32, 2)
+        if tuple(src_of.shape) != tuple(dst_of.shape):
+            raise ValueError("src_of must have the shape of dst_of")
+    N = src_row.shape[0]
+    q, sc = (None, None) if out is None else out
+    q = torch.empty((N, H), dtype=codes.dtype, device=codes.device) if q is None else q
+    sc = torch.empty((N, nb), dtype=torch.float32, device=codes.device) if sc is None else sc
+    _need(q, "out codes", codes.dtype, 2)
+    _need(sc, "out scales", torch.float32, 2)
+    if tuple(q.shape) != (N, H) or tuple(sc.shape) != (N, nb):
+        raise ValueError(f"outputs must be [{N}, {H}] and [{N}, {nb}]")
+    check("moe_permute_grouped_fp8", lib().moe_permute_grouped_fp8(
+        _p(codes), _p(scales), codes.shape[0], H, H // nb, _p(src_row), N, _p(dst_of), dst_of.shape[0],
+        dst_of.shape[1], _p(src_of), _p(q), _p(sc), _stream()))
+    return q, sc
+
+
 def unpermute_combine(y: torch.Tensor, row_of: torch.Tensor, weights: Optional[torch.Tensor] = None,
                       out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                       bias: Optional[torch.Tensor] = None) -> torch.Tensor:
