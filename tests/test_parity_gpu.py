@@ -471,6 +471,22 @@ def test_permute_grouped_fp8_random_maps(m, H, block, J):
         assert np.array_equal(gq, tq) and np.array_equal(gs_.view(np.uint32), ts.view(np.uint32))
 
 
+@pytest.mark.parametrize("H,block", [(128, 16), (24, 8)])
+def test_permute_grouped_fp8_without_groups_writes_zero_rows(m, H, block):
+    """No groups at all: only the zero rows are written, codes and scales alike (the 16-byte and
+    the element-wise paths); other rows keep their contents."""
+    nb = H // block
+    q = np.random.default_rng(5).integers(0, 256, size=(4, H), dtype=np.uint8)
+    sc = np.random.default_rng(6).standard_normal((4, nb), dtype=np.float32)
+    src_row = np.asarray([-1, 2, 9, -2, -1], np.int32)
+    oq = dev(np.full((5, H), 0x77, np.uint8))
+    os_ = dev(np.full((5, nb), np.float32(3.5)))
+    m.permute_grouped_fp8(dev(q), dev(sc), dev(src_row), dev(np.zeros((0, 4), np.int32)), out=(oq, os_))
+    gq, gs_ = host(oq), host(os_)
+    assert (gq[[0, 2, 4]] == 0).all() and (gs_[[0, 2, 4]] == 0).all()
+    assert (gq[[1, 3]] == 0x77).all() and (gs_[[1, 3]] == np.float32(3.5)).all()
+
+
 def test_permute_grouped_without_groups_writes_zero_rows(m):
     x = wl.hidden_states(wl.case_key(32), 4, 16, "bf16")
     src_row = np.asarray([-1, 2, 9, -1], np.int32)
